@@ -1,0 +1,301 @@
+/*
+ * q4_oracle.c -- CPU oracle for the fused GPTQ 4-bit dequantize-and-multiply.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. The GPU library never links, loads or
+ * calls it, and this file shares no code with it.
+ *
+ * What it computes (plain definition, double accumulation):
+ *
+ *   y[m,n] = sum_k x[m,k] * W[k,n],   W[k,n] = s[g(k),n] * (q[k,n] - z[g(k),n])
+ *
+ * Sources:
+ *  - "GPTQ's 'Exllama Kernel Not Installed' Warning", section "Why the kernel
+ *    is missing": weights are 4-bit integers packed into 32-bit words with a
+ *    scale and a zero point per group.
+ *  - same page, section "What the fallback actually does": the fused kernel
+ *    unpacks and dequantizes inside the multiply-accumulate; the fallback
+ *    materializes the dequantized matrix and then runs an ordinary matmul;
+ *    both reach the same answer. Both routes are written out below.
+ *  - "Implementation: Predibase Lorax GPTQ Exllama V1", I/O contract table:
+ *    qweight int32, qzeros int32, scales fp16, optional g_idx int32, bits = 4,
+ *    groupsize = input features per group, output fp16.
+ *  - GPTQModel wiki "Inference Backends", hardware table (ExLlama v2 row):
+ *    FP16 scales, FP32 accumulation. Section "Numeric epilogues": bias is
+ *    added to the wide accumulator before the single final cast.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - Nibble order: code of input row k = 8r+i sits in bits 4i..4i+3 of
+ *    qweight word (r, n); zero of column n = 8c+j in bits 4j..4j+3 of qzeros
+ *    word (g, c). Words are read as their unsigned 32-bit pattern (nibble 7
+ *    sets the sign bit of the int32).
+ *  - No zero-point offset: the stored nibble is z itself.
+ *  - g(k) = g_idx[k] when g_idx is given, else k / G. groupsize <= 0 means a
+ *    single group (G = K). The number of groups is ceil(K / G).
+ *  - The dequantized value in fp32, s * (q - z), is exact (an 11-bit
+ *    significand times an integer of magnitude <= 15 needs <= 15 bits).
+ *    Its fp16 form dq16 is one round-to-nearest-even of that exact product.
+ *  - Accumulation is in double, in increasing k; the bias (if any) is added
+ *    in double after the sum.
+ *
+ * Error returns: 0 = OK, 1 = bad shape/argument, 2 = g_idx out of range.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------------
+ * binary16 conversions, written from the IEEE 754 binary16 definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent field 0
+ * holds zero and subnormals (f * 2^-24), field 31 holds inf and NaN.
+ * ------------------------------------------------------------------------- */
+
+double q4o_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* Round a non-negative double to the nearest integer, ties to even. */
+static double rne_int(double r)
+{
+    double fl = floor(r);
+    double d = r - fl;
+    if (d > 0.5) return fl + 1.0;
+    if (d < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* Round a double to the nearest binary16 value, ties to even.
+ * For a finite |v| with binade exponent E (2^E <= |v| < 2^(E+1)), the
+ * binary16 spacing is 2^(E-10) for E >= -14 and 2^-24 below. With E clamped
+ * to >= -14 and n = rne(|v| / 2^(E-10)), the encoding is (E+14)*1024 + n:
+ * this is continuous across binades (n = 2048 carries into the next exponent)
+ * and into the subnormals (E = -14 gives the raw subnormal fraction n).
+ * Any encoding >= 0x7C00 is an overflow to infinity. */
+uint16_t q4o_double_to_half_rne(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);          /* a = m * 2^e2, m in [0.5, 1) -> E = e2 - 1 */
+    int E = e2 - 1;
+    if (E < -14) E = -14;
+    if (E > 15) return (uint16_t)(sign | 0x7C00);
+    double n = rne_int(ldexp(a, 10 - E));   /* exact scaling by a power of 2 */
+    double enc = (double)(E + 14) * 1024.0 + n;
+    if (enc >= 31744.0) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)enc);
+}
+
+void q4o_half_to_double_array(int64_t n, const uint16_t* in, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = q4o_half_to_double(in[i]);
+}
+
+void q4o_double_to_half_array(int64_t n, const double* in, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = q4o_double_to_half_rne(in[i]);
+}
+
+/* ---------------------------------------------------------------------------
+ * Unpacking and group lookup.
+ * ------------------------------------------------------------------------- */
+
+static inline unsigned nibble(int32_t word, int i)
+{
+    return ((uint32_t)word >> (4 * i)) & 0xFu;
+}
+
+/* q[k][n]: 4-bit code of input row k, output column n. */
+static inline unsigned code_q(const int32_t* qweight, int64_t N, int64_t k, int64_t n)
+{
+    return nibble(qweight[(k / 8) * N + n], (int)(k % 8));
+}
+
+/* z[g][n]: 4-bit zero point of group g, column n. */
+static inline unsigned code_z(const int32_t* qzeros, int64_t N, int64_t g, int64_t n)
+{
+    return nibble(qzeros[g * (N / 8) + n / 8], (int)(n % 8));
+}
+
+static inline int64_t group_of(const int32_t* g_idx, int64_t G, int64_t k)
+{
+    return g_idx ? (int64_t)g_idx[k] : k / G;
+}
+
+static int check_args(int64_t M, int64_t K, int64_t N, int64_t* G, const int32_t* g_idx)
+{
+    if (M < 0 || K <= 0 || N <= 0 || K % 8 || N % 8) return 1;
+    if (*G <= 0) *G = K;
+    int64_t ng = (K + *G - 1) / *G;
+    if (g_idx)
+        for (int64_t k = 0; k < K; ++k)
+            if (g_idx[k] < 0 || g_idx[k] >= ng) return 2;
+    return 0;
+}
+
+int q4o_num_groups(int64_t K, int64_t G)
+{
+    if (G <= 0) G = K;
+    return (int)((K + G - 1) / G);
+}
+
+int q4o_unpack_qweight(const int32_t* qweight, int64_t K, int64_t N, uint8_t* q)
+{
+    if (K <= 0 || N <= 0 || K % 8) return 1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            q[k * N + n] = (uint8_t)code_q(qweight, N, k, n);
+    return 0;
+}
+
+int q4o_unpack_qzeros(const int32_t* qzeros, int64_t ng, int64_t N, uint8_t* z)
+{
+    if (ng <= 0 || N <= 0 || N % 8) return 1;
+    for (int64_t g = 0; g < ng; ++g)
+        for (int64_t n = 0; n < N; ++n)
+            z[g * N + n] = (uint8_t)code_z(qzeros, N, g, n);
+    return 0;
+}
+
+/* W[k][n] = s * (q - z) in fp32 (exact, see the header). */
+static inline float dequant_one(const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, const int32_t* g_idx,
+                                int64_t N, int64_t G, int64_t k, int64_t n)
+{
+    int64_t g = group_of(g_idx, G, k);
+    float s = (float)q4o_half_to_double(scales[g * N + n]);
+    float d = (float)((int)code_q(qweight, N, k, n) - (int)code_z(qzeros, N, g, n));
+    return s * d;
+}
+
+int q4o_dequant32(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                  const int32_t* g_idx, int64_t K, int64_t N, int64_t G, float* W)
+{
+    int rc = check_args(0, K, N, &G, g_idx);
+    if (rc) return rc;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            W[k * N + n] = dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
+    return 0;
+}
+
+/* dq16[k][n] = RNE_fp16(s * (q - z)), binary16 bit patterns. */
+int q4o_dequant16(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                  const int32_t* g_idx, int64_t K, int64_t N, int64_t G, uint16_t* dq)
+{
+    int rc = check_args(0, K, N, &G, g_idx);
+    if (rc) return rc;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            dq[k * N + n] = q4o_double_to_half_rne(
+                (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n));
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The two routes to y. Both sum in increasing k in double and add the bias
+ * last, so they are bit-identical by construction; the test suite checks it.
+ * ------------------------------------------------------------------------- */
+
+/* Fused route: dequantize each weight inside the k loop, never store W. */
+int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                     const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                     int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
+{
+    int rc = check_args(M, K, N, &G, g_idx);
+    if (rc) return rc;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
+                double p = q4o_half_to_double(x[m * K + k]) * w;
+                acc += p;
+                aabs += fabs(p);
+            }
+            if (bias) acc += q4o_half_to_double(bias[n]);
+            y[m * N + n] = acc;
+            if (A) A[m * N + n] = aabs;
+        }
+    return 0;
+}
+
+/* Fallback route: materialize the dequantized W[K][N], then a plain matmul. */
+int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                        int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+{
+    int rc = check_args(M, K, N, &G, g_idx);
+    if (rc) return rc;
+    float* W = (float*)malloc((size_t)K * (size_t)N * sizeof(float));
+    if (!W) return 1;
+    q4o_dequant32(qweight, qzeros, scales, g_idx, K, N, G, W);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += q4o_half_to_double(x[m * K + k]) * (double)W[k * N + n];
+            if (bias) acc += q4o_half_to_double(bias[n]);
+            y[m * N + n] = acc;
+        }
+    free(W);
+    return 0;
+}
+
+/* Fused route at selected output elements (m[i], n[i]), i < count. Used for
+ * full-size layers where the whole product would take the CPU too long. */
+int q4o_matmul_fused_at(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                        int64_t M, int64_t K, int64_t N, int64_t G,
+                        int64_t count, const int64_t* ms, const int64_t* ns,
+                        double* y, double* A)
+{
+    int rc = check_args(M, K, N, &G, g_idx);
+    if (rc) return rc;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        double acc = 0.0, aabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
+            double p = q4o_half_to_double(x[m * K + k]) * w;
+            acc += p;
+            aabs += fabs(p);
+        }
+        if (bias) acc += q4o_half_to_double(bias[n]);
+        y[i] = acc;
+        if (A) A[i] = aabs;
+    }
+    return 0;
+}
+
+int q4o_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

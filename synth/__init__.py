@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the GPTQ 4-bit linear layer.
+
+This module is shared by the tests, the benchmark and the smoke check. It
+serves both the CPU oracle and the HIP library, so it holds none of the
+method's arithmetic: no unpacking, no dequantization, no products. It only
+draws random tensors of the right dtype, shape and value distribution.
+
+Tensor formats (the GPTQ checkpoint layout, "GPTQ's 'Exllama Kernel Not
+Installed' Warning", section "Why the kernel is missing": 4-bit integers
+packed into 32-bit words, one scale and one zero point per group; the I/O
+contract table of "Implementation: Predibase Lorax GPTQ Exllama V1"):
+
+- ``qweight`` int32 ``[K/8, N]``: word (r, n) holds the 4-bit codes of rows
+  k = 8r .. 8r+7 of column n, code of k = 8r+i in bits 4i .. 4i+3.
+- ``qzeros``  int32 ``[ceil(K/G), N/8]``: word (g, c) holds the zero points of
+  columns n = 8c .. 8c+7 of group g, in the same nibble order.
+- ``scales``  fp16  ``[ceil(K/G), N]``.
+- ``g_idx``   int32 ``[K]`` or ``None`` (group of input row k).
+- ``x``       fp16  ``[M, K]``, ``bias`` fp16 ``[N]``.
+
+Uniform 4-bit codes are drawn as uniform 32-bit words: the eight nibbles of
+a uniformly random 32-bit word are independent and uniform on {0..15}, which
+is exactly "q ~ U{0..15}, then packed" without any packing code here.
+
+Draw order per layer (fixed so that a seed names one tensor set): qweight
+words, qzeros words, scales, x, bias (if asked), act-order permutation (if
+asked). Scales ~ U[0.005, 0.02] rounded to fp16, x ~ N(0, 1) rounded to
+fp16, bias ~ N(0, 0.1) rounded to fp16. Act-order: a seeded permutation pi
+of 0..K-1 and g_idx[k] = (position of k in pi) // G, so every group keeps
+exactly G members but they are scattered over K.
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Layer",
+    "layer_seed",
+    "make_layer",
+    "make_x",
+    "LLAMA7B_BLOCK",
+    "LLAMA70B_MLP",
+    "WORKLOADS",
+]
+
+
+@dataclasses.dataclass
+class Layer:
+    """One synthetic quantized linear layer plus an activation batch."""
+
+    K: int
+    N: int
+    G: int
+    qweight: np.ndarray           # int32 [K/8, N]
+    qzeros: np.ndarray            # int32 [ceil(K/G), N/8]
+    scales: np.ndarray            # float16 [ceil(K/G), N]
+    g_idx: Optional[np.ndarray]   # int32 [K] or None
+    x: np.ndarray                 # float16 [M, K]
+    bias: Optional[np.ndarray]    # float16 [N] or None
+    seed: int
+
+    @property
+    def M(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def n_groups(self) -> int:
+        return -(-self.K // self.G)
+
+    def metric_bytes(self) -> int:
+        """Bytes of packed weights + scales + packed zeros (the streamed state)."""
+        return int(self.qweight.nbytes + self.scales.nbytes + self.qzeros.nbytes)
+
+
+def layer_seed(*parts) -> int:
+    """Stable 32-bit seed from a tuple of names/numbers (crc32, not hash())."""
+    return zlib.crc32("/".join(str(p) for p in parts).encode()) & 0xFFFFFFFF
+
+
+def _words(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32).view(np.int32)
+
+
+def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = False,
+               bias: bool = False, scale_lo: float = 0.005, scale_hi: float = 0.02) -> Layer:
+    """Draw one layer with the value distributions described in the module doc."""
+    if K % 8 or N % 8:
+        raise ValueError("K and N must be multiples of 8")
+    if G <= 0:
+        G = K
+    ng = -(-K // G)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    qweight = _words(rng, (K // 8, N))
+    qzeros = _words(rng, (ng, N // 8))
+    scales = rng.uniform(scale_lo, scale_hi, size=(ng, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    b = rng.normal(0.0, 0.1, size=(N,)).astype(np.float16) if bias else None
+    g_idx = None
+    if act_order:
+        pi = rng.permutation(K)
+        pos = np.empty(K, dtype=np.int64)
+        pos[pi] = np.arange(K)
+        g_idx = (pos // G).astype(np.int32)
+    return Layer(K=K, N=N, G=G, qweight=qweight, qzeros=qzeros, scales=scales,
+                 g_idx=g_idx, x=x, bias=b, seed=seed)
+
+
+def make_x(M: int, K: int, seed: int) -> np.ndarray:
+    """A fresh fp16 activation batch x ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((M, K)).astype(np.float16)
+
+
+# Llama-7B-shaped decoder block: q, k, v, o (4096x4096), gate, up (4096x11008),
+# down (11008x4096); bias on the q projection only.
+LLAMA7B_BLOCK = [
+    ("q_proj", 4096, 4096, True),
+    ("k_proj", 4096, 4096, False),
+    ("v_proj", 4096, 4096, False),
+    ("o_proj", 4096, 4096, False),
+    ("gate_proj", 4096, 11008, False),
+    ("up_proj", 4096, 11008, False),
+    ("down_proj", 11008, 4096, False),
+]
+
+# Llama-70B-shaped MLP layers (gate/up share a shape).
+LLAMA70B_MLP = [
+    ("gate_proj", 8192, 28672),
+    ("down_proj", 28672, 8192),
+]
+
+# The five workloads, by name.
+WORKLOADS = {
+    "tiny": dict(K=512, N=512, G=128, M=[1]),
+    "llama7b_block_decode": dict(layers=LLAMA7B_BLOCK, G=128, M=[1]),
+    "llama7b_actorder": dict(shapes=[(4096, 11008), (11008, 4096)], G=128, M=[1, 4]),
+    "llama70b_mlp_decode": dict(layers=LLAMA70B_MLP, G=128, M=[1, 2, 4, 8, 16]),
+    "prefill": dict(shapes=[(4096, 11008), (11008, 4096)], G=[128, 32], M=[2048]),
+}

@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- a library routine, exact rational brute force, a closed form or an
+invariant the pages state -- so that a dropped term, a wrong sign or index, or
+a transposed operand in the oracle fails at least one of them.
+
+Passages:
+ - "GPTQ's 'Exllama Kernel Not Installed' Warning", "Why the kernel is
+   missing": codes packed into 32-bit words, a scale and a zero per group.
+ - same page, "What the fallback actually does": fused route and fallback
+   route reach the same answer.
+ - "Implementation: Predibase Lorax GPTQ Exllama V1", Description and I/O
+   contract: g_idx None or trivial means no act-order.
+ - GPTQModel wiki "Inference Backends", "Runtime cache lifetime": the
+   act-order reorder comes from one stable argsort of g_idx.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from tests.packing import pack_cols, pack_rows, pack_word_py
+
+# ---------------------------------------------------------------- binary16 ---
+
+def test_half_to_double_exhaustive(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.half_to_double(bits)
+    ref = bits.view(np.float16).astype(np.float64)        # library routine
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _finite_halves():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return np.sort(np.unique(v[np.isfinite(v)].astype(np.float64)))
+
+
+def test_double_to_half_exact_values(oracle_mod):
+    vals = _finite_halves()
+    got = oracle_mod.double_to_half(vals)
+    ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_double_to_half_midpoints_ties_to_even(oracle_mod):
+    vals = _finite_halves()
+    mids = (vals[:-1] + vals[1:]) / 2.0             # exact in float64
+    got = oracle_mod.double_to_half(mids)
+    ref = mids.astype(np.float16).view(np.uint16)  # numpy rounds ties to even
+    assert np.array_equal(got, ref)
+    # and a hand case: 1 + 2^-11 is the midpoint of 1 and 1 + 2^-10 -> 1 (even)
+    assert oracle_mod.double_to_half([1.0 + 2.0 ** -11])[0] == 0x3C00
+    assert oracle_mod.double_to_half([1.0 + 3 * 2.0 ** -11])[0] == 0x3C02
+
+
+def test_double_to_half_random_and_edges(oracle_mod):
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 6, 200000),
+        np.array([65504.0, 65519.999, 65520.0, 70000.0, -65520.0, 2.0 ** -24,
+                  2.0 ** -25, 2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 1e-30, -0.0, 0.0,
+                  np.inf, -np.inf]),
+    ])
+    got = oracle_mod.double_to_half(vals)
+    ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    nan = oracle_mod.double_to_half([np.nan])[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+
+
+# ---------------------------------------------------------------- unpack ---
+
+def test_hand_words():
+    import oracle
+    # nibble i of word (0, n) is the code of row k = i, lowest bits first
+    qw = np.array([[0x76543210, pack_word_py(range(8, 16))]], dtype=np.int64).astype(np.int32)
+    assert qw[0, 1] < 0                         # 0xFEDCBA98 sets the sign bit
+    q = oracle.unpack_qweight(qw, 8)
+    assert q[:, 0].tolist() == list(range(8))
+    assert q[:, 1].tolist() == list(range(8, 16))
+    # zeros are packed along N: word (g, c) holds columns 8c..8c+7
+    qz = np.array([[0x76543210, pack_word_py(range(8, 16))]], dtype=np.int32)
+    z = oracle.unpack_qzeros(qz, 16)
+    assert z[0].tolist() == list(range(16))
+
+
+def test_golden_nibble_fixture(oracle_mod):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nibble_order.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    for word_hex, codes in rows:
+        w = np.array([[np.uint32(int(word_hex, 16))]], dtype=np.uint32).view(np.int32)
+        q = oracle_mod.unpack_qweight(w, 8)[:, 0]
+        assert "".join("%x" % c for c in q) == codes, word_hex
+        z = oracle_mod.unpack_qzeros(w, 8)[0]
+        assert "".join("%x" % c for c in z) == codes, word_hex
+
+
+@pytest.mark.parametrize("K,N", [(8, 8), (64, 24), (512, 512)])
+def test_pack_unpack_round_trip(oracle_mod, K, N):
+    rng = np.random.default_rng(K * 1000 + N)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    assert np.array_equal(oracle_mod.unpack_qweight(pack_rows(q), K), q)
+    z = rng.integers(0, 16, size=(K // 8, N), dtype=np.uint8)
+    assert np.array_equal(oracle_mod.unpack_qzeros(pack_cols(z), N), z)
+
+
+# ---------------------------------------------------------------- dequant ---
+
+def _codes_layer(rng, K, N, G, scale_bits=None):
+    ng = -(-K // G)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(ng, N), dtype=np.uint8)
+    if scale_bits is None:
+        s = rng.uniform(0.005, 0.02, size=(ng, N)).astype(np.float16)
+    else:
+        s = scale_bits
+    return q, z, s
+
+
+def test_dequant_brute_force_fractions(oracle_mod):
+    rng = np.random.default_rng(7)
+    K, N, G = 64, 16, 32
+    q, z, s = _codes_layer(rng, K, N, G)
+    s[0, 0] = np.float16(-0.0107)   # negative scale
+    s[1, 3] = np.float16(6.0e-6)    # subnormal scale
+    W = oracle_mod.dequant32(pack_rows(q), pack_cols(z), s, None, K, N, G)
+    for k in range(K):
+        for n in range(N):
+            g = k // G
+            exact = Fraction(float(s[g, n])) * (int(q[k, n]) - int(z[g, n]))
+            assert Fraction(float(W[k, n])) == exact, (k, n)
+
+
+def test_dequant16_is_rne_of_exact_product(oracle_mod):
+    rng = np.random.default_rng(8)
+    K, N, G = 256, 64, 32
+    q, z, s = _codes_layer(rng, K, N, G)
+    dq = oracle_mod.dequant16(pack_rows(q), pack_cols(z), s, None, K, N, G)
+    d = q.astype(np.int32) - np.repeat(z.astype(np.int32), G, axis=0)
+    exact = np.repeat(s.astype(np.float32), G, axis=0) * d.astype(np.float32)  # exact in fp32
+    ref = exact.astype(np.float16).view(np.uint16)                              # library RNE
+    assert np.array_equal(dq, ref)
+
+
+def test_dequant_closed_forms(oracle_mod):
+    rng = np.random.default_rng(9)
+    K, N, G = 64, 32, 32
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    # q == z in every group -> W == 0 exactly
+    zq = np.zeros((K // G, N), dtype=np.uint8)
+    qeq = np.repeat(rng.integers(0, 16, size=(K // G, N), dtype=np.uint8), G, axis=0)
+    zq[:] = qeq[::G]
+    s = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    W = oracle_mod.dequant32(pack_rows(qeq), pack_cols(zq), s, None, K, N, G)
+    assert np.all(W == 0)
+    # s == 1, z == 0 -> W == q
+    one = np.ones((K // G, N), dtype=np.float16)
+    W = oracle_mod.dequant32(pack_rows(q), pack_cols(np.zeros((K // G, N), np.uint8)), one,
+                             None, K, N, G)
+    assert np.array_equal(W, q.astype(np.float32))
+    # s == 2^-j, z == 8 -> W == (q - 8) * 2^-j, exact in fp16 as well
+    for j in (0, 3, 10):
+        sj = np.full((K // G, N), 2.0 ** -j, dtype=np.float16)
+        z8 = np.full((K // G, N), 8, dtype=np.uint8)
+        dq = oracle_mod.dequant16(pack_rows(q), pack_cols(z8), sj, None, K, N, G)
+        ref = ((q.astype(np.float64) - 8) * 2.0 ** -j).astype(np.float16).view(np.uint16)
+        assert np.array_equal(dq, ref)
+
+
+def test_group_indexing_uses_k_over_g(oracle_mod):
+    """Scale of group g multiplies rows g*G .. g*G+G-1 only (wrong index or a
+    transposed scale table fails this)."""
+    K, N, G = 96, 8, 32
+    q = np.full((K, N), 9, dtype=np.uint8)
+    z = np.full((3, N), 8, dtype=np.uint8)
+    s = np.array([[1.0] * N, [2.0] * N, [4.0] * N], dtype=np.float16)
+    s[2, 5] = 0.5
+    W = oracle_mod.dequant32(pack_rows(q), pack_cols(z), s, None, K, N, G)
+    assert np.all(W[:32] == 1) and np.all(W[32:64] == 2)
+    assert np.all(W[64:, 5] == 0.5) and np.all(W[64:, :5] == 4)
+    # ragged last group: K = 96, G = 64 -> 2 groups, the second has 32 rows
+    s2 = np.array([[1.0] * N, [3.0] * N], dtype=np.float16)
+    W = oracle_mod.dequant32(pack_rows(q), pack_cols(z[:2]), s2, None, K, N, 64)
+    assert np.all(W[:64] == 1) and np.all(W[64:] == 3)
+
+
+# ---------------------------------------------------------------- matmul ---
+
+def _exact_product(x16, q, z, s, G, g_idx=None, bias=None):
+    """Exact rational y = x @ W (+ bias) with Python integers.
+    x (fp16) is a multiple of 2^-24; W = s*(q-z) is a multiple of 2^-24 too
+    (any fp16 scale is), so every product is an integer times 2^-48."""
+    M, K = x16.shape
+    N = q.shape[1]
+    X = [[int(Fraction(float(v)) * (1 << 24)) for v in row] for row in x16]
+    Wi = [[0] * N for _ in range(K)]
+    for k in range(K):
+        g = int(g_idx[k]) if g_idx is not None else k // G
+        for n in range(N):
+            Wi[k][n] = int(Fraction(float(s[g, n])) * (1 << 24)) * (int(q[k, n]) - int(z[g, n]))
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = 0
+            for k in range(K):
+                acc += X[m][k] * Wi[k][n]
+            r = Fraction(acc, 1 << 48)
+            if bias is not None:
+                r += Fraction(float(bias[n]))
+            row.append(r)
+        out.append(row)
+    return out
+
+
+def test_matmul_exact_brute_force_small(oracle_mod):
+    rng = np.random.default_rng(11)
+    M, K, N, G = 3, 96, 16, 32
+    q, z, s = _codes_layer(rng, K, N, G)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    b = rng.normal(0, 0.1, size=N).astype(np.float16)
+    y, A = oracle_mod.matmul(x, pack_rows(q), pack_cols(z), s, None, K, N, G, bias=b)
+    ex = _exact_product(x, q, z, s, G, bias=b)
+    for m in range(M):
+        for n in range(N):
+            # s >= 2^-8 makes W a multiple of 2^-18 and x is a multiple of
+            # 2^-24, so every partial sum is a multiple of 2^-42 below 2^8:
+            # exact in double
+            assert Fraction(y[m, n]) == ex[m][n], (m, n)
+
+
+def test_matmul_exact_brute_force_tiny_workload(oracle_mod):
+    """The 512x512 G=128 layer: with |x| < 8 and |W| <= 0.3 every partial sum
+    is a multiple of 2^-42 below 2^11, so the double sum is exact."""
+    L = synth.make_layer(512, 512, 128, 1, seed=synth.layer_seed("tiny", 0))
+    import oracle
+    q = oracle.unpack_qweight(L.qweight, 512)
+    z = oracle.unpack_qzeros(L.qzeros, 512)
+    # cross-check the unpack against the independent packer first
+    assert np.array_equal(pack_rows(q), L.qweight)
+    assert np.array_equal(pack_cols(z), L.qzeros)
+    assert np.max(np.abs(L.x.astype(np.float64))) < 8
+    y, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 512, 512, 128)
+    X = (L.x.astype(np.float64) * 2.0 ** 24).astype(np.int64)          # exact
+    S = (np.repeat(L.scales, 128, axis=0).astype(np.float64) * 2.0 ** 18).astype(np.int64)
+    assert np.array_equal(S.astype(np.float64) * 2.0 ** -18,
+                          np.repeat(L.scales, 128, axis=0).astype(np.float64))  # s >= 2^-8
+    Wi = S * (q.astype(np.int64) - np.repeat(z.astype(np.int64), 128, axis=0))
+    # integer matmul in Python ints column by column (no overflow possible)
+    ref = [sum(int(a) * int(b) for a, b in zip(X[0], Wi[:, n])) for n in range(512)]
+    got = [Fraction(v) * (1 << 42) for v in y[0]]
+    assert got == [Fraction(r) for r in ref]
+
+
+def test_matmul_special_case_numpy(oracle_mod):
+    """s = 1, z = 0: W is the integer code matrix and y = x @ q exactly, which
+    numpy's float64 matmul also gives exactly for these magnitudes."""
+    rng = np.random.default_rng(12)
+    M, K, N, G = 4, 256, 40, 64
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = np.zeros((K // G, N), dtype=np.uint8)
+    s = np.ones((K // G, N), dtype=np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y, A = oracle_mod.matmul(x, pack_rows(q), pack_cols(z), s, None, K, N, G)
+    ref = x.astype(np.float64) @ q.astype(np.float64)
+    assert np.array_equal(y, ref)
+    assert np.array_equal(A, np.abs(x.astype(np.float64)) @ q.astype(np.float64))
+
+
+def test_fused_equals_fallback_bitwise(oracle_mod):
+    L = synth.make_layer(1024, 264, 128, 5, seed=3, act_order=True, bias=True)
+    a, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G,
+                             bias=L.bias, route="fused")
+    b, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G,
+                             bias=L.bias, route="fallback")
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_matmul_at_matches_full(oracle_mod):
+    L = synth.make_layer(512, 136, 32, 6, seed=4, bias=True)
+    y, A = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, L.K, L.N, L.G,
+                             bias=L.bias)
+    rng = np.random.default_rng(0)
+    ms = rng.integers(0, 6, 50)
+    ns = rng.integers(0, 136, 50)
+    ys, As = oracle_mod.matmul_at(L.x, L.qweight, L.qzeros, L.scales, None, L.K, L.N, L.G,
+                                  ms, ns, bias=L.bias)
+    assert np.array_equal(ys, y[ms, ns]) and np.array_equal(As, A[ms, ns])
+
+
+def test_trivial_g_idx_equals_none(oracle_mod):
+    L = synth.make_layer(512, 64, 128, 2, seed=5)
+    g = (np.arange(512) // 128).astype(np.int32)
+    a, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 512, 64, 128)
+    b, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, g, 512, 64, 128)
+    assert np.array_equal(a, b)
+
+
+def _physically_permuted(oracle_mod, L):
+    perm = np.argsort(L.g_idx, kind="stable")            # library stable argsort
+    assert np.array_equal(L.g_idx[perm], np.arange(L.K) // L.G)
+    q = oracle_mod.unpack_qweight(L.qweight, L.K)
+    return perm, pack_rows(q[perm]), L.x[:, perm]
+
+
+def test_act_order_equals_physical_permutation_exact(oracle_mod):
+    """Non-trivial g_idx == trivial g_idx on K-permuted weights and activations.
+    Small K: both double sums are exact, so the results are bit-identical."""
+    L = synth.make_layer(256, 48, 32, 3, seed=6, act_order=True)
+    perm, qw_p, x_p = _physically_permuted(oracle_mod, L)
+    a, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G)
+    b, _ = oracle_mod.matmul(x_p, qw_p, L.qzeros, L.scales, None, L.K, L.N, L.G)
+    assert np.array_equal(a, b)
+
+
+def test_act_order_equals_physical_permutation_large(oracle_mod):
+    """Same invariant at K = 4096: two summation orders, |diff| <= 2 K 2^-53 A."""
+    L = synth.make_layer(4096, 64, 128, 2, seed=7, act_order=True)
+    perm, qw_p, x_p = _physically_permuted(oracle_mod, L)
+    a, A = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G)
+    b, _ = oracle_mod.matmul(x_p, qw_p, L.qzeros, L.scales, None, L.K, L.N, L.G)
+    assert np.all(np.abs(a - b) <= 2 * L.K * 2.0 ** -53 * A)
+    assert not np.array_equal(L.g_idx, np.arange(L.K) // L.G)
+
+
+def test_act_order_wrong_permutation_is_detected(oracle_mod):
+    """The invariant has teeth: permuting x with a different permutation moves
+    the result far outside the bound."""
+    L = synth.make_layer(256, 16, 32, 1, seed=8, act_order=True)
+    perm, qw_p, x_p = _physically_permuted(oracle_mod, L)
+    a, A = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G)
+    b, _ = oracle_mod.matmul(L.x[:, np.argsort(perm)], qw_p, L.qzeros, L.scales, None,
+                             L.K, L.N, L.G)
+    assert not np.all(np.abs(a - b) <= 1e-3 * A)
+
+
+def test_group_replication_invariant(oracle_mod):
+    """G=128 with each group's (s, z) copied into four G=32 groups gives the
+    identical W, hence the identical y."""
+    L = synth.make_layer(512, 64, 128, 2, seed=9)
+    z = oracle_mod.unpack_qzeros(L.qzeros, 64)
+    z4 = np.repeat(z, 4, axis=0)
+    s4 = np.repeat(L.scales, 4, axis=0)
+    a, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 512, 64, 128)
+    b, _ = oracle_mod.matmul(L.x, L.qweight, pack_cols(z4), s4, None, 512, 64, 32)
+    assert np.array_equal(a, b)
+
+
+def test_bias_adds_exactly(oracle_mod):
+    L = synth.make_layer(512, 64, 128, 2, seed=10, bias=True)
+    a, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 512, 64, 128)
+    b, _ = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 512, 64, 128,
+                             bias=L.bias)
+    # all partial sums are exact here (see the tiny-workload pin), so the
+    # difference is the bias itself, exactly
+    assert np.array_equal(b - a, np.broadcast_to(L.bias.astype(np.float64), a.shape))
+
+
+def test_degenerate_and_error_cases(oracle_mod):
+    L = synth.make_layer(64, 16, 32, 0, seed=11)
+    y, A = oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, None, 64, 16, 32)
+    assert y.shape == (0, 16)
+    # groupsize <= 0: one group over all of K
+    L1 = synth.make_layer(64, 16, -1, 2, seed=12)
+    assert L1.scales.shape == (1, 16)
+    y1, _ = oracle_mod.matmul(L1.x, L1.qweight, L1.qzeros, L1.scales, None, 64, 16, -1)
+    y2, _ = oracle_mod.matmul(L1.x, L1.qweight, L1.qzeros, L1.scales, None, 64, 16, 64)
+    assert np.array_equal(y1, y2)
+    with pytest.raises(oracle_mod.OracleError):
+        bad = np.full(64, 2, dtype=np.int32)   # only groups 0, 1 exist
+        oracle_mod.matmul(L.x, L.qweight, L.qzeros, L.scales, bad, 64, 16, 32)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.dequant32(L.qweight, L.qzeros, L.scales, None, 60, 16, 32)
+
+
+def test_tolerance_scale_is_sum_abs(oracle_mod):
+    """A = sum_k |x W|: with all-positive x and W it equals y itself."""
+    K, N, G = 64, 8, 32
+    q = np.full((K, N), 12, dtype=np.uint8)
+    z = np.full((2, N), 4, dtype=np.uint8)
+    s = np.full((2, N), 0.25, dtype=np.float16)
+    x = np.full((1, K), 0.5, dtype=np.float16)
+    y, A = oracle_mod.matmul(x, pack_rows(q), pack_cols(z), s, None, K, N, G)
+    assert np.all(y == K * 0.5 * 2.0) and np.array_equal(A, y)
+    y2, A2 = oracle_mod.matmul(-x, pack_rows(q), pack_cols(z), s, None, K, N, G)
+    assert np.array_equal(y2, -y) and np.array_equal(A2, A)
