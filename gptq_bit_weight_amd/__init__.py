@@ -1,0 +1,254 @@
+"""Python binding of libq4: the fused GPTQ 4-bit dequantize-and-multiply on
+AMD Instinct MI355X (gfx950).
+
+The binding only marshals arguments: it checks dtype, device, shape and
+contiguity of torch tensors, passes their device pointers and the current
+HIP stream to the C ABI (``include/q4.h``) and turns status codes into
+exceptions. Every step of the computation runs in the library's HIP kernels;
+there is no Python or CPU fallback -- if ``libq4.so`` is missing or fails to
+load, importing the library raises.
+
+    import gptq_bit_weight_amd as q4
+    W = q4.Q4Matrix(qweight, qzeros, scales, g_idx, groupsize=128)   # q4_make
+    y = W.matmul(x)                                                   # q4_matmul
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "Q4Matrix", "Q4Error", "load_library", "library_path", "check_shape", "plan_actorder",
+    "plan_splits", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libq4.so")
+
+PATH_NONE, PATH_GEMV, PATH_MFMA = 0, 1, 2
+GEMV_MAX_M = 16
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
+
+# Every function include/q4.h declares.
+EXPORTED_SYMBOLS = (
+    "q4_make", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
+    "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
+    "q4_plan_actorder", "q4_plan_splits",
+)
+
+_lib = None
+
+
+class Q4Error(RuntimeError):
+    """A libq4 call failed with Q4_ERR_HIP or Q4_ERR_OOM."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libq4.so (once). Raises ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run: python -m gptq_bit_weight_amd.build")
+    try:
+        lib = ctypes.CDLL(_LIB_PATH)
+    except OSError as e:
+        raise ImportError(f"cannot load {_LIB_PATH}: {e}") from e
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.q4_make.argtypes = [P, P, P, P, I, I, I]
+    lib.q4_make.restype = P
+    lib.q4_matmul.argtypes = [P, P, P, I, P]
+    lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
+    lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, P]
+    for f in (lib.q4_matmul, lib.q4_matmul_bias, lib.q4_matmul_ex):
+        f.restype = I
+    lib.q4_free.argtypes = [P]
+    lib.q4_free.restype = None
+    lib.q4_last_status.argtypes = []
+    lib.q4_last_status.restype = I
+    lib.q4_last_error.argtypes = []
+    lib.q4_last_error.restype = ctypes.c_char_p
+    lib.q4_path_for.argtypes = [P, I]
+    lib.q4_path_for.restype = I
+    lib.q4_dequant_dump.argtypes = [P, I, P, P]
+    lib.q4_dequant_dump.restype = I
+    lib.q4_handle_info.argtypes = [P, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I),
+                                   ctypes.POINTER(I)]
+    lib.q4_handle_info.restype = I
+    lib.q4_check_shape.argtypes = [I, I, I]
+    lib.q4_check_shape.restype = I
+    lib.q4_plan_actorder.argtypes = [P, I, I, P, ctypes.POINTER(I)]
+    lib.q4_plan_actorder.restype = I
+    lib.q4_plan_splits.argtypes = [I, I, I, I]
+    lib.q4_plan_splits.restype = I
+    _lib = lib
+    return lib
+
+
+def _raise(status: int, what: str):
+    msg = (load_library().q4_last_error() or b"").decode(errors="replace")
+    text = f"{what}: {msg}" if msg else what
+    if status == ERR_INVALID_ARG:
+        raise ValueError(text)
+    if status in (ERR_UNSUPPORTED, ERR_DEVICE):
+        raise NotImplementedError(text)
+    raise Q4Error(text)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        _raise(status, what)
+
+
+# ---------------------------------------------------------------- host only ---
+
+def check_shape(K: int, N: int, groupsize: int) -> None:
+    """Raise if (K, N, groupsize) is not accepted by q4_make."""
+    _check(load_library().q4_check_shape(K, N, groupsize), "q4_check_shape")
+
+
+def plan_actorder(g_idx, K: int, groupsize: int):
+    """Host act-order plan: returns (perm, trivial) for an int32 g_idx (numpy)."""
+    import numpy as np
+    g = np.ascontiguousarray(g_idx, dtype=np.int32)
+    if g.shape != (K,):
+        raise ValueError("g_idx must have shape [K]")
+    perm = np.empty(K, dtype=np.int32)
+    triv = ctypes.c_int(0)
+    _check(load_library().q4_plan_actorder(g.ctypes.data, K, groupsize, perm.ctypes.data,
+                                           ctypes.byref(triv)), "q4_plan_actorder")
+    return perm, bool(triv.value)
+
+
+def plan_splits(M: int, K: int, N: int, groupsize: int) -> int:
+    return int(load_library().q4_plan_splits(M, K, N, groupsize))
+
+
+# ---------------------------------------------------------------- device ---
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(t, dtype, name: str, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class Q4Matrix:
+    """A 4-bit GPTQ weight matrix prepared for the MI355X kernels (q4_make).
+
+    qweight int32 [K/8, N], qzeros int32 [K/G, N/8], scales fp16 [K/G, N],
+    g_idx int32 [K] or None; all on the current GPU, contiguous. The handle
+    keeps its own copy in a private layout; later edits of the tensors do
+    not reach it.
+    """
+
+    def __init__(self, qweight, qzeros, scales, g_idx=None, groupsize: int = 128):
+        torch = _torch()
+        lib = load_library()
+        _dev_tensor(qweight, torch.int32, "qweight")
+        if qweight.dim() != 2:
+            raise ValueError("qweight must be 2-D [K/8, N]")
+        K, N = int(qweight.shape[0]) * 8, int(qweight.shape[1])
+        G = K if groupsize == -1 else groupsize
+        ng = -(-K // G) if G > 0 else 0
+        _dev_tensor(qzeros, torch.int32, "qzeros", (ng, N // 8))
+        _dev_tensor(scales, torch.float16, "scales", (ng, N))
+        if g_idx is not None:
+            _dev_tensor(g_idx, torch.int32, "g_idx", (K,))
+        dev = qweight.device
+        for t, nm in ((qzeros, "qzeros"), (scales, "scales"), (g_idx, "g_idx")):
+            if t is not None and t.device != dev:
+                raise ValueError(f"{nm} is on {t.device}, qweight on {dev}")
+        with torch.cuda.device(dev):
+            h = lib.q4_make(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                            g_idx.data_ptr() if g_idx is not None else None, K, N, groupsize)
+        if not h:
+            _raise(lib.q4_last_status(), "q4_make")
+        self._h = ctypes.c_void_p(h)
+        self.K, self.N, self.device = K, N, dev
+        gs, act = ctypes.c_int(0), ctypes.c_int(0)
+        lib.q4_handle_info(self._h, None, None, ctypes.byref(gs), ctypes.byref(act))
+        self.groupsize = int(gs.value)
+        self.act_order = bool(act.value)
+
+    def _handle(self):
+        if self._h is None:
+            raise ValueError("Q4Matrix is closed")
+        return self._h
+
+    def path_for(self, M: int) -> int:
+        return int(load_library().q4_path_for(self._handle(), M))
+
+    def matmul(self, x, bias=None, out=None, *, path: int = 0, splits: int = 0, stream=None):
+        """out[M, N] = fp16(x[M, K] @ W (+ bias)); fp32 accumulation."""
+        torch = _torch()
+        h = self._handle()
+        _dev_tensor(x, torch.float16, "x")
+        if x.dim() != 2 or x.shape[1] != self.K:
+            raise ValueError(f"x must be [M, {self.K}], got {tuple(x.shape)}")
+        M = int(x.shape[0])
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        else:
+            _dev_tensor(out, torch.float16, "out", (M, self.N))
+        if bias is not None:
+            _dev_tensor(bias, torch.float16, "bias", (self.N,))
+        for t, nm in ((x, "x"), (out, "out"), (bias, "bias")):
+            if t is not None and t.device != self.device:
+                raise ValueError(f"{nm} is on {t.device}, the matrix on {self.device}")
+        with torch.cuda.device(self.device):
+            st = load_library().q4_matmul_ex(h, x.data_ptr(), bias.data_ptr() if bias is not None
+                                             else None, out.data_ptr(), M, path, splits,
+                                             _stream_ptr(stream))
+        _check(st, "q4_matmul")
+        return out
+
+    __call__ = matmul
+
+    def dequant_dump(self, path: int = PATH_GEMV, stream=None):
+        """fp16 [K, N]: the dequantized values the kernel of `path` computes."""
+        torch = _torch()
+        w = torch.empty((self.K, self.N), dtype=torch.float16, device=self.device)
+        with torch.cuda.device(self.device):
+            st = load_library().q4_dequant_dump(self._handle(), path, w.data_ptr(),
+                                                _stream_ptr(stream))
+        _check(st, "q4_dequant_dump")
+        return w
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            torch = _torch()
+            torch.cuda.synchronize(self.device)
+            load_library().q4_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,266 @@
+// C ABI of libq4: handle construction, dispatch and debug entry points.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+#include <vector>
+
+#include "q4_internal.h"
+
+namespace q4 {
+
+hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                       int M, int splits, hipStream_t stream);
+hipError_t launch_gemm(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                       int M, hipStream_t stream);
+hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
+                         hipStream_t stream);
+hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
+                            hipStream_t stream);
+hipError_t launch_dump(const q4_matrix* h, uint16_t* w, hipStream_t stream);
+
+namespace {
+
+q4_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(e == hipErrorOutOfMemory ? Q4_ERR_OOM : Q4_ERR_HIP, "%s: %s", what,
+                hipGetErrorString(e));
+}
+
+#define Q4_HIP(call, what)                                  \
+    do {                                                    \
+        hipError_t e_ = (call);                             \
+        if (e_ != hipSuccess) return hip_fail(e_, (what));  \
+    } while (0)
+
+void destroy(q4_matrix* h)
+{
+    if (!h) return;
+    (void)hipFree(h->qweight);
+    (void)hipFree(h->scales);
+    (void)hipFree(h->qzeros);
+    (void)hipFree(h->perm);
+    (void)hipFree(h->inv_perm);
+    (void)hipFree(h->partials);
+    (void)hipFree(h->counters);
+    (void)hipFree(h->xperm);
+    delete h;
+}
+
+q4_status check_device(int* dev)
+{
+    Q4_HIP(hipGetDevice(dev), "hipGetDevice");
+    hipDeviceProp_t prop;
+    Q4_HIP(hipGetDeviceProperties(&prop, *dev), "hipGetDeviceProperties");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(Q4_ERR_DEVICE, "device %d is %s; libq4 is built for gfx950 (MI355X) only", *dev,
+                    prop.gcnArchName);
+    return Q4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                    const int32_t* g_idx, int K, int N, int groupsize, q4_matrix** out)
+{
+    if (!qweight || !qzeros || !scales)
+        return fail(Q4_ERR_INVALID_ARG, "q4_make: qweight, qzeros and scales must be non-null");
+    int G = 0;
+    q4_status st = check_shape(K, N, groupsize, &G);
+    if (st != Q4_OK) return st;
+    if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4))
+        return fail(Q4_ERR_INVALID_ARG, "q4_make: qweight must be 16-byte aligned, scales 8-byte");
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != Q4_OK) return st;
+    // The inputs may still be being written by work on other streams.
+    Q4_HIP(hipDeviceSynchronize(), "q4_make: synchronize");
+
+    const int ng = K / G;
+    std::vector<int32_t> perm;
+    int act = 0;
+    if (g_idx) {
+        std::vector<int32_t> gh(K);
+        Q4_HIP(hipMemcpy(gh.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost),
+               "q4_make: copy g_idx");
+        perm.resize(K);
+        int trivial = 0;
+        st = plan_actorder(gh.data(), K, G, perm.data(), &trivial);
+        if (st != Q4_OK) return st;
+        act = trivial ? 0 : 1;
+    }
+
+    q4_matrix* h = new q4_matrix();
+    h->K = K;
+    h->N = N;
+    h->G = G;
+    h->ng = ng;
+    h->act_order = act;
+    h->device = dev;
+    auto bail = [&](q4_status s) {
+        destroy(h);
+        return s;
+    };
+    hipError_t e;
+    const size_t words = (size_t)(K / 8) * N;
+    if ((e = hipMalloc(&h->qweight, words * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qweight"));
+    if ((e = hipMalloc(&h->scales, (size_t)ng * N * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
+    if ((e = hipMalloc(&h->qzeros, (size_t)ng * (N / 8) * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
+    if ((e = hipMalloc(&h->partials, (size_t)kMaxSplits * 16 * N * 4)) != hipSuccess)
+        return bail(hip_fail(e, "q4_make: workspace"));
+    const int col_tiles = (N + kColTile - 1) / kColTile;
+    if ((e = hipMalloc(&h->counters, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
+    if ((e = hipMemset(h->counters, 0, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
+    if (act) {
+        std::vector<int32_t> inv(K);
+        for (int k = 0; k < K; ++k) inv[perm[k]] = k;
+        if ((e = hipMalloc(&h->perm, (size_t)K * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
+        if ((e = hipMalloc(&h->inv_perm, (size_t)K * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
+        if ((e = hipMemcpy(h->perm, perm.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: perm"));
+        if ((e = hipMemcpy(h->inv_perm, inv.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: perm"));
+    }
+    if ((e = hipMemcpy(h->scales, scales, (size_t)ng * N * 2, hipMemcpyDeviceToDevice)) != hipSuccess)
+        return bail(hip_fail(e, "q4_make: scales"));
+    if ((e = hipMemcpy(h->qzeros, qzeros, (size_t)ng * (N / 8) * 4, hipMemcpyDeviceToDevice)) != hipSuccess)
+        return bail(hip_fail(e, "q4_make: qzeros"));
+    if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight), h->perm, h->qweight, K, N, 0)) != hipSuccess)
+        return bail(hip_fail(e, "q4_make: repack launch"));
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return bail(hip_fail(e, "q4_make: repack"));
+    *out = h;
+    return Q4_OK;
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    return v && *v ? atoi(v) : dflt;
+}
+
+int choose_path(const q4_matrix* h, int M, int forced)
+{
+    (void)h;
+    if (M == 0) return Q4_PATH_NONE;
+    if (forced == Q4_PATH_MFMA) return Q4_PATH_MFMA;
+    if (forced == Q4_PATH_GEMV) return M <= Q4_GEMV_MAX_M ? Q4_PATH_GEMV : -1;
+    return M <= Q4_GEMV_MAX_M ? Q4_PATH_GEMV : Q4_PATH_MFMA;
+}
+
+// Grow the act-order activation workspace to hold M x K halfs.
+q4_status ensure_xperm(const q4_matrix* h, int M)
+{
+    const size_t need = (size_t)M * h->K;
+    std::lock_guard<std::mutex> lock(h->ws_mutex);
+    if (h->xperm_elems >= need) return Q4_OK;
+    // Earlier calls may still read the old buffer: wait for them first.
+    Q4_HIP(hipDeviceSynchronize(), "q4_matmul: workspace grow");
+    (void)hipFree(h->xperm);
+    h->xperm = nullptr;
+    h->xperm_elems = 0;
+    Q4_HIP(hipMalloc(&h->xperm, need * 2), "q4_matmul: act-order workspace");
+    h->xperm_elems = need;
+    return Q4_OK;
+}
+
+q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                      int M, int path, int splits, hipStream_t stream)
+{
+    if (!h) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: null handle");
+    if (M < 0) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: M=%d is negative", M);
+    if (M == 0) return Q4_OK;
+    if (!x || !out) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: x and out must be non-null");
+    if (!aligned(x, 16)) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: x must be 16-byte aligned");
+    if ((long long)M * h->K > INT_MAX || (long long)M * h->N > INT_MAX)
+        return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: M=%d too large for this layer", M);
+    {
+        const char* xb = reinterpret_cast<const char*>(x);
+        const char* ob = reinterpret_cast<const char*>(out);
+        const size_t xs = (size_t)M * h->K * 2, os = (size_t)M * h->N * 2;
+        if (xb < ob + os && ob < xb + xs) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: out overlaps x");
+    }
+    const int kind = choose_path(h, M, path);
+    if (kind < 0)
+        return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the skinny kernel takes M <= %d (M=%d)",
+                    Q4_GEMV_MAX_M, M);
+    if (splits < 0 || splits > kMaxSplits)
+        return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
+
+    const uint16_t* xe = x;
+    if (h->act_order) {
+        q4_status st = ensure_xperm(h, M);
+        if (st != Q4_OK) return st;
+        Q4_HIP(launch_permute_x(x, h->perm, h->xperm, M, h->K, stream), "q4_matmul: permute launch");
+        xe = h->xperm;
+    }
+    if (kind == Q4_PATH_GEMV) {
+        int s = splits ? splits : env_int("Q4_SPLITS", 0);
+        if (s <= 0 || s > kMaxSplits) s = plan_splits(M, h->K, h->N, h->G);
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, s, stream), "q4_matmul: gemv launch");
+    } else {
+        Q4_HIP(launch_gemm(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+    }
+    return Q4_OK;
+}
+
+}  // namespace
+}  // namespace q4
+
+extern "C" {
+
+q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                   const int32_t* g_idx, int K, int N, int groupsize)
+{
+    q4_matrix* h = nullptr;
+    return q4::make_impl(qweight, qzeros, scales, g_idx, K, N, groupsize, &h) == Q4_OK ? h : nullptr;
+}
+
+q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M, hipStream_t stream)
+{
+    return q4::matmul_impl(h, x, nullptr, out, M, 0, 0, stream);
+}
+
+q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                         int M, hipStream_t stream)
+{
+    return q4::matmul_impl(h, x, bias, out, M, 0, 0, stream);
+}
+
+q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                       int M, int path, int splits, hipStream_t stream)
+{
+    if (path != 0 && path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_matmul_ex: unknown path %d", path);
+    return q4::matmul_impl(h, x, bias, out, M, path, splits, stream);
+}
+
+void q4_free(q4_matrix* h) { q4::destroy(h); }
+
+int q4_path_for(const q4_matrix* h, int M)
+{
+    if (!h || M < 0) return -1;
+    return q4::choose_path(h, M, 0);
+}
+
+int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order)
+{
+    if (!h) return -1;
+    if (K) *K = h->K;
+    if (N) *N = h->N;
+    if (groupsize) *groupsize = h->G;
+    if (act_order) *act_order = h->act_order;
+    return 0;
+}
+
+q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream)
+{
+    if (!h || !w) return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: null argument");
+    if (path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: unknown path %d", path);
+    hipError_t e = q4::launch_dump(h, w, stream);
+    if (e != hipSuccess)
+        return q4::fail(Q4_ERR_HIP, "q4_dequant_dump: %s", hipGetErrorString(e));
+    return Q4_OK;
+}
+
+}  // extern "C"

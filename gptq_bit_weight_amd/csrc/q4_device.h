@@ -1,0 +1,139 @@
+// Device-side helpers shared by the libq4 kernels: the in-register unpack and
+// dequantization of one packed 32-bit word, and MFMA operand types.
+//
+// Dequantization ("GPTQ's 'Exllama Kernel Not Installed' Warning", section
+// "What the fallback actually does": the fused kernel unpacks and dequantizes
+// in registers) produces, for each 4-bit code q with zero point z and fp16
+// scale s, the binary16 value RNE(s * (q - z)):
+//
+//  * binary16 0x6400 is 1024.0 (biased exponent 25) and its fraction ulp is
+//    1, so OR-ing a code into fraction bits 0..3 yields exactly 1024 + q;
+//  * (1024 + q) - (1024 + z) = q - z is exact in fp16 (|q - z| <= 15);
+//  * the fp16 product (q - z) * s is the single rounding.
+//
+// Private word layout. The make step stores each word with the code of
+// k = 8r + i in nibble slot (i >> 1) + 4 * (i & 1), i.e. slots 0..7 hold
+// k-offsets 0,2,4,6,1,3,5,7. Then (w >> 4j) & 0x000F000F selects the codes of
+// k-offsets 2j (low half) and 2j + 1 (high half), so the four unpacked
+// registers hold the eight values in natural k order, which is the order of
+// the eight fp16 activations an MFMA lane loads with one 16-byte read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace q4dev {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+__host__ __device__ constexpr int slot_of(int i) { return (i >> 1) + 4 * (i & 1); }
+
+constexpr uint32_t kMagic2 = 0x64006400u;     // (1024.0, 1024.0) in fp16
+constexpr uint32_t kLowNibbles = 0x000F000Fu;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f)
+{
+    static_assert(sizeof(To) == sizeof(From), "size");
+    return __builtin_bit_cast(To, f);
+}
+
+// (1024 + z) in both halves.
+__device__ __forceinline__ h2 zero_pair(uint32_t z)
+{
+    return bitcast<h2>((z | 0x6400u) * 0x00010001u);
+}
+
+// s in both halves (s given as binary16 bits).
+__device__ __forceinline__ h2 scale_pair(uint32_t s_bits)
+{
+    return bitcast<h2>((s_bits & 0xFFFFu) * 0x00010001u);
+}
+
+// r = (a & mask) | orv as one v_and_or_b32. gfx9-family VOP3 encodings take
+// no literal operands and read at most one SGPR, so the compiler otherwise
+// splits this into v_and_b32 + v_or_b32; here the mask sits in an SGPR and
+// the OR constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
+    return r;
+}
+
+// Dequantize one private-layout word into eight fp16 values in k order.
+__device__ __forceinline__ h8 dequant_word(uint32_t w, h2 hz, h2 s2)
+{
+    const uint32_t magic = kMagic2;
+    h8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t u = and_or(w >> (4 * j), kLowNibbles, magic);
+        const h2 v = (bitcast<h2>(u) - hz) * s2;
+        r[2 * j] = v[0];
+        r[2 * j + 1] = v[1];
+    }
+    return r;
+}
+
+// ---- raw buffer loads ------------------------------------------------------
+// A raw buffer descriptor carries the byte size of the tensor; a load whose
+// per-lane offset lies at or beyond it returns zeros without touching memory.
+// The kernels use that for ragged edges instead of branches: an invalid lane
+// or k-step gets an offset of at least kOOB (2^31; every tensor is smaller).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kBufferDword3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferDword3);
+}
+
+__device__ __forceinline__ u4 buf_load16(rsrc_t r, uint32_t off)
+{
+    return bitcast<u4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ u2 buf_load8(rsrc_t r, uint32_t off)
+{
+    return bitcast<u2>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x mfma32(h8 a, h8 b, f16x c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
+{
+    return bitcast<uint16_t>(static_cast<_Float16>(v));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b)
+{
+    return static_cast<float>(bitcast<_Float16>(b));
+}
+
+}  // namespace q4dev

@@ -1,0 +1,295 @@
+// Skinny fused W4A16 kernel for 1 <= M <= 16 (decode).
+//
+// Weight-bound decoding is limited by memory bandwidth ("GPTQ's 'Exllama
+// Kernel Not Installed' Warning", section "What the fallback actually
+// does"), so the kernel streams the packed words once with 16-byte loads,
+// dequantizes them in registers and never writes a dequantized weight.
+//
+// Mapping (one workgroup = 4 waves = 64 output columns x a K range):
+//  * lane l owns columns c = tile*64 + 4*(l % 16) .. +3 (one 16-byte load of
+//    four consecutive words of a qweight row) and k-block kb = l / 16 of
+//    every 32-row k-step: rows 32t + 8kb .. +7, i.e. word row 4t + kb;
+//  * per k-step each lane feeds four v_mfma_f32_16x16x32_f16, one per owned
+//    column: A = activations (row m = l % 16, zero for m >= M), B = the eight
+//    dequantized weights of one word. M is padded to 16 on the matrix pipe,
+//    which has the capacity to spare; the vector ALU only unpacks and
+//    dequantizes;
+//  * the four waves split the workgroup's K range; their fp32 results are
+//    summed in LDS in wave order;
+//  * grid.y splits K across workgroups when there are few column tiles. Each
+//    split writes fp32 partials; the last workgroup of a column tile to
+//    arrive (counted with an agent-scope atomic) sums them in split order, so
+//    the result does not depend on timing. Reductions stay in fp32 (GPTQModel
+//    wiki "Inference Backends", section "Numeric epilogues": FP32 split/tile
+//    reductions, bias added before the single cast).
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace {
+
+using namespace q4dev;
+
+struct GemvArgs {
+    const uint32_t* qweight;
+    const uint16_t* scales;
+    const uint32_t* qzeros;
+    const uint16_t* x;
+    const uint16_t* bias;
+    uint16_t* out;
+    float* partials;
+    uint32_t* counters;
+    int M, K, N, G;
+    int gshift;          // group of k-step t = t >> gshift (31 for a single group)
+    int splits;
+    int batches_per_split;
+    int batches_per_wave;
+};
+
+constexpr int kSteps = q4::kBatchSteps;    // k-steps per batch
+
+// Per-lane constants of the load addressing (byte offsets inside each tensor;
+// an invalid column carries kOOB so every load of it returns zeros).
+struct LaneAddr {
+    uint32_t w;     // qweight: kb-th word row of a k-step, the lane's 4 columns
+    uint32_t x;     // x: row m, k-block kb
+    uint32_t s;     // scales: the lane's 4 columns
+    uint32_t z;     // qzeros: the word holding the lane's columns
+    uint32_t zshift;
+};
+
+struct Rsrc {
+    rsrc_t w, x, s, z;
+};
+
+// One batch of loads for one lane: kSteps k-steps of weights and activations
+// plus the scales/zeros they need. Every load is unconditional; k-steps past
+// the end of K read zeros (weights and activations alike).
+template <bool STEP_GROUPS>
+struct Batch {
+    static constexpr int NG = STEP_GROUPS ? kSteps : 1;
+    u4 w[kSteps];
+    u4 a[kSteps];
+    u2 s[NG];
+    uint32_t z[NG];
+};
+
+template <bool STEP_GROUPS>
+__device__ __forceinline__ void load_batch(Batch<STEP_GROUPS>& b, const GemvArgs& p, const Rsrc& r,
+                                           const LaneAddr& la, int batch)
+{
+    const int ksteps = p.K >> 5;
+    const int t0 = batch * kSteps;
+    const uint32_t row_bytes = (uint32_t)p.N * 4u;
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+        const int t = t0 + i;
+        const uint32_t kill = t < ksteps ? 0u : kOOB;
+        b.w[i] = buf_load16(r.w, la.w + (uint32_t)(4 * t) * row_bytes + kill);
+        b.a[i] = buf_load16(r.x, la.x + (uint32_t)t * 64u + kill);
+    }
+#pragma unroll
+    for (int gi = 0; gi < Batch<STEP_GROUPS>::NG; ++gi) {
+        const int t = t0 + gi;
+        const uint32_t g = (uint32_t)(t >> p.gshift);
+        const uint32_t kill = t < ksteps ? 0u : kOOB;
+        b.s[gi] = buf_load8(r.s, la.s + g * (uint32_t)p.N * 2u + kill);
+        b.z[gi] = buf_load4(r.z, la.z + g * (uint32_t)(p.N >> 3) * 4u + kill);
+    }
+}
+
+template <bool STEP_GROUPS>
+__device__ __forceinline__ void compute_batch(const Batch<STEP_GROUPS>& b, f4 acc[4], uint32_t zshift)
+{
+    h2 hz[4], s2[4];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+        if (i == 0 || STEP_GROUPS) {
+            const int gi = STEP_GROUPS ? i : 0;
+            const uint32_t z4 = b.z[gi] >> zshift;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hz[j] = zero_pair((z4 >> (4 * j)) & 0xFu);
+                s2[j] = scale_pair(b.s[gi][j >> 1] >> (16 * (j & 1)));
+            }
+        }
+        const h8 a = bitcast<h8>(b.a[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j] = mfma16(a, dequant_word(b.w[i][j], hz[j], s2[j]), acc[j]);
+    }
+}
+
+template <bool STEP_GROUPS>
+__global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
+{
+    __shared__ float red[q4::kWaves][16][q4::kColTile];
+    __shared__ int last_flag;
+
+    const int tid = threadIdx.x;
+    // The wave index is uniform across the wave; saying so keeps the batch
+    // bookkeeping in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int kb = lane >> 4;
+    const int m = lane & 15;
+    const int col = blockIdx.x * q4::kColTile + 4 * (lane & 15);
+    const bool col_ok = col < p.N;
+    const int ksteps = p.K >> 5;
+    const int total_batches = (ksteps + kSteps - 1) / kSteps;
+    const int ng = p.K / p.G;
+
+    Rsrc r;
+    r.w = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    r.x = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
+    r.s = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
+    r.z = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
+    LaneAddr la;
+    const uint32_t col_kill = col_ok ? 0u : kOOB;
+    la.w = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)col) * 4u + col_kill;
+    la.x = ((uint32_t)m * (uint32_t)p.K + 8u * kb) * 2u;     // rows m >= M fall outside x
+    la.s = (uint32_t)col * 2u + col_kill;
+    la.z = (uint32_t)(col >> 3) * 4u + col_kill;
+    la.zshift = 4u * (col & 7);
+
+    const int split = blockIdx.y;
+    const int b_split0 = split * p.batches_per_split;
+    const int b_split1 = min(b_split0 + p.batches_per_split, total_batches);
+    const int b0 = b_split0 + wave * p.batches_per_wave;
+    const int b1 = min(b0 + p.batches_per_wave, b_split1);
+
+    f4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    if (b0 < b1) {
+        // Two register buffers: the loads of batch b+1 are in flight while
+        // batch b is unpacked and multiplied. The prefetch index is clamped
+        // to the wave's last batch (a repeated load, never out of range).
+        // sched_barrier keeps the compiler from sinking the prefetch below
+        // the arithmetic it is meant to overlap.
+        Batch<STEP_GROUPS> A, B;
+        load_batch(A, p, r, la, b0);
+        for (int b = b0; b < b1; b += 2) {
+            load_batch(B, p, r, la, min(b + 1, b1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(A, acc, la.zshift);
+            if (b + 1 >= b1) break;
+            load_batch(A, p, r, la, min(b + 2, b1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(B, acc, la.zshift);
+        }
+    }
+
+    // Cross-wave reduction. Lane l holds rows 4*(l/16) + i of the columns
+    // 4*(l%16) + j (16x16 MFMA output layout).
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[wave][4 * kb + i][4 * (lane & 15) + j] = acc[j][i];
+    __syncthreads();
+
+    const int n_elems = p.M * q4::kColTile;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 256 * e;
+        v[e] = 0.f;
+        if (idx < n_elems) {
+            const int r = idx / q4::kColTile, c = idx % q4::kColTile;
+            v[e] = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
+        }
+    }
+
+    const int tile_col0 = blockIdx.x * q4::kColTile;
+    if (p.splits == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = tid + 256 * e;
+            const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
+            if (idx < n_elems && c < p.N) {
+                float y = v[e];
+                if (p.bias) y += f16_bits_to_f32(p.bias[c]);
+                p.out[(size_t)r * p.N + c] = f32_to_f16_bits(y);
+            }
+        }
+        return;
+    }
+
+    // Split-K: publish this split's partial sums, then let the last arriver
+    // of the column tile reduce all splits in split order.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 256 * e;
+        const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
+        if (idx < n_elems && c < p.N)
+            p.partials[((size_t)split * 16 + r) * p.N + c] = v[e];
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (prev == (uint32_t)(p.splits - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 256 * e;
+        const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
+        if (idx < n_elems && c < p.N) {
+            float y = 0.f;
+            for (int s = 0; s < p.splits; ++s)
+                y += __builtin_nontemporal_load(&p.partials[((size_t)s * 16 + r) * p.N + c]);
+            if (p.bias) y += f16_bits_to_f32(p.bias[c]);
+            p.out[(size_t)r * p.N + c] = f32_to_f16_bits(y);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(&p.counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+namespace q4 {
+
+hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                       int M, int splits, hipStream_t stream)
+{
+    GemvArgs p;
+    p.qweight = h->qweight;
+    p.scales = h->scales;
+    p.qzeros = h->qzeros;
+    p.x = x;
+    p.bias = bias;
+    p.out = out;
+    p.partials = h->partials;
+    p.counters = h->counters;
+    p.M = M;
+    p.K = h->K;
+    p.N = h->N;
+    p.G = h->G;
+    p.gshift = 31;
+    for (int sh = 0; sh < 30; ++sh)
+        if ((32 << sh) == h->G && h->G != h->K) p.gshift = sh;
+    const int ksteps = h->K / 32;
+    const int total_batches = (ksteps + kBatchSteps - 1) / kBatchSteps;
+    p.splits = splits;
+    p.batches_per_split = (total_batches + splits - 1) / splits;
+    p.batches_per_wave = (p.batches_per_split + kWaves - 1) / kWaves;
+    dim3 grid((h->N + kColTile - 1) / kColTile, splits);
+    // A batch spans 128 rows from a multiple of 128. With groupsize a multiple
+    // of 128 the batch lies in one group; otherwise (groups of 32 or 64 rows,
+    // or a single group over a K that is not a multiple of 128) the group is
+    // looked up per k-step, which also zeroes the scales of k-steps past K.
+    const bool step_groups = (h->G % (32 * kBatchSteps)) != 0 || (h->K % (32 * kBatchSteps)) != 0;
+    if (step_groups)
+        hipLaunchKernelGGL(q4_gemv_kernel<true>, grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(q4_gemv_kernel<false>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace q4

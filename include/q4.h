@@ -1,0 +1,197 @@
+/*
+ * q4.h -- C ABI of libq4: the fused GPTQ 4-bit dequantize-and-multiply on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   y[m,n] = sum_k x[m,k] * W[k,n],  W[k,n] = s[g(k),n] * (q[k,n] - z[g(k),n])
+ *
+ * The packed 4-bit weights are read from device memory and unpacked and
+ * dequantized in registers; no dequantized weight matrix is ever written to
+ * memory ("GPTQ's 'Exllama Kernel Not Installed' Warning", section "What the
+ * fallback actually does"). The interface follows the handle + matmul pair of
+ * "Implementation: Predibase Lorax GPTQ Exllama V1" (Description: a handle is
+ * made once from qweight, qzeros, scales and an optional g_idx; the matmul
+ * takes a 2-D activation and produces (batch, width)).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers passed to q4_make / q4_matmul* / q4_dequant_dump are
+ *    DEVICE pointers on the current HIP device, to dense row-major data.
+ *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *  - A failing call returns NULL or a non-zero q4_status, enqueues nothing and
+ *    leaves every output untouched; q4_last_error() then holds the reason
+ *    (thread-local, valid until the next failing call on that thread).
+ *  - There is no silent fallback: when a case is not implemented on the GPU
+ *    the call fails with Q4_ERR_UNSUPPORTED.
+ *  - Calls that take a stream enqueue work on it and return without waiting;
+ *    faults inside a kernel surface at the caller's next synchronization.
+ *
+ * Tensor formats (GPTQ checkpoint layout; "GPTQ's 'Exllama Kernel Not
+ * Installed' Warning", section "Why the kernel is missing": 4-bit integers
+ * packed into 32-bit words with a scale and a zero point per group; I/O
+ * contract table of the Lorax page: qweight/qzeros int32, scales fp16, g_idx
+ * int32 or absent, bits = 4):
+ *  - qweight int32 [K/8][N]: word (r, n) holds the codes of input rows
+ *    k = 8r .. 8r+7 of column n, the code of k = 8r+i in bits 4i .. 4i+3.
+ *  - qzeros  int32 [ceil(K/G)][N/8]: word (g, c) holds the zero points of
+ *    columns n = 8c .. 8c+7 of group g, in the same nibble order. The stored
+ *    nibble is the zero point itself (no offset).
+ *  - scales  fp16  [ceil(K/G)][N].
+ *  - g_idx   int32 [K] or NULL: group of input row k. NULL means g(k) = k / G.
+ *  - x fp16 [M][K], out fp16 [M][N], bias fp16 [N].
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct q4_matrix q4_matrix;   /* opaque handle, immutable after q4_make */
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_INVALID_ARG = 1,   /* null pointer, bad shape or value            */
+    Q4_ERR_UNSUPPORTED = 2,   /* valid input the GPU path does not implement */
+    Q4_ERR_DEVICE = 3,        /* current device is not gfx950                */
+    Q4_ERR_HIP = 4,           /* a HIP runtime call failed                   */
+    Q4_ERR_OOM = 5            /* device allocation failed                    */
+} q4_status;
+
+/* Kernel identifiers returned by q4_path_for / accepted by q4_dequant_dump. */
+enum {
+    Q4_PATH_NONE = 0,   /* M == 0: nothing is launched                            */
+    Q4_PATH_GEMV = 1,   /* bandwidth-bound skinny kernel, 1 <= M <= Q4_GEMV_MAX_M */
+    Q4_PATH_MFMA = 2    /* LDS-staged MFMA GEMM for larger M                      */
+};
+
+#define Q4_GEMV_MAX_M 16
+
+/*
+ * q4_make -- build a handle from GPTQ tensors (Lorax page, Description: a
+ * handle is constructed once from quantized weights, zero points, scales and
+ * an optional group index; "detects whether the model uses activation
+ * ordering by checking if g_idx is non-trivial").
+ *
+ * Arguments: device pointers qweight, qzeros, scales (required), g_idx
+ * (optional, NULL allowed); K, N > 0 with K % 32 == 0 and N % 8 == 0;
+ * groupsize in {32, 64, 128, 256} with K % groupsize == 0, or -1 for one
+ * group spanning K (then K % 32 == 0 still applies).
+ *
+ * Act-order: a g_idx equal to k / groupsize for every k is trivial and is
+ * dropped (same result bit for bit as NULL). Otherwise the rows are reordered
+ * by one stable argsort of g_idx (GPTQModel wiki "Inference Backends",
+ * section "Runtime cache lifetime"); the sorted g_idx must equal
+ * k / groupsize (every group exactly groupsize rows), else
+ * Q4_ERR_UNSUPPORTED. g_idx values outside [0, K/groupsize) give
+ * Q4_ERR_INVALID_ARG.
+ *
+ * Ownership: the inputs are read (the call synchronizes the device) and
+ * copied into handle-owned device memory in a private layout of the same
+ * size; the caller keeps and may free or change its tensors afterwards; such
+ * changes do not reach the handle (make a new one). The handle also owns a
+ * small split-K workspace. It never holds a dequantized K x N matrix.
+ *
+ * Returns NULL on error (q4_last_status / q4_last_error tell why).
+ */
+q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                   const int32_t* g_idx, int K, int N, int groupsize);
+
+/*
+ * q4_matmul -- out[M][N] = fp16(x[M][K] @ W) (Lorax page, Description: x @ q4
+ * producing (batch, width)). Accumulation is in fp32 (GPTQModel wiki,
+ * hardware table, ExLlama v2 row: FP32 accumulation, FP16 scales); the only
+ * rounding to fp16 is the final cast (round to nearest even).
+ *
+ * x and out are caller-owned device buffers and must not overlap. M == 0 is
+ * a no-op returning Q4_OK. M < 0, NULL pointers or a NULL handle give
+ * Q4_ERR_INVALID_ARG. M <= Q4_GEMV_MAX_M runs the skinny kernel, larger M the
+ * MFMA GEMM (q4_path_for tells which).
+ *
+ * Concurrency: the handle's workspace is shared by its calls, so calls on one
+ * handle must be ordered on one stream (or synchronized); different handles
+ * are independent.
+ */
+q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M,
+                    hipStream_t stream);
+
+/*
+ * q4_matmul_bias -- as q4_matmul, plus bias[n] added to the fp32 accumulator
+ * before the single cast to fp16 (GPTQModel wiki, section "Numeric epilogues
+ * and input gradients": bias joins the FP32 accumulator before the final
+ * cast). bias may be NULL (then identical to q4_matmul).
+ */
+q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
+                         uint16_t* out, int M, hipStream_t stream);
+
+/*
+ * q4_matmul_ex -- q4_matmul_bias with explicit kernel choice, for tests and
+ * tuning: path = 0 (automatic, as q4_matmul), Q4_PATH_GEMV (needs
+ * 1 <= M <= Q4_GEMV_MAX_M) or Q4_PATH_MFMA (any M >= 1); splits = 0
+ * (planned) or 1..16 K splits for the skinny kernel (ignored by the GEMM).
+ * Results differ between paths and split counts only by fp32 rounding.
+ */
+q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
+                       uint16_t* out, int M, int path, int splits, hipStream_t stream);
+
+/* q4_free -- release a handle (NULL is allowed). The caller must have
+ * synchronized every stream that used it. */
+void q4_free(q4_matrix* h);
+
+/* Status and message of the last failing call on this thread. */
+q4_status q4_last_status(void);
+const char* q4_last_error(void);
+
+/*
+ * q4_path_for -- the kernel q4_matmul would launch for this M (Q4_PATH_*),
+ * or -1 for a NULL handle or M < 0. Lets a caller check which kernel runs
+ * (the first page's advice: verify the kernel, not the absence of a warning).
+ */
+int q4_path_for(const q4_matrix* h, int M);
+
+/*
+ * q4_dequant_dump -- debug: run the unpack + dequantize code of kernel `path`
+ * (Q4_PATH_GEMV or Q4_PATH_MFMA) over the whole handle and write the fp16
+ * values that kernel feeds its multiply-accumulate to w[K][N] (device
+ * buffer, caller-owned, original k order). Each value is
+ * round-to-nearest-even of s * (q - z). Not on the hot path.
+ */
+q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
+
+/* Handle geometry: K, N, groupsize (after -1 -> K), act-order flag (1 when a
+ * non-trivial g_idx was given), split count of the skinny kernel for M. */
+int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order);
+
+/* ------------------------------------------------------------------------
+ * Host-only planning helpers (no HIP calls; usable without a GPU).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * q4_check_shape -- the argument checks q4_make applies to (K, N, groupsize),
+ * without touching memory. Returns Q4_OK, Q4_ERR_INVALID_ARG or
+ * Q4_ERR_UNSUPPORTED (message in q4_last_error).
+ */
+q4_status q4_check_shape(int K, int N, int groupsize);
+
+/*
+ * q4_plan_actorder -- host act-order plan for a host copy of g_idx[K]:
+ * perm[k'] = stable argsort of g_idx (ties by increasing k), *trivial = 1
+ * when g_idx[k] == k / groupsize for all k (perm is then the identity).
+ * Returns Q4_ERR_INVALID_ARG for out-of-range values and Q4_ERR_UNSUPPORTED
+ * when the sorted groups are not exactly groupsize rows each.
+ */
+q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int32_t* perm,
+                           int* trivial);
+
+/*
+ * q4_plan_splits -- number of K splits the skinny kernel uses for (M, K, N,
+ * groupsize); 0 for invalid arguments. Pure function of its inputs.
+ */
+int q4_plan_splits(int M, int K, int N, int groupsize);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

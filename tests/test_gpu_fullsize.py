@@ -1,0 +1,84 @@
+"""GPU parity at the full workload sizes (needs an MI355X), in the launch
+configuration the benchmark times (automatic path and split plan).
+
+The oracle cannot compute whole full-size products in test time, so it
+computes sampled output elements one by one (corners plus random ones); the
+rest is covered by properties that hold at any size: run-to-run bit
+identity and finiteness of every element.
+
+Workloads (shapes only, synthetic values): a Llama-7B-shaped decoder block
+at M = 1 (q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096, bias on
+q), its act-order variant (4096x11008 and 11008x4096, M in {1, 4}), the
+Llama-70B-shaped MLP (8192x28672 and 28672x8192, M in {1, 2, 4, 8, 16}) and
+prefill at M = 2048 (4096x11008 and 11008x4096, groupsize 128 and 32, plus
+act-order).
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import (announce, compare, device_tensors, make_matrix, oracle_sampled,
+                            sample_indices, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = 384
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _check_layer(L, name, *, samples=SAMPLES):
+    torch = torch_mod()
+    announce(f"full-size {name} K={L.K} N={L.N} G={L.G} M={L.M} act={L.g_idx is not None}")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    y1 = W.matmul(t["x"], t["bias"])
+    y2 = W.matmul(t["x"], t["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "run-to-run difference"
+    y = y1.cpu().numpy()
+    assert np.isfinite(y).all()
+    ms, ns = sample_indices(L.M, L.N, samples, L.seed)
+    yD, A = oracle_sampled(L, ms, ns)
+    compare(y[ms, ns], yD, A, name)
+    W.close()
+
+
+@pytest.mark.parametrize("layer", synth.LLAMA7B_BLOCK, ids=[l[0] for l in synth.LLAMA7B_BLOCK])
+def test_llama7b_block_decode(layer):
+    name, K, N, bias = layer
+    L = synth.make_layer(K, N, 128, 1, seed=synth.layer_seed("llama7b_block_decode", name, 1),
+                         bias=bias)
+    _check_layer(L, name)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096)])
+@pytest.mark.parametrize("M", [1, 4])
+def test_llama7b_actorder(K, N, M):
+    L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("llama7b_actorder", K, N, M),
+                         act_order=True)
+    _check_layer(L, f"act-order {K}x{N}")
+
+
+@pytest.mark.parametrize("layer", synth.LLAMA70B_MLP, ids=[l[0] for l in synth.LLAMA70B_MLP])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_llama70b_mlp_decode(layer, M):
+    name, K, N = layer
+    L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("llama70b_mlp_decode", name, M))
+    _check_layer(L, name)
+
+
+@pytest.mark.parametrize("K,N,G,act", [(4096, 11008, 128, False), (11008, 4096, 128, False),
+                                       (4096, 11008, 32, False), (11008, 4096, 32, False),
+                                       (4096, 11008, 128, True)])
+def test_prefill(K, N, G, act):
+    L = synth.make_layer(K, N, G, 2048, seed=synth.layer_seed("prefill", K, N, G, act),
+                         act_order=act)
+    _check_layer(L, f"prefill {K}x{N} G{G}")

@@ -1,0 +1,263 @@
+"""GPU parity of libq4 against the CPU oracle (needs an MI355X).
+
+Every test goes through the C ABI (via the ctypes binding) and compares with
+the oracle on the same seeded inputs:
+ - the dequantized fp16 values the kernels compute are bit-exact with the
+   oracle's RNE(s * (q - z)) (debug dump);
+ - every output element satisfies the acceptance rule in gpu_util;
+ - invariants of the pages: trivial g_idx == no g_idx, act-order == the
+   physically K-permuted layer ("Implementation: Predibase Lorax GPTQ
+   Exllama V1", Description; GPTQModel wiki "Inference Backends", section
+   "Runtime cache lifetime"), fused result == the dequantize-then-matmul
+   fallback's answer ("GPTQ's 'Exllama Kernel Not Installed' Warning",
+   section "What the fallback actually does": the oracle checks that one).
+Sizes span several tiles of both kernels and ragged tails in M, N and K.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (announce, compare, device_tensors, make_matrix, oracle_full, run,
+                            torch_mod)
+from tests.packing import pack_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gptq_bit_weight_amd as q4
+    q4.load_library()            # must load on a GPU machine: no fallback
+    yield
+
+
+def _layer(K, N, G, M, seed, **kw):
+    return synth.make_layer(K, N, G, M, seed=synth.layer_seed("parity", K, N, G, M, seed), **kw)
+
+
+# ------------------------------------------------------------------ dequant --
+
+@pytest.mark.parametrize("K,N,G,act", [(512, 512, 128, False), (1024, 264, 32, True),
+                                       (768, 136, 64, False), (512, 72, 256, True),
+                                       (96, 40, -1, False)])
+def test_dequant_dump_bit_exact(K, N, G, act):
+    import gptq_bit_weight_amd as q4
+    L = _layer(K, N, G, 1, 0, act_order=act)
+    announce(f"dump K={K} N={N} G={G} act={act}")
+    W = make_matrix(L)
+    assert W.act_order == act
+    ref = oracle.dequant16(L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G)
+    for path in (q4.PATH_GEMV, q4.PATH_MFMA):
+        got = W.dequant_dump(path).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref), f"path {path}: {np.sum(got != ref)} values differ"
+
+
+# ---------------------------------------------------------- skinny kernel --
+
+GEMV_CASES = [
+    # K, N, G, M, act_order, bias
+    (512, 512, 128, 1, False, False),      # the tiny 512 x 512 layer
+    (1024, 1096, 128, 1, False, True),     # 17.1 column tiles (ragged), bias
+    (1024, 1096, 32, 3, False, False),     # groups of 32
+    (2048, 200, 64, 16, False, True),      # M at the skinny limit
+    (96, 8, 32, 2, False, False),          # K tail inside a 4-step batch, one column word
+    (160, 72, -1, 5, False, False),        # one group over K (K not a multiple of 128)
+    (1024, 264, 128, 4, True, True),       # act-order
+    (768, 520, 256, 7, True, False),       # act-order, groups of 256
+]
+
+
+@pytest.mark.parametrize("K,N,G,M,act,bias", GEMV_CASES)
+def test_gemv_parity(K, N, G, M, act, bias):
+    import gptq_bit_weight_amd as q4
+    L = _layer(K, N, G, M, 1, act_order=act, bias=bias)
+    announce(f"gemv K={K} N={N} G={G} M={M} act={act} bias={bias}")
+    W = make_matrix(L)
+    assert W.path_for(M) == q4.PATH_GEMV
+    y = run(L, W=W)
+    yD, A = oracle_full(L)
+    compare(y, yD, A, f"gemv K={K} N={N} G={G} M={M}")
+
+
+# ------------------------------------------------------------ MFMA GEMM --
+
+GEMM_CASES = [
+    (512, 328, 128, 17, False, False),     # smallest M on the GEMM path, ragged N
+    (512, 328, 32, 130, False, True),      # ragged M over two row tiles, groups of 32
+    (96, 136, 32, 300, False, False),      # K tail inside the 64-row k-tile
+    (1024, 256, 128, 256, True, True),     # act-order, whole tiles
+    (768, 264, 256, 70, True, False),      # act-order, groups of 256
+    (320, 72, -1, 33, False, False),       # one group over K
+]
+
+
+@pytest.mark.parametrize("K,N,G,M,act,bias", GEMM_CASES)
+def test_gemm_parity(K, N, G, M, act, bias):
+    import gptq_bit_weight_amd as q4
+    L = _layer(K, N, G, M, 2, act_order=act, bias=bias)
+    announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias}")
+    W = make_matrix(L)
+    assert W.path_for(M) == q4.PATH_MFMA
+    y = run(L, W=W)
+    yD, A = oracle_full(L)
+    compare(y, yD, A, f"gemm K={K} N={N} G={G} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_both_kernels_agree_at_small_m(M):
+    import gptq_bit_weight_amd as q4
+    L = _layer(1024, 328, 128, M, 3, bias=True)
+    announce(f"paths M={M}")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    yD, A = oracle_full(L)
+    for path in (q4.PATH_GEMV, q4.PATH_MFMA):
+        compare(run(L, W=W, t=t, path=path), yD, A, f"path {path} M={M}")
+
+
+# ---------------------------------------------------------------- split-K --
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 8, 16])
+def test_splits_valid_and_deterministic(splits):
+    L = _layer(2048, 200, 128, 3, 4, bias=True)
+    announce(f"splits={splits}")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    yD, A = oracle_full(L)
+    a = run(L, W=W, t=t, splits=splits)
+    b = run(L, W=W, t=t, splits=splits)
+    compare(a, yD, A, f"splits={splits}")
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_repeated_split_calls_reset_counters():
+    """The split-K arrival counters are reset by the reducing workgroup, so
+    many back-to-back calls keep giving the same answer."""
+    torch = torch_mod()
+    L = _layer(4096, 512, 128, 1, 5)
+    announce("repeat splits")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    first = W.matmul(t["x"], splits=8)
+    outs = [W.matmul(t["x"], splits=8) for _ in range(50)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), first.view(torch.int16))
+
+
+# ------------------------------------------------------------- invariants --
+
+def test_trivial_g_idx_bit_identical_to_none():
+    torch = torch_mod()
+    L = _layer(1024, 264, 128, 4, 6)
+    announce("trivial g_idx")
+    t = device_tensors(L)
+    triv = torch.arange(1024, dtype=torch.int32, device="cuda") // 128
+    W0 = make_matrix(L, t, g_idx=None)
+    W1 = make_matrix(L, t, g_idx=triv)
+    assert not W1.act_order
+    for M, x in ((4, t["x"]), (40, torch.from_numpy(synth.make_x(40, 1024, 9)).cuda())):
+        assert torch.equal(W0.matmul(x).view(torch.int16), W1.matmul(x).view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 4, 64])
+def test_act_order_bit_identical_to_physical_permutation(M):
+    """A non-trivial g_idx gives exactly the output of a trivial layer built
+    from the K-permuted weights and activations."""
+    torch = torch_mod()
+    L = _layer(1024, 200, 128, M, 7, act_order=True, bias=True)
+    announce(f"act-order invariant M={M}")
+    perm = np.argsort(L.g_idx, kind="stable")
+    q = oracle.unpack_qweight(L.qweight, L.K)
+    t = device_tensors(L)
+    Wa = make_matrix(L, t)
+    assert Wa.act_order
+    Wp = make_matrix(L, dict(t, qweight=torch.from_numpy(pack_rows(q[perm])).cuda()), g_idx=None)
+    xp = torch.from_numpy(np.ascontiguousarray(L.x[:, perm])).cuda()
+    ya = Wa.matmul(t["x"], t["bias"])
+    yp = Wp.matmul(xp, t["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yp.view(torch.int16))
+    yD, A = oracle_full(L)
+    compare(ya.cpu().numpy(), yD, A, "act-order")
+
+
+def test_bias_is_added_once_in_fp32():
+    torch = torch_mod()
+    L = _layer(512, 136, 128, 2, 8, bias=True)
+    announce("bias")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    y0 = W.matmul(t["x"]).float()
+    yb = W.matmul(t["x"], t["bias"]).float()
+    yD, A = oracle_full(L)
+    compare(yb.cpu().numpy().astype(np.float16), yD, A, "bias")
+    diff = (yb - y0 - t["bias"].float()).abs()
+    assert float(diff.max()) <= float(2 ** -9 * (y0.abs().max() + 1))
+
+
+# ------------------------------------------------------------ edge cases --
+
+def test_m_zero_and_argument_errors():
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(256, 64, 128, 2, 10)
+    announce("edges")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    assert W.path_for(0) == q4.PATH_NONE and W.path_for(16) == q4.PATH_GEMV
+    assert W.path_for(17) == q4.PATH_MFMA
+    e = W.matmul(torch.empty((0, 256), dtype=torch.float16, device="cuda"))
+    assert tuple(e.shape) == (0, 64)
+    with pytest.raises(ValueError):
+        W.matmul(t["x"].float())
+    with pytest.raises(ValueError):
+        W.matmul(torch.zeros((2, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        W.matmul(torch.zeros((17, 256), dtype=torch.float16, device="cuda"), path=q4.PATH_GEMV)
+    with pytest.raises(ValueError):
+        W.matmul(t["x"], splits=17)
+    bad = torch.full((256,), 3, dtype=torch.int32, device="cuda")      # only groups 0, 1
+    with pytest.raises(ValueError, match="outside"):
+        q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], bad, groupsize=128)
+    uneven = torch.arange(256, dtype=torch.int32, device="cuda") // 128
+    uneven[0] = 1
+    with pytest.raises(NotImplementedError, match="uniform"):
+        q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], uneven, groupsize=128)
+    with pytest.raises(NotImplementedError):
+        q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], None, groupsize=100)
+    # the handle is a snapshot: editing the source tensor afterwards changes nothing
+    y1 = W.matmul(t["x"]).clone()
+    t["qweight"].zero_()
+    y2 = W.matmul(t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_special_values_propagate():
+    """Zero weights give exact zeros; an infinite scale gives inf/NaN only in
+    its own column (IEEE propagation, no clamping)."""
+    torch = torch_mod()
+    K, N, G, M = 256, 64, 128, 3
+    L = _layer(K, N, G, M, 11)
+    z = oracle.unpack_qzeros(L.qzeros, N)
+    # q == z everywhere in column 5 -> W[:, 5] == 0 -> y[:, 5] == 0 exactly
+    q = oracle.unpack_qweight(L.qweight, K)
+    q[:, 5] = np.repeat(z[:, 5], G)
+    L.qweight = pack_rows(q)
+    L.scales = L.scales.copy()
+    L.scales[1, 9] = np.float16(np.inf)
+    announce("special values")
+    y = run(L)
+    yD, A = oracle_full(L)
+    assert np.all(y[:, 5] == 0)
+    assert np.all(~np.isfinite(y[:, 9]))
+    fin = np.isfinite(yD)
+    keep = np.ones(N, dtype=bool)
+    keep[9] = False
+    compare(y[:, keep], yD[:, keep], A[:, keep], "special")
+    assert fin[:, keep].all()

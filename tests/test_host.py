@@ -1,0 +1,156 @@
+"""CPU-only tests of libq4: the library loads and exports every symbol the
+header declares, and the host-side planning (argument checks, act-order
+plan, split plan) behaves as documented. No GPU call is made here.
+
+Passages: "Implementation: Predibase Lorax GPTQ Exllama V1", Description
+(handle from qweight/qzeros/scales/g_idx; act-order detected by a non-trivial
+g_idx) and I/O contract (bits = 4, groupsize); GPTQModel wiki "Inference
+Backends", section "Runtime cache lifetime" (one stable argsort of g_idx;
+identity permutation skips the gather).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gptq_bit_weight_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "q4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q4.load_library()
+    declared = _header_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name                   # dlsym succeeds
+    assert sorted(q4.EXPORTED_SYMBOLS) == declared
+
+
+def test_library_links_only_hip_runtime():
+    """The product library is self-contained HIP: it does not link torch or
+    the CPU oracle."""
+    import subprocess
+    out = subprocess.run(["ldd", q4.library_path()], capture_output=True, text=True).stdout
+    assert "libamdhip64" in out
+    assert "torch" not in out and "oracle" not in out
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    monkeypatch.setattr(q4, "_lib", None)
+    monkeypatch.setattr(q4, "_LIB_PATH", str(tmp_path / "libq4.so"))
+    with pytest.raises(ImportError):
+        q4.load_library()
+
+
+@pytest.mark.parametrize("K,N,G", [(512, 512, 128), (4096, 11008, 128), (11008, 4096, 128),
+                                   (8192, 28672, 128), (96, 8, 32), (256, 64, 64), (512, 8, 256),
+                                   (96, 16, -1)])
+def test_check_shape_accepts(K, N, G):
+    q4.check_shape(K, N, G)
+
+
+@pytest.mark.parametrize("K,N,G,exc", [
+    (0, 512, 128, ValueError), (512, 0, 128, ValueError), (516, 512, 128, ValueError),
+    (512, 516, 128, ValueError), (512, 512, 100, NotImplementedError),
+    (512, 512, 0, NotImplementedError), (520, 512, -1, NotImplementedError),
+    (384, 512, 256, NotImplementedError),
+])
+def test_check_shape_rejects(K, N, G, exc):
+    with pytest.raises(exc):
+        q4.check_shape(K, N, G)
+
+
+def test_check_shape_message_names_the_problem():
+    with pytest.raises(ValueError, match="multiple of 8"):
+        q4.check_shape(512, 12, 128)
+
+
+def test_plan_actorder_is_stable_argsort():
+    rng = np.random.default_rng(0)
+    K, G = 1024, 128
+    pi = rng.permutation(K)
+    pos = np.empty(K, dtype=np.int64)
+    pos[pi] = np.arange(K)
+    g = (pos // G).astype(np.int32)
+    perm, trivial = q4.plan_actorder(g, K, G)
+    assert not trivial
+    assert np.array_equal(perm, np.argsort(g, kind="stable"))
+    assert np.array_equal(g[perm], np.arange(K) // G)
+
+
+def test_plan_actorder_trivial_is_identity():
+    K, G = 512, 128
+    g = (np.arange(K) // G).astype(np.int32)
+    perm, trivial = q4.plan_actorder(g, K, G)
+    assert trivial and np.array_equal(perm, np.arange(K))
+
+
+def test_plan_actorder_ties_keep_k_order():
+    K, G = 64, 32
+    g = np.array([1, 0] * 32, dtype=np.int32)           # odd rows group 0, even rows group 1
+    perm, trivial = q4.plan_actorder(g, K, G)
+    assert not trivial
+    assert perm.tolist() == list(range(1, 64, 2)) + list(range(0, 64, 2))
+
+
+def test_plan_actorder_rejects_out_of_range_and_nonuniform():
+    K, G = 128, 32
+    g = (np.arange(K) // G).astype(np.int32)
+    bad = g.copy()
+    bad[5] = 4
+    with pytest.raises(ValueError, match="outside"):
+        q4.plan_actorder(bad, K, G)
+    bad = g.copy()
+    bad[5] = -1
+    with pytest.raises(ValueError):
+        q4.plan_actorder(bad, K, G)
+    uneven = g.copy()
+    uneven[0] = 1                                        # group 0: 31 rows, group 1: 33 rows
+    with pytest.raises(NotImplementedError, match="not uniform"):
+        q4.plan_actorder(uneven, K, G)
+
+
+def test_plan_splits():
+    # few column tiles -> several splits, large N -> none; always a power of 2 <= 16
+    for (M, K, N) in [(1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096), (1, 8192, 28672),
+                      (16, 28672, 8192), (1, 512, 512), (4, 96, 8)]:
+        s = q4.plan_splits(M, K, N, 128 if K % 128 == 0 else 32)
+        assert s in (1, 2, 4, 8, 16), (M, K, N, s)
+    assert q4.plan_splits(1, 4096, 4096, 128) > 1
+    assert q4.plan_splits(1, 8192, 28672, 128) <= 2
+    assert q4.plan_splits(0, 4096, 4096, 128) == 0
+    assert q4.plan_splits(1, 4100, 4096, 128) == 0
+
+
+def test_last_error_is_thread_local():
+    import threading
+    lib = q4.load_library()
+    assert lib.q4_check_shape(512, 12, 128) == q4.ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["status"] = lib.q4_last_status()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["status"] == q4.OK
+    assert lib.q4_last_status() == q4.ERR_INVALID_ARG
+    assert b"multiple of 8" in lib.q4_last_error()
+
+
+def test_null_handle_calls_fail_cleanly():
+    lib = q4.load_library()
+    assert lib.q4_path_for(None, 1) == -1
+    assert lib.q4_matmul(None, None, None, 1, None) == q4.ERR_INVALID_ARG
+    assert lib.q4_dequant_dump(None, 1, None, None) == q4.ERR_INVALID_ARG
+    lib.q4_free(None)
