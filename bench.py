@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Throughput of the fused GPTQ W4A16 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--eager]
+
+A step is one pass of the hot path over one batch: the seven quantized linear
+layers of a Llama-7B-shaped decoder block (q, k, v, o 4096x4096; gate, up
+4096x11008; down 11008x4096; groupsize 128; bias on q) at M = 1, run back to
+back through the C ABI (q4_matmul_bias). The value is effective HBM
+bandwidth: bytes of packed weights + scales + packed zeros per step divided by
+the time per step. Inputs are resident in HBM before timing starts. To keep
+the 256 MB last-level cache from serving the weights, the steps rotate over
+ten handle copies of the block (1.05 GB). By default each step is replayed
+from a HIP graph (one graph per copy, captured on the timing stream) so that
+the host launch rate does not bound a ~20 us step; --eager launches directly.
+
+Also reported on the same JSON line:
+  roofline      the skinny kernel's achieved bandwidth: algorithmic bytes per
+                launch / mean launch duration, from HIP events recorded around
+                every launch of an eager pass on the launch stream; traffic
+                comes from committed rocprofv3 counter runs, when their kernel
+                source hash matches the current source, else null;
+  cpu_baseline  the CPU oracle's fused route on whole layers of the block;
+  secondary     the 70B-shaped MLP layers at M = 1 and the prefill GEMM at
+                M = 2048 (TFLOPS against the dense fp16 MFMA peak).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV effective HBM GB/s (% peak) at M=1; TFLOPS (% MFMA peak) at M=2048"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+MALL_DEFEAT_BYTES = 1 << 30     # rotate at least this much distinct weight memory
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gptq_bit_weight_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Layer:
+    """Device-resident layer: C handle copies, x, bias, out, raw pointers."""
+
+    def __init__(self, q4, torch, name, L, copies):
+        dev = torch.device("cuda", 0)
+        qw = torch.from_numpy(L.qweight).to(dev)
+        qz = torch.from_numpy(L.qzeros).to(dev)
+        sc = torch.from_numpy(L.scales).to(dev)
+        gi = torch.from_numpy(L.g_idx).to(dev) if L.g_idx is not None else None
+        self.name, self.K, self.N, self.G, self.M = name, L.K, L.N, L.G, L.M
+        self.mats = [q4.Q4Matrix(qw, qz, sc, gi, groupsize=L.G) for _ in range(copies)]
+        del qw, qz, sc, gi
+        self.x = torch.from_numpy(L.x).to(dev)
+        self.bias = torch.from_numpy(L.bias).to(dev) if L.bias is not None else None
+        self.out = torch.empty((L.M, L.N), dtype=torch.float16, device=dev)
+        self.bytes = L.metric_bytes()
+        self.flops = 2 * L.M * L.K * L.N
+        self.xp = ctypes.c_void_p(self.x.data_ptr())
+        self.bp = ctypes.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
+        self.op = ctypes.c_void_p(self.out.data_ptr())
+
+    def launch(self, lib, copy, stream_ptr):
+        st = lib.q4_matmul_bias(self.mats[copy]._h, self.xp, self.bp, self.op, self.M, stream_ptr)
+        if st:
+            raise RuntimeError(f"q4_matmul_bias({self.name}) failed: {lib.q4_last_error()}")
+
+    def close(self):
+        for m in self.mats:
+            m.close()
+
+
+def build_layers(q4, torch, synth, specs, G, M, workload, copies):
+    layers = []
+    for name, K, N, bias in specs:
+        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed(workload, name, M), bias=bias)
+        layers.append(Layer(q4, torch, name, L, copies))
+    return layers
+
+
+def per_launch_times(lib, torch, layers, copies, rounds, stream):
+    """Mean duration of each layer's kernel from events recorded around every
+    launch on the launch stream (eager launches)."""
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    evs = []
+    with torch.cuda.stream(stream):
+        for r in range(rounds):
+            for c in range(copies):
+                for i, ly in enumerate(layers):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    ly.launch(lib, c, sp)
+                    b.record(stream)
+                    evs.append((i, a, b))
+    stream.synchronize()
+    tot = [0.0] * len(layers)
+    cnt = [0] * len(layers)
+    for i, a, b in evs:
+        tot[i] += a.elapsed_time(b) * 1e-3
+        cnt[i] += 1
+    return [t / c for t, c in zip(tot, cnt)]
+
+
+def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def eager_step(s):
+        c = s % copies
+        for ly in layers:
+            ly.launch(lib, c, sp)
+
+    graphs = None
+    if use_graph:
+        with torch.cuda.stream(stream):
+            for s in range(copies):         # first calls happen eagerly (allocations, if any)
+                eager_step(s)
+        stream.synchronize()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for ly in layers:
+                    ly.launch(lib, c, cap)
+            graphs.append(g)
+
+    def step(s):
+        if graphs is not None:
+            graphs[s % copies].replay()
+        else:
+            eager_step(s)
+
+    with torch.cuda.stream(stream):
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for s in range(steps):
+            step(warmup + s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) * 1e-3, wall, graphs
+
+
+def cpu_baseline(synth, oracle, specs, G, workload, budget_s):
+    """The oracle's fused route on whole layers of the block at M = 1, layers
+    in block order and repeated, until budget_s of CPU time has passed."""
+    done_bytes, elapsed, layers_done = 0, 0.0, 0
+    cache = {}
+    i = 0
+    while elapsed < budget_s and layers_done < 70:
+        name, K, N, bias = specs[i % len(specs)]
+        if name not in cache:
+            cache[name] = synth.make_layer(K, N, G, 1, seed=synth.layer_seed(workload, name, 1),
+                                           bias=bias)
+        L = cache[name]
+        t = time.perf_counter()
+        oracle.matmul(L.x, L.qweight, L.qzeros, L.scales, None, K, N, G, bias=L.bias)
+        elapsed += time.perf_counter() - t
+        done_bytes += L.metric_bytes()
+        layers_done += 1
+        i += 1
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{layers_done} whole M=1 layers of the block in order (fused route, double "
+                  f"accumulation), {elapsed:.1f} s",
+    }
+
+
+def traffic_for(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed counter runs, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def secondary(q4, torch, synth, lib, stream):
+    """Quick figures on the other decode and prefill shapes (one handle each;
+    the 70B layers are rotated over enough copies to exceed the cache)."""
+    out = {}
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for name, K, N in synth.LLAMA70B_MLP:
+        L = synth.make_layer(K, N, 128, 1, seed=synth.layer_seed("llama70b_mlp_decode", name, 1))
+        copies = max(2, math.ceil(MALL_DEFEAT_BYTES / L.metric_bytes()))
+        ly = Layer(q4, torch, name, L, copies)
+        reps = 20 * copies
+        with torch.cuda.stream(stream):
+            for c in range(copies):
+                ly.launch(lib, c, sp)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for r in range(reps):
+                ly.launch(lib, r % copies, sp)
+            b.record(stream)
+        stream.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / reps
+        out[f"llama70b_{name}_m1"] = {"GB/s": round(ly.bytes / t / 1e9, 1),
+                                      "frac": round(ly.bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                                      "us": round(t * 1e6, 2)}
+        ly.close()
+        del ly
+    for K, N in ((4096, 11008), (11008, 4096)):
+        L = synth.make_layer(K, N, 128, 2048, seed=synth.layer_seed("prefill", K, N, 128, False))
+        ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
+        reps = 20
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                ly.launch(lib, 0, sp)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                ly.launch(lib, 0, sp)
+            b.record(stream)
+        stream.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / reps
+        tf = ly.flops / t / 1e12
+        out[f"prefill_{K}x{N}_m2048"] = {"TFLOP/s": round(tf, 1),
+                                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                         "us": round(t * 1e6, 1)}
+        ly.close()
+        del ly
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--eager", action="store_true", help="launch each step directly (no graph)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--counters", action="store_true",
+                    help="no timing: run 20 eager steps of the block, then 5 plain copies of "
+                         "256 MiB (a reference of known size for HBM counters), for rocprofv3 --pmc")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (one GPU's share of a "
+              "sharded layer is the same kernel at a smaller shape). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gptq_bit_weight_amd as q4
+    import synth
+    if not os.path.exists(q4.library_path()):
+        from gptq_bit_weight_amd import build as libbuild
+        libbuild.build()
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    lib = q4.load_library()
+    workload = "llama7b_block_decode"
+    G, M = 128, 1
+    copies = 10
+    log(f"[bench] building {copies} copies of the {len(synth.LLAMA7B_BLOCK)}-layer block")
+    layers = build_layers(q4, torch, synth, synth.LLAMA7B_BLOCK, G, M, workload, copies)
+    block_bytes = sum(ly.bytes for ly in layers)
+    assert copies * block_bytes >= MALL_DEFEAT_BYTES * 0.97
+    stream = torch.cuda.Stream()
+    assert all(ly.mats[0].path_for(M) == q4.PATH_GEMV for ly in layers)
+
+    if args.counters:
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        with torch.cuda.stream(stream):
+            for s in range(20):
+                for ly in layers:
+                    ly.launch(lib, s % copies, sp)
+            src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        log(json.dumps({"counters_run": True, "launches_per_layer": 20, "copy_bytes": 256 << 20,
+                        "layers": [[ly.name, ly.bytes] for ly in layers],
+                        "source_hash": kernel_source_hash()}))
+        return
+
+    log("[bench] per-launch event timing")
+    lt = per_launch_times(lib, torch, layers, copies, rounds=20, stream=stream)
+    kern_bytes = sum(ly.bytes for ly in layers)
+    kern_time = sum(lt)
+    achieved = kern_bytes / kern_time / 1e9
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup "
+        f"({'eager' if args.eager else 'graph replay'})")
+    elapsed, wall, graphs = time_steps(lib, torch, layers, copies, args.steps, args.warmup, stream,
+                                       use_graph=not args.eager)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = block_bytes / (elapsed / args.steps) / 1e9
+    # eager figure for reference (the host launch path, no graph)
+    e_elapsed, _, _ = time_steps(lib, torch, layers, copies, min(args.steps, 500), 20, stream,
+                                 use_graph=False)
+    eager_gbs = block_bytes / (e_elapsed / min(args.steps, 500)) / 1e9
+
+    del graphs
+    for ly in layers:
+        ly.close()
+    del layers
+    torch.cuda.empty_cache()
+
+    sec = {} if args.no_secondary else secondary(q4, torch, synth, lib, stream)
+
+    src_hash = kernel_source_hash()
+    traffic = traffic_for("q4_gemv_kernel", src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload,
+            "layers": [f"{n}:{K}x{N}" for n, K, N, _ in synth.LLAMA7B_BLOCK],
+            "M": M, "groupsize": G, "bias": "q_proj", "bytes_per_step": block_bytes,
+            "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
+            "parallelism": "none",
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "eager_GB/s": round(eager_gbs, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "q4_gemv_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "per_layer_us": {ly_name: round(t * 1e6, 3)
+                             for (ly_name, _, _, _), t in zip(synth.LLAMA7B_BLOCK, lt)},
+            "source_hash": src_hash,
+        },
+        "secondary": sec,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(synth, oracle, synth.LLAMA7B_BLOCK, G, workload,
+                                              args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    log(f"[bench] wall {wall:.2f} s for the timed steps")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,6 +174,7 @@ class Q4Matrix:
         if qweight.dim() != 2:
             raise ValueError("qweight must be 2-D [K/8, N]")
         K, N = int(qweight.shape[0]) * 8, int(qweight.shape[1])
+        check_shape(K, N, groupsize)
         G = K if groupsize == -1 else groupsize
         ng = -(-K // G) if G > 0 else 0
         _dev_tensor(qzeros, torch.int32, "qzeros", (ng, N // 8))

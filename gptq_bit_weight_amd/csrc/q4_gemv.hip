@@ -217,24 +217,29 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
     }
 
     // Split-K: publish this split's partial sums, then let the last arriver
-    // of the column tile reduce all splits in split order.
+    // of the column tile reduce all splits in split order. The partials are
+    // written and read with agent-scope atomic accesses, which go to the
+    // device-coherent level directly; the only ordering needed is that every
+    // wave's stores are complete before the arrival count is bumped. (A full
+    // __threadfence() would write back and invalidate the whole L2 of the
+    // XCD, once per workgroup, which serializes across the chip.)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int idx = tid + 256 * e;
         const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
         if (idx < n_elems && c < p.N)
-            p.partials[((size_t)split * 16 + r) * p.N + c] = v[e];
+            __hip_atomic_store(&p.partials[((size_t)split * 16 + r) * p.N + c], v[e], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL,
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == (uint32_t)(p.splits - 1));
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int idx = tid + 256 * e;
@@ -242,7 +247,8 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
         if (idx < n_elems && c < p.N) {
             float y = 0.f;
             for (int s = 0; s < p.splits; ++s)
-                y += __builtin_nontemporal_load(&p.partials[((size_t)s * 16 + r) * p.N + c]);
+                y += __hip_atomic_load(&p.partials[((size_t)s * 16 + r) * p.N + c], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             if (p.bias) y += f16_bits_to_f32(p.bias[c]);
             p.out[(size_t)r * p.N + c] = f32_to_f16_bits(y);
         }

@@ -14,8 +14,8 @@ constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kColTile = 64;         // columns per workgroup (16 lanes x 4 words)
 constexpr int kBatchSteps = 4;       // k-steps (32 rows each) per unrolled batch
 constexpr int kMaxSplits = 16;       // K splits (grid.y)
-constexpr int kTargetWorkgroups = 512;
-constexpr int kMinBatchesPerWave = 1;
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMinBatchesPerWave = 2;
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
 constexpr int kGemmBM = 128;

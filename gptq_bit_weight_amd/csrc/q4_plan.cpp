@@ -79,9 +79,12 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 
 // Split-K plan of the skinny kernel. One workgroup covers kColTile columns and
 // a contiguous K range that its four waves divide; splits add workgroups
-// along K when the column tiles alone cannot fill the chip. The partial sums
-// cost 8 * splits * M * N bytes of extra traffic (fp32 write + read), so
-// splits stop growing once there are enough workgroups.
+// along K when the column tiles alone cannot fill the chip. Each split costs
+// a round of fp32 partial sums (8 * splits * M * N bytes) and puts the
+// last-arriver reduction on the critical path, so splits only grow while the
+// grid stays within kTargetWorkgroups and every wave keeps at least
+// kMinBatchesPerWave batches. (Measured on MI355X at M = 1..16 over the
+// Llama-7B and Llama-70B layer shapes.)
 int plan_splits(int M, int K, int N, int G)
 {
     if (M <= 0 || K <= 0 || N <= 0 || K % 32) return 0;
@@ -89,7 +92,7 @@ int plan_splits(int M, int K, int N, int G)
     const int col_tiles = (N + kColTile - 1) / kColTile;
     const int batches = (K / 32 + kBatchSteps - 1) / kBatchSteps;
     int s = 1;
-    while (s < kMaxSplits && col_tiles * s < kTargetWorkgroups &&
+    while (2 * s <= kMaxSplits && col_tiles * 2 * s <= kTargetWorkgroups &&
            batches >= 2 * s * kWaves * kMinBatchesPerWave)
         s *= 2;
     return s;
