@@ -16,8 +16,8 @@ the host launch rate does not bound a ~20 us step; --eager launches directly.
 
 Also reported on the same JSON line:
   roofline      the skinny kernel's achieved bandwidth: algorithmic bytes per
-                launch / mean launch duration, from HIP events recorded around
-                every launch of an eager pass on the launch stream; traffic
+                launch / mean launch duration, from HIP events around graph
+                replays of each layer's launches on the launch stream; traffic
                 comes from committed rocprofv3 counter runs, when their kernel
                 source hash matches the current source, else null;
   cpu_baseline  the CPU oracle's fused route on whole layers of the block;
@@ -98,27 +98,35 @@ def build_layers(q4, torch, synth, specs, G, M, workload, copies):
 
 
 def per_launch_times(lib, torch, layers, copies, rounds, stream):
-    """Mean duration of each layer's kernel from events recorded around every
-    launch on the launch stream (eager launches)."""
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    evs = []
-    with torch.cuda.stream(stream):
-        for r in range(rounds):
+    """Mean kernel duration of each layer: `rounds * copies` launches of the
+    layer (rotating over its weight copies) captured in one HIP graph on the
+    launch stream and replayed between two events. Consecutive kernels of a
+    graph start back to back, so elapsed / launches is the mean launch
+    duration (it matches the kernel-trace durations of rocprofv3)."""
+    out = []
+    n = rounds * copies
+    for ly in layers:
+        with torch.cuda.stream(stream):
+            sp = ctypes.c_void_p(stream.cuda_stream)
             for c in range(copies):
-                for i, ly in enumerate(layers):
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    ly.launch(lib, c, sp)
-                    b.record(stream)
-                    evs.append((i, a, b))
-    stream.synchronize()
-    tot = [0.0] * len(layers)
-    cnt = [0] * len(layers)
-    for i, a, b in evs:
-        tot[i] += a.elapsed_time(b) * 1e-3
-        cnt[i] += 1
-    return [t / c for t, c in zip(tot, cnt)]
+                ly.launch(lib, c, sp)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for r in range(n):
+                ly.launch(lib, r % copies, cap)
+        with torch.cuda.stream(stream):
+            g.replay()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        stream.synchronize()
+        out.append(a.elapsed_time(b) * 1e-3 / n)
+        del g
+    return out
 
 
 def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
@@ -374,6 +382,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "algorithmic_bytes_per_launch": round(kern_bytes / len(layers)),
             "per_layer_us": {ly_name: round(t * 1e6, 3)
                              for (ly_name, _, _, _), t in zip(synth.LLAMA7B_BLOCK, lt)},
             "source_hash": src_hash,
