@@ -24,8 +24,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 # -ffp-contract=off: no implicit FMA contraction; every rounding is the one
 # written in the source.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the fp32 epilogues
+# and group folds read them without v_accvgpr_read copies.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-I", INCLUDE, "-I", CSRC]
-DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _sources():

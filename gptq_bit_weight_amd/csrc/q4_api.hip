@@ -17,7 +17,7 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
                          hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
-hipError_t launch_dump(const q4_matrix* h, uint16_t* w, hipStream_t stream);
+hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
 
 namespace {
 
@@ -257,7 +257,7 @@ q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t
     if (!h || !w) return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: null argument");
     if (path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: unknown path %d", path);
-    hipError_t e = q4::launch_dump(h, w, stream);
+    hipError_t e = q4::launch_dump(h, path, w, stream);
     if (e != hipSuccess)
         return q4::fail(Q4_ERR_HIP, "q4_dequant_dump: %s", hipGetErrorString(e));
     return Q4_OK;

@@ -81,6 +81,23 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, h2 hz, h2 s2)
     return r;
 }
 
+// Unpack one private-layout word and subtract the zero point: eight fp16
+// values (q - z) in k order. Every value is a small integer, exact in fp16
+// (|q - z| <= 15).
+__device__ __forceinline__ h8 sub_zero_word(uint32_t w, h2 hz)
+{
+    const uint32_t magic = kMagic2;
+    h8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t u = and_or(w >> (4 * j), kLowNibbles, magic);
+        const h2 v = bitcast<h2>(u) - hz;
+        r[2 * j] = v[0];
+        r[2 * j + 1] = v[1];
+    }
+    return r;
+}
+
 // ---- raw buffer loads ------------------------------------------------------
 // A raw buffer descriptor carries the byte size of the tensor; a load whose
 // per-lane offset lies at or beyond it returns zeros without touching memory.

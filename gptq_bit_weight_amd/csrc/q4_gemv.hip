@@ -11,9 +11,12 @@
 //    every 32-row k-step: rows 32t + 8kb .. +7, i.e. word row 4t + kb;
 //  * per k-step each lane feeds four v_mfma_f32_16x16x32_f16, one per owned
 //    column: A = activations (row m = l % 16, zero for m >= M), B = the eight
-//    dequantized weights of one word. M is padded to 16 on the matrix pipe,
-//    which has the capacity to spare; the vector ALU only unpacks and
-//    dequantizes;
+//    values q - z of one word, exact small integers in fp16. M is padded to
+//    16 on the matrix pipe, which has the capacity to spare; the vector ALU
+//    is the scarce unit here, so the per-group scale is applied once per
+//    group to the fp32 group sum: sum_k x*s*(q - z) = s * sum_k x*(q - z)
+//    (the weight s*(q - z) is exact in fp32, so this is the product with the
+//    exact dequantized weight, accumulated in fp32);
 //  * the four waves split the workgroup's K range; their fp32 results are
 //    summed in LDS in wave order;
 //  * grid.y splits K across workgroups when there are few column tiles. Each
@@ -64,17 +67,21 @@ struct Rsrc {
 // One batch of loads for one lane: kSteps k-steps of weights and activations
 // plus the scales/zeros they need. Every load is unconditional; k-steps past
 // the end of K read zeros (weights and activations alike).
-template <bool STEP_GROUPS>
+//
+// GS = k-steps per group: 1, 2 (groups of 32, 64 rows), 4, 8 (128, 256) or 0
+// (one group over K). Batches start at multiples of 4 k-steps, so with GS >= 4
+// (or 0) a batch lies in one group.
+template <int GS>
 struct Batch {
-    static constexpr int NG = STEP_GROUPS ? kSteps : 1;
+    static constexpr int NG = GS == 1 ? 4 : GS == 2 ? 2 : 1;
     u4 w[kSteps];
     u4 a[kSteps];
     u2 s[NG];
     uint32_t z[NG];
 };
 
-template <bool STEP_GROUPS>
-__device__ __forceinline__ void load_batch(Batch<STEP_GROUPS>& b, const GemvArgs& p, const Rsrc& r,
+template <int GS>
+__device__ __forceinline__ void load_batch(Batch<GS>& b, const GemvArgs& p, const Rsrc& r,
                                            const LaneAddr& la, int batch)
 {
     const int ksteps = p.K >> 5;
@@ -88,38 +95,69 @@ __device__ __forceinline__ void load_batch(Batch<STEP_GROUPS>& b, const GemvArgs
         b.a[i] = buf_load16(r.x, la.x + (uint32_t)t * 64u + kill);
     }
 #pragma unroll
-    for (int gi = 0; gi < Batch<STEP_GROUPS>::NG; ++gi) {
-        const int t = t0 + gi;
-        const uint32_t g = (uint32_t)(t >> p.gshift);
+    for (int gi = 0; gi < Batch<GS>::NG; ++gi) {
+        const int t = t0 + gi * (kSteps / Batch<GS>::NG);
+        const uint32_t g = GS == 0 ? 0u : (uint32_t)(t >> p.gshift);
         const uint32_t kill = t < ksteps ? 0u : kOOB;
         b.s[gi] = buf_load8(r.s, la.s + g * (uint32_t)p.N * 2u + kill);
         b.z[gi] = buf_load4(r.z, la.z + g * (uint32_t)(p.N >> 3) * 4u + kill);
     }
 }
 
-template <bool STEP_GROUPS>
-__device__ __forceinline__ void compute_batch(const Batch<STEP_GROUPS>& b, f4 acc[4], uint32_t zshift)
+// Multiply one batch into the group sums `acc` and fold finished groups into
+// `tot`: tot += s * acc (fp32). FRESH: the batch starts a group (acc restarts
+// from zero); FOLD: the batch ends a group. Only GS = 8 and GS = 0 decide
+// these per batch; smaller groups start and end inside every batch.
+template <int GS, bool FRESH, bool FOLD>
+__device__ __forceinline__ void compute_batch(const Batch<GS>& b, f4 acc[4], f4 tot[4],
+                                              uint32_t zshift)
 {
-    h2 hz[4], s2[4];
+    h2 hz[4];
+    float sf[4];
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-        if (i == 0 || STEP_GROUPS) {
-            const int gi = STEP_GROUPS ? i : 0;
+        constexpr int per = GS == 1 ? 1 : GS == 2 ? 2 : kSteps;   // k-steps per group in a batch
+        const bool starts = (i % per) == 0;
+        const bool fresh = starts && (GS == 1 || GS == 2 || GS == 4 || FRESH);
+        const bool ends = (i % per) == per - 1;
+        const bool fold = ends && (GS == 1 || GS == 2 || GS == 4 || FOLD);
+        if (starts) {
+            const int gi = i / per;
             const uint32_t z4 = b.z[gi] >> zshift;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 hz[j] = zero_pair((z4 >> (4 * j)) & 0xFu);
-                s2[j] = scale_pair(b.s[gi][j >> 1] >> (16 * (j & 1)));
+                sf[j] = f16_bits_to_f32((uint16_t)(b.s[gi][j >> 1] >> (16 * (j & 1))));
             }
         }
         const h8 a = bitcast<h8>(b.a[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[j] = mfma16(a, dequant_word(b.w[i][j], hz[j], s2[j]), acc[j]);
+            acc[j] = mfma16(a, sub_zero_word(b.w[i][j], hz[j]), fresh ? f4{0.f, 0.f, 0.f, 0.f} : acc[j]);
+        if (fold) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tot[j][e] = __builtin_fmaf(sf[j], acc[j][e], tot[j][e]);
+        }
     }
 }
 
-template <bool STEP_GROUPS>
+template <int GS>
+__device__ __forceinline__ void compute_any(const Batch<GS>& b, f4 acc[4], f4 tot[4], uint32_t zshift,
+                                            bool fresh, bool fold)
+{
+    if (GS == 8 || GS == 0) {
+        if (fresh && fold) compute_batch<GS, true, true>(b, acc, tot, zshift);
+        else if (fresh) compute_batch<GS, true, false>(b, acc, tot, zshift);
+        else if (fold) compute_batch<GS, false, true>(b, acc, tot, zshift);
+        else compute_batch<GS, false, false>(b, acc, tot, zshift);
+    } else {
+        compute_batch<GS, true, true>(b, acc, tot, zshift);
+    }
+}
+
+template <int GS>
 __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
 {
     __shared__ float red[q4::kWaves][16][q4::kColTile];
@@ -157,9 +195,12 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
     const int b0 = b_split0 + wave * p.batches_per_wave;
     const int b1 = min(b0 + p.batches_per_wave, b_split1);
 
-    f4 acc[4];
+    f4 acc[4], tot[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+        acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+        tot[j] = f4{0.f, 0.f, 0.f, 0.f};
+    }
 
     if (b0 < b1) {
         // Two register buffers: the loads of batch b+1 are in flight while
@@ -167,16 +208,18 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
         // to the wave's last batch (a repeated load, never out of range).
         // sched_barrier keeps the compiler from sinking the prefetch below
         // the arithmetic it is meant to overlap.
-        Batch<STEP_GROUPS> A, B;
+        Batch<GS> A, B;
         load_batch(A, p, r, la, b0);
         for (int b = b0; b < b1; b += 2) {
             load_batch(B, p, r, la, min(b + 1, b1 - 1));
             __builtin_amdgcn_sched_barrier(0);
-            compute_batch(A, acc, la.zshift);
+            compute_any(A, acc, tot, la.zshift, b == b0 || (GS == 8 && (b & 1) == 0),
+                        b + 1 == b1 || (GS == 8 && (b & 1) == 1));
             if (b + 1 >= b1) break;
             load_batch(A, p, r, la, min(b + 2, b1 - 1));
             __builtin_amdgcn_sched_barrier(0);
-            compute_batch(B, acc, la.zshift);
+            compute_any(B, acc, tot, la.zshift, GS == 8 && ((b + 1) & 1) == 0,
+                        b + 2 == b1 || (GS == 8 && ((b + 1) & 1) == 1));
         }
     }
 
@@ -186,7 +229,7 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            red[wave][4 * kb + i][4 * (lane & 15) + j] = acc[j][i];
+            red[wave][4 * kb + i][4 * (lane & 15) + j] = tot[j][i];
     __syncthreads();
 
     const int n_elems = p.M * q4::kColTile;
@@ -286,15 +329,18 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     p.batches_per_split = (total_batches + splits - 1) / splits;
     p.batches_per_wave = (p.batches_per_split + kWaves - 1) / kWaves;
     dim3 grid((h->N + kColTile - 1) / kColTile, splits);
-    // A batch spans 128 rows from a multiple of 128. With groupsize a multiple
-    // of 128 the batch lies in one group; otherwise (groups of 32 or 64 rows,
-    // or a single group over a K that is not a multiple of 128) the group is
-    // looked up per k-step, which also zeroes the scales of k-steps past K.
-    const bool step_groups = (h->G % (32 * kBatchSteps)) != 0 || (h->K % (32 * kBatchSteps)) != 0;
-    if (step_groups)
-        hipLaunchKernelGGL(q4_gemv_kernel<true>, grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(q4_gemv_kernel<false>, grid, dim3(256), 0, stream, p);
+    // k-steps per group: a batch spans 4 k-steps starting at a multiple of 4,
+    // so groups of 128 or 256 rows never straddle a batch; one group over K
+    // (per-channel) never changes at all.
+    const int gs = h->G == h->K ? 0 : h->G / 32;
+    switch (gs) {
+    case 1: hipLaunchKernelGGL(q4_gemv_kernel<1>, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(q4_gemv_kernel<2>, grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(q4_gemv_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(q4_gemv_kernel<8>, grid, dim3(256), 0, stream, p); break;
+    case 0: hipLaunchKernelGGL(q4_gemv_kernel<0>, grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

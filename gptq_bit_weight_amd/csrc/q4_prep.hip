@@ -55,8 +55,12 @@ __global__ __launch_bounds__(256) void q4_permute_x_kernel(const uint16_t* __res
     }
 }
 
-// Debug dump: w[k][n] (original row order) = the fp16 value the kernels feed
-// to the MFMA for weight (k, n), computed with the kernels' dequant_word.
+// Debug dump: w[k][n] (original row order) = the dequantized weight (k, n) as
+// each kernel forms it, rounded to fp16. FACTORED (skinny kernel): the
+// kernel's own (q - z) from sub_zero_word times the fp32 scale, which is the
+// exact weight the kernel applies, then one RNE rounding. Otherwise (GEMM):
+// the fp16 value dequant_word feeds to the MFMA.
+template <bool FACTORED>
 __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict__ qweight,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint32_t* __restrict__ qzeros,
@@ -71,8 +75,14 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const int g = kk / G;
         const uint32_t word = qweight[(size_t)(kk >> 3) * N + n];
         const uint32_t z = (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
-        const h8 v = dequant_word(word, zero_pair(z), scale_pair(scales[(size_t)g * N + n]));
-        w[idx] = bitcast<uint16_t>(v[kk & 7]);
+        const uint16_t sb = scales[(size_t)g * N + n];
+        if (FACTORED) {
+            const h8 d = sub_zero_word(word, zero_pair(z));
+            w[idx] = f32_to_f16_bits(f16_bits_to_f32(sb) * static_cast<float>(d[kk & 7]));
+        } else {
+            const h8 v = dequant_word(word, zero_pair(z), scale_pair(sb));
+            w[idx] = bitcast<uint16_t>(v[kk & 7]);
+        }
     }
 }
 
@@ -104,10 +114,15 @@ hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp
     return hipGetLastError();
 }
 
-hipError_t launch_dump(const q4_matrix* h, uint16_t* w, hipStream_t stream)
+hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream)
 {
-    hipLaunchKernelGGL(q4_dump_kernel, dim3(grid_for((size_t)h->K * h->N)), dim3(256), 0, stream,
-                       h->qweight, h->scales, h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+    const dim3 grid(grid_for((size_t)h->K * h->N));
+    if (path == Q4_PATH_GEMV)
+        hipLaunchKernelGGL(q4_dump_kernel<true>, grid, dim3(256), 0, stream, h->qweight, h->scales,
+                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+    else
+        hipLaunchKernelGGL(q4_dump_kernel<false>, grid, dim3(256), 0, stream, h->qweight, h->scales,
+                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     return hipGetLastError();
 }
 
