@@ -171,8 +171,9 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
     if (M == 0) return Q4_OK;
     if (!x || !out) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: x and out must be non-null");
     if (!aligned(x, 16)) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: x must be 16-byte aligned");
-    if ((long long)M * h->K > INT_MAX || (long long)M * h->N > INT_MAX)
-        return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: M=%d too large for this layer", M);
+    // Byte offsets inside x stay below 2^31 (out-of-range lanes add 2^31).
+    if ((long long)M * h->K * 2 > INT_MAX || (long long)M * h->N > INT_MAX)
+        return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: M=%d too large for this layer (M*K*2 must be < 2^31)", M);
     {
         const char* xb = reinterpret_cast<const char*>(x);
         const char* ob = reinterpret_cast<const char*>(out);

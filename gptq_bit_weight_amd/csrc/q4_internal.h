@@ -18,7 +18,7 @@ constexpr int kTargetWorkgroups = 256;
 constexpr int kMinBatchesPerWave = 2;
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 256;

@@ -47,8 +47,11 @@ q4_status check_shape(int K, int N, int groupsize, int* G_out)
         return fail(Q4_ERR_UNSUPPORTED, "K=%d is not a multiple of 32 (the kernels' k-block)", K);
     if (K % G)
         return fail(Q4_ERR_UNSUPPORTED, "K=%d is not a multiple of groupsize=%d", K, G);
-    if ((long long)K * (long long)N / 8 > (1LL << 31) - 1)
-        return fail(Q4_ERR_UNSUPPORTED, "K*N/8 exceeds 2^31 words");
+    // Byte offsets inside the packed weights stay below 2^31 (the kernels mark
+    // out-of-range lanes by adding 2^31).
+    if ((long long)K * (long long)N / 2 > (1LL << 31) - 1)
+        return fail(Q4_ERR_UNSUPPORTED, "K*N/2 = %lld bytes of packed weights exceeds 2^31 - 1",
+                    (long long)K * (long long)N / 2);
     if (G_out) *G_out = G;
     return Q4_OK;
 }
