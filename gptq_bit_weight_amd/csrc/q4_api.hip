@@ -11,8 +11,10 @@ namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                        int M, int splits, hipStream_t stream);
-hipError_t launch_gemm(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, hipStream_t stream);
+hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                           int M, hipStream_t stream);
+hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                            int M, hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
@@ -47,7 +49,7 @@ void destroy(q4_matrix* h)
     delete h;
 }
 
-q4_status check_device(int* dev)
+q4_status check_device(int* dev, int* num_cu)
 {
     Q4_HIP(hipGetDevice(dev), "hipGetDevice");
     hipDeviceProp_t prop;
@@ -55,6 +57,7 @@ q4_status check_device(int* dev)
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(Q4_ERR_DEVICE, "device %d is %s; libq4 is built for gfx950 (MI355X) only", *dev,
                     prop.gcnArchName);
+    *num_cu = prop.multiProcessorCount;
     return Q4_OK;
 }
 
@@ -70,8 +73,8 @@ q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_
     if (st != Q4_OK) return st;
     if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4))
         return fail(Q4_ERR_INVALID_ARG, "q4_make: qweight must be 16-byte aligned, scales 8-byte");
-    int dev = -1;
-    st = check_device(&dev);
+    int dev = -1, num_cu = 0;
+    st = check_device(&dev, &num_cu);
     if (st != Q4_OK) return st;
     // The inputs may still be being written by work on other streams.
     Q4_HIP(hipDeviceSynchronize(), "q4_make: synchronize");
@@ -97,6 +100,7 @@ q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_
     h->ng = ng;
     h->act_order = act;
     h->device = dev;
+    h->num_cu = num_cu;
     auto bail = [&](q4_status s) {
         destroy(h);
         return s;
@@ -186,6 +190,8 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
                     Q4_GEMV_MAX_M, M);
     if (splits < 0 || splits > kMaxSplits)
         return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
+    if (kind == Q4_PATH_MFMA && splits > 2)
+        return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1 or 2", splits);
 
     const uint16_t* xe = x;
     if (h->act_order) {
@@ -199,7 +205,19 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (s <= 0 || s > kMaxSplits) s = plan_splits(M, h->K, h->N, h->G);
         Q4_HIP(launch_gemv(h, xe, bias, out, M, s, stream), "q4_matmul: gemv launch");
     } else {
-        Q4_HIP(launch_gemm(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+        // Two GEMM variants: register-staged tiles (80 KiB of LDS, two
+        // workgroups per CU) when there are at least two output tiles per CU,
+        // else the direct-to-LDS pipeline (one workgroup per CU, deeper
+        // prefetch). `splits` picks one explicitly (1 or 2) for tests.
+        int variant = splits;
+        if (variant == 0) {
+            const long long tiles = (long long)((h->N + kGemmBN - 1) / kGemmBN) * ((M + kGemmBM - 1) / kGemmBM);
+            variant = tiles >= 2LL * h->num_cu ? 1 : 2;
+        }
+        if (variant == 1)
+            Q4_HIP(launch_gemm_regs(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+        else
+            Q4_HIP(launch_gemm_dma(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
     }
     return Q4_OK;
 }

@@ -1,29 +1,41 @@
-// Prefill fused W4A16 GEMM (M > 16) on the matrix cores.
+// Prefill fused W4A16 GEMM (M > 16) on the matrix cores: direct-to-LDS
+// pipelined variant.
 //
 // The multiply itself is a dense contraction, so it runs on
 // v_mfma_f32_32x32x16_f16 with fp32 accumulation (GPTQModel wiki "Inference
 // Backends", hardware table, ExLlama v2 row: FP32 accumulation, FP16 scales).
-// The weight tile is staged in LDS still packed (4 bits per weight) and each
-// wave dequantizes the words it feeds to the MFMA in registers, so no fp16
-// weight tile is ever written to device memory ("GPTQ's 'Exllama Kernel Not
-// Installed' Warning", section "What the fallback actually does").
+// The weights travel from memory to LDS still packed (4 bits per weight);
+// each workgroup dequantizes its packed tile once into an fp16 tile in LDS,
+// which the matrix cores read. No fp16 weight tile is ever written to device
+// memory ("GPTQ's 'Exllama Kernel Not Installed' Warning", section "What the
+// fallback actually does").
 //
 // Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN = 256 x 128
-// output tile; each wave owns 128 x 64 (4 x 2 MFMA tiles of 32 x 32), so every
-// dequantized word feeds 4 MFMAs and the vector ALU stays well under the
-// matrix pipe. K advances in BK = 64 rows: the activation tile (256 x 64 fp16,
-// row stride padded to 72 halfs so 16-byte LDS reads of 8 consecutive rows
-// hit distinct banks) and the packed weight tile (8 x 128 words) are
-// double-buffered in LDS; the next tile's global loads are in flight while
-// the current one is multiplied.
+// output tile; each wave owns 128 x 64 (4 x 2 MFMA tiles of 32 x 32). K
+// advances in BK = 64 rows per tile.
 //
-// Global loads are bounds-checked raw buffer loads (out-of-range offsets
-// read zeros), so ragged M, N and K need no branches.
+// Data movement per k-tile (all global reads are bounds-checked raw buffer
+// loads that write straight into LDS, so ragged M, N and K need no branches
+// and no registers carry the tiles):
+//  * activations (256 x 64 fp16) and packed weights (8 x 128 words plus the
+//    tile's scale and zero rows) each use a ring of 3 LDS stages and are
+//    loaded 2 tiles ahead. Each stage is its own __shared__ array and the
+//    k-loop is unrolled by 3, so the compiler can see that the LDS reads of
+//    one stage never alias the loads landing in another and does not wait
+//    for them;
+//  * while the waves multiply tile t, every thread dequantizes 4 packed words
+//    of tile t+1 (one column, 32 rows of one group) into the next fp16 weight
+//    tile (a third ring of 3), so each weight is unpacked once per workgroup.
+// LDS rows of 64 fp16 (128 bytes) are stored with the 16-byte chunk c of row
+// r at slot c ^ ((r >> 1) & 7): a 16-byte read is served 16 lanes at a time,
+// and 16 consecutive rows at one chunk then cover all 64 banks exactly once.
 //
 // Workgroup order: when the row tiles divide evenly over the 8 XCDs (the
 // round-robin dispatch puts workgroup i on XCD i % 8), every XCD works on its
 // own row tiles, so each XCD's L2 keeps its activation rows resident while
 // the packed weights stream through; otherwise row-major order.
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -31,17 +43,25 @@ namespace {
 
 using namespace q4dev;
 
-constexpr int BM = q4::kGemmBM;
-constexpr int BN = q4::kGemmBN;
-constexpr int BK = q4::kGemmBK;
-constexpr int AST = BK + 8;          // LDS row stride of the activation tile (halfs)
-constexpr int NT = q4::kGemmThreads;
+constexpr int BM = q4::kGemmBM;      // 256
+constexpr int BN = q4::kGemmBN;      // 128
+constexpr int BK = q4::kGemmBK;      // 64
+constexpr int NT = q4::kGemmThreads; // 256
 constexpr int WTM = BM / 2;          // wave tile rows
 constexpr int WTN = BN / 2;          // wave tile columns
-constexpr int MI = WTM / 32;         // 32x32 MFMA tiles per wave along M
-constexpr int NJ = WTN / 32;         // ... along N
-constexpr int A_LOADS = BM * BK / 8 / NT;    // 16-byte activation loads per thread per tile
-static_assert(BN * BK / 8 / 4 == NT, "one 16-byte weight load per thread per tile");
+constexpr int MI = WTM / 32;
+constexpr int NJ = WTN / 32;
+constexpr int STAGES = 3;
+constexpr int A_TILE_BYTES = BM * BK * 2;          // 32 KiB
+constexpr int BP_WORD_BYTES = (BK / 8) * BN * 4;   // 4 KiB of packed words
+constexpr int BP_SZ_BYTES = 256;                    // one row of scales or zero words
+constexpr int BP_TILE_BYTES = BP_WORD_BYTES + 4 * BP_SZ_BYTES;   // + scales/zeros of 2 groups
+constexpr int B16_TILE_BYTES = BN * BK * 2;        // 16 KiB
+constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);  // 8 direct loads per thread
+static_assert(BP_WORD_BYTES == NT * 16, "one packed-weight load per thread");
+static_assert(BK == 64 && BN == 128 && NT == 256, "index arithmetic below assumes these");
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmArgs {
     const uint32_t* qweight;
@@ -53,65 +73,133 @@ struct GemmArgs {
     int M, K, N, G;
 };
 
-struct TileRegs {
-    u4 a[A_LOADS];
-    u4 b;
-};
+// Byte offset of 16-byte chunk c of row r in a swizzled 64-fp16-per-row tile.
+__device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
 
-// Scales/zeros of the NJ columns a lane multiplies, for up to two groups of a
-// k-tile (groups of 32 rows).
-struct GroupRegs {
-    uint32_t s[2][NJ];
-    uint32_t z[2][NJ];
-};
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for).
+#define Q4_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-struct Lane {
-    uint32_t a_off[A_LOADS];   // activation byte offsets (k0 = 0)
-    uint32_t a_kc;             // k offset (rows) of this thread's activation chunks
-    uint32_t b_off;            // weight byte offset (k0 = 0), column kill folded in
-    uint32_t s_off[NJ];        // scale byte offsets (group 0)
-    uint32_t z_off[NJ];        // zero-word byte offsets (group 0)
-    uint32_t z_shift[NJ];
-};
-
-template <int NG>
-__device__ __forceinline__ void load_tile(TileRegs& t, GroupRegs& gr, const GemmArgs& p,
-                                          const Lane& ln, rsrc_t rx, rsrc_t rw, rsrc_t rs,
-                                          rsrc_t rz, int k0)
+__device__ __forceinline__ void wait_vm(int n)
 {
-    const uint32_t a_kill = (ln.a_kc + (uint32_t)k0 < (uint32_t)p.K) ? 0u : kOOB;
-#pragma unroll
-    for (int e = 0; e < A_LOADS; ++e) t.a[e] = buf_load16(rx, ln.a_off[e] + (uint32_t)k0 * 2u + a_kill);
-    t.b = buf_load16(rw, ln.b_off + (uint32_t)(k0 >> 3) * (uint32_t)p.N * 4u);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        const int k = k0 + 32 * gi;
-        const uint32_t g = (uint32_t)(min(k, p.K - 1) / p.G);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            gr.s[gi][j] = buf_load2(rs, ln.s_off[j] + g * (uint32_t)p.N * 2u);
-            gr.z[gi][j] = buf_load4(rz, ln.z_off[j] + g * (uint32_t)(p.N >> 3) * 4u);
-        }
+    switch (n) {
+    case 8: Q4_VMCNT(8); break;
+    case 10: Q4_VMCNT(10); break;
+    case 18: Q4_VMCNT(18); break;
+    default: Q4_VMCNT(0); break;
     }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* As, uint32_t* Bs, int tid)
+// Workgroup barrier for the LDS pipeline. __syncthreads() also waits for
+// every outstanding vector-memory load (its release fence covers the
+// direct-to-LDS loads still in flight), which would drain the pipeline; the
+// waits this pipeline needs are issued explicitly before the barrier (vmcnt
+// for the stages about to be read, lgkmcnt for this thread's LDS writes).
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier()
 {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct Ctx {
+    rsrc_t rx, rw, rs, rz;
+    uint32_t a_off[A_LOADS];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
+    uint32_t a_k[A_LOADS];     // k of each chunk for k0 = 0
+    uint32_t bp_off;           // packed-weight byte offset for k0 = 0 (column kill folded in)
+    uint32_t sz_off;           // scale or zero-word byte offset of this lane (row 0, kill folded in)
+    bool sz_is_zero;           // this wave loads zero words (else scales)
+    int sz_group;              // 0: first group of the tile, 1: second (groups of 32 rows)
+};
+
+// Direct-to-LDS loads of activation tile kt into the stage `dst_stage`
+// (A_LOADS per thread).
+__device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* dst_stage, int wave, int kt)
+{
+    const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) {
-        const int c = tid + NT * e;
-        const int row = c >> 3, kc = c & 7;
-        *reinterpret_cast<u4*>(As + row * AST + 8 * kc) = t.a[e];
+        const uint32_t kill = (c.a_k[e] + k0 < (uint32_t)p.K) ? 0u : kOOB;
+        char* dst = dst_stage + (e * 4 + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void*)dst, 16, (int)(c.a_off[e] + k0 * 2u + kill), 0, 0, 0);
     }
-    const int brow = tid >> 5, bcol = tid & 31;
-    *reinterpret_cast<u4*>(Bs + brow * BN + 4 * bcol) = t.b;
 }
 
-template <int NG>
-__global__ __launch_bounds__(NT) void q4_gemm_kernel(GemmArgs p)
+// Direct-to-LDS loads of packed tile kt into stage st: the packed words (one
+// 16-byte load per thread) and one row of scales or zero words per wave
+// (2 loads per thread).
+__device__ __forceinline__ void load_b(const Ctx& c, const GemmArgs& p, char* base, int wave, int kt)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * AST];
-    __shared__ __attribute__((aligned(16))) uint32_t Bs[2][(BK / 8) * BN];
+    const uint32_t row0 = (uint32_t)kt * (BK / 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rw, (lds_void*)(base + wave * 1024), 16,
+                                             (int)(c.bp_off + row0 * (uint32_t)p.N * 4u), 0, 0, 0);
+    const int k = kt * BK + 32 * c.sz_group;
+    const uint32_t kill = k < p.K ? 0u : kOOB;
+    const uint32_t g = (uint32_t)(min(k, p.K - 1) / p.G);
+    char* dst = base + BP_WORD_BYTES + (2 * c.sz_group + (c.sz_is_zero ? 1 : 0)) * BP_SZ_BYTES;
+    if (c.sz_is_zero)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rz, (lds_void*)dst, 4,
+                                                 (int)(c.sz_off + g * (uint32_t)(p.N >> 3) * 4u + kill), 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (lds_void*)dst, 4,
+                                                 (int)(c.sz_off + g * (uint32_t)p.N * 2u + kill), 0, 0, 0);
+}
+
+// Dequantize this thread's 4 packed words of a tile (column n, word rows
+// r0..r0+3, all in one group) into the fp16 tile.
+__device__ __forceinline__ void dequant_tile(const char* bp, char* b16, int n, int r0, int k0, int K)
+{
+    const int gi = r0 >> 2;   // which of the tile's two group rows (equal unless groups of 32)
+    const uint16_t sb = reinterpret_cast<const uint16_t*>(bp + BP_WORD_BYTES + (2 * gi) * BP_SZ_BYTES)[n];
+    const uint32_t zw = reinterpret_cast<const uint32_t*>(bp + BP_WORD_BYTES + (2 * gi + 1) * BP_SZ_BYTES)[n >> 3];
+    const h2 hz = zero_pair((zw >> (4 * (n & 7))) & 0xFu);
+    const h2 s2 = scale_pair(sb);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(bp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        h8 v = dequant_word(words[r * BN + n], hz, s2);
+        if (k0 + 8 * r >= K) v = h8{0, 0, 0, 0, 0, 0, 0, 0};     // rows past K (tail tile)
+        // The fp16 weight tiles are never targets of the direct-to-LDS loads,
+        // but the compiler cannot prove that for a computed address and would
+        // wait for every load in flight before this store; it is issued as
+        // inline asm instead. (LDS operations complete in order, so the
+        // compiler's own lgkmcnt waits stay correct with one more in flight.)
+        const uint32_t addr = (uint32_t)(uintptr_t)(b16 + swz(n, r));
+        asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v));
+    }
+}
+
+__global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_a2[A_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_bp0[BP_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_bp1[BP_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_bp2[BP_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_w0[B16_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_w1[B16_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_w2[B16_TILE_BYTES];
+    // Stage I of each ring, chosen at compile time so that every LDS access
+    // names its __shared__ array directly.
+    auto stage_a = [&](auto I) -> char* {
+        if constexpr (decltype(I)::value == 0) return lds_a0;
+        else if constexpr (decltype(I)::value == 1) return lds_a1;
+        else return lds_a2;
+    };
+    auto stage_b = [&](auto I) -> char* {
+        if constexpr (decltype(I)::value == 0) return lds_bp0;
+        else if constexpr (decltype(I)::value == 1) return lds_bp1;
+        else return lds_bp2;
+    };
+    auto stage_w = [&](auto I) -> char* {
+        if constexpr (decltype(I)::value == 0) return lds_w0;
+        else if constexpr (decltype(I)::value == 1) return lds_w1;
+        else return lds_w2;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,7 +207,6 @@ __global__ __launch_bounds__(NT) void q4_gemm_kernel(GemmArgs p)
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lhi = lane >> 5;
 
-    // Tile order (see the header).
     const int nt = (p.N + BN - 1) / BN, mt = (p.M + BM - 1) / BM;
     const int id = blockIdx.x;
     int mtile, ntile;
@@ -133,33 +220,43 @@ __global__ __launch_bounds__(NT) void q4_gemm_kernel(GemmArgs p)
     }
     const int m0 = mtile * BM, n0 = ntile * BN;
 
-    const rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    const rsrc_t rw = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    Ctx c;
     const int ng = p.K / p.G;
-    const rsrc_t rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
-    const rsrc_t rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
-
-    Lane ln;
-    ln.a_kc = 8u * (uint32_t)(tid & 7);
+    c.rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
+    c.rw = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    c.rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
+    c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) {
-        const int row = (tid + NT * e) >> 3;
-        ln.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + ln.a_kc) * 2u;   // rows >= M fall outside x
+        // instruction e of wave w fills rows 8*(4e + w) .. +7 of the stage;
+        // lane i lands in slot i % 8 of row i / 8, which holds chunk
+        // slot ^ ((row >> 1) & 7) (see swz)
+        const int row = 8 * (4 * e + wave) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        c.a_k[e] = 8u * (uint32_t)chunk;
+        c.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + c.a_k[e]) * 2u;
     }
     {
-        const int brow = tid >> 5, n = n0 + 4 * (tid & 31);
-        ln.b_off = ((uint32_t)brow * (uint32_t)p.N + (uint32_t)n) * 4u + (n < p.N ? 0u : kOOB);
+        // packed tile: wave w fills word rows 2w, 2w+1; lane i takes 4 columns
+        const int brow = 2 * wave + (lane >> 5), col = n0 + 4 * (lane & 31);
+        c.bp_off = ((uint32_t)brow * (uint32_t)p.N + (uint32_t)col) * 4u + (col < p.N ? 0u : kOOB);
     }
-    int lane_cols[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wn * WTN + 32 * j + l32;
-        lane_cols[j] = n;
-        const uint32_t kill = n < p.N ? 0u : kOOB;
-        ln.s_off[j] = (uint32_t)n * 2u + kill;
-        ln.z_off[j] = (uint32_t)(n >> 3) * 4u + kill;
-        ln.z_shift[j] = 4u * (uint32_t)(n & 7);
+    {
+        // scales/zeros: waves 0/1 load the scale / zero row of the tile's first
+        // group, waves 2/3 those of its second group (groups of 32 rows)
+        c.sz_is_zero = (wave & 1) != 0;
+        c.sz_group = wave >> 1;
+        if (c.sz_is_zero) {
+            const int col = n0 + 8 * lane;          // zero word lane -> columns col .. col+7
+            c.sz_off = (uint32_t)(col >> 3) * 4u + (lane < 16 && col < p.N ? 0u : kOOB);
+        } else {
+            const int col = n0 + 2 * lane;          // scale pair lane -> columns col, col+1
+            c.sz_off = (uint32_t)col * 2u + (col < p.N ? 0u : kOOB);
+        }
     }
+    // dequant assignment: column dq_n of the tile, word rows dq_r0 .. dq_r0+3
+    const int dq_n = tid & (BN - 1);
+    const int dq_r0 = 4 * (tid >> 7);
 
     f16x acc[MI][NJ];
 #pragma unroll
@@ -170,60 +267,75 @@ __global__ __launch_bounds__(NT) void q4_gemm_kernel(GemmArgs p)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int ktiles = (p.K + BK - 1) / BK;
-    TileRegs tr;
-    GroupRegs gcur, gnext;
-    load_tile<NG>(tr, gcur, p, ln, rx, rw, rs, rz, 0);
-    store_tile(tr, As[0], Bs[0], tid);
-    __syncthreads();
 
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < ktiles;
-        if (more) load_tile<NG>(tr, gnext, p, ln, rx, rw, rs, rz, (kt + 1) * BK);
-        __builtin_amdgcn_sched_barrier(0);
+    // Prologue: tiles 0 and 1 in flight (packed first, then activations);
+    // packed tile 0 dequantized.
+    load_b(c, p, stage_b(I0{}), wave, 0);
+    load_a(c, p, stage_a(I0{}), wave, 0);
+    if (ktiles > 1) {
+        load_b(c, p, stage_b(I1{}), wave, 1);
+        load_a(c, p, stage_a(I1{}), wave, 1);
+    }
+    Q4_VMCNT(0);
+    lds_barrier();
+    dequant_tile(stage_b(I0{}), stage_w(I0{}), dq_n, dq_r0, 0, p.K);
 
-        h2 hz[NG][NJ], s2[NG][NJ];
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                hz[gi][j] = zero_pair((gcur.z[gi][j] >> ln.z_shift[j]) & 0xFu);
-                s2[gi][j] = scale_pair(gcur.s[gi][j]);
-            }
+    // One k-tile: S = kt % 3 is a compile-time stage index.
+    auto step = [&](auto S_tag, int kt) {
+        constexpr int S = decltype(S_tag)::value;
+        using IS = std::integral_constant<int, S>;
+        using IS1 = std::integral_constant<int, (S + 1) % STAGES>;
+        using IS2 = std::integral_constant<int, (S + 2) % STAGES>;
+        // Issue tile kt+2: packed first, then activations.
+        int n_cur = 0;
+        if (kt + 2 < ktiles) {
+            load_b(c, p, stage_b(IS2{}), wave, kt + 2);
+            load_a(c, p, stage_a(IS2{}), wave, kt + 2);
+            n_cur = A_LOADS + 2;
+        }
+        // This step reads activation tile kt (issued two steps ago) and packed
+        // tile kt+1 (issued one step ago, before that step's activations):
+        // the activation loads of tile kt+1 and this step's loads may remain.
+        wait_vm((kt + 1 < ktiles ? A_LOADS : 0) + n_cur);
+        lds_barrier();
 
-        const uint16_t* A = As[buf];
-        const uint32_t* B = Bs[buf];
+        const char* A = stage_a(IS{});
+        const char* B = stage_w(IS{});
         const int k0 = kt * BK;
+        // Rows past K hold zeros in both tiles (activation loads past K are
+        // out of range; the dequant writes zeros there), so the last tile
+        // needs no special case. The dequant of tile kt+1 runs unconditionally
+        // (past the last tile it fills a buffer nobody reads).
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
-            if (k0 + 16 * sub < p.K) {
-                const int gi = NG == 2 ? (sub >> 1) : 0;
-                h8 b[NJ];
+            if (sub == 1) {
+                // dequantize packed tile kt+1 while the matrix cores run
+                dequant_tile(stage_b(IS1{}), stage_w(IS1{}), dq_n, dq_r0, k0 + BK, p.K);
+            }
+            h8 b[NJ];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    b[j] = dequant_word(B[(2 * sub + lhi) * BN + wn * WTN + 32 * j + l32], hz[gi][j],
-                                        s2[gi][j]);
+            for (int j = 0; j < NJ; ++j)
+                b[j] = *reinterpret_cast<const h8*>(B + swz(wn * WTN + 32 * j + l32, 2 * sub + lhi));
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const h8 a = *reinterpret_cast<const h8*>(A + (wm * WTM + 32 * i + l32) * AST +
-                                                              16 * sub + 8 * lhi);
+            for (int i = 0; i < MI; ++i) {
+                const h8 a = *reinterpret_cast<const h8*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a, b[j], acc[i][j]);
-                }
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a, b[j], acc[i][j]);
             }
         }
-        if (more) {
-            store_tile(tr, As[buf ^ 1], Bs[buf ^ 1], tid);
-            gcur = gnext;
-        }
-        __syncthreads();
+        lds_barrier();
+    };
+    for (int kt = 0; kt < ktiles; kt += STAGES) {
+        step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < ktiles) step(std::integral_constant<int, 1>{}, kt + 1);
+        if (kt + 2 < ktiles) step(std::integral_constant<int, 2>{}, kt + 2);
     }
 
     // Epilogue: fp32 bias, one round-to-nearest-even cast, store. Lane l holds
     // rows 8*(r/4) + 4*(l/32) + r%4 of column l%32 of each 32 x 32 tile.
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int n = lane_cols[j];
+        const int n = n0 + wn * WTN + 32 * j + l32;
         if (n >= p.N) continue;
         const float bv = p.bias ? f16_bits_to_f32(p.bias[n]) : 0.f;
 #pragma unroll
@@ -240,7 +352,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_kernel(GemmArgs p)
 
 namespace q4 {
 
-hipError_t launch_gemm(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                        int M, hipStream_t stream)
 {
     GemmArgs p;
@@ -255,12 +367,7 @@ hipError_t launch_gemm(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     p.N = h->N;
     p.G = h->G;
     const int tiles = ((h->N + BN - 1) / BN) * ((M + BM - 1) / BM);
-    // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
-    // change once inside it.
-    if (h->G % BK != 0 && h->G != h->K)
-        hipLaunchKernelGGL(q4_gemm_kernel<2>, dim3(tiles), dim3(NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL(q4_gemm_kernel<1>, dim3(tiles), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(q4_gemm_dma_kernel, dim3(tiles), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 

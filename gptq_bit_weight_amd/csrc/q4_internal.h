@@ -40,6 +40,7 @@ struct q4_matrix {
     int K = 0, N = 0, G = 0, ng = 0;
     int act_order = 0;
     int device = -1;
+    int num_cu = 256;
     uint32_t* qweight = nullptr;   // [K/8][N], nibble slots interleaved (see q4_device.h)
     uint16_t* scales = nullptr;    // [ng][N] fp16
     uint32_t* qzeros = nullptr;    // [ng][N/8]

@@ -128,9 +128,11 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
 /*
  * q4_matmul_ex -- q4_matmul_bias with explicit kernel choice, for tests and
  * tuning: path = 0 (automatic, as q4_matmul), Q4_PATH_GEMV (needs
- * 1 <= M <= Q4_GEMV_MAX_M) or Q4_PATH_MFMA (any M >= 1); splits = 0
- * (planned) or 1..16 K splits for the skinny kernel (ignored by the GEMM).
- * Results differ between paths and split counts only by fp32 rounding.
+ * 1 <= M <= Q4_GEMV_MAX_M) or Q4_PATH_MFMA (any M >= 1). splits: for the
+ * skinny kernel 0 (planned) or 1..16 K splits; for the GEMM 0 (automatic),
+ * 1 (register-staged tiles) or 2 (direct-to-LDS pipeline), else
+ * Q4_ERR_INVALID_ARG. Results differ between paths, split counts and
+ * variants only by fp32 rounding.
  */
 q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
                        uint16_t* out, int M, int path, int splits, hipStream_t stream);

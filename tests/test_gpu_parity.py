@@ -95,16 +95,33 @@ GEMM_CASES = [
 ]
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("K,N,G,M,act,bias", GEMM_CASES)
-def test_gemm_parity(K, N, G, M, act, bias):
+def test_gemm_parity(K, N, G, M, act, bias, variant):
+    """variant 0: automatic; 1: register-staged tiles; 2: direct-to-LDS pipeline."""
     import gptq_bit_weight_amd as q4
     L = _layer(K, N, G, M, 2, act_order=act, bias=bias)
-    announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias}")
+    announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias} variant={variant}")
     W = make_matrix(L)
     assert W.path_for(M) == q4.PATH_MFMA
-    y = run(L, W=W)
+    y = run(L, W=W, path=q4.PATH_MFMA, splits=variant)
     yD, A = oracle_full(L)
-    compare(y, yD, A, f"gemm K={K} N={N} G={G} M={M}")
+    compare(y, yD, A, f"gemm K={K} N={N} G={G} M={M} variant={variant}")
+
+
+def test_gemm_variants_bit_identical():
+    """Both GEMM variants accumulate each output over k in the same order with
+    the same MFMA shape, so their results must agree bit for bit."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(1024, 520, 128, 300, 21, bias=True)
+    announce("gemm variants")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=1)
+    b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
@@ -221,6 +238,8 @@ def test_m_zero_and_argument_errors():
         W.matmul(torch.zeros((17, 256), dtype=torch.float16, device="cuda"), path=q4.PATH_GEMV)
     with pytest.raises(ValueError):
         W.matmul(t["x"], splits=17)
+    with pytest.raises(ValueError):
+        W.matmul(t["x"], path=q4.PATH_MFMA, splits=3)
     bad = torch.full((256,), 3, dtype=torch.int32, device="cuda")      # only groups 0, 1
     with pytest.raises(ValueError, match="outside"):
         q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], bad, groupsize=128)
