@@ -10,16 +10,19 @@ back through the C ABI (q4_matmul_bias). The value is effective HBM
 bandwidth: bytes of packed weights + scales + packed zeros per step divided by
 the time per step. Inputs are resident in HBM before timing starts. To keep
 the 256 MB last-level cache from serving the weights, the steps rotate over
-ten handle copies of the block (1.05 GB). By default each step is replayed
-from a HIP graph (one graph per copy, captured on the timing stream) so that
-the host launch rate does not bound a ~20 us step; --eager launches directly.
+ten handle copies of the block (1.05 GB). By default the steps are replayed
+from HIP graphs captured on the timing stream (one graph of ten consecutive
+steps, one per copy for a remainder) so that neither the host launch rate nor
+a per-graph launch cost bounds a ~35 us step; --eager launches directly.
 
 Also reported on the same JSON line:
   roofline      the skinny kernel's achieved bandwidth: algorithmic bytes per
                 launch / mean launch duration, from HIP events around graph
-                replays of each layer's launches on the launch stream; traffic
-                comes from committed rocprofv3 counter runs, when their kernel
-                source hash matches the current source, else null;
+                replays of each layer's launches on the launch stream (each
+                layer rotating over >= 1 GiB of weight copies, so the weights
+                come from HBM as in the block steps); traffic comes from
+                committed rocprofv3 counter runs, when their kernel source hash
+                matches the current source, else null;
   cpu_baseline  the CPU oracle's fused route on whole layers of the block;
   secondary     the 70B-shaped MLP layers at M = 1 and the prefill GEMM at
                 M = 2048 (TFLOPS against the dense fp16 MFMA peak).
@@ -63,13 +66,12 @@ class Layer:
 
     def __init__(self, q4, torch, name, L, copies):
         dev = torch.device("cuda", 0)
-        qw = torch.from_numpy(L.qweight).to(dev)
-        qz = torch.from_numpy(L.qzeros).to(dev)
-        sc = torch.from_numpy(L.scales).to(dev)
-        gi = torch.from_numpy(L.g_idx).to(dev) if L.g_idx is not None else None
+        self.q4 = q4
+        self.src = (torch.from_numpy(L.qweight).to(dev), torch.from_numpy(L.qzeros).to(dev),
+                    torch.from_numpy(L.scales).to(dev),
+                    torch.from_numpy(L.g_idx).to(dev) if L.g_idx is not None else None)
         self.name, self.K, self.N, self.G, self.M = name, L.K, L.N, L.G, L.M
-        self.mats = [q4.Q4Matrix(qw, qz, sc, gi, groupsize=L.G) for _ in range(copies)]
-        del qw, qz, sc, gi
+        self.mats = [self._make() for _ in range(copies)]
         self.x = torch.from_numpy(L.x).to(dev)
         self.bias = torch.from_numpy(L.bias).to(dev) if L.bias is not None else None
         self.out = torch.empty((L.M, L.N), dtype=torch.float16, device=dev)
@@ -79,6 +81,19 @@ class Layer:
         self.bp = ctypes.c_void_p(self.bias.data_ptr()) if self.bias is not None else None
         self.op = ctypes.c_void_p(self.out.data_ptr())
 
+    def _make(self):
+        qw, qz, sc, gi = self.src
+        return self.q4.Q4Matrix(qw, qz, sc, gi, groupsize=self.G)
+
+    def grow(self, copies):
+        """Make handle copies until there are `copies` of them."""
+        while len(self.mats) < copies:
+            self.mats.append(self._make())
+
+    def shrink(self, copies):
+        while len(self.mats) > copies:
+            self.mats.pop().close()
+
     def launch(self, lib, copy, stream_ptr):
         st = lib.q4_matmul_bias(self.mats[copy]._h, self.xp, self.bp, self.op, self.M, stream_ptr)
         if st:
@@ -87,6 +102,7 @@ class Layer:
     def close(self):
         for m in self.mats:
             m.close()
+        self.mats = []
 
 
 def build_layers(q4, torch, synth, specs, G, M, workload, copies):
@@ -97,15 +113,20 @@ def build_layers(q4, torch, synth, specs, G, M, workload, copies):
     return layers
 
 
-def per_launch_times(lib, torch, layers, copies, rounds, stream):
-    """Mean kernel duration of each layer: `rounds * copies` launches of the
-    layer (rotating over its weight copies) captured in one HIP graph on the
-    launch stream and replayed between two events. Consecutive kernels of a
-    graph start back to back, so elapsed / launches is the mean launch
-    duration (it matches the kernel-trace durations of rocprofv3)."""
+def per_launch_times(lib, torch, layers, min_launches, stream):
+    """Mean kernel duration of each layer, with its weights coming from HBM:
+    the layer's launches rotate over ceil(1 GiB / layer bytes) handle copies
+    (made for this measurement and freed after it), at least `min_launches`
+    of them, captured in one HIP graph on the launch stream and replayed
+    between two events. Consecutive kernels of a graph start back to back, so
+    elapsed / launches is the mean launch duration (the figure the kernel
+    trace of rocprofv3 reports for the same launches)."""
     out = []
-    n = rounds * copies
     for ly in layers:
+        base = len(ly.mats)
+        copies = max(base, math.ceil(MALL_DEFEAT_BYTES / ly.bytes))
+        ly.grow(copies)
+        n = copies * max(1, math.ceil(min_launches / copies))
         with torch.cuda.stream(stream):
             sp = ctypes.c_void_p(stream.cuda_stream)
             for c in range(copies):
@@ -126,6 +147,8 @@ def per_launch_times(lib, torch, layers, copies, rounds, stream):
         stream.synchronize()
         out.append(a.elapsed_time(b) * 1e-3 / n)
         del g
+        ly.shrink(base)
+        torch.cuda.empty_cache()
     return out
 
 
@@ -143,6 +166,8 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
             for s in range(copies):         # first calls happen eagerly (allocations, if any)
                 eager_step(s)
         stream.synchronize()
+        # one graph per copy (one step each) and one graph of `copies`
+        # consecutive steps, so that a graph launch is not paid per step
         graphs = []
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
@@ -151,23 +176,36 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
                 for ly in layers:
                     ly.launch(lib, c, cap)
             graphs.append(g)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for c in range(copies):
+                for ly in layers:
+                    ly.launch(lib, c, cap)
+        graphs.append(g)
 
-    def step(s):
-        if graphs is not None:
-            graphs[s % copies].replay()
-        else:
-            eager_step(s)
+    def run(first, count):
+        """Steps first .. first+count-1 (step s uses weight copy s % copies)."""
+        s = first
+        while s < first + count:
+            if graphs is None:
+                eager_step(s)
+                s += 1
+            elif s % copies == 0 and s + copies <= first + count:
+                graphs[copies].replay()
+                s += copies
+            else:
+                graphs[s % copies].replay()
+                s += 1
 
     with torch.cuda.stream(stream):
-        for s in range(warmup):
-            step(s)
+        run(0, warmup)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         wall0 = time.perf_counter()
         t0.record(stream)
-        for s in range(steps):
-            step(warmup + s)
+        run(warmup, steps)
         t1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -176,11 +214,12 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
 
 def cpu_baseline(synth, oracle, specs, G, workload, budget_s):
     """The oracle's fused route on whole layers of the block at M = 1, layers
-    in block order and repeated, until budget_s of CPU time has passed."""
+    in block order and repeated (at least one whole block), until budget_s of
+    CPU time has passed."""
     done_bytes, elapsed, layers_done = 0, 0.0, 0
     cache = {}
     i = 0
-    while elapsed < budget_s and layers_done < 70:
+    while elapsed < budget_s or layers_done < len(specs):
         name, K, N, bias = specs[i % len(specs)]
         if name not in cache:
             cache[name] = synth.make_layer(K, N, G, 1, seed=synth.layer_seed(workload, name, 1),
@@ -326,8 +365,9 @@ def main():
         return
 
     log("[bench] per-launch event timing")
-    lt = per_launch_times(lib, torch, layers, copies, rounds=20, stream=stream)
+    lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
     kern_bytes = sum(ly.bytes for ly in layers)
+    n_layers = len(layers)
     kern_time = sum(lt)
     achieved = kern_bytes / kern_time / 1e9
 
@@ -382,7 +422,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": round(kern_bytes / len(layers)),
+            "algorithmic_bytes_per_launch": round(kern_bytes / n_layers),
             "per_layer_us": {ly_name: round(t * 1e6, 3)
                              for (ly_name, _, _, _), t in zip(synth.LLAMA7B_BLOCK, lt)},
             "source_hash": src_hash,

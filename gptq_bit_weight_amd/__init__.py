@@ -20,7 +20,7 @@ from typing import Optional
 
 __all__ = [
     "Q4Matrix", "Q4Error", "load_library", "library_path", "check_shape", "plan_actorder",
-    "plan_splits", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
+    "plan_gemv", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
 EXPORTED_SYMBOLS = (
     "q4_make", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
-    "q4_plan_actorder", "q4_plan_splits",
+    "q4_plan_actorder", "q4_plan_gemv",
 )
 
 _lib = None
@@ -65,7 +65,7 @@ def load_library():
     lib.q4_make.restype = P
     lib.q4_matmul.argtypes = [P, P, P, I, P]
     lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
-    lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, P]
+    lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, I, P]
     for f in (lib.q4_matmul, lib.q4_matmul_bias, lib.q4_matmul_ex):
         f.restype = I
     lib.q4_free.argtypes = [P]
@@ -85,8 +85,8 @@ def load_library():
     lib.q4_check_shape.restype = I
     lib.q4_plan_actorder.argtypes = [P, I, I, P, ctypes.POINTER(I)]
     lib.q4_plan_actorder.restype = I
-    lib.q4_plan_splits.argtypes = [I, I, I, I]
-    lib.q4_plan_splits.restype = I
+    lib.q4_plan_gemv.argtypes = [I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.q4_plan_gemv.restype = I
     _lib = lib
     return lib
 
@@ -126,8 +126,14 @@ def plan_actorder(g_idx, K: int, groupsize: int):
     return perm, bool(triv.value)
 
 
-def plan_splits(M: int, K: int, N: int, groupsize: int) -> int:
-    return int(load_library().q4_plan_splits(M, K, N, groupsize))
+def plan_gemv(M: int, K: int, N: int, groupsize: int, num_cu: int = 256) -> tuple:
+    """(column tiles per wave, K splits) the skinny kernel uses for this shape
+    on a chip of num_cu CUs."""
+    lib = load_library()
+    ct, sp = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.q4_plan_gemv(M, K, N, groupsize, num_cu, ctypes.byref(ct), ctypes.byref(sp)),
+           "q4_plan_gemv")
+    return int(ct.value), int(sp.value)
 
 
 # ---------------------------------------------------------------- device ---
@@ -205,8 +211,14 @@ class Q4Matrix:
     def path_for(self, M: int) -> int:
         return int(load_library().q4_path_for(self._handle(), M))
 
-    def matmul(self, x, bias=None, out=None, *, path: int = 0, splits: int = 0, stream=None):
-        """out[M, N] = fp16(x[M, K] @ W (+ bias)); fp32 accumulation."""
+    def matmul(self, x, bias=None, out=None, *, path: int = 0, variant: int = 0, splits: int = 0,
+               stream=None):
+        """out[M, N] = fp16(x[M, K] @ W (+ bias)); fp32 accumulation.
+
+        path: 0 automatic, PATH_GEMV or PATH_MFMA. variant: skinny kernel --
+        16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 automatic,
+        1 register-staged, 2 direct-to-LDS. splits: skinny kernel K splits
+        (0 planned, 1..16); must be 0 for the GEMM."""
         torch = _torch()
         h = self._handle()
         _dev_tensor(x, torch.float16, "x")
@@ -224,7 +236,7 @@ class Q4Matrix:
                 raise ValueError(f"{nm} is on {t.device}, the matrix on {self.device}")
         with torch.cuda.device(self.device):
             st = load_library().q4_matmul_ex(h, x.data_ptr(), bias.data_ptr() if bias is not None
-                                             else None, out.data_ptr(), M, path, splits,
+                                             else None, out.data_ptr(), M, path, variant, splits,
                                              _stream_ptr(stream))
         _check(st, "q4_matmul")
         return out

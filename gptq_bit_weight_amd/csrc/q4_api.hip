@@ -10,7 +10,7 @@
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int splits, hipStream_t stream);
+                       int M, int col_tiles, int splits, hipStream_t stream);
 hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                            int M, hipStream_t stream);
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
@@ -106,13 +106,13 @@ q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_
         return s;
     };
     hipError_t e;
-    const size_t words = (size_t)(K / 8) * N;
+    const size_t words = packed_words(K, N);
     if ((e = hipMalloc(&h->qweight, words * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qweight"));
     if ((e = hipMalloc(&h->scales, (size_t)ng * N * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
     if ((e = hipMalloc(&h->qzeros, (size_t)ng * (N / 8) * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
     if ((e = hipMalloc(&h->partials, (size_t)kMaxSplits * 16 * N * 4)) != hipSuccess)
         return bail(hip_fail(e, "q4_make: workspace"));
-    const int col_tiles = (N + kColTile - 1) / kColTile;
+    const int col_tiles = (N + 15) / 16;
     if ((e = hipMalloc(&h->counters, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
     if ((e = hipMemset(h->counters, 0, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
     if (act) {
@@ -134,12 +134,6 @@ q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_
     if ((e = hipDeviceSynchronize()) != hipSuccess) return bail(hip_fail(e, "q4_make: repack"));
     *out = h;
     return Q4_OK;
-}
-
-int env_int(const char* name, int dflt)
-{
-    const char* v = getenv(name);
-    return v && *v ? atoi(v) : dflt;
 }
 
 int choose_path(const q4_matrix* h, int M, int forced)
@@ -168,7 +162,7 @@ q4_status ensure_xperm(const q4_matrix* h, int M)
 }
 
 q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                      int M, int path, int splits, hipStream_t stream)
+                      int M, int path, int variant, int splits, hipStream_t stream)
 {
     if (!h) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: null handle");
     if (M < 0) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: M=%d is negative", M);
@@ -188,10 +182,17 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
     if (kind < 0)
         return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the skinny kernel takes M <= %d (M=%d)",
                     Q4_GEMV_MAX_M, M);
-    if (splits < 0 || splits > kMaxSplits)
-        return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
-    if (kind == Q4_PATH_MFMA && splits > 2)
-        return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1 or 2", splits);
+    if (kind == Q4_PATH_GEMV) {
+        if (splits < 0 || splits > kMaxSplits)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
+        if (variant != 0 && variant != 1 && variant != 2 && variant != 4)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: skinny-kernel tiles %d not 0, 1, 2 or 4", variant);
+    } else {
+        if (splits != 0)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the GEMM takes no K splits (got %d)", splits);
+        if (variant < 0 || variant > 2)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1 or 2", variant);
+    }
 
     const uint16_t* xe = x;
     if (h->act_order) {
@@ -201,15 +202,16 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         xe = h->xperm;
     }
     if (kind == Q4_PATH_GEMV) {
-        int s = splits ? splits : env_int("Q4_SPLITS", 0);
-        if (s <= 0 || s > kMaxSplits) s = plan_splits(M, h->K, h->N, h->G);
-        Q4_HIP(launch_gemv(h, xe, bias, out, M, s, stream), "q4_matmul: gemv launch");
+        int ct = 0, s = 0;
+        plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
+        if (variant) ct = variant;
+        if (splits) s = splits;
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, stream), "q4_matmul: gemv launch");
     } else {
         // Two GEMM variants: register-staged tiles (80 KiB of LDS, two
         // workgroups per CU) when there are at least two output tiles per CU,
         // else the direct-to-LDS pipeline (one workgroup per CU, deeper
-        // prefetch). `splits` picks one explicitly (1 or 2) for tests.
-        int variant = splits;
+        // prefetch). `variant` picks one explicitly (1 or 2).
         if (variant == 0) {
             const long long tiles = (long long)((h->N + kGemmBN - 1) / kGemmBN) * ((M + kGemmBM - 1) / kGemmBM);
             variant = tiles >= 2LL * h->num_cu ? 1 : 2;
@@ -236,21 +238,21 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
 
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M, hipStream_t stream)
 {
-    return q4::matmul_impl(h, x, nullptr, out, M, 0, 0, stream);
+    return q4::matmul_impl(h, x, nullptr, out, M, 0, 0, 0, stream);
 }
 
 q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                          int M, hipStream_t stream)
 {
-    return q4::matmul_impl(h, x, bias, out, M, 0, 0, stream);
+    return q4::matmul_impl(h, x, bias, out, M, 0, 0, 0, stream);
 }
 
 q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int path, int splits, hipStream_t stream)
+                       int M, int path, int variant, int splits, hipStream_t stream)
 {
     if (path != 0 && path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_matmul_ex: unknown path %d", path);
-    return q4::matmul_impl(h, x, bias, out, M, path, splits, stream);
+    return q4::matmul_impl(h, x, bias, out, M, path, variant, splits, stream);
 }
 
 void q4_free(q4_matrix* h) { q4::destroy(h); }

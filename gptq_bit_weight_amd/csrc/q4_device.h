@@ -34,7 +34,6 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 __host__ __device__ constexpr int slot_of(int i) { return (i >> 1) + 4 * (i & 1); }
 
 constexpr uint32_t kMagic2 = 0x64006400u;     // (1024.0, 1024.0) in fp16
-constexpr uint32_t kLowNibbles = 0x000F000Fu;
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& f)
@@ -43,10 +42,20 @@ __device__ __forceinline__ To bitcast(const From& f)
     return __builtin_bit_cast(To, f);
 }
 
-// (1024 + z) in both halves.
-__device__ __forceinline__ h2 zero_pair(uint32_t z)
+// The zero point z of a column in the two forms the unpack subtracts: 1024 + z
+// and -(64 + z), each in both halves. (64 + z has binary16 exponent 6, whose
+// fraction ulp is 1/16, so its bits are 0x5400 + 16 z.)
+struct zero_t {
+    h2 hz;     // 1024 + z
+    h2 nz16;   // -(64 + z)
+};
+
+__device__ __forceinline__ zero_t zero_pair(uint32_t z)
 {
-    return bitcast<h2>((z | 0x6400u) * 0x00010001u);
+    zero_t r;
+    r.hz = bitcast<h2>((z | 0x6400u) * 0x00010001u);
+    r.nz16 = bitcast<h2>((0xD400u + (z << 4)) * 0x00010001u);
+    return r;
 }
 
 // s in both halves (s given as binary16 bits).
@@ -66,43 +75,44 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
     return r;
 }
 
-// Dequantize one private-layout word into eight fp16 values in k order.
-__device__ __forceinline__ h8 dequant_word(uint32_t w, h2 hz, h2 s2)
+// Unpack one private-layout word and subtract the zero point: eight fp16
+// values (q - z) in k order, each a small integer, exact in fp16
+// (|q - z| <= 15). Pair j (k-offsets 2j, 2j + 1) sits in nibble slots j and
+// j + 4, i.e. bits 4j and 16 + 4j:
+//  * pairs 0 and 2 (bits 0 and 16 of w and of w >> 8) are OR-ed into the
+//    fraction of 0x6400, giving 1024 + q, and (1024 + q) - (1024 + z) is
+//    exact;
+//  * pairs 1 and 3 are masked where they sit (bits 4 and 20), giving
+//    1024 + 16 q, and one fused multiply-add (1024 + 16 q) / 16 - (64 + z) =
+//    q - z is exact as well (a power-of-two scaling and a sum of small
+//    integers), which saves the shifts that would line them up.
+__device__ __forceinline__ h8 sub_zero_word(uint32_t w, zero_t z)
 {
     const uint32_t magic = kMagic2;
-    h8 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t u = and_or(w >> (4 * j), kLowNibbles, magic);
-        const h2 v = (bitcast<h2>(u) - hz) * s2;
-        r[2 * j] = v[0];
-        r[2 * j + 1] = v[1];
-    }
-    return r;
+    const uint32_t w8 = w >> 8;
+    const h2 sixteenth = bitcast<h2>(0x2C002C00u);     // (1/16, 1/16)
+    const h2 v0 = bitcast<h2>(and_or(w, 0x000F000Fu, magic)) - z.hz;
+    const h2 v1 = __builtin_elementwise_fma(bitcast<h2>(and_or(w, 0x00F000F0u, magic)), sixteenth, z.nz16);
+    const h2 v2 = bitcast<h2>(and_or(w8, 0x000F000Fu, magic)) - z.hz;
+    const h2 v3 = __builtin_elementwise_fma(bitcast<h2>(and_or(w8, 0x00F000F0u, magic)), sixteenth, z.nz16);
+    return h8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
-// Unpack one private-layout word and subtract the zero point: eight fp16
-// values (q - z) in k order. Every value is a small integer, exact in fp16
-// (|q - z| <= 15).
-__device__ __forceinline__ h8 sub_zero_word(uint32_t w, h2 hz)
+// Dequantize one private-layout word into eight fp16 values in k order:
+// RNE(s * (q - z)), the exact difference times the scale, rounded once.
+__device__ __forceinline__ h8 dequant_word(uint32_t w, zero_t z, h2 s2)
 {
-    const uint32_t magic = kMagic2;
-    h8 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t u = and_or(w >> (4 * j), kLowNibbles, magic);
-        const h2 v = bitcast<h2>(u) - hz;
-        r[2 * j] = v[0];
-        r[2 * j + 1] = v[1];
-    }
-    return r;
+    const h8 d = sub_zero_word(w, z);
+    const h8 s8 = h8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]};
+    return d * s8;
 }
 
 // ---- raw buffer loads ------------------------------------------------------
 // A raw buffer descriptor carries the byte size of the tensor; a load whose
 // per-lane offset lies at or beyond it returns zeros without touching memory.
 // The kernels use that for ragged edges instead of branches: an invalid lane
-// or k-step gets an offset of at least kOOB (2^31; every tensor is smaller).
+// or k-step gets an offset of at least kOOB (2^31; every tensor is smaller),
+// or a whole wave's load goes through a descriptor of size 0.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr uint32_t kOOB = 0x80000000u;
@@ -113,24 +123,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferDword3);
 }
 
-__device__ __forceinline__ u4 buf_load16(rsrc_t r, uint32_t off)
+// off: per-lane byte offset; soff: a wave-uniform byte offset added to it
+// (held in a scalar register, so a per-block step costs no vector ALU).
+__device__ __forceinline__ u4 buf_load16(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return bitcast<u4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return bitcast<u4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
 }
 
-__device__ __forceinline__ u2 buf_load8(rsrc_t r, uint32_t off)
+__device__ __forceinline__ u2 buf_load8(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return bitcast<u2>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return bitcast<u2>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0));
 }
 
-__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off)
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0);
 }
 
-__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off)
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
 }
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c)

@@ -19,7 +19,10 @@
 // and no registers carry the tiles):
 //  * activations (256 x 64 fp16) and packed weights (8 x 128 words plus the
 //    tile's scale and zero rows) each use a ring of 3 LDS stages and are
-//    loaded 2 tiles ahead. Each stage is its own __shared__ array and the
+//    loaded 2 tiles ahead. A k-tile's packed words are 8 contiguous bytes of
+//    each 16-byte chunk (kb, n) of the private layout (words i = 2h, 2h + 1
+//    of k-block b for k-tile 2b + h); they land in LDS as [kb][n][2], and
+//    tile row r (rows 8r .. 8r+7 of the tile) is word r >> 2 of chunk r & 3. Each stage is its own __shared__ array and the
 //    k-loop is unrolled by 3, so the compiler can see that the LDS reads of
 //    one stage never alias the loads landing in another and does not wait
 //    for them;
@@ -58,7 +61,9 @@ constexpr int BP_SZ_BYTES = 256;                    // one row of scales or zero
 constexpr int BP_TILE_BYTES = BP_WORD_BYTES + 4 * BP_SZ_BYTES;   // + scales/zeros of 2 groups
 constexpr int B16_TILE_BYTES = BN * BK * 2;        // 16 KiB
 constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);  // 8 direct loads per thread
-static_assert(BP_WORD_BYTES == NT * 16, "one packed-weight load per thread");
+constexpr int BP_LOADS = BP_WORD_BYTES / (NT * 4);  // 4-byte packed-word loads per thread
+constexpr int B_LOADS = BP_LOADS + 1;               // + one scale or zero-word load
+static_assert(BP_LOADS == 4, "one packed-word load per chunk row kb");
 static_assert(BK == 64 && BN == 128 && NT == 256, "index arithmetic below assumes these");
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -84,9 +89,9 @@ __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 12
 __device__ __forceinline__ void wait_vm(int n)
 {
     switch (n) {
-    case 8: Q4_VMCNT(8); break;
-    case 10: Q4_VMCNT(10); break;
-    case 18: Q4_VMCNT(18); break;
+    case A_LOADS: Q4_VMCNT(A_LOADS); break;
+    case A_LOADS + B_LOADS: Q4_VMCNT(A_LOADS + B_LOADS); break;
+    case 2 * A_LOADS + B_LOADS: Q4_VMCNT(2 * A_LOADS + B_LOADS); break;
     default: Q4_VMCNT(0); break;
     }
 }
@@ -106,7 +111,8 @@ struct Ctx {
     rsrc_t rx, rw, rs, rz;
     uint32_t a_off[A_LOADS];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
     uint32_t a_k[A_LOADS];     // k of each chunk for k0 = 0
-    uint32_t bp_off;           // packed-weight byte offset for k0 = 0 (column kill folded in)
+    uint32_t bp_off;           // packed-weight byte offset of this lane's word in k-tile 0, kb = 0
+    uint32_t bp_kill;          // kOOB for a column past N
     uint32_t sz_off;           // scale or zero-word byte offset of this lane (row 0, kill folded in)
     bool sz_is_zero;           // this wave loads zero words (else scales)
     int sz_group;              // 0: first group of the tile, 1: second (groups of 32 rows)
@@ -126,13 +132,17 @@ __device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* ds
 }
 
 // Direct-to-LDS loads of packed tile kt into stage st: the packed words (one
-// 16-byte load per thread) and one row of scales or zero words per wave
-// (2 loads per thread).
+// 4-byte load per chunk row kb per thread; instruction kb of wave w fills
+// 256 bytes of the [kb][n][2] layout) and one row of scales or zero words
+// per wave (B_LOADS loads per thread).
 __device__ __forceinline__ void load_b(const Ctx& c, const GemmArgs& p, char* base, int wave, int kt)
 {
-    const uint32_t row0 = (uint32_t)kt * (BK / 8);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rw, (lds_void*)(base + wave * 1024), 16,
-                                             (int)(c.bp_off + row0 * (uint32_t)p.N * 4u), 0, 0, 0);
+    const uint32_t tile_off = (uint32_t)(kt >> 1) * (uint32_t)p.N * 64u + 8u * (uint32_t)(kt & 1);
+#pragma unroll
+    for (int kb = 0; kb < BP_LOADS; ++kb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.rw, (lds_void*)(base + (kb * 4 + wave) * 256), 4,
+            (int)((c.bp_off + (uint32_t)kb * (uint32_t)p.N * 16u + tile_off) | c.bp_kill), 0, 0, 0);
     const int k = kt * BK + 32 * c.sz_group;
     const uint32_t kill = k < p.K ? 0u : kOOB;
     const uint32_t g = (uint32_t)(min(k, p.K - 1) / p.G);
@@ -152,13 +162,13 @@ __device__ __forceinline__ void dequant_tile(const char* bp, char* b16, int n, i
     const int gi = r0 >> 2;   // which of the tile's two group rows (equal unless groups of 32)
     const uint16_t sb = reinterpret_cast<const uint16_t*>(bp + BP_WORD_BYTES + (2 * gi) * BP_SZ_BYTES)[n];
     const uint32_t zw = reinterpret_cast<const uint32_t*>(bp + BP_WORD_BYTES + (2 * gi + 1) * BP_SZ_BYTES)[n >> 3];
-    const h2 hz = zero_pair((zw >> (4 * (n & 7))) & 0xFu);
+    const zero_t hz = zero_pair((zw >> (4 * (n & 7))) & 0xFu);
     const h2 s2 = scale_pair(sb);
     const uint32_t* words = reinterpret_cast<const uint32_t*>(bp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
-        h8 v = dequant_word(words[r * BN + n], hz, s2);
+        h8 v = dequant_word(words[((r & 3) * BN + n) * 2 + (r >> 2)], hz, s2);
         if (k0 + 8 * r >= K) v = h8{0, 0, 0, 0, 0, 0, 0, 0};     // rows past K (tail tile)
         // The fp16 weight tiles are never targets of the direct-to-LDS loads,
         // but the compiler cannot prove that for a computed address and would
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
     Ctx c;
     const int ng = p.K / p.G;
     c.rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    c.rw = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    c.rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * 64u);
     c.rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
     c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
 #pragma unroll
@@ -237,9 +247,11 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
         c.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + c.a_k[e]) * 2u;
     }
     {
-        // packed tile: wave w fills word rows 2w, 2w+1; lane i takes 4 columns
-        const int brow = 2 * wave + (lane >> 5), col = n0 + 4 * (lane & 31);
-        c.bp_off = ((uint32_t)brow * (uint32_t)p.N + (uint32_t)col) * 4u + (col < p.N ? 0u : kOOB);
+        // packed tile: lane pair (2i, 2i + 1) of wave w takes the two words of
+        // column n0 + 32w + i
+        const int col = n0 + 32 * wave + (lane >> 1);
+        c.bp_off = (uint32_t)col * 16u + 4u * (uint32_t)(lane & 1);
+        c.bp_kill = col < p.N ? 0u : kOOB;
     }
     {
         // scales/zeros: waves 0/1 load the scale / zero row of the tile's first
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
         if (kt + 2 < ktiles) {
             load_b(c, p, stage_b(IS2{}), wave, kt + 2);
             load_a(c, p, stage_a(IS2{}), wave, kt + 2);
-            n_cur = A_LOADS + 2;
+            n_cur = A_LOADS + B_LOADS;
         }
         // This step reads activation tile kt (issued two steps ago) and packed
         // tile kt+1 (issued one step ago, before that step's activations):

@@ -20,7 +20,10 @@
 // row stride padded to 72 halfs so 16-byte LDS reads of 8 consecutive rows
 // hit distinct banks) and the packed weight tile (8 x 128 words) are
 // double-buffered in LDS; the next tile's global loads are in flight while
-// the current one is multiplied.
+// the current one is multiplied. A k-tile's packed words are 8 contiguous
+// bytes of each 16-byte chunk (kb, n) of the private layout (words 2h, 2h + 1
+// of k-block b for k-tile 2b + h); in LDS they are stored as [kb][h'][n], so
+// tile row r (rows 8r .. 8r+7 of the tile) is row (r & 3) * 2 + (r >> 2).
 //
 // Global loads are bounds-checked raw buffer loads (out-of-range offsets
 // read zeros), so ragged M, N and K need no branches.
@@ -46,7 +49,7 @@ constexpr int WTN = BN / 2;          // wave tile columns
 constexpr int MI = WTM / 32;         // 32x32 MFMA tiles per wave along M
 constexpr int NJ = WTN / 32;         // ... along N
 constexpr int A_LOADS = BM * BK / 8 / NT;    // 16-byte activation loads per thread per tile
-static_assert(BN * BK / 8 / 4 == NT, "one 16-byte weight load per thread per tile");
+static_assert(BN * BK / 8 / 4 == NT, "two 8-byte (two-word) weight loads per thread per tile");
 
 struct GemmArgs {
     const uint32_t* qweight;
@@ -60,7 +63,7 @@ struct GemmArgs {
 
 struct TileRegs {
     u4 a[A_LOADS];
-    u4 b;
+    u2 b[2];       // words (2h, 2h + 1) of chunk (kb, n), n = two adjacent columns
 };
 
 // Scales/zeros of the NJ columns a lane multiplies, for up to two groups of a
@@ -73,7 +76,8 @@ struct GroupRegs {
 struct Lane {
     uint32_t a_off[A_LOADS];   // activation byte offsets (k0 = 0)
     uint32_t a_kc;             // k offset (rows) of this thread's activation chunks
-    uint32_t b_off;            // weight byte offset (k0 = 0), column kill folded in
+    uint32_t b_off[2];         // weight byte offsets of the two chunks (k-tile 0)
+    uint32_t b_kill[2];        // kOOB for a column past N
     uint32_t s_off[NJ];        // scale byte offsets (group 0)
     uint32_t z_off[NJ];        // zero-word byte offsets (group 0)
     uint32_t z_shift[NJ];
@@ -87,7 +91,9 @@ __device__ __forceinline__ void load_tile(TileRegs& t, GroupRegs& gr, const Gemm
     const uint32_t a_kill = (ln.a_kc + (uint32_t)k0 < (uint32_t)p.K) ? 0u : kOOB;
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) t.a[e] = buf_load16(rx, ln.a_off[e] + (uint32_t)k0 * 2u + a_kill);
-    t.b = buf_load16(rw, ln.b_off + (uint32_t)(k0 >> 3) * (uint32_t)p.N * 4u);
+    const uint32_t tile_off = (uint32_t)(k0 >> 7) * (uint32_t)p.N * 64u + 8u * (uint32_t)((k0 >> 6) & 1);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) t.b[v] = buf_load8(rw, (ln.b_off[v] + tile_off) | ln.b_kill[v]);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         const int k = k0 + 32 * gi;
@@ -108,8 +114,9 @@ __device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* As, uint
         const int row = c >> 3, kc = c & 7;
         *reinterpret_cast<u4*>(As + row * AST + 8 * kc) = t.a[e];
     }
-    const int brow = tid >> 5, bcol = tid & 31;
-    *reinterpret_cast<u4*>(Bs + brow * BN + 4 * bcol) = t.b;
+    const int kb = tid >> 6, n = 2 * (tid & 63);
+    *reinterpret_cast<u2*>(Bs + (2 * kb) * BN + n) = u2{t.b[0][0], t.b[1][0]};
+    *reinterpret_cast<u2*>(Bs + (2 * kb + 1) * BN + n) = u2{t.b[0][1], t.b[1][1]};
 }
 
 template <int NG>
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_regs_kernel(GemmArgs p)
     const int m0 = mtile * BM, n0 = ntile * BN;
 
     const rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    const rsrc_t rw = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    const rsrc_t rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * 64u);
     const int ng = p.K / p.G;
     const rsrc_t rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
     const rsrc_t rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
@@ -151,9 +158,11 @@ __global__ __launch_bounds__(NT) void q4_gemm_regs_kernel(GemmArgs p)
         const int row = (tid + NT * e) >> 3;
         ln.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + ln.a_kc) * 2u;   // rows >= M fall outside x
     }
-    {
-        const int brow = tid >> 5, n = n0 + 4 * (tid & 31);
-        ln.b_off = ((uint32_t)brow * (uint32_t)p.N + (uint32_t)n) * 4u + (n < p.N ? 0u : kOOB);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int kb = tid >> 6, n = n0 + 2 * (tid & 63) + v;
+        ln.b_off[v] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u;
+        ln.b_kill[v] = n < p.N ? 0u : kOOB;
     }
     int lane_cols[NJ];
 #pragma unroll
@@ -187,7 +196,8 @@ __global__ __launch_bounds__(NT) void q4_gemm_regs_kernel(GemmArgs p)
         if (more) load_tile<NG>(tr, gnext, p, ln, rx, rw, rs, rz, (kt + 1) * BK);
         __builtin_amdgcn_sched_barrier(0);
 
-        h2 hz[NG][NJ], s2[NG][NJ];
+        zero_t hz[NG][NJ];
+        h2 s2[NG][NJ];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
@@ -206,8 +216,11 @@ __global__ __launch_bounds__(NT) void q4_gemm_regs_kernel(GemmArgs p)
                 h8 b[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    b[j] = dequant_word(B[(2 * sub + lhi) * BN + wn * WTN + 32 * j + l32], hz[gi][j],
-                                        s2[gi][j]);
+                {
+                    const int r = 2 * sub + lhi;   // tile row
+                    b[j] = dequant_word(B[((r & 3) * 2 + (r >> 2)) * BN + wn * WTN + 32 * j + l32],
+                                        hz[gi][j], s2[gi][j]);
+                }
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     const h8 a = *reinterpret_cast<const h8*>(A + (wm * WTM + 32 * i + l32) * AST +

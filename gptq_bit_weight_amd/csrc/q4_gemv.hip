@@ -5,32 +5,52 @@
 // does"), so the kernel streams the packed words once with 16-byte loads,
 // dequantizes them in registers and never writes a dequantized weight.
 //
-// Mapping (one workgroup = 4 waves = 64 output columns x a K range):
-//  * lane l owns columns c = tile*64 + 4*(l % 16) .. +3 (one 16-byte load of
-//    four consecutive words of a qweight row) and k-block kb = l / 16 of
-//    every 32-row k-step: rows 32t + 8kb .. +7, i.e. word row 4t + kb;
-//  * per k-step each lane feeds four v_mfma_f32_16x16x32_f16, one per owned
-//    column: A = activations (row m = l % 16, zero for m >= M), B = the eight
-//    values q - z of one word, exact small integers in fp16. M is padded to
-//    16 on the matrix pipe, which has the capacity to spare; the vector ALU
-//    is the scarce unit here, so the per-group scale is applied once per
-//    group to the fp32 group sum: sum_k x*s*(q - z) = s * sum_k x*(q - z)
-//    (the weight s*(q - z) is exact in fp32, so this is the product with the
-//    exact dequantized weight, accumulated in fp32);
-//  * the four waves split the workgroup's K range; their fp32 results are
-//    summed in LDS in wave order;
-//  * grid.y splits K across workgroups when there are few column tiles. Each
-//    split writes fp32 partials; the last workgroup of a column tile to
-//    arrive (counted with an agent-scope atomic) sums them in split order, so
-//    the result does not depend on timing. Reductions stay in fp32 (GPTQModel
-//    wiki "Inference Backends", section "Numeric epilogues": FP32 split/tile
-//    reductions, bias added before the single cast).
+// Mapping. A workgroup of 8 waves owns CT 16-column tiles (16 * CT output
+// columns); its waves split its K range in whole 128-row k-blocks.
+//  * lane l works on column c = l % 16 of every tile and on k-block quarter
+//    kb = l / 16. One 16-byte load of the private layout (chunk (b, kb, c))
+//    gives it the eight rows 32 * (4b + i) + 8 * kb .. +7 for each of the
+//    four k-steps i of block b, which is exactly the B operand of four
+//    v_mfma_f32_16x16x32_f16 (lane l: rows 8 * (l / 16) .. +7 of column
+//    l % 16). A is the activations (row m = l % 16), shared by the CT tiles.
+//    M is padded to 16 on the matrix pipe, which has the capacity to spare:
+//    output rows m >= M are never stored, so what A holds in those rows does
+//    not matter. That lets one 16-byte load serve XS = 16 / R k-steps when
+//    M <= R (R = 4 or 8): lane group s of each 16-lane row loads the R rows of
+//    k-step s, and a DPP row shift moves them into lanes 0 .. R-1 for that
+//    step's MFMA, instead of one mostly empty load per k-step.
+//  * B is the exact small integers q - z in fp16, and the per-group scale is
+//    applied once per group to the fp32 MFMA sum:
+//    sum_k x * s * (q - z) = s * sum_k x * (q - z). The weight s * (q - z) is
+//    exact in fp32, so this is the product with the exact dequantized weight,
+//    accumulated in fp32, and the vector ALU does one unpack and one packed
+//    subtract per two weights.
+//  * each wave keeps D k-blocks of loads in flight (a ring of register
+//    buffers, refilled as soon as a block is multiplied), so a CU has
+//    8 waves x D x 1 KiB x CT of weights outstanding. Every load takes a
+//    fixed per-lane offset plus a wave-uniform offset in a scalar register,
+//    so the loop spends its vector instructions on the unpack alone;
+//  * the waves' fp32 results are summed in LDS in wave order;
+//  * grid.y splits K across workgroups when the column tiles alone cannot
+//    give every CU a workgroup. Each split writes fp32 partials; the last
+//    workgroup of a column tile to arrive (counted with an agent-scope
+//    atomic) sums them in split order, so the result does not depend on
+//    timing. Reductions stay in fp32 (GPTQModel wiki "Inference Backends",
+//    section "Numeric epilogues": FP32 split/tile reductions, bias added
+//    before the single cast).
 #include "q4_device.h"
 #include "q4_internal.h"
 
 namespace {
 
 using namespace q4dev;
+
+constexpr int WV = q4::kGemvWaves;     // waves per workgroup
+constexpr int NT = 64 * WV;            // threads per workgroup
+// k-blocks in flight per wave: kGemvDepth for one column tile, half that for
+// two or four (their buffers are larger; this keeps two workgroups per CU).
+template <int CT>
+constexpr int depth() { return CT >= 2 ? q4::kGemvDepth / 2 : q4::kGemvDepth; }
 
 struct GemvArgs {
     const uint32_t* qweight;
@@ -42,219 +62,242 @@ struct GemvArgs {
     float* partials;
     uint32_t* counters;
     int M, K, N, G;
-    int gshift;          // group of k-step t = t >> gshift (31 for a single group)
+    int ng;                 // K / G
+    int gshift;             // group of k-step t (32 rows) = t >> gshift (31: one group)
+    int kblocks;            // ceil(K / 128)
+    int blocks_per_split;
+    int blocks_per_wave;
     int splits;
-    int batches_per_split;
-    int batches_per_wave;
 };
 
-constexpr int kSteps = q4::kBatchSteps;    // k-steps per batch
-
-// Per-lane constants of the load addressing (byte offsets inside each tensor;
-// an invalid column carries kOOB so every load of it returns zeros).
-struct LaneAddr {
-    uint32_t w;     // qweight: kb-th word row of a k-step, the lane's 4 columns
-    uint32_t x;     // x: row m, k-block kb
-    uint32_t s;     // scales: the lane's 4 columns
-    uint32_t z;     // qzeros: the word holding the lane's columns
-    uint32_t zshift;
+// One k-block of loads for one lane. NGB = groups per block: 4 (groups of 32
+// rows), 2 (64) or 1 (128, 256, or one group over K).
+template <int NGB, int CT>
+struct Block {
+    u4 w[CT];
+    u4 a[4];
+    uint32_t s[NGB][CT];
+    uint32_t z[NGB][CT];
 };
 
+// Per-lane byte offsets, fixed for the whole kernel; each block adds a
+// wave-uniform offset held in a scalar register. Columns past N read column
+// N - 1 (their results are never stored); activation rows m >= M lie past the
+// end of x and read zeros.
+template <int CT>
+struct Lane {
+    uint32_t w[CT];          // (kb * N + n_j) * 16
+    uint32_t s[CT];          // n_j * 2
+    uint32_t z[CT];          // (n_j / 8) * 4
+    uint32_t x;              // ((l % R) * K + 8 * kb + 32 * ((l % 16) / R)) * 2
+    uint32_t zshift;         // 4 * (n_j % 8), equal for every j
+};
+
+// Descriptors of the four tensors, and one of size 0: a load through it
+// returns zeros and moves no data. Only the last k-block of a K that is not a
+// multiple of 128 needs it (TAIL): its k-steps past K and its groups past K / G.
 struct Rsrc {
-    rsrc_t w, x, s, z;
+    rsrc_t w, x, s, z, none;
 };
 
-// One batch of loads for one lane: kSteps k-steps of weights and activations
-// plus the scales/zeros they need. Every load is unconditional; k-steps past
-// the end of K read zeros (weights and activations alike).
-//
-// GS = k-steps per group: 1, 2 (groups of 32, 64 rows), 4, 8 (128, 256) or 0
-// (one group over K). Batches start at multiples of 4 k-steps, so with GS >= 4
-// (or 0) a batch lies in one group.
-template <int GS>
-struct Batch {
-    static constexpr int NG = GS == 1 ? 4 : GS == 2 ? 2 : 1;
-    u4 w[kSteps];
-    u4 a[kSteps];
-    u2 s[NG];
-    uint32_t z[NG];
-};
-
-template <int GS>
-__device__ __forceinline__ void load_batch(Batch<GS>& b, const GemvArgs& p, const Rsrc& r,
-                                           const LaneAddr& la, int batch)
+// Load k-block b (0 <= b < kblocks). The per-block offsets are wave-uniform
+// (scalar registers; the k-step offset 64 i of the activations folds into the
+// instruction's immediate offset).
+// XS = k-steps per activation load (1, 2 or 4); B.a[0 .. 4/XS - 1] are loaded.
+template <int NGB, int CT, int XS, bool TAIL>
+__device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p, const Rsrc& r,
+                                           const Lane<CT>& ln, int b)
 {
+    const uint32_t wso = (uint32_t)b * (uint32_t)p.N * 64u;
+#pragma unroll
+    for (int j = 0; j < CT; ++j) B.w[j] = buf_load16(r.w, ln.w[j], wso);
     const int ksteps = p.K >> 5;
-    const int t0 = batch * kSteps;
-    const uint32_t row_bytes = (uint32_t)p.N * 4u;
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-        const int t = t0 + i;
-        const uint32_t kill = t < ksteps ? 0u : kOOB;
-        b.w[i] = buf_load16(r.w, la.w + (uint32_t)(4 * t) * row_bytes + kill);
-        b.a[i] = buf_load16(r.x, la.x + (uint32_t)t * 64u + kill);
+    for (int i = 0; i < 4 / XS; ++i) {
+        const rsrc_t rx = (!TAIL || 4 * b + i < ksteps) ? r.x : r.none;
+        B.a[i] = buf_load16(rx, ln.x + 64u * XS * i, (uint32_t)b * 256u);
     }
 #pragma unroll
-    for (int gi = 0; gi < Batch<GS>::NG; ++gi) {
-        const int t = t0 + gi * (kSteps / Batch<GS>::NG);
-        const uint32_t g = GS == 0 ? 0u : (uint32_t)(t >> p.gshift);
-        const uint32_t kill = t < ksteps ? 0u : kOOB;
-        b.s[gi] = buf_load8(r.s, la.s + g * (uint32_t)p.N * 2u + kill);
-        b.z[gi] = buf_load4(r.z, la.z + g * (uint32_t)(p.N >> 3) * 4u + kill);
-    }
-}
-
-// Multiply one batch into the group sums `acc` and fold finished groups into
-// `tot`: tot += s * acc (fp32). FRESH: the batch starts a group (acc restarts
-// from zero); FOLD: the batch ends a group. Only GS = 8 and GS = 0 decide
-// these per batch; smaller groups start and end inside every batch.
-template <int GS, bool FRESH, bool FOLD>
-__device__ __forceinline__ void compute_batch(const Batch<GS>& b, f4 acc[4], f4 tot[4],
-                                              uint32_t zshift)
-{
-    h2 hz[4];
-    float sf[4];
+    for (int gi = 0; gi < NGB; ++gi) {
+        const int g = (4 * b + gi * (4 / NGB)) >> p.gshift;
+        const bool ok = !TAIL || g < p.ng;
+        const rsrc_t rs = ok ? r.s : r.none;
+        const rsrc_t rz = ok ? r.z : r.none;
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-        constexpr int per = GS == 1 ? 1 : GS == 2 ? 2 : kSteps;   // k-steps per group in a batch
-        const bool starts = (i % per) == 0;
-        const bool fresh = starts && (GS == 1 || GS == 2 || GS == 4 || FRESH);
-        const bool ends = (i % per) == per - 1;
-        const bool fold = ends && (GS == 1 || GS == 2 || GS == 4 || FOLD);
-        if (starts) {
-            const int gi = i / per;
-            const uint32_t z4 = b.z[gi] >> zshift;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hz[j] = zero_pair((z4 >> (4 * j)) & 0xFu);
-                sf[j] = f16_bits_to_f32((uint16_t)(b.s[gi][j >> 1] >> (16 * (j & 1))));
-            }
-        }
-        const h8 a = bitcast<h8>(b.a[i]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[j] = mfma16(a, sub_zero_word(b.w[i][j], hz[j]), fresh ? f4{0.f, 0.f, 0.f, 0.f} : acc[j]);
-        if (fold) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tot[j][e] = __builtin_fmaf(sf[j], acc[j][e], tot[j][e]);
+        for (int j = 0; j < CT; ++j) {
+            B.s[gi][j] = buf_load2(rs, ln.s[j], (uint32_t)g * (uint32_t)p.N * 2u);
+            B.z[gi][j] = buf_load4(rz, ln.z[j], (uint32_t)g * (uint32_t)(p.N >> 3) * 4u);
         }
     }
 }
 
-template <int GS>
-__device__ __forceinline__ void compute_any(const Batch<GS>& b, f4 acc[4], f4 tot[4], uint32_t zshift,
-                                            bool fresh, bool fold)
+// Rows shifted down a 16-lane row by SH lanes (DPP row_shl; lanes past the
+// end of the row read zero).
+template <int SH>
+__device__ __forceinline__ u4 row_shl(u4 v)
 {
-    if (GS == 8 || GS == 0) {
-        if (fresh && fold) compute_batch<GS, true, true>(b, acc, tot, zshift);
-        else if (fresh) compute_batch<GS, true, false>(b, acc, tot, zshift);
-        else if (fold) compute_batch<GS, false, true>(b, acc, tot, zshift);
-        else compute_batch<GS, false, false>(b, acc, tot, zshift);
-    } else {
-        compute_batch<GS, true, true>(b, acc, tot, zshift);
+    u4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[e], 0x100 + SH, 0xF, 0xF, true);
+    return o;
+}
+
+// The A operand of k-step i: with XS > 1, rows 0 .. R-1 (R = 16 / XS) come
+// from lane group i % XS of the load that holds step i, shifted down the row.
+// (i is a constant after unrolling, so the switch folds away.)
+template <int XS>
+__device__ __forceinline__ h8 a_operand(const u4 a[4], int i)
+{
+    constexpr int R = 16 / XS;
+    const u4 v = a[i / XS];
+    switch (R * (i % XS)) {
+    case 4: return bitcast<h8>(row_shl<4>(v));
+    case 8: return bitcast<h8>(row_shl<8>(v));
+    case 12: return bitcast<h8>(row_shl<12>(v));
+    default: return bitcast<h8>(v);
     }
 }
 
-template <int GS>
-__global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
+// Multiply one block into the totals: per group, the MFMA sums of x * (q - z)
+// over its k-steps, then tot += s * sum in fp32.
+template <int NGB, int CT, int XS>
+__device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT], uint32_t zshift)
 {
-    __shared__ float red[q4::kWaves][16][q4::kColTile];
+    constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
+#pragma unroll
+    for (int gi = 0; gi < NGB; ++gi) {
+        zero_t zp[CT];
+        float sf[CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            zp[j] = zero_pair((B.z[gi][j] >> zshift) & 0xFu);
+            sf[j] = f16_bits_to_f32((uint16_t)B.s[gi][j]);
+        }
+        f4 acc[CT];
+#pragma unroll
+        for (int ii = 0; ii < SPG; ++ii) {
+            const int i = gi * SPG + ii;
+            const h8 a = a_operand<XS>(B.a, i);
+#pragma unroll
+            for (int j = 0; j < CT; ++j)
+                acc[j] = mfma16(a, sub_zero_word(B.w[j][i], zp[j]), ii == 0 ? f4{0.f, 0.f, 0.f, 0.f} : acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[j][e] = __builtin_fmaf(sf[j], acc[j][e], tot[j][e]);
+    }
+}
+
+template <int NGB, int CT, int XS, bool TAIL>
+__global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
+{
+    constexpr int COLS = 16 * CT;
+    __shared__ float red[WV][16][COLS];
     __shared__ int last_flag;
 
     const int tid = threadIdx.x;
-    // The wave index is uniform across the wave; saying so keeps the batch
+    // The wave index is uniform across the wave; saying so keeps the block
     // bookkeeping in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int kb = lane >> 4;
-    const int m = lane & 15;
-    const int col = blockIdx.x * q4::kColTile + 4 * (lane & 15);
-    const bool col_ok = col < p.N;
-    const int ksteps = p.K >> 5;
-    const int total_batches = (ksteps + kSteps - 1) / kSteps;
-    const int ng = p.K / p.G;
+    const int c16 = lane & 15;
+    // Workgroup i runs on XCD i % 8 (round-robin dispatch). Neighbouring
+    // tiles share the cache lines of their scales and packed zeros (a 128-byte
+    // line holds 64 columns of scales, 256 of zeros), and the XCDs' L2 caches
+    // are separate, so each XCD takes a contiguous run of tiles.
+    const int T = gridDim.x;
+    const int tile = (T & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
+    const int n0 = tile * COLS;
 
     Rsrc r;
-    r.w = make_rsrc(p.qweight, (uint32_t)(p.K >> 3) * (uint32_t)p.N * 4u);
+    r.w = make_rsrc(p.qweight, (uint32_t)p.kblocks * (uint32_t)p.N * 64u);
     r.x = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    r.s = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
-    r.z = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
-    LaneAddr la;
-    const uint32_t col_kill = col_ok ? 0u : kOOB;
-    la.w = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)col) * 4u + col_kill;
-    la.x = ((uint32_t)m * (uint32_t)p.K + 8u * kb) * 2u;     // rows m >= M fall outside x
-    la.s = (uint32_t)col * 2u + col_kill;
-    la.z = (uint32_t)(col >> 3) * 4u + col_kill;
-    la.zshift = 4u * (col & 7);
+    r.s = make_rsrc(p.scales, (uint32_t)p.ng * (uint32_t)p.N * 2u);
+    r.z = make_rsrc(p.qzeros, (uint32_t)p.ng * (uint32_t)(p.N >> 3) * 4u);
+    r.none = make_rsrc(p.qweight, 0u);   // (used by TAIL only)
+    Lane<CT> ln;
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int n = min(n0 + 16 * j + c16, p.N - 1);
+        ln.w[j] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u;
+        ln.s[j] = (uint32_t)n * 2u;
+        ln.z[j] = (uint32_t)(n >> 3) * 4u;
+    }
+    {
+        // rows m >= M fall past the end of x and read zeros
+        constexpr int R = 16 / XS;
+        ln.x = ((uint32_t)(c16 % R) * (uint32_t)p.K + 8u * (uint32_t)kb + 32u * (uint32_t)(c16 / R)) * 2u;
+    }
+    ln.zshift = 4u * (uint32_t)(c16 & 7);
 
     const int split = blockIdx.y;
-    const int b_split0 = split * p.batches_per_split;
-    const int b_split1 = min(b_split0 + p.batches_per_split, total_batches);
-    const int b0 = b_split0 + wave * p.batches_per_wave;
-    const int b1 = min(b0 + p.batches_per_wave, b_split1);
+    const int bs0 = split * p.blocks_per_split;
+    const int bs1 = min(bs0 + p.blocks_per_split, p.kblocks);
+    const int b0 = bs0 + wave * p.blocks_per_wave;
+    const int nb = min(b0 + p.blocks_per_wave, bs1) - b0;   // may be <= 0
 
-    f4 acc[4], tot[4];
+    f4 tot[CT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-        tot[j] = f4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < CT; ++j) tot[j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    if (b0 < b1) {
-        // Two register buffers: the loads of batch b+1 are in flight while
-        // batch b is unpacked and multiplied. The prefetch index is clamped
-        // to the wave's last batch (a repeated load, never out of range).
-        // sched_barrier keeps the compiler from sinking the prefetch below
-        // the arithmetic it is meant to overlap.
-        Batch<GS> A, B;
-        load_batch(A, p, r, la, b0);
-        for (int b = b0; b < b1; b += 2) {
-            load_batch(B, p, r, la, min(b + 1, b1 - 1));
+    constexpr int D = depth<CT>();
+    if (nb > 0) {
+        // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
+        // Once a block is multiplied its buffer is refilled with the block D
+        // further on. Past the wave's last block the loads repeat that block
+        // (addresses stay in range, the data comes from cache) and the last
+        // round skips those buffers, so the loop body has no branches and the
+        // compiler's wait before each multiply covers exactly that block's
+        // loads. sched_barrier keeps each block's loads and arithmetic in
+        // program order: the loads issue in the same order in the prologue
+        // and in the loop (so the waits at the loop head need not assume the
+        // worse of two orders), and no work of a later block (which would
+        // wait for its loads) is hoisted into an earlier one.
+        const int bl = b0 + nb - 1;
+        Block<NGB, CT> buf[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_block<NGB, CT, XS, TAIL>(buf[d], p, r, ln, min(b0 + d, bl));
             __builtin_amdgcn_sched_barrier(0);
-            compute_any(A, acc, tot, la.zshift, b == b0 || (GS == 8 && (b & 1) == 0),
-                        b + 1 == b1 || (GS == 8 && (b & 1) == 1));
-            if (b + 1 >= b1) break;
-            load_batch(A, p, r, la, min(b + 2, b1 - 1));
+        }
+        const int rounds = (nb + D - 1) / D;
+        for (int rd = 1; rd < rounds; ++rd) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute_block<NGB, CT, XS>(buf[d], tot, ln.zshift);
+                load_block<NGB, CT, XS, TAIL>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < last) compute_block<NGB, CT, XS>(buf[d], tot, ln.zshift);
             __builtin_amdgcn_sched_barrier(0);
-            compute_any(B, acc, tot, la.zshift, GS == 8 && ((b + 1) & 1) == 0,
-                        b + 2 == b1 || (GS == 8 && ((b + 1) & 1) == 1));
         }
     }
 
-    // Cross-wave reduction. Lane l holds rows 4*(l/16) + i of the columns
-    // 4*(l%16) + j (16x16 MFMA output layout).
+    // Cross-wave reduction. Lane l holds rows 4 * (l / 16) + i of column l % 16
+    // of each tile (16x16 MFMA output layout).
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < CT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            red[wave][4 * kb + i][4 * (lane & 15) + j] = tot[j][i];
+            if (4 * kb + i < p.M) red[wave][4 * kb + i][16 * j + c16] = tot[j][i];
     __syncthreads();
 
-    const int n_elems = p.M * q4::kColTile;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = tid + 256 * e;
-        v[e] = 0.f;
-        if (idx < n_elems) {
-            const int r = idx / q4::kColTile, c = idx % q4::kColTile;
-            v[e] = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
-        }
-    }
-
-    const int tile_col0 = blockIdx.x * q4::kColTile;
+    const int n_elems = p.M * COLS;
     if (p.splits == 1) {
+        for (int idx = tid; idx < n_elems; idx += NT) {
+            const int m = idx / COLS, c = idx % COLS, n = n0 + c;
+            if (n >= p.N) continue;
+            float y = red[0][m][c];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = tid + 256 * e;
-            const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
-            if (idx < n_elems && c < p.N) {
-                float y = v[e];
-                if (p.bias) y += f16_bits_to_f32(p.bias[c]);
-                p.out[(size_t)r * p.N + c] = f32_to_f16_bits(y);
-            }
+            for (int w = 1; w < WV; ++w) y += red[w][m][c];
+            if (p.bias) y += f16_bits_to_f32(p.bias[n]);
+            p.out[(size_t)m * p.N + n] = f32_to_f16_bits(y);
         }
         return;
     }
@@ -266,38 +309,61 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
     // wave's stores are complete before the arrival count is bumped. (A full
     // __threadfence() would write back and invalidate the whole L2 of the
     // XCD, once per workgroup, which serializes across the chip.)
+    for (int idx = tid; idx < n_elems; idx += NT) {
+        const int m = idx / COLS, c = idx % COLS, n = n0 + c;
+        if (n >= p.N) continue;
+        float y = red[0][m][c];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = tid + 256 * e;
-        const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
-        if (idx < n_elems && c < p.N)
-            __hip_atomic_store(&p.partials[((size_t)split * 16 + r) * p.N + c], v[e], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int w = 1; w < WV; ++w) y += red[w][m][c];
+        __hip_atomic_store(&p.partials[((size_t)split * 16 + m) * p.N + n], y, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[blockIdx.x], 1u, __ATOMIC_RELAXED,
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == (uint32_t)(p.splits - 1));
     }
     __syncthreads();
     if (!last_flag) return;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = tid + 256 * e;
-        const int r = idx / q4::kColTile, c = tile_col0 + idx % q4::kColTile;
-        if (idx < n_elems && c < p.N) {
-            float y = 0.f;
-            for (int s = 0; s < p.splits; ++s)
-                y += __hip_atomic_load(&p.partials[((size_t)s * 16 + r) * p.N + c], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (p.bias) y += f16_bits_to_f32(p.bias[c]);
-            p.out[(size_t)r * p.N + c] = f32_to_f16_bits(y);
-        }
+    for (int idx = tid; idx < n_elems; idx += NT) {
+        const int m = idx / COLS, c = idx % COLS, n = n0 + c;
+        if (n >= p.N) continue;
+        float y = 0.f;
+        for (int s = 0; s < p.splits; ++s)
+            y += __hip_atomic_load(&p.partials[((size_t)s * 16 + m) * p.N + n], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (p.bias) y += f16_bits_to_f32(p.bias[n]);
+        p.out[(size_t)m * p.N + n] = f32_to_f16_bits(y);
     }
     if (tid == 0)
-        __hip_atomic_store(&p.counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NGB, int XS, bool TAIL>
+hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
+{
+    const dim3 block(NT);
+    switch (ct) {
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL>), dim3((p.N + 15) / 16, splits), block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL>), dim3((p.N + 31) / 32, splits), block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL>), dim3((p.N + 63) / 64, splits), block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Activation loads: one per 4 k-steps for M <= 4, per 2 for M <= 8, else one
+// per k-step. A K that is not a multiple of 128 (one partial block) takes the
+// one-per-step form, whose past-K steps are masked per load.
+template <int NGB>
+hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
+{
+    if (p.K % 128) return launch_ct<NGB, 1, true>(p, ct, splits, stream);
+    if (p.M <= 4) return launch_ct<NGB, 4, false>(p, ct, splits, stream);
+    if (p.M <= 8) return launch_ct<NGB, 2, false>(p, ct, splits, stream);
+    return launch_ct<NGB, 1, false>(p, ct, splits, stream);
 }
 
 }  // namespace
@@ -305,8 +371,9 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs p)
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int splits, hipStream_t stream)
+                       int M, int col_tiles, int splits, hipStream_t stream)
 {
+    if (M < 1 || M > 16 || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
     GemvArgs p;
     p.qweight = h->qweight;
     p.scales = h->scales;
@@ -320,28 +387,25 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     p.K = h->K;
     p.N = h->N;
     p.G = h->G;
+    p.ng = h->ng;
+    // k-steps (32 rows) per group = 2^gshift; one group over K never changes
     p.gshift = 31;
-    for (int sh = 0; sh < 30; ++sh)
-        if ((32 << sh) == h->G && h->G != h->K) p.gshift = sh;
-    const int ksteps = h->K / 32;
-    const int total_batches = (ksteps + kBatchSteps - 1) / kBatchSteps;
+    if (h->G != h->K)
+        for (int sh = 0; sh < 4; ++sh)
+            if ((32 << sh) == h->G) p.gshift = sh;
+    p.kblocks = num_kblocks(h->K);
     p.splits = splits;
-    p.batches_per_split = (total_batches + splits - 1) / splits;
-    p.batches_per_wave = (p.batches_per_split + kWaves - 1) / kWaves;
-    dim3 grid((h->N + kColTile - 1) / kColTile, splits);
-    // k-steps per group: a batch spans 4 k-steps starting at a multiple of 4,
-    // so groups of 128 or 256 rows never straddle a batch; one group over K
-    // (per-channel) never changes at all.
-    const int gs = h->G == h->K ? 0 : h->G / 32;
-    switch (gs) {
-    case 1: hipLaunchKernelGGL(q4_gemv_kernel<1>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(q4_gemv_kernel<2>, grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(q4_gemv_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(q4_gemv_kernel<8>, grid, dim3(256), 0, stream, p); break;
-    case 0: hipLaunchKernelGGL(q4_gemv_kernel<0>, grid, dim3(256), 0, stream, p); break;
+    p.blocks_per_split = (p.kblocks + splits - 1) / splits;
+    p.blocks_per_wave = (p.blocks_per_split + kGemvWaves - 1) / kGemvWaves;
+    // groups per 128-row block: groups of 32 or 64 rows split a block; larger
+    // groups (and one group over K) cover it whole
+    const int ngb = (h->G == h->K || h->G >= 128) ? 1 : 128 / h->G;
+    switch (ngb) {
+    case 1: return launch_ngb<1>(p, col_tiles, splits, stream);
+    case 2: return launch_ngb<2>(p, col_tiles, splits, stream);
+    case 4: return launch_ngb<4>(p, col_tiles, splits, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace q4

@@ -9,13 +9,23 @@
 
 namespace q4 {
 
+// ---- private weight layout -------------------------------------------------
+// The packed weights are stored in k-blocks of 128 rows. Inside block b, the
+// 16-byte chunk (b, kb, n) (kb = 0..3) holds four words of column n; word i of
+// it packs rows 32 * (4b + i) + 8 * kb .. +7. Chunks are ordered
+// [b][kb][n], so one 16-byte load gives a lane the eight rows it feeds to an
+// MFMA lane in each of four consecutive 32-row k-steps, and the 64 rows a
+// prefill k-tile needs are 8 contiguous bytes of every chunk. K is padded to
+// a whole block with code 0 (the kernels give those rows zero activations).
+constexpr int kBlockK = 128;
+constexpr int num_kblocks(int K) { return (K + kBlockK - 1) / kBlockK; }
+constexpr size_t packed_words(int K, int N) { return (size_t)num_kblocks(K) * (kBlockK / 8) * (size_t)N; }
+
 // ---- skinny (M <= 16) kernel geometry ------------------------------------
-constexpr int kWaves = 4;            // waves per workgroup
-constexpr int kColTile = 64;         // columns per workgroup (16 lanes x 4 words)
-constexpr int kBatchSteps = 4;       // k-steps (32 rows each) per unrolled batch
-constexpr int kMaxSplits = 16;       // K splits (grid.y)
-constexpr int kTargetWorkgroups = 256;
-constexpr int kMinBatchesPerWave = 2;
+constexpr int kGemvWaves = 8;        // waves per workgroup (they split its K range)
+constexpr int kGemvDepth = 4;        // k-blocks in flight per wave
+constexpr int kMaxSplits = 16;       // K splits across workgroups (grid.y)
+constexpr int kMaxColTiles = 4;      // 16-column MFMA tiles per wave
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
 constexpr int kGemmBM = 256;
@@ -30,7 +40,9 @@ const char* last_message();
 
 q4_status check_shape(int K, int N, int groupsize, int* G_out);
 q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* trivial);
-int plan_splits(int M, int K, int N, int G);
+// Skinny-kernel launch plan: 16-column tiles per wave (1, 2 or 4) and K
+// splits across workgroups (1..kMaxSplits) for a chip of num_cu CUs.
+void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits);
 
 }  // namespace q4
 
@@ -41,14 +53,14 @@ struct q4_matrix {
     int act_order = 0;
     int device = -1;
     int num_cu = 256;
-    uint32_t* qweight = nullptr;   // [K/8][N], nibble slots interleaved (see q4_device.h)
+    uint32_t* qweight = nullptr;   // packed_words(K, N): private block layout (above)
     uint16_t* scales = nullptr;    // [ng][N] fp16
     uint32_t* qzeros = nullptr;    // [ng][N/8]
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
     // skinny-kernel split-K workspace: partial sums and arrival counters
     float* partials = nullptr;     // [kMaxSplits][16][N]
-    uint32_t* counters = nullptr;  // [ceil(N / kColTile)]
+    uint32_t* counters = nullptr;  // [ceil(N / 16)]: one per column tile at the narrowest tiling
     // act-order activation workspace, grown on demand: x[:, perm] as fp16 [M][K]
     mutable std::mutex ws_mutex;
     mutable uint16_t* xperm = nullptr;

@@ -47,11 +47,12 @@ q4_status check_shape(int K, int N, int groupsize, int* G_out)
         return fail(Q4_ERR_UNSUPPORTED, "K=%d is not a multiple of 32 (the kernels' k-block)", K);
     if (K % G)
         return fail(Q4_ERR_UNSUPPORTED, "K=%d is not a multiple of groupsize=%d", K, G);
-    // Byte offsets inside the packed weights stay below 2^31 (the kernels mark
-    // out-of-range lanes by adding 2^31).
-    if ((long long)K * (long long)N / 2 > (1LL << 31) - 1)
-        return fail(Q4_ERR_UNSUPPORTED, "K*N/2 = %lld bytes of packed weights exceeds 2^31 - 1",
-                    (long long)K * (long long)N / 2);
+    // Byte offsets inside the packed weights (K padded to whole 128-row
+    // blocks) stay below 2^31: the kernels mark out-of-range lanes by setting
+    // bit 31 of the offset.
+    const long long packed = (long long)num_kblocks(K) * (kBlockK / 2) * (long long)N;
+    if (packed > (1LL << 31) - 1)
+        return fail(Q4_ERR_UNSUPPORTED, "%lld bytes of packed weights exceed 2^31 - 1", packed);
     if (G_out) *G_out = G;
     return Q4_OK;
 }
@@ -80,25 +81,45 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
     return Q4_OK;
 }
 
-// Split-K plan of the skinny kernel. One workgroup covers kColTile columns and
-// a contiguous K range that its four waves divide; splits add workgroups
-// along K when the column tiles alone cannot fill the chip. Each split costs
-// a round of fp32 partial sums (8 * splits * M * N bytes) and puts the
-// last-arriver reduction on the critical path, so splits only grow while the
-// grid stays within kTargetWorkgroups and every wave keeps at least
-// kMinBatchesPerWave batches. (Measured on MI355X at M = 1..16 over the
-// Llama-7B and Llama-70B layer shapes.)
-int plan_splits(int M, int K, int N, int G)
+// Launch plan of the skinny kernel. A workgroup covers 16 * col_tiles
+// columns and a contiguous range of 128-row k-blocks that its waves divide.
+//  * col_tiles: each 16-column tile is one workgroup's share of the chip, so
+//    the tiles should fill whole rounds of CUs: balance(ct) = tiles /
+//    (CUs x rounds). Wider tiles reuse each activation fragment across more
+//    columns, which pays more the more rows M has (the activation loads grow
+//    with M); gain(ct, M) below is that benefit as measured on MI355X over
+//    the Llama-7B/70B layer shapes. The plan takes the widest tile with the
+//    best balance x gain.
+//  * splits: K ranges across workgroups, only when the column tiles alone
+//    cannot give every CU a workgroup, and only while every wave of every
+//    split keeps a k-block. Each split adds a round of fp32 partials and a
+//    last-arriver reduction to the critical path.
+void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits)
 {
-    if (M <= 0 || K <= 0 || N <= 0 || K % 32) return 0;
-    (void)G;
-    const int col_tiles = (N + kColTile - 1) / kColTile;
-    const int batches = (K / 32 + kBatchSteps - 1) / kBatchSteps;
+    if (num_cu <= 0) num_cu = 256;
+    // gain x 100 for 1, 2, 4 tiles: M <= 4, M <= 8, M <= 16
+    static const int gain[3][3] = {{100, 110, 120}, {100, 140, 150}, {100, 160, 190}};
+    const int mi = M <= 4 ? 0 : M <= 8 ? 1 : 2;
+    // (groups of 32 rows carry four scale/zero sets per block; four tiles of
+    // them do not fit the register file)
+    const int max_ct = G == 32 ? 2 : kMaxColTiles;
+    int ct = 1;
+    long long best = -1;
+    for (int c = 1, ci = 0; c <= max_ct; c *= 2, ++ci) {
+        const long long tiles = (N + 16 * c - 1) / (16 * c);
+        const long long rounds = (tiles + num_cu - 1) / num_cu;
+        const long long score = tiles * 1000 * gain[mi][ci] / (rounds * num_cu);
+        if (score >= best) {
+            best = score;
+            ct = c;
+        }
+    }
+    const int tiles = (N + 16 * ct - 1) / (16 * ct);
+    const int kb = num_kblocks(K);
     int s = 1;
-    while (2 * s <= kMaxSplits && col_tiles * 2 * s <= kTargetWorkgroups &&
-           batches >= 2 * s * kWaves * kMinBatchesPerWave)
-        s *= 2;
-    return s;
+    while (2 * s <= kMaxSplits && tiles * 2 * s <= num_cu && kb >= 2 * s * kGemvWaves) s *= 2;
+    *col_tiles = ct;
+    *splits = s;
 }
 
 }  // namespace q4
@@ -128,11 +149,16 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
     return q4::plan_actorder(g_idx_host, K, G, perm, trivial);
 }
 
-int q4_plan_splits(int M, int K, int N, int groupsize)
+q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles, int* splits)
 {
+    if (!col_tiles || !splits) return q4::fail(Q4_ERR_INVALID_ARG, "q4_plan_gemv: null pointer");
     int G;
-    if (M <= 0 || q4::check_shape(K, N, groupsize, &G) != Q4_OK) return 0;
-    return q4::plan_splits(M, K, N, G);
+    q4_status st = q4::check_shape(K, N, groupsize, &G);
+    if (st != Q4_OK) return st;
+    if (M < 1 || M > Q4_GEMV_MAX_M)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_plan_gemv: M=%d outside [1, %d]", M, Q4_GEMV_MAX_M);
+    q4::plan_gemv(M, K, N, G, num_cu, col_tiles, splits);
+    return Q4_OK;
 }
 
 }  // extern "C"

@@ -3,10 +3,13 @@
 // Repack ("runtime initialization can ... prepack tiles, shuffle
 // scales/zeros", GPTQModel wiki "Inference Backends", section "Packing,
 // conversion, and runtime initialization"): qweight is rewritten once into
-// the kernels' private nibble order (q4_device.h) and, for act-order, with
-// its rows in the order of one stable argsort of g_idx (same page, section
-// "Runtime cache lifetime"), so that every group becomes a contiguous run of
-// groupsize rows. The size stays K/8 x N words.
+// the kernels' private layout -- 128-row k-blocks of 16-byte chunks, word i
+// of chunk (b, kb, n) packing rows 32 * (4b + i) + 8 * kb .. +7 of column n
+// (q4_internal.h), each word in the nibble slot order of q4_device.h -- and,
+// for act-order, with its rows in the order of one stable argsort of g_idx
+// (same page, section "Runtime cache lifetime"), so that every group becomes
+// a contiguous run of groupsize rows. Rows past K (up to the next multiple of
+// 128) hold code 0.
 //
 // Act-order activations ("Implementation: Predibase Lorax GPTQ Exllama V1",
 // Description: a scratch buffer reorders activations in the act-order case):
@@ -18,24 +21,38 @@ namespace {
 
 using namespace q4dev;
 
-// One thread per output word (r', n): gather the eight codes of sorted rows
-// k' = 8r' .. 8r'+7 from their original rows perm[k'] and store them in the
-// private nibble slots.
+// Row k' of the private layout: its chunk (b, kb), the word i inside the
+// chunk and the element e inside the word.
+__device__ __forceinline__ size_t private_word(int kk, int n, int N, int* e)
+{
+    const int b = kk >> 7, i = (kk >> 5) & 3, kb = (kk >> 3) & 3;
+    *e = kk & 7;
+    return ((size_t)(4 * b + kb) * N + n) * 4 + i;
+}
+
+// One thread per output word: gather the eight codes of (sorted) rows
+// k' = 32 * (4b + i) + 8 * kb + e from their original rows perm[k'] and store
+// them in the private nibble slots.
 __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restrict__ src,
                                                         const int32_t* __restrict__ perm,
                                                         uint32_t* __restrict__ dst, int K, int N)
 {
-    const size_t total = (size_t)(K / 8) * N;
+    const size_t total = q4::packed_words(K, N);
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
-        const int r = (int)(idx / N), n = (int)(idx % N);
+        const int i = (int)(idx & 3);
+        const size_t chunk = idx >> 2;
+        const int n = (int)(chunk % N);
+        const int q = (int)(chunk / N);                  // 4 * b + kb
+        const int k0 = 32 * (4 * (q >> 2) + i) + 8 * (q & 3);
         uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = 8 * r + i;
+        for (int e = 0; e < 8; ++e) {
+            const int kk = k0 + e;
+            if (kk >= K) break;
             const int k = perm ? perm[kk] : kk;
             const uint32_t code = (src[(size_t)(k >> 3) * N + n] >> (4 * (k & 7))) & 0xFu;
-            w |= code << (4 * slot_of(i));
+            w |= code << (4 * slot_of(e));
         }
         dst[idx] = w;
     }
@@ -73,15 +90,16 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const int k = (int)(idx / N), n = (int)(idx % N);
         const int kk = inv_perm ? inv_perm[k] : k;       // sorted position of row k
         const int g = kk / G;
-        const uint32_t word = qweight[(size_t)(kk >> 3) * N + n];
+        int e;
+        const uint32_t word = qweight[private_word(kk, n, N, &e)];
         const uint32_t z = (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
         const uint16_t sb = scales[(size_t)g * N + n];
         if (FACTORED) {
             const h8 d = sub_zero_word(word, zero_pair(z));
-            w[idx] = f32_to_f16_bits(f16_bits_to_f32(sb) * static_cast<float>(d[kk & 7]));
+            w[idx] = f32_to_f16_bits(f16_bits_to_f32(sb) * static_cast<float>(d[e]));
         } else {
             const h8 v = dequant_word(word, zero_pair(z), scale_pair(sb));
-            w[idx] = bitcast<uint16_t>(v[kk & 7]);
+            w[idx] = bitcast<uint16_t>(v[e]);
         }
     }
 }
@@ -101,7 +119,7 @@ namespace q4 {
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          hipStream_t stream)
 {
-    hipLaunchKernelGGL(q4_repack_kernel, dim3(grid_for((size_t)(K / 8) * N)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(q4_repack_kernel, dim3(grid_for(packed_words(K, N))), dim3(256), 0, stream,
                        src, perm, dst, K, N);
     return hipGetLastError();
 }

@@ -89,7 +89,8 @@ enum {
  *
  * Ownership: the inputs are read (the call synchronizes the device) and
  * copied into handle-owned device memory in a private layout of the same
- * size; the caller keeps and may free or change its tensors afterwards; such
+ * size (K rounded up to a multiple of 128 rows for the packed weights); the
+ * caller keeps and may free or change its tensors afterwards; such
  * changes do not reach the handle (make a new one). The handle also owns a
  * small split-K workspace. It never holds a dequantized K x N matrix.
  *
@@ -127,15 +128,19 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
 
 /*
  * q4_matmul_ex -- q4_matmul_bias with explicit kernel choice, for tests and
- * tuning: path = 0 (automatic, as q4_matmul), Q4_PATH_GEMV (needs
- * 1 <= M <= Q4_GEMV_MAX_M) or Q4_PATH_MFMA (any M >= 1). splits: for the
- * skinny kernel 0 (planned) or 1..16 K splits; for the GEMM 0 (automatic),
- * 1 (register-staged tiles) or 2 (direct-to-LDS pipeline), else
- * Q4_ERR_INVALID_ARG. Results differ between paths, split counts and
- * variants only by fp32 rounding.
+ * tuning. path = 0 (automatic, as q4_matmul), Q4_PATH_GEMV (needs
+ * 1 <= M <= Q4_GEMV_MAX_M) or Q4_PATH_MFMA (any M >= 1).
+ *   skinny kernel: variant = 16-column MFMA tiles per wave, 0 (planned), 1, 2
+ *                  or 4; splits = K splits across workgroups, 0 (planned) or
+ *                  1..16;
+ *   GEMM:          variant = 0 (automatic), 1 (register-staged tiles) or
+ *                  2 (direct-to-LDS pipeline); splits must be 0.
+ * Anything else is Q4_ERR_INVALID_ARG. Results differ between paths,
+ * variants and split counts only by fp32 rounding.
  */
 q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
-                       uint16_t* out, int M, int path, int splits, hipStream_t stream);
+                       uint16_t* out, int M, int path, int variant, int splits,
+                       hipStream_t stream);
 
 /* q4_free -- release a handle (NULL is allowed). The caller must have
  * synchronized every stream that used it. */
@@ -162,7 +167,7 @@ int q4_path_for(const q4_matrix* h, int M);
 q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
 
 /* Handle geometry: K, N, groupsize (after -1 -> K), act-order flag (1 when a
- * non-trivial g_idx was given), split count of the skinny kernel for M. */
+ * non-trivial g_idx was given). Returns 0, or -1 for a NULL handle. */
 int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order);
 
 /* ------------------------------------------------------------------------
@@ -187,10 +192,14 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
                            int* trivial);
 
 /*
- * q4_plan_splits -- number of K splits the skinny kernel uses for (M, K, N,
- * groupsize); 0 for invalid arguments. Pure function of its inputs.
+ * q4_plan_gemv -- the skinny kernel's launch plan for (M, K, N, groupsize) on
+ * a chip of num_cu compute units (<= 0: 256): 16-column tiles per wave
+ * (*col_tiles: 1, 2 or 4) and K splits across workgroups (*splits: 1..16).
+ * Host-only. Q4_ERR_INVALID_ARG for M outside [1, Q4_GEMV_MAX_M] or null
+ * outputs; the q4_check_shape status for an unsupported shape.
  */
-int q4_plan_splits(int M, int K, int N, int groupsize);
+q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles,
+                       int* splits);
 
 #ifdef __cplusplus
 }

@@ -46,13 +46,13 @@ def make_matrix(L, t=None, g_idx="layer"):
     return q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], gi, groupsize=L.G if L.G != L.K else -1)
 
 
-def run(L, *, path=0, splits=0, W=None, t=None, x=None, bias="layer"):
+def run(L, *, path=0, variant=0, splits=0, W=None, t=None, x=None, bias="layer"):
     torch = torch_mod()
     t = t or device_tensors(L)
     W = W or make_matrix(L, t)
     xb = t["x"] if x is None else x
     b = t["bias"] if bias == "layer" else bias
-    y = W.matmul(xb, b, path=path, splits=splits)
+    y = W.matmul(xb, b, path=path, variant=variant, splits=splits)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 

@@ -71,16 +71,18 @@ GEMV_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tiles", [0, 1, 2, 4])
 @pytest.mark.parametrize("K,N,G,M,act,bias", GEMV_CASES)
-def test_gemv_parity(K, N, G, M, act, bias):
+def test_gemv_parity(K, N, G, M, act, bias, tiles):
+    """tiles: 16-column MFMA tiles per wave (0: planned)."""
     import gptq_bit_weight_amd as q4
     L = _layer(K, N, G, M, 1, act_order=act, bias=bias)
-    announce(f"gemv K={K} N={N} G={G} M={M} act={act} bias={bias}")
+    announce(f"gemv K={K} N={N} G={G} M={M} act={act} bias={bias} tiles={tiles}")
     W = make_matrix(L)
     assert W.path_for(M) == q4.PATH_GEMV
-    y = run(L, W=W)
+    y = run(L, W=W, path=q4.PATH_GEMV, variant=tiles)
     yD, A = oracle_full(L)
-    compare(y, yD, A, f"gemv K={K} N={N} G={G} M={M}")
+    compare(y, yD, A, f"gemv K={K} N={N} G={G} M={M} tiles={tiles}")
 
 
 # ------------------------------------------------------------ MFMA GEMM --
@@ -104,7 +106,7 @@ def test_gemm_parity(K, N, G, M, act, bias, variant):
     announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias} variant={variant}")
     W = make_matrix(L)
     assert W.path_for(M) == q4.PATH_MFMA
-    y = run(L, W=W, path=q4.PATH_MFMA, splits=variant)
+    y = run(L, W=W, path=q4.PATH_MFMA, variant=variant)
     yD, A = oracle_full(L)
     compare(y, yD, A, f"gemm K={K} N={N} G={G} M={M} variant={variant}")
 
@@ -118,8 +120,8 @@ def test_gemm_variants_bit_identical():
     announce("gemm variants")
     t = device_tensors(L)
     W = make_matrix(L, t)
-    a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=1)
-    b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=2)
+    a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=1)
+    b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=2)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
@@ -138,16 +140,17 @@ def test_both_kernels_agree_at_small_m(M):
 
 # ---------------------------------------------------------------- split-K --
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 8, 16])
-def test_splits_valid_and_deterministic(splits):
+@pytest.mark.parametrize("splits,tiles", [(1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (8, 1),
+                                          (16, 1), (3, 2), (4, 4), (16, 4)])
+def test_splits_valid_and_deterministic(splits, tiles):
     L = _layer(2048, 200, 128, 3, 4, bias=True)
-    announce(f"splits={splits}")
+    announce(f"splits={splits} tiles={tiles}")
     t = device_tensors(L)
     W = make_matrix(L, t)
     yD, A = oracle_full(L)
-    a = run(L, W=W, t=t, splits=splits)
-    b = run(L, W=W, t=t, splits=splits)
-    compare(a, yD, A, f"splits={splits}")
+    a = run(L, W=W, t=t, variant=tiles, splits=splits)
+    b = run(L, W=W, t=t, variant=tiles, splits=splits)
+    compare(a, yD, A, f"splits={splits} tiles={tiles}")
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
@@ -240,6 +243,10 @@ def test_m_zero_and_argument_errors():
         W.matmul(t["x"], splits=17)
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_MFMA, splits=3)
+    with pytest.raises(ValueError):
+        W.matmul(t["x"], path=q4.PATH_MFMA, variant=3)
+    with pytest.raises(ValueError):
+        W.matmul(t["x"], path=q4.PATH_GEMV, variant=3)
     bad = torch.full((256,), 3, dtype=torch.int32, device="cuda")      # only groups 0, 1
     with pytest.raises(ValueError, match="outside"):
         q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], bad, groupsize=128)

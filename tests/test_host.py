@@ -119,16 +119,37 @@ def test_plan_actorder_rejects_out_of_range_and_nonuniform():
         q4.plan_actorder(uneven, K, G)
 
 
-def test_plan_splits():
-    # few column tiles -> several splits, large N -> none; always a power of 2 <= 16
+def test_plan_gemv():
+    # column tiles in {1, 2, 4}, splits a power of 2 <= 16; splits only when the
+    # column tiles cannot give every CU a workgroup
     for (M, K, N) in [(1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096), (1, 8192, 28672),
-                      (16, 28672, 8192), (1, 512, 512), (4, 96, 8)]:
-        s = q4.plan_splits(M, K, N, 128 if K % 128 == 0 else 32)
-        assert s in (1, 2, 4, 8, 16), (M, K, N, s)
-    assert q4.plan_splits(1, 4096, 4096, 128) > 1
-    assert q4.plan_splits(1, 8192, 28672, 128) <= 2
-    assert q4.plan_splits(0, 4096, 4096, 128) == 0
-    assert q4.plan_splits(1, 4100, 4096, 128) == 0
+                      (16, 28672, 8192), (16, 8192, 28672), (1, 512, 512), (4, 96, 8)]:
+        ct, s = q4.plan_gemv(M, K, N, 128 if K % 128 == 0 else 32, num_cu=256)
+        assert ct in (1, 2, 4) and s in (1, 2, 4, 8, 16), (M, K, N, ct, s)
+        tiles = -(-N // (16 * ct))
+        assert s == 1 or tiles * s <= 256, (M, K, N, ct, s)
+    assert q4.plan_gemv(1, 4096, 4096, 128, num_cu=256) == (1, 1)       # 256 tiles of 16
+    assert q4.plan_gemv(16, 4096, 4096, 128, num_cu=256) == (1, 1)      # wider: half the CUs idle
+    assert q4.plan_gemv(1, 4096, 11008, 128, num_cu=256) == (1, 1)      # 688 tiles fill 3 rounds
+    assert q4.plan_gemv(8, 4096, 11008, 128, num_cu=256) == (4, 1)      # reuse wins with 8 rows
+    assert q4.plan_gemv(1, 28672, 8192, 128, num_cu=256) == (2, 1)      # 256 tiles of 32
+    assert q4.plan_gemv(1, 8192, 28672, 128, num_cu=256) == (4, 1)
+    assert q4.plan_gemv(16, 8192, 28672, 32, num_cu=256)[0] == 2        # groups of 32: at most 2
+    assert q4.plan_gemv(1, 4096, 1024, 128, num_cu=256) == (1, 4)       # 64 tiles, 32 blocks
+    assert q4.plan_gemv(1, 512, 512, 128, num_cu=256) == (1, 1)         # 4 blocks: too few to split
+    with pytest.raises(ValueError):
+        q4.plan_gemv(0, 4096, 4096, 128)
+    with pytest.raises(ValueError):
+        q4.plan_gemv(17, 4096, 4096, 128)
+    with pytest.raises(NotImplementedError):
+        q4.plan_gemv(1, 4128, 4096, 128)      # K % groupsize != 0
+
+
+def test_check_shape_size_limit():
+    # packed bytes (K padded to 128-row blocks) must stay below 2^31
+    q4.check_shape(65536, 65536 - 8, 128)
+    with pytest.raises(NotImplementedError, match="2\\^31"):
+        q4.check_shape(65536, 65536 + 8, 128)
 
 
 def test_last_error_is_thread_local():
