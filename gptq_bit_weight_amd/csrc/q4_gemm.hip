@@ -318,22 +318,30 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
         // out of range; the dequant writes zeros there), so the last tile
         // needs no special case. The dequant of tile kt+1 runs unconditionally
         // (past the last tile it fills a buffer nobody reads).
+        // The operands of 16-row sub-step s + 1 are read from LDS while the
+        // matrix cores work on sub-step s (two register sets), so the LDS
+        // latency hides behind the MFMAs of the one wave per SIMD.
+        h8 fa[2][MI], fb[2][NJ];
+        auto read_frag = [&](int f, int sub) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                fb[f][j] = *reinterpret_cast<const h8*>(B + swz(wn * WTN + 32 * j + l32, 2 * sub + lhi));
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                fa[f][i] = *reinterpret_cast<const h8*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
+        };
+        read_frag(0, 0);
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
+            if (sub + 1 < BK / 16) read_frag((sub + 1) & 1, sub + 1);
             if (sub == 1) {
                 // dequantize packed tile kt+1 while the matrix cores run
                 dequant_tile(stage_b(IS1{}), stage_w(IS1{}), dq_n, dq_r0, k0 + BK, p.K);
             }
-            h8 b[NJ];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                b[j] = *reinterpret_cast<const h8*>(B + swz(wn * WTN + 32 * j + l32, 2 * sub + lhi));
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const h8 a = *reinterpret_cast<const h8*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a, b[j], acc[i][j]);
-            }
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(fa[sub & 1][i], fb[sub & 1][j], acc[i][j]);
         }
         lds_barrier();
     };
