@@ -24,8 +24,10 @@ Also reported on the same JSON line:
                 committed rocprofv3 counter runs, when their kernel source hash
                 matches the current source, else null;
   cpu_baseline  the CPU oracle's fused route on whole layers of the block;
-  secondary     the 70B-shaped MLP layers at M = 1 and the prefill GEMM at
-                M = 2048 (TFLOPS against the dense fp16 MFMA peak).
+  secondary     the same block with q/k/v and gate/up fused into one call each
+                (4 launches a step), the 70B-shaped MLP layers at M = 1 and the
+                prefill GEMM at M = 2048 (TFLOPS against the dense fp16 MFMA
+                peak).
 """
 from __future__ import annotations
 
@@ -255,10 +257,36 @@ def traffic_for(kernel: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+def fused_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500):
+    """The same block with the layers that take the same input fused into one
+    call each (q/k/v and gate/up concatenated along N: 4 launches a step), the
+    same weights, copies rotated and graphs replayed as in the main figure."""
+    specs = {name: (K, N, bias) for name, K, N, bias in synth.LLAMA7B_BLOCK}
+    layers = []
+    for gname, names in synth.LLAMA7B_FUSED:
+        parts = [synth.make_layer(specs[n][0], specs[n][1], G, M, seed=synth.layer_seed(workload, n, M),
+                                  bias=specs[n][2]) for n in names]
+        layers.append(Layer(q4, torch, gname, synth.concat_layers(parts), copies))
+    step_bytes = sum(ly.bytes for ly in layers)
+    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 50, stream, use_graph=True)
+    del graphs
+    lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
+    for ly in layers:
+        ly.close()
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (elapsed / steps) / 1e9
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_step": round(elapsed / steps * 1e6, 2), "launches_per_step": len(layers),
+            "per_layer_us": {ly.name: round(t * 1e6, 3) for ly, t in zip(layers, lt)}}
+
+
 def secondary(q4, torch, synth, lib, stream):
     """Quick figures on the other decode and prefill shapes (one handle each;
-    the 70B layers are rotated over enough copies to exceed the cache)."""
+    the 70B layers are rotated over enough copies to exceed the cache), and
+    the 7B block with projection fusion."""
     out = {}
+    out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
+                                                "llama7b_block_decode", 10)
     sp = ctypes.c_void_p(stream.cuda_stream)
     for name, K, N in synth.LLAMA70B_MLP:
         L = synth.make_layer(K, N, 128, 1, seed=synth.layer_seed("llama70b_mlp_decode", name, 1))

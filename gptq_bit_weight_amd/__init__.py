@@ -33,7 +33,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
 
 # Every function include/q4.h declares.
 EXPORTED_SYMBOLS = (
-    "q4_make", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
+    "q4_make", "q4_make_cat", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv",
 )
@@ -63,6 +63,8 @@ def load_library():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.q4_make.argtypes = [P, P, P, P, I, I, I]
     lib.q4_make.restype = P
+    lib.q4_make_cat.argtypes = [I, P, P, P, P, I, P, I]
+    lib.q4_make_cat.restype = P
     lib.q4_matmul.argtypes = [P, P, P, I, P]
     lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
     lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, I, P]
@@ -174,34 +176,79 @@ class Q4Matrix:
     """
 
     def __init__(self, qweight, qzeros, scales, g_idx=None, groupsize: int = 128):
+        self._build([(qweight, qzeros, scales)], g_idx, groupsize)
+
+    @classmethod
+    def concat(cls, parts, g_idx=None, groupsize: int = 128):
+        """One matrix over the column concatenation of layers that share the
+        input (QKV or gate/up fusion; q4_make_cat). parts: sequence of
+        (qweight, qzeros, scales) with equal K; g_idx shared by all parts.
+        Output columns follow part order; split() cuts an output into parts."""
+        self = cls.__new__(cls)
+        self._build(list(parts), g_idx, groupsize)
+        return self
+
+    def _build(self, parts, g_idx, groupsize):
         torch = _torch()
         lib = load_library()
-        _dev_tensor(qweight, torch.int32, "qweight")
-        if qweight.dim() != 2:
-            raise ValueError("qweight must be 2-D [K/8, N]")
-        K, N = int(qweight.shape[0]) * 8, int(qweight.shape[1])
-        check_shape(K, N, groupsize)
-        G = K if groupsize == -1 else groupsize
-        ng = -(-K // G) if G > 0 else 0
-        _dev_tensor(qzeros, torch.int32, "qzeros", (ng, N // 8))
-        _dev_tensor(scales, torch.float16, "scales", (ng, N))
+        if not parts:
+            raise ValueError("at least one part is needed")
+        K = None
+        ns = []
+        for i, (qweight, qzeros, scales) in enumerate(parts):
+            _dev_tensor(qweight, torch.int32, f"qweight[{i}]")
+            if qweight.dim() != 2:
+                raise ValueError("qweight must be 2-D [K/8, N]")
+            k_i, n_i = int(qweight.shape[0]) * 8, int(qweight.shape[1])
+            if K is not None and k_i != K:
+                raise ValueError(f"part {i} has K={k_i}, part 0 has K={K}")
+            K = k_i
+            check_shape(K, n_i, groupsize)
+            G = K if groupsize == -1 else groupsize
+            ng = -(-K // G) if G > 0 else 0
+            _dev_tensor(qzeros, torch.int32, f"qzeros[{i}]", (ng, n_i // 8))
+            _dev_tensor(scales, torch.float16, f"scales[{i}]", (ng, n_i))
+            ns.append(n_i)
+        check_shape(K, sum(ns), groupsize)
         if g_idx is not None:
             _dev_tensor(g_idx, torch.int32, "g_idx", (K,))
-        dev = qweight.device
-        for t, nm in ((qzeros, "qzeros"), (scales, "scales"), (g_idx, "g_idx")):
-            if t is not None and t.device != dev:
-                raise ValueError(f"{nm} is on {t.device}, qweight on {dev}")
+        dev = parts[0][0].device
+        for i, part in enumerate(parts):
+            for t, nm in zip(part, ("qweight", "qzeros", "scales")):
+                if t.device != dev:
+                    raise ValueError(f"{nm}[{i}] is on {t.device}, qweight[0] on {dev}")
+        if g_idx is not None and g_idx.device != dev:
+            raise ValueError(f"g_idx is on {g_idx.device}, qweight[0] on {dev}")
+        gp = g_idx.data_ptr() if g_idx is not None else None
         with torch.cuda.device(dev):
-            h = lib.q4_make(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
-                            g_idx.data_ptr() if g_idx is not None else None, K, N, groupsize)
+            if len(parts) == 1:
+                qw, qz, sc = parts[0]
+                h = lib.q4_make(qw.data_ptr(), qz.data_ptr(), sc.data_ptr(), gp, K, ns[0], groupsize)
+                what = "q4_make"
+            else:
+                arr = lambda vals: (ctypes.c_void_p * len(vals))(*vals)
+                h = lib.q4_make_cat(len(parts), arr([p[0].data_ptr() for p in parts]),
+                                    arr([p[1].data_ptr() for p in parts]),
+                                    arr([p[2].data_ptr() for p in parts]), gp, K,
+                                    (ctypes.c_int * len(ns))(*ns), groupsize)
+                what = "q4_make_cat"
         if not h:
-            _raise(lib.q4_last_status(), "q4_make")
+            _raise(lib.q4_last_status(), what)
         self._h = ctypes.c_void_p(h)
-        self.K, self.N, self.device = K, N, dev
+        self.K, self.N, self.device = K, sum(ns), dev
+        self.part_n = tuple(ns)
         gs, act = ctypes.c_int(0), ctypes.c_int(0)
         lib.q4_handle_info(self._h, None, None, ctypes.byref(gs), ctypes.byref(act))
         self.groupsize = int(gs.value)
         self.act_order = bool(act.value)
+
+    def split(self, out):
+        """Views of an output [M, N] as one [M, N_i] per part (column order)."""
+        views, off = [], 0
+        for n in self.part_n:
+            views.append(out[:, off:off + n])
+            off += n
+        return views
 
     def _handle(self):
         if self._h is None:

@@ -16,7 +16,7 @@ hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                             int M, hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
-                         hipStream_t stream);
+                         int n_total, int col_off, hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
 hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
@@ -63,16 +63,33 @@ q4_status check_device(int* dev, int* num_cu)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
-                    const int32_t* g_idx, int K, int N, int groupsize, q4_matrix** out)
+// One handle over the column concatenation of `parts` layers that share K,
+// groupsize and g_idx (part i supplies columns [off_i, off_i + N[i]) of the
+// result, in part order). q4_make is the one-part case.
+q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
+                    const uint16_t* const* scales, const int32_t* g_idx, int K, const int* Np,
+                    int groupsize, const char* who, q4_matrix** out)
 {
-    if (!qweight || !qzeros || !scales)
-        return fail(Q4_ERR_INVALID_ARG, "q4_make: qweight, qzeros and scales must be non-null");
+    if (parts < 1 || parts > kMaxParts)
+        return fail(Q4_ERR_INVALID_ARG, "%s: parts=%d outside [1, %d]", who, parts, kMaxParts);
+    if (!qweight || !qzeros || !scales || !Np)
+        return fail(Q4_ERR_INVALID_ARG, "%s: null array argument", who);
+    long long ntot = 0;
+    for (int i = 0; i < parts; ++i) {
+        if (!qweight[i] || !qzeros[i] || !scales[i])
+            return fail(Q4_ERR_INVALID_ARG, "%s: qweight, qzeros and scales must be non-null (part %d)", who, i);
+        if (Np[i] <= 0 || Np[i] % 8)
+            return fail(Q4_ERR_INVALID_ARG, "%s: N=%d of part %d is not a positive multiple of 8", who, Np[i], i);
+        if (!aligned(qweight[i], 16) || !aligned(scales[i], 8) || !aligned(qzeros[i], 4))
+            return fail(Q4_ERR_INVALID_ARG, "%s: qweight must be 16-byte aligned, scales 8-byte (part %d)",
+                        who, i);
+        ntot += Np[i];
+    }
+    if (ntot > INT_MAX) return fail(Q4_ERR_UNSUPPORTED, "%s: %lld columns in total", who, ntot);
+    const int N = (int)ntot;
     int G = 0;
     q4_status st = check_shape(K, N, groupsize, &G);
     if (st != Q4_OK) return st;
-    if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4))
-        return fail(Q4_ERR_INVALID_ARG, "q4_make: qweight must be 16-byte aligned, scales 8-byte");
     int dev = -1, num_cu = 0;
     st = check_device(&dev, &num_cu);
     if (st != Q4_OK) return st;
@@ -125,12 +142,21 @@ q4_status make_impl(const int32_t* qweight, const int32_t* qzeros, const uint16_
         if ((e = hipMemcpy(h->inv_perm, inv.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: perm"));
     }
-    if ((e = hipMemcpy(h->scales, scales, (size_t)ng * N * 2, hipMemcpyDeviceToDevice)) != hipSuccess)
-        return bail(hip_fail(e, "q4_make: scales"));
-    if ((e = hipMemcpy(h->qzeros, qzeros, (size_t)ng * (N / 8) * 4, hipMemcpyDeviceToDevice)) != hipSuccess)
-        return bail(hip_fail(e, "q4_make: qzeros"));
-    if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight), h->perm, h->qweight, K, N, 0)) != hipSuccess)
-        return bail(hip_fail(e, "q4_make: repack launch"));
+    // Part i's scales and zero words are columns off_i .. off_i + N_i of the
+    // handle's rows (zero words: off_i / 8 .., every offset a multiple of 8).
+    int off = 0;
+    for (int i = 0; i < parts; ++i) {
+        if ((e = hipMemcpy2D(h->scales + off, (size_t)N * 2, scales[i], (size_t)Np[i] * 2, (size_t)Np[i] * 2,
+                             (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: scales"));
+        if ((e = hipMemcpy2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, qzeros[i], (size_t)(Np[i] / 8) * 4,
+                             (size_t)(Np[i] / 8) * 4, (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: qzeros"));
+        if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight[i]), h->perm, h->qweight, K, Np[i], N,
+                               off, 0)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: repack launch"));
+        off += Np[i];
+    }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return bail(hip_fail(e, "q4_make: repack"));
     *out = h;
     return Q4_OK;
@@ -233,7 +259,19 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
                    const int32_t* g_idx, int K, int N, int groupsize)
 {
     q4_matrix* h = nullptr;
-    return q4::make_impl(qweight, qzeros, scales, g_idx, K, N, groupsize, &h) == Q4_OK ? h : nullptr;
+    return q4::make_impl(1, &qweight, &qzeros, &scales, g_idx, K, &N, groupsize, "q4_make", &h) == Q4_OK
+               ? h
+               : nullptr;
+}
+
+q4_matrix* q4_make_cat(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
+                       const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
+                       int groupsize)
+{
+    q4_matrix* h = nullptr;
+    return q4::make_impl(parts, qweight, qzeros, scales, g_idx, K, N, groupsize, "q4_make_cat", &h) == Q4_OK
+               ? h
+               : nullptr;
 }
 
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M, hipStream_t stream)

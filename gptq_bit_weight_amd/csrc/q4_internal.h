@@ -26,6 +26,7 @@ constexpr int kGemvWaves = 8;        // waves per workgroup (they split its K ra
 constexpr int kGemvDepth = 4;        // k-blocks in flight per wave
 constexpr int kMaxSplits = 16;       // K splits across workgroups (grid.y)
 constexpr int kMaxColTiles = 4;      // 16-column MFMA tiles per wave
+constexpr int kMaxParts = 64;        // layers one q4_make_cat handle may concatenate
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
 constexpr int kGemmBM = 256;

@@ -30,12 +30,14 @@ __device__ __forceinline__ size_t private_word(int kk, int n, int N, int* e)
     return ((size_t)(4 * b + kb) * N + n) * 4 + i;
 }
 
-// One thread per output word: gather the eight codes of (sorted) rows
+// One thread per output word of one part (N columns of a handle with n_total,
+// placed at column col_off): gather the eight codes of (sorted) rows
 // k' = 32 * (4b + i) + 8 * kb + e from their original rows perm[k'] and store
 // them in the private nibble slots.
 __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restrict__ src,
                                                         const int32_t* __restrict__ perm,
-                                                        uint32_t* __restrict__ dst, int K, int N)
+                                                        uint32_t* __restrict__ dst, int K, int N,
+                                                        int n_total, int col_off)
 {
     const size_t total = q4::packed_words(K, N);
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restri
             const uint32_t code = (src[(size_t)(k >> 3) * N + n] >> (4 * (k & 7))) & 0xFu;
             w |= code << (4 * slot_of(e));
         }
-        dst[idx] = w;
+        dst[((size_t)q * n_total + col_off + n) * 4 + i] = w;
     }
 }
 
@@ -117,10 +119,10 @@ int grid_for(size_t total)
 namespace q4 {
 
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
-                         hipStream_t stream)
+                         int n_total, int col_off, hipStream_t stream)
 {
     hipLaunchKernelGGL(q4_repack_kernel, dim3(grid_for(packed_words(K, N))), dim3(256), 0, stream,
-                       src, perm, dst, K, N);
+                       src, perm, dst, K, N, n_total, col_off);
     return hipGetLastError();
 }
 

@@ -148,6 +148,29 @@ void q4_free(q4_matrix* h);
 
 /* Status and message of the last failing call on this thread. */
 q4_status q4_last_status(void);
+/*
+ * q4_make_cat -- one handle over the column concatenation of `parts` layers
+ * (1 <= parts <= 64) that take the same input: QKV or gate/up projection
+ * fusion (GPTQModel wiki "Inference Backends", section "How AUTO selection
+ * works": eligible QKV or gate/up calls are combined into one after backend
+ * selection). One q4_matmul then computes all parts with one launch.
+ *
+ * Arguments: arrays of `parts` device pointers qweight[i] [K/8][N[i]],
+ * qzeros[i] [K/groupsize][N[i]/8], scales[i] [K/groupsize][N[i]] (layouts as
+ * in q4_make); N[i] > 0 and a multiple of 8 (host array); one g_idx shared by
+ * every part (NULL allowed), K and groupsize as in q4_make.
+ *
+ * The handle behaves as one layer with N = sum N[i] columns: output column
+ * off_i + n (off_i = N[0] + ... + N[i-1]) is column n of part i, and a bias
+ * passed to q4_matmul_bias is the concatenation of the parts' biases. Each
+ * column's result is the one a handle of its own part gives (same kernel,
+ * same order of accumulation when the plan takes the same K splits).
+ * Ownership and errors as q4_make; every part's arguments are checked.
+ */
+q4_matrix* q4_make_cat(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
+                       const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
+                       int groupsize);
+
 const char* q4_last_error(void);
 
 /*

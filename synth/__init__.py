@@ -109,6 +109,30 @@ def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = F
                  g_idx=g_idx, x=x, bias=b, seed=seed)
 
 
+def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
+    """The layers `parts` (same K, G and g_idx) side by side: their packed
+    weights, packed zeros, scales and biases concatenated along N, in part
+    order, with one shared activation batch (parts[0].x unless given). A part
+    without bias contributes zeros. Pure data plumbing, as QKV or gate/up
+    projections that take the same input are stacked."""
+    p0 = parts[0]
+    for p in parts[1:]:
+        if p.K != p0.K or p.G != p0.G:
+            raise ValueError("parts must share K and G")
+        if (p.g_idx is None) != (p0.g_idx is None) or (
+                p.g_idx is not None and not np.array_equal(p.g_idx, p0.g_idx)):
+            raise ValueError("parts must share g_idx")
+    bias = None
+    if any(p.bias is not None for p in parts):
+        bias = np.concatenate([p.bias if p.bias is not None else np.zeros(p.N, np.float16)
+                               for p in parts])
+    return Layer(K=p0.K, N=sum(p.N for p in parts), G=p0.G,
+                 qweight=np.ascontiguousarray(np.concatenate([p.qweight for p in parts], axis=1)),
+                 qzeros=np.ascontiguousarray(np.concatenate([p.qzeros for p in parts], axis=1)),
+                 scales=np.ascontiguousarray(np.concatenate([p.scales for p in parts], axis=1)),
+                 g_idx=p0.g_idx, x=p0.x if x is None else x, bias=bias, seed=p0.seed)
+
+
 def make_x(M: int, K: int, seed: int) -> np.ndarray:
     """A fresh fp16 activation batch x ~ N(0, 1)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -116,7 +140,8 @@ def make_x(M: int, K: int, seed: int) -> np.ndarray:
 
 
 # Llama-7B-shaped decoder block: q, k, v, o (4096x4096), gate, up (4096x11008),
-# down (11008x4096); bias on the q projection only.
+# down (11008x4096); bias on the q projection only. LLAMA7B_FUSED groups the
+# layers that take the same input (q/k/v, gate/up) for one call each.
 LLAMA7B_BLOCK = [
     ("q_proj", 4096, 4096, True),
     ("k_proj", 4096, 4096, False),
@@ -126,6 +151,8 @@ LLAMA7B_BLOCK = [
     ("up_proj", 4096, 11008, False),
     ("down_proj", 11008, 4096, False),
 ]
+LLAMA7B_FUSED = [("qkv_proj", ("q_proj", "k_proj", "v_proj")), ("o_proj", ("o_proj",)),
+                 ("gate_up_proj", ("gate_proj", "up_proj")), ("down_proj", ("down_proj",))]
 
 # Llama-70B-shaped MLP layers (gate/up share a shape).
 LLAMA70B_MLP = [

@@ -390,3 +390,26 @@ def test_tolerance_scale_is_sum_abs(oracle_mod):
     assert np.all(y == K * 0.5 * 2.0) and np.array_equal(A, y)
     y2, A2 = oracle_mod.matmul(-x, pack_rows(q), pack_cols(z), s, None, K, N, G)
     assert np.array_equal(y2, -y) and np.array_equal(A2, A)
+
+
+def test_concatenated_layers_equal_their_parts(oracle_mod):
+    """Projection fusion is a column concatenation: the oracle on the stacked
+    layers equals the parts' results side by side, bit for bit (every column
+    is computed independently), including the packed zeros of parts whose
+    widths are not multiples of 64 and a part without bias."""
+    K, G = 256, 64
+    parts = [synth.make_layer(K, n, G, 3, seed=s, bias=b)
+             for n, s, b in ((40, 1, True), (16, 2, False), (72, 3, True))]
+    x = parts[0].x
+    cat = synth.concat_layers(parts, x)
+    assert cat.N == 128 and cat.qzeros.shape == (K // G, 16)
+    y, A = oracle_mod.matmul(x, cat.qweight, cat.qzeros, cat.scales, None, K, cat.N, G, bias=cat.bias)
+    outs = [oracle_mod.matmul(x, p.qweight, p.qzeros, p.scales, None, K, p.N, G, bias=p.bias)
+            for p in parts]
+    assert np.array_equal(y, np.hstack([o[0] for o in outs]))
+    assert np.array_equal(A, np.hstack([o[1] for o in outs]))
+    dq = oracle_mod.dequant16(cat.qweight, cat.qzeros, cat.scales, None, K, cat.N, G)
+    assert np.array_equal(dq, np.hstack([oracle_mod.dequant16(p.qweight, p.qzeros, p.scales, None,
+                                                              K, p.N, G) for p in parts]))
+    with pytest.raises(ValueError):
+        synth.concat_layers([parts[0], synth.make_layer(128, 16, G, 3, seed=4)])
