@@ -169,7 +169,8 @@ def _stream_ptr(stream) -> int:
 class Q4Matrix:
     """A 4-bit GPTQ weight matrix prepared for the MI355X kernels (q4_make).
 
-    qweight int32 [K/8, N], qzeros int32 [K/G, N/8], scales fp16 [K/G, N],
+    qweight int32 [K/8, N], qzeros int32 [K/G, N/8] (None for a symmetric
+    layer stored without zeros: every zero point is 8), scales fp16 [K/G, N],
     g_idx int32 [K] or None; all on the current GPU, contiguous. The handle
     keeps its own copy in a private layout; later edits of the tensors do
     not reach it.
@@ -206,7 +207,8 @@ class Q4Matrix:
             check_shape(K, n_i, groupsize)
             G = K if groupsize == -1 else groupsize
             ng = -(-K // G) if G > 0 else 0
-            _dev_tensor(qzeros, torch.int32, f"qzeros[{i}]", (ng, n_i // 8))
+            if qzeros is not None:      # None: symmetric, every zero point is 8
+                _dev_tensor(qzeros, torch.int32, f"qzeros[{i}]", (ng, n_i // 8))
             _dev_tensor(scales, torch.float16, f"scales[{i}]", (ng, n_i))
             ns.append(n_i)
         check_shape(K, sum(ns), groupsize)
@@ -215,7 +217,7 @@ class Q4Matrix:
         dev = parts[0][0].device
         for i, part in enumerate(parts):
             for t, nm in zip(part, ("qweight", "qzeros", "scales")):
-                if t.device != dev:
+                if t is not None and t.device != dev:
                     raise ValueError(f"{nm}[{i}] is on {t.device}, qweight[0] on {dev}")
         if g_idx is not None and g_idx.device != dev:
             raise ValueError(f"g_idx is on {g_idx.device}, qweight[0] on {dev}")
@@ -223,12 +225,13 @@ class Q4Matrix:
         with torch.cuda.device(dev):
             if len(parts) == 1:
                 qw, qz, sc = parts[0]
-                h = lib.q4_make(qw.data_ptr(), qz.data_ptr(), sc.data_ptr(), gp, K, ns[0], groupsize)
+                h = lib.q4_make(qw.data_ptr(), qz.data_ptr() if qz is not None else None, sc.data_ptr(),
+                                gp, K, ns[0], groupsize)
                 what = "q4_make"
             else:
                 arr = lambda vals: (ctypes.c_void_p * len(vals))(*vals)
                 h = lib.q4_make_cat(len(parts), arr([p[0].data_ptr() for p in parts]),
-                                    arr([p[1].data_ptr() for p in parts]),
+                                    arr([p[1].data_ptr() if p[1] is not None else None for p in parts]),
                                     arr([p[2].data_ptr() for p in parts]), gp, K,
                                     (ctypes.c_int * len(ns))(*ns), groupsize)
                 what = "q4_make_cat"

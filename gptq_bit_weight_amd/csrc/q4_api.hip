@@ -72,15 +72,15 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
 {
     if (parts < 1 || parts > kMaxParts)
         return fail(Q4_ERR_INVALID_ARG, "%s: parts=%d outside [1, %d]", who, parts, kMaxParts);
-    if (!qweight || !qzeros || !scales || !Np)
+    if (!qweight || !scales || !Np)
         return fail(Q4_ERR_INVALID_ARG, "%s: null array argument", who);
     long long ntot = 0;
     for (int i = 0; i < parts; ++i) {
-        if (!qweight[i] || !qzeros[i] || !scales[i])
-            return fail(Q4_ERR_INVALID_ARG, "%s: qweight, qzeros and scales must be non-null (part %d)", who, i);
+        if (!qweight[i] || !scales[i])
+            return fail(Q4_ERR_INVALID_ARG, "%s: qweight and scales must be non-null (part %d)", who, i);
         if (Np[i] <= 0 || Np[i] % 8)
             return fail(Q4_ERR_INVALID_ARG, "%s: N=%d of part %d is not a positive multiple of 8", who, Np[i], i);
-        if (!aligned(qweight[i], 16) || !aligned(scales[i], 8) || !aligned(qzeros[i], 4))
+        if (!aligned(qweight[i], 16) || !aligned(scales[i], 8) || (qzeros && !aligned(qzeros[i], 4)))
             return fail(Q4_ERR_INVALID_ARG, "%s: qweight must be 16-byte aligned, scales 8-byte (part %d)",
                         who, i);
         ntot += Np[i];
@@ -149,9 +149,17 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
         if ((e = hipMemcpy2D(h->scales + off, (size_t)N * 2, scales[i], (size_t)Np[i] * 2, (size_t)Np[i] * 2,
                              (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: scales"));
-        if ((e = hipMemcpy2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, qzeros[i], (size_t)(Np[i] / 8) * 4,
-                             (size_t)(Np[i] / 8) * 4, (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
-            return bail(hip_fail(e, "q4_make: qzeros"));
+        // A part without zeros is symmetric: every zero point is
+        // 2^(bits-1) = 8 (GPTQModel wiki "Inference Backends", section
+        // "Packing, conversion, and runtime initialization", row "Missing
+        // zeros"), i.e. zero words 0x88888888.
+        const int32_t* qz = qzeros ? qzeros[i] : nullptr;
+        if (qz)
+            e = hipMemcpy2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, qz, (size_t)(Np[i] / 8) * 4,
+                            (size_t)(Np[i] / 8) * 4, (size_t)ng, hipMemcpyDeviceToDevice);
+        else
+            e = hipMemset2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, 0x88, (size_t)(Np[i] / 8) * 4, (size_t)ng);
+        if (e != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
         if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight[i]), h->perm, h->qweight, K, Np[i], N,
                                off, 0)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: repack launch"));

@@ -74,8 +74,12 @@ enum {
  * an optional group index; "detects whether the model uses activation
  * ordering by checking if g_idx is non-trivial").
  *
- * Arguments: device pointers qweight, qzeros, scales (required), g_idx
- * (optional, NULL allowed); K, N > 0 with K % 32 == 0 and N % 8 == 0;
+ * Arguments: device pointers qweight and scales (required), qzeros (NULL for
+ * a symmetric layer stored without zeros: every zero point is then
+ * 2^(bits-1) = 8, as GPTQModel wiki "Inference Backends", section "Packing,
+ * conversion, and runtime initialization", row "Missing zeros" synthesizes
+ * it), g_idx (optional, NULL allowed); K, N > 0 with K % 32 == 0 and
+ * N % 8 == 0;
  * groupsize in {32, 64, 128, 256} with K % groupsize == 0, or -1 for one
  * group spanning K (then K % 32 == 0 still applies).
  *
@@ -157,8 +161,9 @@ q4_status q4_last_status(void);
  *
  * Arguments: arrays of `parts` device pointers qweight[i] [K/8][N[i]],
  * qzeros[i] [K/groupsize][N[i]/8], scales[i] [K/groupsize][N[i]] (layouts as
- * in q4_make); N[i] > 0 and a multiple of 8 (host array); one g_idx shared by
- * every part (NULL allowed), K and groupsize as in q4_make.
+ * in q4_make; qzeros[i] NULL, or qzeros itself NULL, for symmetric parts);
+ * N[i] > 0 and a multiple of 8 (host array); one g_idx shared by every part
+ * (NULL allowed), K and groupsize as in q4_make.
  *
  * The handle behaves as one layer with N = sum N[i] columns: output column
  * off_i + n (off_i = N[0] + ... + N[i-1]) is column n of part i, and a bias

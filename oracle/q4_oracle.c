@@ -30,6 +30,11 @@
  *    word (g, c). Words are read as their unsigned 32-bit pattern (nibble 7
  *    sets the sign bit of the int32).
  *  - No zero-point offset: the stored nibble is z itself.
+ *  - No stored zeros (qzeros NULL): a symmetric layer, whose zero point is
+ *    2^(bits-1) = 8 for every group and column (GPTQModel wiki "Inference
+ *    Backends", section "Packing, conversion, and runtime initialization",
+ *    packing-control row "Missing zeros": symmetric modules synthesize
+ *    2 ** (bits - 1)).
  *  - g(k) = g_idx[k] when g_idx is given, else k / G. groupsize <= 0 means a
  *    single group (G = K). The number of groups is ceil(K / G).
  *  - The dequantized value in fp32, s * (q - z), is exact (an 11-bit
@@ -129,9 +134,11 @@ static inline unsigned code_q(const int32_t* qweight, int64_t N, int64_t k, int6
     return nibble(qweight[(k / 8) * N + n], (int)(k % 8));
 }
 
-/* z[g][n]: 4-bit zero point of group g, column n. */
+/* z[g][n]: 4-bit zero point of group g, column n; 8 for a symmetric layer
+ * stored without zeros (qzeros NULL). */
 static inline unsigned code_z(const int32_t* qzeros, int64_t N, int64_t g, int64_t n)
 {
+    if (!qzeros) return 8u;
     return nibble(qzeros[g * (N / 8) + n / 8], (int)(n % 8));
 }
 

@@ -287,3 +287,36 @@ def test_special_values_propagate():
     keep[9] = False
     compare(y[:, keep], yD[:, keep], A[:, keep], "special")
     assert fin[:, keep].all()
+
+
+# ------------------------------------------------------ format variants --
+
+@pytest.mark.parametrize("M", [1, 6, 40])
+def test_symmetric_layer_without_zeros(M):
+    """qzeros absent: a symmetric layer whose zero points are all 8 (the
+    oracle's reading of the "Missing zeros" row), on both kernels; the dump
+    stays bit-exact and a fused handle may mix symmetric and stored-zero
+    parts."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(1024, 200, 128, M, 31, bias=True)
+    announce(f"symmetric M={M}")
+    t = device_tensors(L)
+    W = q4.Q4Matrix(t["qweight"], None, t["scales"], None, groupsize=128)
+    y = W.matmul(t["x"], t["bias"])
+    torch.cuda.synchronize()
+    yD, A = oracle.matmul(L.x, L.qweight, None, L.scales, None, L.K, L.N, L.G, bias=L.bias)
+    compare(y.cpu().numpy(), yD, A, f"symmetric M={M}")
+    ref = oracle.dequant16(L.qweight, None, L.scales, None, L.K, L.N, L.G)
+    for path in (q4.PATH_GEMV, q4.PATH_MFMA):
+        assert np.array_equal(W.dequant_dump(path).cpu().numpy().view(np.uint16), ref)
+    # fused: [symmetric part | stored-zero part]
+    L2 = _layer(1024, 64, 128, M, 32)
+    t2 = device_tensors(L2)
+    Wc = q4.Q4Matrix.concat([(t["qweight"], None, t["scales"]),
+                             (t2["qweight"], t2["qzeros"], t2["scales"])], groupsize=128)
+    yc = Wc.matmul(t["x"])
+    torch.cuda.synchronize()
+    y1, A1 = oracle.matmul(L.x, L.qweight, None, L.scales, None, L.K, L.N, L.G)
+    y2, A2 = oracle.matmul(L.x, L2.qweight, L2.qzeros, L2.scales, None, L.K, L2.N, L.G)
+    compare(yc.cpu().numpy(), np.hstack([y1, y2]), np.hstack([A1, A2]), f"symmetric fused M={M}")

@@ -413,3 +413,21 @@ def test_concatenated_layers_equal_their_parts(oracle_mod):
                                                               K, p.N, G) for p in parts]))
     with pytest.raises(ValueError):
         synth.concat_layers([parts[0], synth.make_layer(128, 16, G, 3, seed=4)])
+
+
+def test_missing_zeros_mean_symmetric_eight(oracle_mod):
+    """qzeros absent (a symmetric layer): the zero point is 2^(bits-1) = 8
+    ("Inference Backends", packing-control row "Missing zeros"). Pinned two
+    ways: equal to explicit zero words 0x88888888, and the closed form
+    W = s * (q - 8) on hand-built codes."""
+    L = synth.make_layer(256, 40, 64, 2, seed=11)
+    eights = np.full_like(L.qzeros, np.int32(np.uint32(0x88888888).view(np.int32)))
+    a = oracle_mod.matmul(L.x, L.qweight, None, L.scales, None, 256, 40, 64)
+    b = oracle_mod.matmul(L.x, L.qweight, eights, L.scales, None, 256, 40, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(oracle_mod.dequant16(L.qweight, None, L.scales, None, 256, 40, 64),
+                          oracle_mod.dequant16(L.qweight, eights, L.scales, None, 256, 40, 64))
+    K, N, G = 16, 8, 16
+    q = np.arange(K * N, dtype=np.int64).reshape(K, N) % 16
+    W = oracle_mod.dequant32(pack_rows(q), None, np.ones((1, N), np.float16), None, K, N, G)
+    assert np.array_equal(W, (q - 8).astype(np.float32))
