@@ -180,11 +180,19 @@ int choose_path(const q4_matrix* h, int M, int forced)
 }
 
 // Grow the act-order activation workspace to hold M x K halfs.
-q4_status ensure_xperm(const q4_matrix* h, int M)
+q4_status ensure_xperm(const q4_matrix* h, int M, hipStream_t stream)
 {
     const size_t need = (size_t)M * h->K;
     std::lock_guard<std::mutex> lock(h->ws_mutex);
     if (h->xperm_elems >= need) return Q4_OK;
+    // Growing synchronizes the device and allocates, which a stream under
+    // graph capture cannot do: say so instead of breaking the capture.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(Q4_ERR_INVALID_ARG,
+                    "q4_matmul: the act-order workspace must grow to M=%d under stream capture; "
+                    "make one uncaptured call with this M (or larger) first", M);
     // Earlier calls may still read the old buffer: wait for them first.
     Q4_HIP(hipDeviceSynchronize(), "q4_matmul: workspace grow");
     (void)hipFree(h->xperm);
@@ -230,7 +238,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
 
     const uint16_t* xe = x;
     if (h->act_order) {
-        q4_status st = ensure_xperm(h, M);
+        q4_status st = ensure_xperm(h, M, stream);
         if (st != Q4_OK) return st;
         Q4_HIP(launch_permute_x(x, h->perm, h->xperm, M, h->K, stream), "q4_matmul: permute launch");
         xe = h->xperm;

@@ -117,6 +117,13 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
  * Concurrency: the handle's workspace is shared by its calls, so calls on one
  * handle must be ordered on one stream (or synchronized); different handles
  * are independent.
+ *
+ * Graph capture: a call may be captured into a HIP graph and replayed; it
+ * enqueues kernels only (no memset or copy nodes; the skinny kernel's split-K
+ * counters are reset by the kernel). An act-order handle grows its
+ * activation workspace on the first call with a larger M, which cannot
+ * happen under capture: such a call returns Q4_ERR_INVALID_ARG, so make one
+ * uncaptured call with the largest M first.
  */
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M,
                     hipStream_t stream);

@@ -320,3 +320,38 @@ def test_symmetric_layer_without_zeros(M):
     y1, A1 = oracle.matmul(L.x, L.qweight, None, L.scales, None, L.K, L.N, L.G)
     y2, A2 = oracle.matmul(L.x, L2.qweight, L2.qzeros, L2.scales, None, L.K, L2.N, L.G)
     compare(yc.cpu().numpy(), np.hstack([y1, y2]), np.hstack([A1, A2]), f"symmetric fused M={M}")
+
+
+# ------------------------------------------------------------ HIP graphs --
+
+@pytest.mark.parametrize("M,splits,act", [(1, 4, False), (3, 0, True), (40, 0, False), (64, 0, True)])
+def test_graph_replay_matches_eager(M, splits, act):
+    """q4_matmul captured in a HIP graph and replayed several times, with the
+    program's own eager work and synchronizations between replays, gives the
+    eager result every time: the split-K arrival counters are reset by the
+    kernel itself and nothing in the captured path is a memset node."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(2048, 328, 128, M, 40 + M, act_order=act, bias=True)
+    announce(f"graph M={M} splits={splits} act={act}")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref = W.matmul(t["x"], t["bias"], splits=splits, stream=s).clone()
+    s.synchronize()
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        W.matmul(t["x"], t["bias"], out=out, splits=splits, stream=torch.cuda.current_stream())
+    for r in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        # eager work between replays on the same handle
+        W.matmul(t["x"], splits=splits)
+        torch.cuda.synchronize()
+    yD, A = oracle_full(L)
+    compare(out.cpu().numpy(), yD, A, f"graph M={M}")
