@@ -267,7 +267,8 @@ class Q4Matrix:
 
         path: 0 automatic, PATH_GEMV or PATH_MFMA. variant: skinny kernel --
         16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 automatic,
-        1 register-staged, 2 direct-to-LDS. splits: skinny kernel K splits
+        1 register-staged, 2 direct-to-LDS, 3 weights streamed into
+        registers (the automatic choice). splits: skinny kernel K splits
         (0 planned, 1..16); must be 0 for the GEMM."""
         torch = _torch()
         h = self._handle()

@@ -15,6 +15,8 @@ hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t
                            int M, hipStream_t stream);
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                             int M, hipStream_t stream);
+hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                              int M, hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          int n_total, int col_off, hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
@@ -232,8 +234,8 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
     } else {
         if (splits != 0)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the GEMM takes no K splits (got %d)", splits);
-        if (variant < 0 || variant > 2)
-            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1 or 2", variant);
+        if (variant < 0 || variant > 3)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1, 2 or 3", variant);
     }
 
     const uint16_t* xe = x;
@@ -250,16 +252,17 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (splits) s = splits;
         Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, stream), "q4_matmul: gemv launch");
     } else {
-        // Two GEMM variants: register-staged tiles (80 KiB of LDS, two
-        // workgroups per CU) when there are at least two output tiles per CU,
-        // else the direct-to-LDS pipeline (one workgroup per CU, deeper
-        // prefetch). `variant` picks one explicitly (1 or 2).
-        if (variant == 0) {
-            const long long tiles = (long long)((h->N + kGemmBN - 1) / kGemmBN) * ((M + kGemmBM - 1) / kGemmBM);
-            variant = tiles >= 2LL * h->num_cu ? 1 : 2;
-        }
+        // Three GEMM variants share tile shape and accumulation order: the
+        // automatic choice streams the weights into registers (activations
+        // in a 2-stage LDS ring, two workgroups per CU), which measured
+        // fastest on every prefill shape; `variant` 1 (register-staged
+        // tiles) and 2 (direct-to-LDS pipeline with one dequantization per
+        // workgroup) select the others.
+        if (variant == 0) variant = 3;
         if (variant == 1)
             Q4_HIP(launch_gemm_regs(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+        else if (variant == 3)
+            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
         else
             Q4_HIP(launch_gemm_dma(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
     }

@@ -301,8 +301,12 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
         // Issue tile kt+2: packed first, then activations.
         int n_cur = 0;
         if (kt + 2 < ktiles) {
+            // the waits below count loads in this order: keep it
+            __builtin_amdgcn_sched_barrier(0);
             load_b(c, p, stage_b(IS2{}), wave, kt + 2);
+            __builtin_amdgcn_sched_barrier(0);
             load_a(c, p, stage_a(IS2{}), wave, kt + 2);
+            __builtin_amdgcn_sched_barrier(0);
             n_cur = A_LOADS + B_LOADS;
         }
         // This step reads activation tile kt (issued two steps ago) and packed

@@ -144,8 +144,9 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
  *   skinny kernel: variant = 16-column MFMA tiles per wave, 0 (planned), 1, 2
  *                  or 4; splits = K splits across workgroups, 0 (planned) or
  *                  1..16;
- *   GEMM:          variant = 0 (automatic), 1 (register-staged tiles) or
- *                  2 (direct-to-LDS pipeline); splits must be 0.
+ *   GEMM:          variant = 0 (automatic: 3), 1 (register-staged tiles),
+ *                  2 (direct-to-LDS pipeline) or 3 (activations in LDS,
+ *                  weights streamed into registers); splits must be 0.
  * Anything else is Q4_ERR_INVALID_ARG. Results differ between paths,
  * variants and split counts only by fp32 rounding.
  */

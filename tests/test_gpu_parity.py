@@ -97,10 +97,11 @@ GEMM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("K,N,G,M,act,bias", GEMM_CASES)
 def test_gemm_parity(K, N, G, M, act, bias, variant):
-    """variant 0: automatic; 1: register-staged tiles; 2: direct-to-LDS pipeline."""
+    """variant 0: automatic; 1: register-staged tiles; 2: direct-to-LDS pipeline;
+    3: activations in LDS, weights streamed into registers."""
     import gptq_bit_weight_amd as q4
     L = _layer(K, N, G, M, 2, act_order=act, bias=bias)
     announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias} variant={variant}")
@@ -122,8 +123,9 @@ def test_gemm_variants_bit_identical():
     W = make_matrix(L, t)
     a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=1)
     b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=2)
+    c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=3)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    assert torch.equal(a, b) and torch.equal(a, c)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
@@ -244,7 +246,7 @@ def test_m_zero_and_argument_errors():
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_MFMA, splits=3)
     with pytest.raises(ValueError):
-        W.matmul(t["x"], path=q4.PATH_MFMA, variant=3)
+        W.matmul(t["x"], path=q4.PATH_MFMA, variant=4)
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_GEMV, variant=3)
     bad = torch.full((256,), 3, dtype=torch.int32, device="cuda")      # only groups 0, 1
