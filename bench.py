@@ -25,9 +25,11 @@ Also reported on the same JSON line:
                 matches the current source, else null;
   cpu_baseline  the CPU oracle's fused route on whole layers of the block;
   secondary     the same block with q/k/v and gate/up fused into one call each
-                (4 launches a step), the 70B-shaped MLP layers at M = 1 and the
-                prefill GEMM at M = 2048 (TFLOPS against the dense fp16 MFMA
-                peak).
+                (4 launches a step); the 70B-shaped MLP layers at M = 1, 2, 4,
+                8, 16 and the act-order 7B MLP layers at M = 1, 4 (GB/s, each
+                layer over >= 1 GiB of copies); the prefill GEMM at M = 2048 on
+                the 7B MLP shapes, groupsize 128 and 32 and act-order
+                (TFLOPS against the dense fp16 MFMA peak).
 """
 from __future__ import annotations
 
@@ -54,10 +56,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources that decide what the skinny kernel does and how it is launched
+# (its code, the shared device helpers and geometry, the weight layout the
+# repack writes, the launch plan and the dispatch): counter figures taken for
+# it stay valid while these are unchanged.
+GEMV_SOURCES = ("q4_gemv.hip", "q4_device.h", "q4_internal.h", "q4_prep.hip", "q4_plan.cpp",
+                "q4_api.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gptq_bit_weight_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMV_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -280,37 +290,41 @@ def fused_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500
             "per_layer_us": {ly.name: round(t * 1e6, 3) for ly, t in zip(layers, lt)}}
 
 
-def secondary(q4, torch, synth, lib, stream):
-    """Quick figures on the other decode and prefill shapes (one handle each;
-    the 70B layers are rotated over enough copies to exceed the cache), and
-    the 7B block with projection fusion."""
+def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=False):
+    """GB/s of each layer in `specs` ((name, K, N)) at each M: one layer's
+    handles rotate over >= 1 GiB of copies (per_launch_times), the same
+    handles serve every M (only the activations change)."""
     out = {}
-    out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
-                                                "llama7b_block_decode", 10)
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    for name, K, N in synth.LLAMA70B_MLP:
-        L = synth.make_layer(K, N, 128, 1, seed=synth.layer_seed("llama70b_mlp_decode", name, 1))
-        copies = max(2, math.ceil(MALL_DEFEAT_BYTES / L.metric_bytes()))
-        ly = Layer(q4, torch, name, L, copies)
-        reps = 20 * copies
-        with torch.cuda.stream(stream):
-            for c in range(copies):
-                ly.launch(lib, c, sp)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for r in range(reps):
-                ly.launch(lib, r % copies, sp)
-            b.record(stream)
-        stream.synchronize()
-        t = a.elapsed_time(b) * 1e-3 / reps
-        out[f"llama70b_{name}_m1"] = {"GB/s": round(ly.bytes / t / 1e9, 1),
-                                      "frac": round(ly.bytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                                      "us": round(t * 1e6, 2)}
+    for name, K, N in specs:
+        L = synth.make_layer(K, N, 128, max(Ms), seed=synth.layer_seed(workload, name, act_order),
+                             act_order=act_order)
+        ly = Layer(q4, torch, name, L, 1)
+        x_all = ly.x
+        for M in Ms:
+            ly.x = x_all[:M].contiguous()
+            ly.M = M
+            ly.out = torch.empty((M, N), dtype=torch.float16, device=x_all.device)
+            ly.xp = ctypes.c_void_p(ly.x.data_ptr())
+            ly.op = ctypes.c_void_p(ly.out.data_ptr())
+            t = per_launch_times(lib, torch, [ly], min_launches=200, stream=stream)[0]
+            gbs = ly.bytes / t / 1e9
+            out[f"{name}_m{M}"] = {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "us": round(t * 1e6, 2)}
         ly.close()
         del ly
-    for K, N in ((4096, 11008), (11008, 4096)):
-        L = synth.make_layer(K, N, 128, 2048, seed=synth.layer_seed("prefill", K, N, 128, False))
+        torch.cuda.empty_cache()
+    return out
+
+
+def prefill_rates(q4, torch, synth, lib, stream, M=2048):
+    """TFLOP/s of the prefill GEMM on the 7B MLP shapes: groupsize 128 and 32,
+    and act-order at 128 (the weights are 23-26 MB; compute, not memory,
+    bounds these)."""
+    out = {}
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for K, N, G, act in ((4096, 11008, 128, False), (11008, 4096, 128, False), (4096, 11008, 32, False),
+                         (11008, 4096, 32, False), (4096, 11008, 128, True)):
+        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("prefill", K, N, G, act), act_order=act)
         ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
         reps = 20
         with torch.cuda.stream(stream):
@@ -325,12 +339,28 @@ def secondary(q4, torch, synth, lib, stream):
         stream.synchronize()
         t = a.elapsed_time(b) * 1e-3 / reps
         tf = ly.flops / t / 1e12
-        out[f"prefill_{K}x{N}_m2048"] = {"TFLOP/s": round(tf, 1),
-                                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                         "us": round(t * 1e6, 1)}
+        out[f"{K}x{N}_g{G}{'_act' if act else ''}_m{M}"] = {
+            "TFLOP/s": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)}
         ly.close()
         del ly
     torch.cuda.empty_cache()
+    return out
+
+
+def secondary(q4, torch, synth, lib, stream):
+    """Figures on the other workloads: the 7B block with projection fusion,
+    the 70B MLP layers at M = 1, 2, 4, 8, 16 (where the skinny kernel stops
+    being bandwidth-bound), the act-order 7B MLP layers at M = 1 and 4, and
+    the prefill GEMM at M = 2048."""
+    out = {}
+    out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
+                                                "llama7b_block_decode", 10)
+    out["llama70b_mlp_decode"] = decode_sweep(q4, torch, synth, lib, stream, "llama70b_mlp_decode",
+                                              synth.LLAMA70B_MLP, (1, 2, 4, 8, 16))
+    out["llama7b_actorder_decode"] = decode_sweep(
+        q4, torch, synth, lib, stream, "llama7b_actorder_decode",
+        (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (1, 4), act_order=True)
+    out["prefill"] = prefill_rates(q4, torch, synth, lib, stream)
     return out
 
 
@@ -342,6 +372,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch each step directly (no graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="print only the secondary figures (one JSON line), e.g. to profile their kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--counters", action="store_true",
                     help="no timing: run 20 eager steps of the block, then 5 plain copies of "
@@ -366,6 +398,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     lib = q4.load_library()
+    if args.secondary_only:
+        print(json.dumps({"secondary": secondary(q4, torch, synth, lib, torch.cuda.Stream())}), flush=True)
+        return
     workload = "llama7b_block_decode"
     G, M = 128, 1
     copies = 10
