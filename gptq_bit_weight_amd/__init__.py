@@ -20,7 +20,7 @@ from typing import Optional
 
 __all__ = [
     "Q4Matrix", "Q4Error", "load_library", "library_path", "check_shape", "plan_actorder",
-    "plan_gemv", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
+    "plan_gemv", "plan_gemv_gather", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
 EXPORTED_SYMBOLS = (
     "q4_make", "q4_make_cat", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
-    "q4_plan_actorder", "q4_plan_gemv",
+    "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
 )
 
 _lib = None
@@ -89,6 +89,10 @@ def load_library():
     lib.q4_plan_actorder.restype = I
     lib.q4_plan_gemv.argtypes = [I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.q4_plan_gemv.restype = I
+    lib.q4_gemv_gather.argtypes = [P, I, I]
+    lib.q4_gemv_gather.restype = I
+    lib.q4_plan_gemv_gather.argtypes = [I, I, I]
+    lib.q4_plan_gemv_gather.restype = I
     _lib = lib
     return lib
 
@@ -136,6 +140,16 @@ def plan_gemv(M: int, K: int, N: int, groupsize: int, num_cu: int = 256) -> tupl
     _check(lib.q4_plan_gemv(M, K, N, groupsize, num_cu, ctypes.byref(ct), ctypes.byref(sp)),
            "q4_plan_gemv")
     return int(ct.value), int(sp.value)
+
+
+def plan_gemv_gather(M: int, K: int, splits: int) -> bool:
+    """Whether the skinny kernel builds act-order activations x[:, perm] in
+    LDS itself for this M, K and number of K splits (only unsplit launches
+    with M <= 2 whose activations fit 40 KiB)."""
+    r = int(load_library().q4_plan_gemv_gather(M, K, splits))
+    if r < 0:
+        raise ValueError(f"q4_plan_gemv_gather: bad arguments M={M} K={K} splits={splits}")
+    return bool(r)
 
 
 # ---------------------------------------------------------------- device ---
@@ -260,6 +274,15 @@ class Q4Matrix:
 
     def path_for(self, M: int) -> int:
         return int(load_library().q4_path_for(self._handle(), M))
+
+    def gemv_gather(self, M: int, splits: int = 0) -> bool:
+        """For an act-order handle: whether the skinny kernel builds x[:, perm]
+        in LDS itself at this M and K splits (0: planned), rather than a
+        separate permute kernel running first."""
+        r = int(load_library().q4_gemv_gather(self._handle(), M, splits))
+        if r < 0:
+            raise ValueError(f"q4_gemv_gather: bad arguments M={M} splits={splits}")
+        return bool(r)
 
     def matmul(self, x, bias=None, out=None, *, path: int = 0, variant: int = 0, splits: int = 0,
                stream=None):

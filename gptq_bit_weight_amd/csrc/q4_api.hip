@@ -10,7 +10,7 @@
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, hipStream_t stream);
+                       int M, int col_tiles, int splits, bool gather_x, hipStream_t stream);
 hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                            int M, hipStream_t stream);
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
@@ -45,6 +45,7 @@ void destroy(q4_matrix* h)
     (void)hipFree(h->qzeros);
     (void)hipFree(h->perm);
     (void)hipFree(h->inv_perm);
+    (void)hipFree(h->inv16);
     (void)hipFree(h->partials);
     (void)hipFree(h->counters);
     (void)hipFree(h->xperm);
@@ -143,6 +144,14 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
             return bail(hip_fail(e, "q4_make: perm"));
         if ((e = hipMemcpy(h->inv_perm, inv.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: perm"));
+        // 16-bit copy for the skinny kernel's own activation staging, which
+        // takes layers of at most kGemvXRows rows
+        if (num_kblocks(K) * kBlockK <= kGemvXRows) {
+            std::vector<uint16_t> inv16(inv.begin(), inv.end());
+            if ((e = hipMalloc(&h->inv16, (size_t)K * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
+            if ((e = hipMemcpy(h->inv16, inv16.data(), (size_t)K * 2, hipMemcpyHostToDevice)) != hipSuccess)
+                return bail(hip_fail(e, "q4_make: perm"));
+        }
     }
     // Part i's scales and zero words are columns off_i .. off_i + N_i of the
     // handle's rows (zero words: off_i / 8 .., every offset a multiple of 8).
@@ -238,19 +247,25 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1, 2 or 3", variant);
     }
 
+    int ct = 0, s = 0;
+    bool gather = false;
+    if (kind == Q4_PATH_GEMV) {
+        plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
+        if (variant) ct = variant;
+        if (splits) s = splits;
+        // act-order: without K splits, the skinny kernel stages x[:, perm]
+        // in LDS itself when all of it fits
+        gather = h->act_order && h->inv16 && gemv_gathers_x(M, h->K, s);
+    }
     const uint16_t* xe = x;
-    if (h->act_order) {
+    if (h->act_order && !gather) {
         q4_status st = ensure_xperm(h, M, stream);
         if (st != Q4_OK) return st;
         Q4_HIP(launch_permute_x(x, h->perm, h->xperm, M, h->K, stream), "q4_matmul: permute launch");
         xe = h->xperm;
     }
     if (kind == Q4_PATH_GEMV) {
-        int ct = 0, s = 0;
-        plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
-        if (variant) ct = variant;
-        if (splits) s = splits;
-        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, stream), "q4_matmul: gemv launch");
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, stream), "q4_matmul: gemv launch");
     } else {
         // Three GEMM variants share tile shape and accumulation order: the
         // automatic choice streams the weights into registers (activations
@@ -318,6 +333,15 @@ int q4_path_for(const q4_matrix* h, int M)
 {
     if (!h || M < 0) return -1;
     return q4::choose_path(h, M, 0);
+}
+
+int q4_gemv_gather(const q4_matrix* h, int M, int splits)
+{
+    if (!h || M < 1 || M > Q4_GEMV_MAX_M || splits < 0 || splits > q4::kMaxSplits) return -1;
+    if (!h->act_order || !h->inv16) return 0;
+    int ct = 0, s = 0;
+    q4::plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
+    return q4::gemv_gathers_x(M, h->K, splits ? splits : s) ? 1 : 0;
 }
 
 int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order)

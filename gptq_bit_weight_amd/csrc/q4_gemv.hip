@@ -38,6 +38,20 @@
 //    timing. Reductions stay in fp32 (GPTQModel wiki "Inference Backends",
 //    section "Numeric epilogues": FP32 split/tile reductions, bias added
 //    before the single cast).
+//
+// Act-order. The weights are stored in sorted-group order, so k-step rows
+// need the activations x[:, perm] (the Lorax GPTQ Exllama V1 page,
+// Description: a temporary buffer reorders the activations in the act-order
+// case). When K is not split, M <= 2 and x fits, each workgroup builds that
+// permuted copy in LDS itself instead of a separate permute launch (XL):
+// every thread loads 16-byte chunks of x in the original order (eight rows
+// k of one activation row) and the sorted positions inv[k] of those rows,
+// issues the ring's first weight loads, and then writes each half to its
+// sorted position in LDS. The loads are contiguous and independent, so they
+// travel with the weights; only the LDS stores scatter. (Gathering
+// x[m][perm[k']] from memory instead costs a scattered 2-byte load per
+// element in every workgroup.) The loop then reads its A operands from LDS.
+// Rows from K to the end of the last block are stored as zeros.
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -57,6 +71,7 @@ struct GemvArgs {
     const uint16_t* scales;
     const uint32_t* qzeros;
     const uint16_t* x;
+    const uint16_t* inv;    // act-order: original row -> sorted position (XL)
     const uint16_t* bias;
     uint16_t* out;
     float* partials;
@@ -68,6 +83,7 @@ struct GemvArgs {
     int blocks_per_split;
     int blocks_per_wave;
     int splits;
+    int ldx;                // XL: halfs per LDS activation row (kblocks * 128 + pad)
 };
 
 // One k-block of loads for one lane. NGB = groups per block: 4 (groups of 32
@@ -97,14 +113,16 @@ struct Lane {
 // returns zeros and moves no data. Only the last k-block of a K that is not a
 // multiple of 128 needs it (TAIL): its k-steps past K and its groups past K / G.
 struct Rsrc {
-    rsrc_t w, x, s, z, none;
+    rsrc_t w, x, s, z, none, inv;
 };
 
 // Load k-block b (0 <= b < kblocks). The per-block offsets are wave-uniform
 // (scalar registers; the k-step offset 64 i of the activations folds into the
 // instruction's immediate offset).
 // XS = k-steps per activation load (1, 2 or 4); B.a[0 .. 4/XS - 1] are loaded.
-template <int NGB, int CT, int XS, bool TAIL>
+// XL: the activations come from the workgroup's LDS copy instead; they are
+// read when the block is multiplied.
+template <int NGB, int CT, int XS, bool TAIL, bool XL>
 __device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p, const Rsrc& r,
                                            const Lane<CT>& ln, int b)
 {
@@ -112,10 +130,12 @@ __device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p,
 #pragma unroll
     for (int j = 0; j < CT; ++j) B.w[j] = buf_load16(r.w, ln.w[j], wso);
     const int ksteps = p.K >> 5;
+    if constexpr (!XL) {
 #pragma unroll
-    for (int i = 0; i < 4 / XS; ++i) {
-        const rsrc_t rx = (!TAIL || 4 * b + i < ksteps) ? r.x : r.none;
-        B.a[i] = buf_load16(rx, ln.x + 64u * XS * i, (uint32_t)b * 256u);
+        for (int i = 0; i < 4 / XS; ++i) {
+            const rsrc_t rx = (!TAIL || 4 * b + i < ksteps) ? r.x : r.none;
+            B.a[i] = buf_load16(rx, ln.x + 64u * XS * i, (uint32_t)b * 256u);
+        }
     }
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
@@ -160,10 +180,22 @@ __device__ __forceinline__ h8 a_operand(const u4 a[4], int i)
 
 // Multiply one block into the totals: per group, the MFMA sums of x * (q - z)
 // over its k-steps, then tot += s * sum in fp32.
-template <int NGB, int CT, int XS>
-__device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT], uint32_t zshift)
+// XL: block b's activations are read from the LDS copy (xl = this lane's
+// address in it for the first block of the workgroup's range, bs0).
+template <int NGB, int CT, int XS, bool XL>
+__device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT], uint32_t zshift,
+                                              const char* xl, int b, int bs0)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
+    u4 av[4];
+    if constexpr (XL) {
+        const char* src = xl + (b - bs0) * 256;
+#pragma unroll
+        for (int i = 0; i < 4 / XS; ++i) av[i] = *reinterpret_cast<const u4*>(src + 64 * XS * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4 / XS; ++i) av[i] = B.a[i];
+    }
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
         zero_t zp[CT];
@@ -177,7 +209,7 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT
 #pragma unroll
         for (int ii = 0; ii < SPG; ++ii) {
             const int i = gi * SPG + ii;
-            const h8 a = a_operand<XS>(B.a, i);
+            const h8 a = a_operand<XS>(av, i);
 #pragma unroll
             for (int j = 0; j < CT; ++j)
                 acc[j] = mfma16(a, sub_zero_word(B.w[j][i], zp[j]), ii == 0 ? f4{0.f, 0.f, 0.f, 0.f} : acc[j]);
@@ -189,12 +221,46 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT
     }
 }
 
-template <int NGB, int CT, int XS, bool TAIL>
+// Act-order staging (XL). Thread tid owns the 8-row units u = tid + NT * j
+// (j < XJ) of the original order: iv[j] holds inv[8u .. 8u + 7], xv[j][i]
+// the activations x[m0 + i][8u .. 8u + 7]. Rows m >= M lie past the end of x
+// (the loads return zeros) and units past K are not stored.
+constexpr int XR = 2;   // activation rows per staging round
+
+template <int XJ>
+__device__ __forceinline__ void stage_load(u4 (&xv)[XJ][XR], const GemvArgs& p, const Rsrc& r, int tid, int m0)
+{
+#pragma unroll
+    for (int i = 0; i < XR; ++i)
+#pragma unroll
+        for (int j = 0; j < XJ; ++j)
+            xv[j][i] = buf_load16(r.x, ((uint32_t)(m0 + i) * (uint32_t)p.K + 8u * (uint32_t)(tid + NT * j)) * 2u);
+}
+
+template <int XJ>
+__device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR], const u4 (&iv)[XJ],
+                                            const GemvArgs& p, int tid, int m0)
+{
+    const int units = p.K >> 3;
+#pragma unroll
+    for (int i = 0; i < XR; ++i)
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            if (m0 + i >= p.M || tid + NT * j >= units) continue;
+            uint16_t* row = xs + (size_t)(m0 + i) * p.ldx;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                row[(iv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu] = (uint16_t)(xv[j][i][e >> 1] >> (16 * (e & 1)));
+        }
+}
+
+template <int NGB, int CT, int XS, bool TAIL, bool XL>
 __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 {
     constexpr int COLS = 16 * CT;
     __shared__ float red[WV][16][COLS];
     __shared__ int last_flag;
+    extern __shared__ u4 xs_dyn[];   // XL: the workgroup's activations, [M][ldx] halfs
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so keeps the block
@@ -217,6 +283,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     r.s = make_rsrc(p.scales, (uint32_t)p.ng * (uint32_t)p.N * 2u);
     r.z = make_rsrc(p.qzeros, (uint32_t)p.ng * (uint32_t)(p.N >> 3) * 4u);
     r.none = make_rsrc(p.qweight, 0u);   // (used by TAIL only)
+    if constexpr (XL) r.inv = make_rsrc(p.inv, (uint32_t)p.K * 2u);
     Lane<CT> ln;
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
@@ -225,9 +292,9 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         ln.s[j] = (uint32_t)n * 2u;
         ln.z[j] = (uint32_t)(n >> 3) * 4u;
     }
+    constexpr int R = 16 / XS;
     {
         // rows m >= M fall past the end of x and read zeros
-        constexpr int R = 16 / XS;
         ln.x = ((uint32_t)(c16 % R) * (uint32_t)p.K + 8u * (uint32_t)kb + 32u * (uint32_t)(c16 / R)) * 2u;
     }
     ln.zshift = 4u * (uint32_t)(c16 & 7);
@@ -238,43 +305,77 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     const int b0 = bs0 + wave * p.blocks_per_wave;
     const int nb = min(b0 + p.blocks_per_wave, bs1) - b0;   // may be <= 0
 
+    // XL: this lane's A-operand address in the LDS copy for block bs0 = 0
+    // (rows m >= M read row M - 1; those output rows are not stored)
+    uint16_t* xs = reinterpret_cast<uint16_t*>(xs_dyn);
+    const char* xl = reinterpret_cast<const char*>(
+        xs + (size_t)min(c16 % R, p.M - 1) * p.ldx + 8 * kb + 32 * (c16 / R));
+
     f4 tot[CT];
 #pragma unroll
     for (int j = 0; j < CT; ++j) tot[j] = f4{0.f, 0.f, 0.f, 0.f};
 
     constexpr int D = depth<CT>();
-    if (nb > 0) {
-        // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
-        // Once a block is multiplied its buffer is refilled with the block D
-        // further on. Past the wave's last block the loads repeat that block
-        // (addresses stay in range, the data comes from cache) and the last
-        // round skips those buffers, so the loop body has no branches and the
-        // compiler's wait before each multiply covers exactly that block's
-        // loads. sched_barrier keeps each block's loads and arithmetic in
-        // program order: the loads issue in the same order in the prologue
-        // and in the loop (so the waits at the loop head need not assume the
-        // worse of two orders), and no work of a later block (which would
-        // wait for its loads) is hoisted into an earlier one.
-        const int bl = b0 + nb - 1;
-        Block<NGB, CT> buf[D];
+    // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
+    // Once a block is multiplied its buffer is refilled with the block D
+    // further on. Past the wave's last block the loads repeat that block
+    // (addresses stay in range, the data comes from cache) and the last
+    // round skips those buffers, so the loop body has no branches and the
+    // compiler's wait before each multiply covers exactly that block's
+    // loads. sched_barrier keeps each block's loads and arithmetic in
+    // program order: the loads issue in the same order in the prologue
+    // and in the loop (so the waits at the loop head need not assume the
+    // worse of two orders), and no work of a later block (which would
+    // wait for its loads) is hoisted into an earlier one.
+    const int bl = b0 + nb - 1;
+    Block<NGB, CT> buf[D];
+    // XL: the first XR activation rows and the sorted positions go out
+    // before the weights, so storing them waits for them alone.
+    constexpr int XJ = XL ? q4::kGemvXUnits : 1;
+    u4 iv[XJ];
+    u4 xv[XJ][XR];
+    if constexpr (XL) {
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) iv[j] = buf_load16(r.inv, (uint32_t)(tid + NT * j) * 16u);
+        stage_load<XJ>(xv, p, r, tid, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (With XL the first loads are issued by every wave, so that the staging
+    // stores' waits need not cover both a path with and one without them; K
+    // is not split then, so block bl = kblocks - 1 exists for a wave without
+    // blocks.)
+    if (XL || nb > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            load_block<NGB, CT, XS, TAIL>(buf[d], p, r, ln, min(b0 + d, bl));
+            load_block<NGB, CT, XS, TAIL, XL>(buf[d], p, r, ln, min(b0 + d, bl));
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    if constexpr (XL) {
+        stage_store<XJ>(xs, xv, iv, p, tid, 0);
+        for (int m0 = XR; m0 < p.M; m0 += XR) {
+            stage_load<XJ>(xv, p, r, tid, m0);
+            stage_store<XJ>(xs, xv, iv, p, tid, m0);
+        }
+        // rows K .. end of the last block
+        const int pad = p.kblocks * 128 - p.K;
+        for (int idx = tid; idx < p.M * pad; idx += NT) xs[(size_t)(idx / pad) * p.ldx + p.K + idx % pad] = 0;
+        __syncthreads();
+    }
+    if (nb > 0) {
         const int rounds = (nb + D - 1) / D;
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS>(buf[d], tot, ln.zshift);
-                load_block<NGB, CT, XS, TAIL>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
+                compute_block<NGB, CT, XS, XL>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
+                load_block<NGB, CT, XS, TAIL, XL>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS>(buf[d], tot, ln.zshift);
+            if (d < last) compute_block<NGB, CT, XS, XL>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -341,14 +442,15 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NGB, int XS, bool TAIL>
+template <int NGB, int XS, bool TAIL, bool XL>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
     const dim3 block(NT);
+    const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL>), dim3((p.N + 15) / 16, splits), block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL>), dim3((p.N + 31) / 32, splits), block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL>), dim3((p.N + 63) / 64, splits), block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL>), dim3((p.N + 63) / 64, splits), block, lds, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -357,13 +459,28 @@ hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 // Activation loads: one per 4 k-steps for M <= 4, per 2 for M <= 8, else one
 // per k-step. A K that is not a multiple of 128 (one partial block) takes the
 // one-per-step form, whose past-K steps are masked per load.
-template <int NGB>
+// (Staged act-order activations come with M <= 2 only.)
+template <int NGB, bool XL>
 hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
-    if (p.K % 128) return launch_ct<NGB, 1, true>(p, ct, splits, stream);
-    if (p.M <= 4) return launch_ct<NGB, 4, false>(p, ct, splits, stream);
-    if (p.M <= 8) return launch_ct<NGB, 2, false>(p, ct, splits, stream);
-    return launch_ct<NGB, 1, false>(p, ct, splits, stream);
+    if (p.K % 128) return launch_ct<NGB, 1, true, XL>(p, ct, splits, stream);
+    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL>(p, ct, splits, stream);
+    if constexpr (!XL) {
+        if (p.M <= 8) return launch_ct<NGB, 2, false, XL>(p, ct, splits, stream);
+        return launch_ct<NGB, 1, false, XL>(p, ct, splits, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool XL>
+hipError_t launch_xl(const GemvArgs& p, int ngb, int ct, int splits, hipStream_t stream)
+{
+    switch (ngb) {
+    case 1: return launch_ngb<1, XL>(p, ct, splits, stream);
+    case 2: return launch_ngb<2, XL>(p, ct, splits, stream);
+    case 4: return launch_ngb<4, XL>(p, ct, splits, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -371,14 +488,16 @@ hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, hipStream_t stream)
+                       int M, int col_tiles, int splits, bool gather_x, hipStream_t stream)
 {
     if (M < 1 || M > 16 || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+    if (gather_x && (!h->inv16 || !gemv_gathers_x(M, h->K, splits))) return hipErrorInvalidValue;
     GemvArgs p;
     p.qweight = h->qweight;
     p.scales = h->scales;
     p.qzeros = h->qzeros;
     p.x = x;
+    p.inv = gather_x ? h->inv16 : nullptr;
     p.bias = bias;
     p.out = out;
     p.partials = h->partials;
@@ -397,15 +516,12 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     p.splits = splits;
     p.blocks_per_split = (p.kblocks + splits - 1) / splits;
     p.blocks_per_wave = (p.blocks_per_split + kGemvWaves - 1) / kGemvWaves;
+    p.ldx = gather_x ? p.kblocks * 128 + kGemvXPad : 0;
     // groups per 128-row block: groups of 32 or 64 rows split a block; larger
     // groups (and one group over K) cover it whole
     const int ngb = (h->G == h->K || h->G >= 128) ? 1 : 128 / h->G;
-    switch (ngb) {
-    case 1: return launch_ngb<1>(p, col_tiles, splits, stream);
-    case 2: return launch_ngb<2>(p, col_tiles, splits, stream);
-    case 4: return launch_ngb<4>(p, col_tiles, splits, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return gather_x ? launch_xl<true>(p, ngb, col_tiles, splits, stream)
+                    : launch_xl<false>(p, ngb, col_tiles, splits, stream);
 }
 
 }  // namespace q4

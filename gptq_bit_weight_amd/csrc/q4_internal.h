@@ -27,6 +27,18 @@ constexpr int kGemvDepth = 4;        // k-blocks in flight per wave
 constexpr int kMaxSplits = 16;       // K splits across workgroups (grid.y)
 constexpr int kMaxColTiles = 4;      // 16-column MFMA tiles per wave
 constexpr int kMaxParts = 64;        // layers one q4_make_cat handle may concatenate
+// Act-order layers: when K is not split and M <= kGemvXMaxM, each workgroup
+// of the skinny kernel stages all of x[:, perm] in LDS itself if K (padded to
+// whole blocks) is at most kGemvXRows rows (kGemvXUnits 8-row units per
+// thread) and the M rows, each padded by kGemvXPad halfs, fit in
+// kGemvXLdsHalfs halfs (40 KiB); otherwise a separate kernel permutes x
+// first. (Every workgroup repeats the staging, so its cost grows with M: at
+// M = 4 it measured no faster than the separate permute.)
+constexpr int kGemvXMaxM = 2;
+constexpr int kGemvXUnits = 3;
+constexpr int kGemvXRows = kGemvXUnits * 8 * 64 * kGemvWaves;
+constexpr int kGemvXPad = 8;
+constexpr int kGemvXLdsHalfs = 20480;
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
 constexpr int kGemmBM = 256;
@@ -44,6 +56,9 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 // Skinny-kernel launch plan: 16-column tiles per wave (1, 2 or 4) and K
 // splits across workgroups (1..kMaxSplits) for a chip of num_cu CUs.
 void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits);
+// Whether the skinny kernel stages act-order activations itself for this
+// M, K and number of K splits.
+bool gemv_gathers_x(int M, int K, int splits);
 
 }  // namespace q4
 
@@ -59,6 +74,7 @@ struct q4_matrix {
     uint32_t* qzeros = nullptr;    // [ng][N/8]
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
+    uint16_t* inv16 = nullptr;     // the same in 16 bits, when K <= kGemvXRows
     // skinny-kernel split-K workspace: partial sums and arrival counters
     float* partials = nullptr;     // [kMaxSplits][16][N]
     uint32_t* counters = nullptr;  // [ceil(N / 16)]: one per column tile at the narrowest tiling

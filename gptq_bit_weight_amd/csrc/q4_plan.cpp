@@ -122,6 +122,13 @@ void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* spli
     *splits = s;
 }
 
+bool gemv_gathers_x(int M, int K, int splits)
+{
+    const long long rows = (long long)num_kblocks(K) * kBlockK;
+    return splits == 1 && M >= 1 && M <= kGemvXMaxM && rows <= kGemvXRows &&
+           (long long)M * (rows + kGemvXPad) <= kGemvXLdsHalfs;
+}
+
 }  // namespace q4
 
 extern "C" {
@@ -147,6 +154,12 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_plan_actorder: groupsize=%d does not divide K=%d",
                         groupsize, K);
     return q4::plan_actorder(g_idx_host, K, G, perm, trivial);
+}
+
+int q4_plan_gemv_gather(int M, int K, int splits)
+{
+    if (M < 1 || M > Q4_GEMV_MAX_M || K < 1 || splits < 1 || splits > q4::kMaxSplits) return -1;
+    return q4::gemv_gathers_x(M, K, splits) ? 1 : 0;
 }
 
 q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles, int* splits)

@@ -118,12 +118,20 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
  * handle must be ordered on one stream (or synchronized); different handles
  * are independent.
  *
+ * Act-order (non-trivial g_idx): the weights are stored in sorted-group
+ * order, so the product needs the activations x[:, perm] (the Lorax GPTQ
+ * Exllama V1 page, Description: a temporary buffer reorders the activations
+ * in the act-order case). Without K splits and for M <= 2, the skinny kernel
+ * builds them in LDS itself when they fit (q4_gemv_gather); otherwise, and
+ * for the GEMM, a separate kernel first writes x[:, perm] to the handle's
+ * workspace.
+ *
  * Graph capture: a call may be captured into a HIP graph and replayed; it
  * enqueues kernels only (no memset or copy nodes; the skinny kernel's split-K
  * counters are reset by the kernel). An act-order handle grows its
- * activation workspace on the first call with a larger M, which cannot
- * happen under capture: such a call returns Q4_ERR_INVALID_ARG, so make one
- * uncaptured call with the largest M first.
+ * activation workspace on the first call with a larger M that needs the
+ * separate permute, which cannot happen under capture: such a call returns
+ * Q4_ERR_INVALID_ARG, so make one uncaptured call with the largest M first.
  */
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M,
                     hipStream_t stream);
@@ -202,6 +210,15 @@ int q4_path_for(const q4_matrix* h, int M);
  */
 q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
 
+/*
+ * q4_gemv_gather -- 1 when, for this act-order handle, M and K splits
+ * (0: the automatic plan), the skinny kernel builds x[:, perm] in LDS itself,
+ * 0 when q4_matmul runs the separate permute kernel first (and for handles
+ * without act-order). -1 for a NULL handle, M outside [1, Q4_GEMV_MAX_M] or
+ * splits outside [0, 16].
+ */
+int q4_gemv_gather(const q4_matrix* h, int M, int splits);
+
 /* Handle geometry: K, N, groupsize (after -1 -> K), act-order flag (1 when a
  * non-trivial g_idx was given). Returns 0, or -1 for a NULL handle. */
 int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order);
@@ -236,6 +253,15 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
  */
 q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles,
                        int* splits);
+
+/*
+ * q4_plan_gemv_gather -- host-only form of q4_gemv_gather's rule: 1 when
+ * splits == 1, M <= 2, K padded to whole 128-row blocks is at most 12288
+ * rows and M of those rows, each padded by 8 halfs, fit 20480 halfs (40 KiB
+ * of LDS); else 0. -1 for M outside [1, Q4_GEMV_MAX_M], K < 1 or splits outside
+ * [1, 16].
+ */
+int q4_plan_gemv_gather(int M, int K, int splits);
 
 #ifdef __cplusplus
 }

@@ -208,6 +208,42 @@ def test_act_order_bit_identical_to_physical_permutation(M):
     compare(ya.cpu().numpy(), yD, A, "act-order")
 
 
+@pytest.mark.parametrize("K,N,G,M,splits,tiles,gathers", [
+    (1024, 200, 128, 1, 0, 0, True),   # staged in the kernel
+    (1024, 200, 128, 2, 1, 2, True),   # two rows, two tiles
+    (1024, 200, 64, 1, 0, 4, True),    # groups of 64, four tiles
+    (992, 72, 32, 2, 1, 0, True),      # K not a multiple of 128: zero rows to the block end
+    (1024, 200, 128, 1, 3, 0, False),  # split K: separate permute
+    (1024, 200, 128, 3, 1, 0, False),  # M > 2: separate permute
+    (12416, 64, 128, 1, 1, 0, False),  # 97 blocks exceed 12288 rows: separate permute
+    (12288, 64, 128, 1, 1, 1, True),   # three 8-row units per thread
+    (10112, 64, 128, 2, 1, 0, True),   # 2 x 10120 halfs: the LDS limit
+])
+def test_act_order_gather_matches_permuted_layer(K, N, G, M, splits, tiles, gathers):
+    """The skinny kernel's own staging of x[:, perm] (or the separate permute,
+    when it does not apply) gives the output of a trivial layer built from
+    the K-permuted weights and activations with the same launch, bit for bit,
+    and matches the oracle."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(K, N, G, M, 11, act_order=True, bias=True)
+    announce(f"act-order staging K={K} N={N} G={G} M={M} splits={splits} tiles={tiles}")
+    perm = np.argsort(L.g_idx, kind="stable")
+    q = oracle.unpack_qweight(L.qweight, L.K)
+    t = device_tensors(L)
+    Wa = make_matrix(L, t)
+    s = splits or q4.plan_gemv(M, K, N, G)[1]
+    assert q4.plan_gemv_gather(M, K, s) == gathers and Wa.gemv_gather(M, splits) == gathers
+    Wp = make_matrix(L, dict(t, qweight=torch.from_numpy(pack_rows(q[perm])).cuda()), g_idx=None)
+    xp = torch.from_numpy(np.ascontiguousarray(L.x[:, perm])).cuda()
+    ya = Wa.matmul(t["x"], t["bias"], path=q4.PATH_GEMV, variant=tiles, splits=splits)
+    yp = Wp.matmul(xp, t["bias"], path=q4.PATH_GEMV, variant=tiles, splits=s)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int16), yp.view(torch.int16))
+    yD, A = oracle_full(L)
+    compare(ya.cpu().numpy(), yD, A, "act-order staging")
+
+
 def test_bias_is_added_once_in_fp32():
     torch = torch_mod()
     L = _layer(512, 136, 128, 2, 8, bias=True)

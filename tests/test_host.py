@@ -145,6 +145,25 @@ def test_plan_gemv():
         q4.plan_gemv(1, 4128, 4096, 128)      # K % groupsize != 0
 
 
+def test_plan_gemv_gather():
+    """Act-order activations are staged by the skinny kernel itself only when
+    K is not split, M <= 2, K padded to whole blocks is at most 12288 rows and
+    M rows of it (8 halfs of padding each) fit 20480 halfs; otherwise a
+    separate permute runs."""
+    g = q4.plan_gemv_gather
+    assert g(1, 4096, 1) and g(2, 4096, 1)              # 7B gate/up at M = 1, 2
+    assert not g(3, 4096, 1) and not g(4, 1024, 1)      # M > 2: separate permute
+    assert g(1, 11008, 1)                               # 7B down at M = 1: 11008 rows
+    assert not g(2, 11008, 1)                           # 2 x 11016 halfs > 20480
+    assert g(2, 10112, 1) and not g(2, 10240, 1)        # 2 x 10120 fits, 2 x 10248 does not
+    assert not g(1, 4096, 2)                            # split K
+    assert not g(1, 12416, 1) and g(1, 12288, 1)        # 97 blocks exceed 12288 rows
+    assert g(1, 12200, 1)                               # 96 blocks once padded
+    for bad in ((0, 4096, 1), (17, 4096, 1), (1, 4096, 0), (1, 4096, 17), (1, 0, 1)):
+        with pytest.raises(ValueError):
+            g(*bad)
+
+
 def test_check_shape_size_limit():
     # packed bytes (K padded to 128-row blocks) must stay below 2^31
     q4.check_shape(65536, 65536 - 8, 128)
