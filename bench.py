@@ -319,28 +319,38 @@ def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=F
 def prefill_rates(q4, torch, synth, lib, stream, M=2048):
     """TFLOP/s of the prefill GEMM on the 7B MLP shapes: groupsize 128 and 32,
     and act-order at 128 (the weights are 23-26 MB; compute, not memory,
-    bounds these)."""
+    bounds these). Twenty launches are captured in one graph and replayed
+    three times after a warm-up replay; the median replay gives the time."""
     out = {}
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    reps = 20
     for K, N, G, act in ((4096, 11008, 128, False), (11008, 4096, 128, False), (4096, 11008, 32, False),
                          (11008, 4096, 32, False), (4096, 11008, 128, True)):
         L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("prefill", K, N, G, act), act_order=act)
         ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
-        reps = 20
         with torch.cuda.stream(stream):
-            for _ in range(3):
-                ly.launch(lib, 0, sp)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                ly.launch(lib, 0, sp)
-            b.record(stream)
+            ly.launch(lib, 0, ctypes.c_void_p(stream.cuda_stream))   # sizes the act-order workspace
         stream.synchronize()
-        t = a.elapsed_time(b) * 1e-3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for _ in range(reps):
+                ly.launch(lib, 0, cap)
+        times = []
+        with torch.cuda.stream(stream):
+            g.replay()
+            for _ in range(3):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                stream.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3 / reps)
+        t = sorted(times)[1]
         tf = ly.flops / t / 1e12
         out[f"{K}x{N}_g{G}{'_act' if act else ''}_m{M}"] = {
             "TFLOP/s": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)}
+        del g
         ly.close()
         del ly
     torch.cuda.empty_cache()

@@ -87,14 +87,18 @@ struct Ctx {
     uint32_t z_shift[NJ];
 };
 
+// The k offset of the tile is wave-uniform (a scalar register); rows past M
+// lie past the end of x through the per-lane offset alone. Only with KT can a
+// chunk lie past K (in the last tile); its lanes are pushed out of range.
+template <bool KT>
 __device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* stage, int wave, int kt)
 {
     const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) {
-        const uint32_t kill = (c.a_k[e] + k0 < (uint32_t)p.K) ? 0u : kOOB;
+        const uint32_t kill = (!KT || c.a_k[e] + k0 < (uint32_t)p.K) ? 0u : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void*)(stage + (e * 4 + wave) * 1024), 16,
-                                                 (int)(c.a_off[e] + k0 * 2u + kill), 0, 0, 0);
+                                                 (int)(c.a_off[e] + kill), (int)(k0 * 2u), 0, 0);
     }
 }
 
@@ -233,12 +237,12 @@ __global__ __launch_bounds__(NT) void q4_gemm_stream_kernel(GemmArgs p)
         Q4S_VMCNT(0);
         lds_barrier();
         const int kn = min(kt + 1, ktiles - 1);
-        load_a(c, p, nxt, wave, kn);
+        load_a<KT>(c, p, nxt, wave, kn);
         load_b(Rn, c, p, kn);
         mma(cur, Rc, kt);
     };
 
-    load_a(c, p, lds_a0, wave, 0);
+    load_a<KT>(c, p, lds_a0, wave, 0);
     load_b(R0, c, p, 0);
     int kt = 0;
     for (; kt + 1 < ktiles; kt += 2) {
