@@ -74,6 +74,35 @@ __global__ __launch_bounds__(256) void q4_permute_x_kernel(const uint16_t* __res
     }
 }
 
+// The same, one activation row per workgroup: the row is copied into LDS
+// with 16-byte loads, then each thread writes eight consecutive outputs with
+// one 16-byte store, gathering them from LDS. Memory sees contiguous reads
+// and writes only. Needs K % 8 == 0, 16-byte aligned rows and 2K bytes of
+// LDS.
+__global__ __launch_bounds__(256) void q4_permute_rows_kernel(const uint16_t* __restrict__ x,
+                                                              const int32_t* __restrict__ perm,
+                                                              uint16_t* __restrict__ xp, int K)
+{
+    extern __shared__ q4dev::u4 row_lds[];
+    uint16_t* row = reinterpret_cast<uint16_t*>(row_lds);
+    const size_t base = (size_t)blockIdx.x * K;
+    const int chunks = K >> 3;
+    const q4dev::u4* src = reinterpret_cast<const q4dev::u4*>(x + base);
+    for (int c = threadIdx.x; c < chunks; c += 256) row_lds[c] = src[c];
+    __syncthreads();
+    q4dev::u4* dst = reinterpret_cast<q4dev::u4*>(xp + base);
+    const q4dev::u4* pv = reinterpret_cast<const q4dev::u4*>(perm);
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        const q4dev::u4 p0 = pv[2 * c], p1 = pv[2 * c + 1];
+        q4dev::u4 o;
+        o[0] = (uint32_t)row[p0[0]] | ((uint32_t)row[p0[1]] << 16);
+        o[1] = (uint32_t)row[p0[2]] | ((uint32_t)row[p0[3]] << 16);
+        o[2] = (uint32_t)row[p1[0]] | ((uint32_t)row[p1[1]] << 16);
+        o[3] = (uint32_t)row[p1[2]] | ((uint32_t)row[p1[3]] << 16);
+        dst[c] = o;
+    }
+}
+
 // Debug dump: w[k][n] (original row order) = the dequantized weight (k, n) as
 // each kernel forms it, rounded to fp16. FACTORED (skinny kernel): the
 // kernel's own (q - z) from sub_zero_word times the fp32 scale, which is the
@@ -129,8 +158,16 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream)
 {
-    hipLaunchKernelGGL(q4_permute_x_kernel, dim3(grid_for((size_t)M * K)), dim3(256), 0, stream, x,
-                       perm, xp, M, K);
+    // One workgroup per row has too little parallelism for a few rows (the
+    // skinny kernel's M): those take the element-wise form. x rows are
+    // 16-byte aligned when x is (K is a multiple of 8).
+    constexpr int kMaxRowLds = 64 * 1024;
+    if (M > Q4_GEMV_MAX_M && (size_t)K * 2 <= kMaxRowLds && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(xp) % 16 == 0 && reinterpret_cast<uintptr_t>(perm) % 16 == 0)
+        hipLaunchKernelGGL(q4_permute_rows_kernel, dim3(M), dim3(256), (size_t)K * 2, stream, x, perm, xp, K);
+    else
+        hipLaunchKernelGGL(q4_permute_x_kernel, dim3(grid_for((size_t)M * K)), dim3(256), 0, stream, x,
+                           perm, xp, M, K);
     return hipGetLastError();
 }
 
