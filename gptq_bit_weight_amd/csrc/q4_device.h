@@ -130,6 +130,15 @@ __device__ __forceinline__ u4 buf_load16(rsrc_t r, uint32_t off, uint32_t soff =
     return bitcast<u4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
 }
 
+// The same with the non-temporal hint (cache policy nt): for data read
+// exactly once, such as the skinny kernel's weights, which then do not
+// displace lines that are reused.
+__device__ __forceinline__ u4 buf_load16_nt(rsrc_t r, uint32_t off, uint32_t soff = 0)
+{
+    constexpr int kNonTemporal = 2;
+    return bitcast<u4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, kNonTemporal));
+}
+
 __device__ __forceinline__ u2 buf_load8(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
     return bitcast<u2>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0));

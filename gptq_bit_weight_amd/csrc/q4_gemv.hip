@@ -25,6 +25,8 @@
 //    exact in fp32, so this is the product with the exact dequantized weight,
 //    accumulated in fp32, and the vector ALU does one unpack and one packed
 //    subtract per two weights.
+//  * the weights are read exactly once, with the non-temporal hint (5-7%
+//    faster on the 7B layers than default caching);
 //  * each wave keeps D k-blocks of loads in flight (a ring of register
 //    buffers, refilled as soon as a block is multiplied), so a CU has
 //    8 waves x D x 1 KiB x CT of weights outstanding. Every load takes a
@@ -128,7 +130,7 @@ __device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p,
 {
     const uint32_t wso = (uint32_t)b * (uint32_t)p.N * 64u;
 #pragma unroll
-    for (int j = 0; j < CT; ++j) B.w[j] = buf_load16(r.w, ln.w[j], wso);
+    for (int j = 0; j < CT; ++j) B.w[j] = buf_load16_nt(r.w, ln.w[j], wso);
     const int ksteps = p.K >> 5;
     if constexpr (!XL) {
 #pragma unroll
