@@ -11,12 +11,16 @@ each function follows and for the readings taken where the pages are silent.
 Functions:
   half_to_double(bits)         exact binary16 -> float64
   double_to_half(values)       float64 -> binary16 bits, round to nearest even
+  bf16_to_double(bits)         exact bfloat16 -> float64
+  double_to_bf16(values)       float64 -> bfloat16 bits, round to nearest even
   unpack_qweight(qweight, K)   uint8 [K, N] codes
   unpack_qzeros(qzeros, N)     uint8 [ng, N] zero points
   dequant32(...)               float32 [K, N], W = s * (q - z) (exact)
   dequant16(...)               uint16 [K, N], binary16 bits of RNE(W)
-  matmul(..., route)           float64 y [M, N] (and A = sum |x*W|), fused or fallback
-  matmul_at(..., ms, ns)       float64 y, A at selected output elements
+  dequant_bf16(...)            uint16 [K, N], bfloat16 bits of RNE(W)
+  matmul(..., route, xfmt)     float64 y [M, N] (and A = sum |x*W|), fused or fallback;
+                               x and bias as binary16 ("f16") or bfloat16 ("bf16") bits
+  matmul_at(..., ms, ns, xfmt) float64 y, A at selected output elements
 """
 from __future__ import annotations
 
@@ -55,12 +59,17 @@ def _load():
     lib.q4o_unpack_qzeros.argtypes = [_P, _I, _I, _P]
     lib.q4o_dequant32.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
     lib.q4o_dequant16.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
-    lib.q4o_matmul_fused.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
-    lib.q4o_matmul_fallback.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]
-    lib.q4o_matmul_fused_at.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                        _I, _P, _P, _P, _P]
+    lib.q4o_bf16_to_double_array.argtypes = [_I, _P, _P]
+    lib.q4o_double_to_bf16_array.argtypes = [_I, _P, _P]
+    lib.q4o_dequant_bf16.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
+    _F = ctypes.c_int
+    lib.q4o_matmul_fused_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
+    lib.q4o_matmul_fallback_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]
+    lib.q4o_matmul_fused_at_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                            _I, _P, _P, _P, _P]
     for f in ("q4o_unpack_qweight", "q4o_unpack_qzeros", "q4o_dequant32", "q4o_dequant16",
-              "q4o_matmul_fused", "q4o_matmul_fallback", "q4o_matmul_fused_at"):
+              "q4o_dequant_bf16", "q4o_matmul_fused_fmt", "q4o_matmul_fallback_fmt",
+              "q4o_matmul_fused_at_fmt"):
         getattr(lib, f).restype = ctypes.c_int
     lib.q4o_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -123,6 +132,30 @@ def double_to_half(values) -> np.ndarray:
     return out
 
 
+def bf16_to_double(bits) -> np.ndarray:
+    b = _bits16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().q4o_bf16_to_double_array(b.size, _ptr(b), _ptr(out))
+    return out
+
+
+def double_to_bf16(values) -> np.ndarray:
+    """Round to bfloat16 (ties to even); returns uint16 bit patterns."""
+    v = _c(values, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().q4o_double_to_bf16_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+_XFMT = {"f16": 0, "bf16": 1}
+
+
+def _xfmt(xfmt: str) -> int:
+    if xfmt not in _XFMT:
+        raise OracleError(f"unknown activation format {xfmt!r}")
+    return _XFMT[xfmt]
+
+
 def unpack_qweight(qweight, K: int) -> np.ndarray:
     qw = _c(qweight, np.int32)
     N = qw.shape[1]
@@ -160,10 +193,21 @@ def dequant16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int) -> np.ndar
     return dq
 
 
+def dequant_bf16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of RNE(s * (q - z))."""
+    qw, qz, s, gi = _weights(qweight, qzeros, scales, g_idx)
+    dq = np.empty((K, N), dtype=np.uint16)
+    _check(_load().q4o_dequant_bf16(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, _ptr(dq)),
+           "dequant_bf16")
+    return dq
+
+
 def matmul(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bias=None,
-           route: str = "fused") -> Tuple[np.ndarray, Optional[np.ndarray]]:
+           route: str = "fused", xfmt: str = "f16") -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """y = x @ W (+ bias) in float64. Returns (y, A) for the fused route, where
-    A[m, n] = sum_k |x[m,k] * W[k,n]|, and (y, None) for the fallback route."""
+    A[m, n] = sum_k |x[m,k] * W[k,n]|, and (y, None) for the fallback route.
+    x and bias are bit patterns in format xfmt ("f16" or "bf16")."""
+    fmt = _xfmt(xfmt)
     xb = _bits16(x)
     M = xb.shape[0]
     if xb.shape != (M, K):
@@ -174,19 +218,20 @@ def matmul(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bias=None,
     lib = _load()
     if route == "fused":
         A = np.empty((M, N), dtype=np.float64)
-        _check(lib.q4o_matmul_fused(_ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), _ptr(b),
-                                    M, K, N, G, _ptr(y), _ptr(A)), "matmul_fused")
+        _check(lib.q4o_matmul_fused_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
+                                        _ptr(b), M, K, N, G, _ptr(y), _ptr(A)), "matmul_fused")
         return y, A
     if route == "fallback":
-        _check(lib.q4o_matmul_fallback(_ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), _ptr(b),
-                                       M, K, N, G, _ptr(y)), "matmul_fallback")
+        _check(lib.q4o_matmul_fallback_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
+                                           _ptr(b), M, K, N, G, _ptr(y)), "matmul_fallback")
         return y, None
     raise OracleError(f"unknown route {route!r}")
 
 
 def matmul_at(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, ms, ns,
-              bias=None) -> Tuple[np.ndarray, np.ndarray]:
+              bias=None, xfmt: str = "f16") -> Tuple[np.ndarray, np.ndarray]:
     """Fused-route y and A at output elements (ms[i], ns[i])."""
+    fmt = _xfmt(xfmt)
     xb = _bits16(x)
     M = xb.shape[0]
     qw, qz, s, gi = _weights(qweight, qzeros, scales, g_idx)
@@ -195,8 +240,9 @@ def matmul_at(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, ms, ns,
     ns = _c(ns, np.int64)
     y = np.empty(ms.shape, dtype=np.float64)
     A = np.empty(ms.shape, dtype=np.float64)
-    _check(_load().q4o_matmul_fused_at(_ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), _ptr(b),
-                                       M, K, N, G, ms.size, _ptr(ms), _ptr(ns), _ptr(y), _ptr(A)),
+    _check(_load().q4o_matmul_fused_at_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
+                                           _ptr(b), M, K, N, G, ms.size, _ptr(ms), _ptr(ns),
+                                           _ptr(y), _ptr(A)),
            "matmul_fused_at")
     return y, A
 

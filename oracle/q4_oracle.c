@@ -42,6 +42,12 @@
  *    Its fp16 form dq16 is one round-to-nearest-even of that exact product.
  *  - Accumulation is in double, in increasing k; the bias (if any) is added
  *    in double after the sum.
+ *  - Activation format: GPTQModel wiki "Inference Backends", hardware table
+ *    (ExLlama v2 row), keeps the activation dtype (FP16, BF16 or FP32) with
+ *    FP16 scales and FP32 accumulation. The matmul entry points with a format
+ *    argument read x and the bias as binary16 (xfmt 0) or bfloat16 (xfmt 1);
+ *    the weights are the same either way. q4o_dequant_bf16 gives the weight
+ *    rounded once to bfloat16, RNE_bf16(s * (q - z)).
  *
  * Error returns: 0 = OK, 1 = bad shape/argument, 2 = g_idx out of range.
  */
@@ -107,6 +113,68 @@ uint16_t q4o_double_to_half_rne(double v)
     double enc = (double)(E + 14) * 1024.0 + n;
     if (enc >= 31744.0) return (uint16_t)(sign | 0x7C00);
     return (uint16_t)(sign | (uint16_t)enc);
+}
+
+/* ---------------------------------------------------------------------------
+ * bfloat16 conversions, from its definition: the upper half of a binary32
+ * word -- 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits; exponent
+ * field 0 holds zero and subnormals (f * 2^-133), field 255 inf and NaN.
+ * ------------------------------------------------------------------------- */
+
+double q4o_bf16_to_double(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xFF;
+    int f = b & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16 value, ties to even: the binary16
+ * construction above with 7 fraction bits and exponent range -126..127. The
+ * spacing is 2^(E-7) for E >= -126 and 2^-133 below; the encoding
+ * (E+126)*128 + n carries across binades and into the subnormals; any
+ * encoding >= 0x7F80 is an overflow to infinity. */
+uint16_t q4o_double_to_bf16_rne(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < -126) E = -126;
+    if (E > 127) return (uint16_t)(sign | 0x7F80);
+    double n = rne_int(ldexp(a, 7 - E));
+    double enc = (double)(E + 126) * 128.0 + n;
+    if (enc >= 32640.0) return (uint16_t)(sign | 0x7F80);
+    return (uint16_t)(sign | (uint16_t)enc);
+}
+
+void q4o_bf16_to_double_array(int64_t n, const uint16_t* in, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = q4o_bf16_to_double(in[i]);
+}
+
+void q4o_double_to_bf16_array(int64_t n, const double* in, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = q4o_double_to_bf16_rne(in[i]);
+}
+
+typedef double (*to_double_fn)(uint16_t);
+
+/* xfmt 0: binary16, 1: bfloat16; NULL for anything else. */
+static to_double_fn format_of(int xfmt)
+{
+    return xfmt == 0 ? q4o_half_to_double : xfmt == 1 ? q4o_bf16_to_double : NULL;
 }
 
 void q4o_half_to_double_array(int64_t n, const uint16_t* in, double* out)
@@ -217,16 +285,32 @@ int q4o_dequant16(const int32_t* qweight, const int32_t* qzeros, const uint16_t*
     return 0;
 }
 
+/* dqb[k][n] = RNE_bf16(s * (q - z)), bfloat16 bit patterns. */
+int q4o_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                     const int32_t* g_idx, int64_t K, int64_t N, int64_t G, uint16_t* dq)
+{
+    int rc = check_args(0, K, N, &G, g_idx);
+    if (rc) return rc;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            dq[k * N + n] = q4o_double_to_bf16_rne(
+                (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n));
+    return 0;
+}
+
 /* ---------------------------------------------------------------------------
  * The two routes to y. Both sum in increasing k in double and add the bias
  * last, so they are bit-identical by construction; the test suite checks it.
+ * x and the bias are read in format xfmt (0 binary16, 1 bfloat16).
  * ------------------------------------------------------------------------- */
 
 /* Fused route: dequantize each weight inside the k loop, never store W. */
-int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                     const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                     int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
+int q4o_matmul_fused_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                         const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                         int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
 {
+    to_double_fn to_d = format_of(xfmt);
+    if (!to_d) return 1;
     int rc = check_args(M, K, N, &G, g_idx);
     if (rc) return rc;
 #pragma omp parallel for collapse(2) schedule(static)
@@ -235,22 +319,31 @@ int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* q
             double acc = 0.0, aabs = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
-                double p = q4o_half_to_double(x[m * K + k]) * w;
+                double p = to_d(x[m * K + k]) * w;
                 acc += p;
                 aabs += fabs(p);
             }
-            if (bias) acc += q4o_half_to_double(bias[n]);
+            if (bias) acc += to_d(bias[n]);
             y[m * N + n] = acc;
             if (A) A[m * N + n] = aabs;
         }
     return 0;
 }
 
-/* Fallback route: materialize the dequantized W[K][N], then a plain matmul. */
-int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                        int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                     const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                     int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
 {
+    return q4o_matmul_fused_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y, A);
+}
+
+/* Fallback route: materialize the dequantized W[K][N], then a plain matmul. */
+int q4o_matmul_fallback_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                            const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                            int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+{
+    to_double_fn to_d = format_of(xfmt);
+    if (!to_d) return 1;
     int rc = check_args(M, K, N, &G, g_idx);
     if (rc) return rc;
     float* W = (float*)malloc((size_t)K * (size_t)N * sizeof(float));
@@ -261,22 +354,31 @@ int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
-                acc += q4o_half_to_double(x[m * K + k]) * (double)W[k * N + n];
-            if (bias) acc += q4o_half_to_double(bias[n]);
+                acc += to_d(x[m * K + k]) * (double)W[k * N + n];
+            if (bias) acc += to_d(bias[n]);
             y[m * N + n] = acc;
         }
     free(W);
     return 0;
 }
 
+int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                        int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+{
+    return q4o_matmul_fallback_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y);
+}
+
 /* Fused route at selected output elements (m[i], n[i]), i < count. Used for
  * full-size layers where the whole product would take the CPU too long. */
-int q4o_matmul_fused_at(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                        int64_t M, int64_t K, int64_t N, int64_t G,
-                        int64_t count, const int64_t* ms, const int64_t* ns,
-                        double* y, double* A)
+int q4o_matmul_fused_at_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                            const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                            int64_t M, int64_t K, int64_t N, int64_t G,
+                            int64_t count, const int64_t* ms, const int64_t* ns,
+                            double* y, double* A)
 {
+    to_double_fn to_d = format_of(xfmt);
+    if (!to_d) return 1;
     int rc = check_args(M, K, N, &G, g_idx);
     if (rc) return rc;
     for (int64_t i = 0; i < count; ++i)
@@ -287,15 +389,25 @@ int q4o_matmul_fused_at(const uint16_t* x, const int32_t* qweight, const int32_t
         double acc = 0.0, aabs = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
-            double p = q4o_half_to_double(x[m * K + k]) * w;
+            double p = to_d(x[m * K + k]) * w;
             acc += p;
             aabs += fabs(p);
         }
-        if (bias) acc += q4o_half_to_double(bias[n]);
+        if (bias) acc += to_d(bias[n]);
         y[i] = acc;
         if (A) A[i] = aabs;
     }
     return 0;
+}
+
+int q4o_matmul_fused_at(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                        int64_t M, int64_t K, int64_t N, int64_t G,
+                        int64_t count, const int64_t* ms, const int64_t* ns,
+                        double* y, double* A)
+{
+    return q4o_matmul_fused_at_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G,
+                                   count, ms, ns, y, A);
 }
 
 int q4o_num_threads(void)

@@ -16,7 +16,9 @@ contract table of "Implementation: Predibase Lorax GPTQ Exllama V1"):
   columns n = 8c .. 8c+7 of group g, in the same nibble order.
 - ``scales``  fp16  ``[ceil(K/G), N]``.
 - ``g_idx``   int32 ``[K]`` or ``None`` (group of input row k).
-- ``x``       fp16  ``[M, K]``, ``bias`` fp16 ``[N]``.
+- ``x``       fp16  ``[M, K]``, ``bias`` fp16 ``[N]``; or, with
+  ``xfmt="bf16"``, both as bfloat16 bit patterns (uint16), the same draws
+  rounded to bfloat16 instead (scales stay fp16).
 
 Uniform 4-bit codes are drawn as uniform 32-bit words: the eight nibbles of
 a uniformly random 32-bit word are independent and uniform on {0..15}, which
@@ -42,6 +44,7 @@ __all__ = [
     "layer_seed",
     "make_layer",
     "make_x",
+    "to_bf16_bits",
     "LLAMA7B_BLOCK",
     "LLAMA70B_MLP",
     "WORKLOADS",
@@ -59,9 +62,10 @@ class Layer:
     qzeros: np.ndarray            # int32 [ceil(K/G), N/8]
     scales: np.ndarray            # float16 [ceil(K/G), N]
     g_idx: Optional[np.ndarray]   # int32 [K] or None
-    x: np.ndarray                 # float16 [M, K]
-    bias: Optional[np.ndarray]    # float16 [N] or None
+    x: np.ndarray                 # float16 [M, K] (xfmt "bf16": uint16 bfloat16 bits)
+    bias: Optional[np.ndarray]    # float16 [N] or None (xfmt "bf16": uint16 bits)
     seed: int
+    xfmt: str = "f16"
 
     @property
     def M(self) -> int:
@@ -85,9 +89,21 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32).view(np.int32)
 
 
+def to_bf16_bits(values) -> np.ndarray:
+    """Random draws as bfloat16 bit patterns (uint16): the float32 value's
+    upper half, rounded to nearest with ties to even (finite inputs; input
+    preparation only)."""
+    u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
 def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = False,
-               bias: bool = False, scale_lo: float = 0.005, scale_hi: float = 0.02) -> Layer:
+               bias: bool = False, scale_lo: float = 0.005, scale_hi: float = 0.02,
+               xfmt: str = "f16") -> Layer:
     """Draw one layer with the value distributions described in the module doc."""
+    if xfmt not in ("f16", "bf16"):
+        raise ValueError(f"unknown activation format {xfmt!r}")
     if K % 8 or N % 8:
         raise ValueError("K and N must be multiples of 8")
     if G <= 0:
@@ -97,8 +113,12 @@ def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = F
     qweight = _words(rng, (K // 8, N))
     qzeros = _words(rng, (ng, N // 8))
     scales = rng.uniform(scale_lo, scale_hi, size=(ng, N)).astype(np.float16)
-    x = rng.standard_normal((M, K)).astype(np.float16)
-    b = rng.normal(0.0, 0.1, size=(N,)).astype(np.float16) if bias else None
+    if xfmt == "f16":
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        b = rng.normal(0.0, 0.1, size=(N,)).astype(np.float16) if bias else None
+    else:
+        x = to_bf16_bits(rng.standard_normal((M, K)))
+        b = to_bf16_bits(rng.normal(0.0, 0.1, size=(N,))) if bias else None
     g_idx = None
     if act_order:
         pi = rng.permutation(K)
@@ -106,7 +126,7 @@ def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = F
         pos[pi] = np.arange(K)
         g_idx = (pos // G).astype(np.int32)
     return Layer(K=K, N=N, G=G, qweight=qweight, qzeros=qzeros, scales=scales,
-                 g_idx=g_idx, x=x, bias=b, seed=seed)
+                 g_idx=g_idx, x=x, bias=b, seed=seed, xfmt=xfmt)
 
 
 def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
@@ -119,18 +139,22 @@ def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
     for p in parts[1:]:
         if p.K != p0.K or p.G != p0.G:
             raise ValueError("parts must share K and G")
+        if p.xfmt != p0.xfmt:
+            raise ValueError("parts must share the activation format")
         if (p.g_idx is None) != (p0.g_idx is None) or (
                 p.g_idx is not None and not np.array_equal(p.g_idx, p0.g_idx)):
             raise ValueError("parts must share g_idx")
     bias = None
     if any(p.bias is not None for p in parts):
-        bias = np.concatenate([p.bias if p.bias is not None else np.zeros(p.N, np.float16)
+        zero = np.float16 if p0.xfmt == "f16" else np.uint16       # +0 either way
+        bias = np.concatenate([p.bias if p.bias is not None else np.zeros(p.N, zero)
                                for p in parts])
     return Layer(K=p0.K, N=sum(p.N for p in parts), G=p0.G,
                  qweight=np.ascontiguousarray(np.concatenate([p.qweight for p in parts], axis=1)),
                  qzeros=np.ascontiguousarray(np.concatenate([p.qzeros for p in parts], axis=1)),
                  scales=np.ascontiguousarray(np.concatenate([p.scales for p in parts], axis=1)),
-                 g_idx=p0.g_idx, x=p0.x if x is None else x, bias=bias, seed=p0.seed)
+                 g_idx=p0.g_idx, x=p0.x if x is None else x, bias=bias, seed=p0.seed,
+                 xfmt=p0.xfmt)
 
 
 def make_x(M: int, K: int, seed: int) -> np.ndarray:

@@ -431,3 +431,113 @@ def test_missing_zeros_mean_symmetric_eight(oracle_mod):
     q = np.arange(K * N, dtype=np.int64).reshape(K, N) % 16
     W = oracle_mod.dequant32(pack_rows(q), None, np.ones((1, N), np.float16), None, K, N, G)
     assert np.array_equal(W, (q - 8).astype(np.float32))
+
+
+# ---------------------------------------------------------------- bfloat16 ---
+# Activation format: GPTQModel wiki "Inference Backends", hardware table
+# (ExLlama v2 row): the activation dtype (FP16, BF16 or FP32) is kept, with
+# FP16 scales and FP32 accumulation. bfloat16 is the upper half of a binary32
+# word, so numpy's float32 decoding and torch's float32 -> bfloat16 rounding
+# are independent references for the oracle's own conversions.
+
+def _torch_bf16_bits(v32):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_decode_exhaustive(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = oracle_mod.bf16_to_double(bits.astype(np.uint16))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # closed forms
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x0080: 2.0 ** -126,
+             0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127}
+    for b, v in cases.items():
+        assert oracle_mod.bf16_to_double(np.array([b], dtype=np.uint16))[0] == v, hex(b)
+
+
+def test_double_to_bf16_matches_torch(oracle_mod):
+    rng = np.random.default_rng(21)
+    pats = rng.integers(0, 1 << 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    pats[:20000] = (pats[:20000] & 0xFFFF0000) | 0x8000        # exact ties
+    pats[20000:30000] &= 0x807FFFFF                             # bfloat16 subnormal range
+    v = pats.view(np.float32)
+    keep = np.isfinite(v)
+    v = v[keep]
+    got = oracle_mod.double_to_bf16(v.astype(np.float64))
+    ref = _torch_bf16_bits(v)
+    assert np.array_equal(got, ref)
+
+
+def test_double_to_bf16_hand_cases(oracle_mod):
+    d = oracle_mod.double_to_bf16
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to the even fraction
+    assert d([1 + 2.0 ** -8])[0] == 0x3F80
+    assert d([1 + 3 * 2.0 ** -8])[0] == 0x3F82
+    assert d([1 + 2.0 ** -8 + 2.0 ** -30])[0] == 0x3F81
+    assert d([-(1 + 2.0 ** -8)])[0] == 0xBF80
+    assert d([(2 - 2.0 ** -8) * 2.0 ** 127])[0] == 0x7F80     # halfway to 2^128: overflow
+    assert d([(2 - 2.0 ** -7) * 2.0 ** 127])[0] == 0x7F7F
+    assert d([2.0 ** -134])[0] == 0x0000                      # half the smallest subnormal
+    assert d([3 * 2.0 ** -134])[0] == 0x0002
+    assert d([70000.0])[0] == 0x4789                          # beyond binary16's range
+
+
+def test_dequant_bf16_is_one_rounding(oracle_mod):
+    L = synth.make_layer(256, 64, 32, 1, seed=synth.layer_seed("bf16 pin", 1))
+    W = oracle_mod.dequant32(L.qweight, L.qzeros, L.scales, None, 256, 64, 32)
+    got = oracle_mod.dequant_bf16(L.qweight, L.qzeros, L.scales, None, 256, 64, 32)
+    assert np.array_equal(got, _torch_bf16_bits(W))
+    # the rounding matters: truncating the fp32 word differs somewhere
+    assert not np.array_equal(got, (W.view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_bf16_route_equals_f16_route_on_shared_values(oracle_mod):
+    """Activations with at most 8 significant bits inside binary16's normal
+    range are exact in both formats: the two formats then give the same y."""
+    rng = np.random.default_rng(22)
+    M, K, N, G = 3, 256, 48, 64
+    L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("bf16 pin", 2), act_order=True)
+    xv = rng.integers(-255, 256, size=(M, K)).astype(np.float64) * 2.0 ** -6
+    bv = rng.integers(-255, 256, size=N).astype(np.float64) * 2.0 ** -9
+    x16, b16 = xv.astype(np.float16), bv.astype(np.float16)
+    xb = (xv.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = (bv.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle_mod.bf16_to_double(xb), xv)
+    y16, A16 = oracle_mod.matmul(x16, L.qweight, L.qzeros, L.scales, L.g_idx, K, N, G, bias=b16)
+    yb, Ab = oracle_mod.matmul(xb, L.qweight, L.qzeros, L.scales, L.g_idx, K, N, G, bias=bb,
+                               xfmt="bf16")
+    assert np.array_equal(y16, yb) and np.array_equal(A16, Ab)
+    yf, _ = oracle_mod.matmul(xb, L.qweight, L.qzeros, L.scales, L.g_idx, K, N, G, bias=bb,
+                              xfmt="bf16", route="fallback")
+    assert np.array_equal(yf, yb)
+    ms, ns = np.array([0, 2, 1]), np.array([5, 47, 0])
+    ya, _ = oracle_mod.matmul_at(xb, L.qweight, L.qzeros, L.scales, L.g_idx, K, N, G, ms, ns,
+                                 bias=bb, xfmt="bf16")
+    assert np.array_equal(ya, yb[ms, ns])
+
+
+def test_bf16_activations_beyond_binary16_range(oracle_mod):
+    """Single non-zero activations give y = x * W exactly: 2^40 (beyond
+    binary16) and 2^-130 (a bfloat16 subnormal); zero activations give the
+    bias."""
+    K, N, G = 128, 16, 32
+    L = synth.make_layer(K, N, G, 1, seed=synth.layer_seed("bf16 pin", 3))
+    W = oracle_mod.dequant32(L.qweight, L.qzeros, L.scales, None, K, N, G).astype(np.float64)
+    x = np.zeros((3, K), dtype=np.uint16)
+    x[0, 7] = 0x5380                  # 2^40
+    x[1, 99] = 0x0008                 # 8 * 2^-133 = 2^-130
+    bias = np.arange(N, dtype=np.uint16) + 0x3F80        # 1, 1 + 2^-7, ...
+    y, _ = oracle_mod.matmul(x, L.qweight, L.qzeros, L.scales, None, K, N, G, xfmt="bf16")
+    assert np.array_equal(y[0], 2.0 ** 40 * W[7]) and np.array_equal(y[1], 2.0 ** -130 * W[99])
+    assert not y[2].any()
+    yb, _ = oracle_mod.matmul(x, L.qweight, L.qzeros, L.scales, None, K, N, G, bias=bias,
+                              xfmt="bf16")
+    assert np.array_equal(yb[2], 1 + np.arange(N) * 2.0 ** -7)
+    with pytest.raises(ValueError):
+        oracle_mod.matmul(x, L.qweight, L.qzeros, L.scales, None, K, N, G, xfmt="f32")
