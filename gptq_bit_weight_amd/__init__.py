@@ -36,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "q4_make", "q4_make_cat", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
+    "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16",
 )
 
 _lib = None
@@ -68,7 +69,10 @@ def load_library():
     lib.q4_matmul.argtypes = [P, P, P, I, P]
     lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
     lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, I, P]
-    for f in (lib.q4_matmul, lib.q4_matmul_bias, lib.q4_matmul_ex):
+    lib.q4_matmul_bf16.argtypes = [P, P, P, P, I, P]
+    lib.q4_matmul_ex_bf16.argtypes = [P, P, P, P, I, I, I, I, P]
+    for f in (lib.q4_matmul, lib.q4_matmul_bias, lib.q4_matmul_ex, lib.q4_matmul_bf16,
+              lib.q4_matmul_ex_bf16):
         f.restype = I
     lib.q4_free.argtypes = [P]
     lib.q4_free.restype = None
@@ -80,6 +84,8 @@ def load_library():
     lib.q4_path_for.restype = I
     lib.q4_dequant_dump.argtypes = [P, I, P, P]
     lib.q4_dequant_dump.restype = I
+    lib.q4_dequant_dump_bf16.argtypes = [P, I, P, P]
+    lib.q4_dequant_dump_bf16.restype = I
     lib.q4_handle_info.argtypes = [P, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I),
                                    ctypes.POINTER(I)]
     lib.q4_handle_info.restype = I
@@ -286,44 +292,57 @@ class Q4Matrix:
 
     def matmul(self, x, bias=None, out=None, *, path: int = 0, variant: int = 0, splits: int = 0,
                stream=None):
-        """out[M, N] = fp16(x[M, K] @ W (+ bias)); fp32 accumulation.
+        """out[M, N] = x[M, K] @ W (+ bias), accumulated in fp32 and rounded
+        once to the activations' dtype: float16, or bfloat16 (bias and out
+        then bfloat16 too; the weights and fp16 scales are the same).
 
         path: 0 automatic, PATH_GEMV or PATH_MFMA. variant: skinny kernel --
         16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 automatic,
         1 register-staged, 2 direct-to-LDS, 3 weights streamed into
-        registers (the automatic choice). splits: skinny kernel K splits
-        (0 planned, 1..16); must be 0 for the GEMM."""
+        registers (the automatic choice; the only one for bfloat16).
+        splits: skinny kernel K splits (0 planned, 1..16); must be 0 for the
+        GEMM."""
         torch = _torch()
         h = self._handle()
-        _dev_tensor(x, torch.float16, "x")
+        if getattr(x, "dtype", None) not in (torch.float16, torch.bfloat16):
+            raise ValueError(f"x must be float16 or bfloat16, got {getattr(x, 'dtype', type(x))}")
+        dt = x.dtype
+        _dev_tensor(x, dt, "x")
         if x.dim() != 2 or x.shape[1] != self.K:
             raise ValueError(f"x must be [M, {self.K}], got {tuple(x.shape)}")
         M = int(x.shape[0])
         if out is None:
-            out = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+            out = torch.empty((M, self.N), dtype=dt, device=x.device)
         else:
-            _dev_tensor(out, torch.float16, "out", (M, self.N))
+            _dev_tensor(out, dt, "out", (M, self.N))
         if bias is not None:
-            _dev_tensor(bias, torch.float16, "bias", (self.N,))
+            _dev_tensor(bias, dt, "bias", (self.N,))
         for t, nm in ((x, "x"), (out, "out"), (bias, "bias")):
             if t is not None and t.device != self.device:
                 raise ValueError(f"{nm} is on {t.device}, the matrix on {self.device}")
+        lib = load_library()
+        fn, name = ((lib.q4_matmul_ex_bf16, "q4_matmul_bf16") if dt == torch.bfloat16
+                    else (lib.q4_matmul_ex, "q4_matmul"))
         with torch.cuda.device(self.device):
-            st = load_library().q4_matmul_ex(h, x.data_ptr(), bias.data_ptr() if bias is not None
-                                             else None, out.data_ptr(), M, path, variant, splits,
-                                             _stream_ptr(stream))
-        _check(st, "q4_matmul")
+            st = fn(h, x.data_ptr(), bias.data_ptr() if bias is not None else None,
+                    out.data_ptr(), M, path, variant, splits, _stream_ptr(stream))
+        _check(st, name)
         return out
 
     __call__ = matmul
 
-    def dequant_dump(self, path: int = PATH_GEMV, stream=None):
-        """fp16 [K, N]: the dequantized values the kernel of `path` computes."""
+    def dequant_dump(self, path: int = PATH_GEMV, stream=None, dtype=None):
+        """[K, N] in dtype (float16, or bfloat16 for the bfloat16 kernels): the
+        dequantized values the kernel of `path` computes."""
         torch = _torch()
-        w = torch.empty((self.K, self.N), dtype=torch.float16, device=self.device)
+        dtype = dtype or torch.float16
+        if dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"dtype must be float16 or bfloat16, got {dtype}")
+        w = torch.empty((self.K, self.N), dtype=dtype, device=self.device)
+        lib = load_library()
+        fn = lib.q4_dequant_dump_bf16 if dtype == torch.bfloat16 else lib.q4_dequant_dump
         with torch.cuda.device(self.device):
-            st = load_library().q4_dequant_dump(self._handle(), path, w.data_ptr(),
-                                                _stream_ptr(stream))
+            st = fn(self._handle(), path, w.data_ptr(), _stream_ptr(stream))
         _check(st, "q4_dequant_dump")
         return w
 

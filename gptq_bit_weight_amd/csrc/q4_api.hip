@@ -10,18 +10,18 @@
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, bool gather_x, hipStream_t stream);
+                       int M, int col_tiles, int splits, bool gather_x, bool bf16, hipStream_t stream);
 hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                            int M, hipStream_t stream);
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                             int M, hipStream_t stream);
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, hipStream_t stream);
+                              int M, bool bf16, hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          int n_total, int col_off, hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
-hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
+hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream);
 
 namespace {
 
@@ -215,7 +215,7 @@ q4_status ensure_xperm(const q4_matrix* h, int M, hipStream_t stream)
 }
 
 q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                      int M, int path, int variant, int splits, hipStream_t stream)
+                      int M, int path, int variant, int splits, bool bf16, hipStream_t stream)
 {
     if (!h) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: null handle");
     if (M < 0) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: M=%d is negative", M);
@@ -245,6 +245,9 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the GEMM takes no K splits (got %d)", splits);
         if (variant < 0 || variant > 3)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1, 2 or 3", variant);
+        if (bf16 && variant != 0 && variant != 3)
+            return fail(Q4_ERR_UNSUPPORTED,
+                        "q4_matmul: bfloat16 activations run on GEMM variant 3 only (got %d)", variant);
     }
 
     int ct = 0, s = 0;
@@ -265,7 +268,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         xe = h->xperm;
     }
     if (kind == Q4_PATH_GEMV) {
-        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, stream), "q4_matmul: gemv launch");
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, bf16, stream), "q4_matmul: gemv launch");
     } else {
         // Three GEMM variants share tile shape and accumulation order: the
         // automatic choice streams the weights into registers (activations
@@ -277,7 +280,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (variant == 1)
             Q4_HIP(launch_gemm_regs(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
         else if (variant == 3)
-            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, stream), "q4_matmul: gemm launch");
         else
             Q4_HIP(launch_gemm_dma(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
     }
@@ -310,13 +313,13 @@ q4_matrix* q4_make_cat(int parts, const int32_t* const* qweight, const int32_t* 
 
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M, hipStream_t stream)
 {
-    return q4::matmul_impl(h, x, nullptr, out, M, 0, 0, 0, stream);
+    return q4::matmul_impl(h, x, nullptr, out, M, 0, 0, 0, false, stream);
 }
 
 q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                          int M, hipStream_t stream)
 {
-    return q4::matmul_impl(h, x, bias, out, M, 0, 0, 0, stream);
+    return q4::matmul_impl(h, x, bias, out, M, 0, 0, 0, false, stream);
 }
 
 q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
@@ -324,7 +327,21 @@ q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
 {
     if (path != 0 && path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_matmul_ex: unknown path %d", path);
-    return q4::matmul_impl(h, x, bias, out, M, path, variant, splits, stream);
+    return q4::matmul_impl(h, x, bias, out, M, path, variant, splits, false, stream);
+}
+
+q4_status q4_matmul_bf16(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                         int M, hipStream_t stream)
+{
+    return q4::matmul_impl(h, x, bias, out, M, 0, 0, 0, true, stream);
+}
+
+q4_status q4_matmul_ex_bf16(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                            int M, int path, int variant, int splits, hipStream_t stream)
+{
+    if (path != 0 && path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_matmul_ex_bf16: unknown path %d", path);
+    return q4::matmul_impl(h, x, bias, out, M, path, variant, splits, true, stream);
 }
 
 void q4_free(q4_matrix* h) { q4::destroy(h); }
@@ -354,15 +371,25 @@ int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_
     return 0;
 }
 
+static q4_status dump_impl(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream,
+                           const char* who)
+{
+    if (!h || !w) return q4::fail(Q4_ERR_INVALID_ARG, "%s: null argument", who);
+    if (path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
+        return q4::fail(Q4_ERR_INVALID_ARG, "%s: unknown path %d", who, path);
+    hipError_t e = q4::launch_dump(h, path, w, bf16, stream);
+    if (e != hipSuccess) return q4::fail(Q4_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+    return Q4_OK;
+}
+
 q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream)
 {
-    if (!h || !w) return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: null argument");
-    if (path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
-        return q4::fail(Q4_ERR_INVALID_ARG, "q4_dequant_dump: unknown path %d", path);
-    hipError_t e = q4::launch_dump(h, path, w, stream);
-    if (e != hipSuccess)
-        return q4::fail(Q4_ERR_HIP, "q4_dequant_dump: %s", hipGetErrorString(e));
-    return Q4_OK;
+    return dump_impl(h, path, w, false, stream, "q4_dequant_dump");
+}
+
+q4_status q4_dequant_dump_bf16(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream)
+{
+    return dump_impl(h, path, w, true, stream, "q4_dequant_dump_bf16");
 }
 
 }  // extern "C"

@@ -107,6 +107,67 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, zero_t z, h2 s2)
     return d * s8;
 }
 
+// ---- bfloat16 activations ---------------------------------------------------
+// The activation dtype is kept (GPTQModel wiki "Inference Backends", hardware
+// table, ExLlama v2 row: FP16/BF16 activations, FP16 scales, FP32
+// accumulation). With bfloat16 activations the MFMA takes bfloat16 operands,
+// so the weights are formed in fp32 and packed to bfloat16 (the upper half of
+// a binary32 word):
+//  * the unpacked halves h = 1024 + q (pairs 0, 2) and 1024 + 16 q (pairs 1,
+//    3) give f * h + c = t * (q - z) exactly in one fused multiply-add each
+//    (v_fma_mix_f32 reads the fp16 half directly), with f = t, c =
+//    -(1024 + z) t for pairs 0 and 2, f = t / 16, c = -(64 + z) t for pairs 1
+//    and 3. For t = 1 the result is the exact small integer q - z; for t = s
+//    (an fp16 scale, 11 significant bits) the constants and the product
+//    t (q - z) need at most 22 bits, so each step is exact in fp32;
+//  * the pack rounds to nearest even: exact for q - z, the one rounding of
+//    s (q - z) to bfloat16 otherwise.
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef float ff2 __attribute__((ext_vector_type(2)));
+
+struct mix_t {
+    float t;     // scale of the result (1 for q - z)
+    float c0;    // -(1024 + z) t
+    float c1;    // -(64 + z) t
+};
+
+__device__ __forceinline__ mix_t mix_consts(uint32_t z, float t)
+{
+    mix_t m;
+    m.t = t;
+    m.c0 = -(1024.0f + (float)z) * t;
+    m.c1 = -(64.0f + (float)z) * t;
+    return m;
+}
+
+// Two fp32 values rounded to bfloat16 (nearest, ties to even), packed
+// (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return bitcast<uint32_t>(__builtin_convertvector(ff2{lo, hi}, b2));
+}
+
+__device__ __forceinline__ uint32_t mix_pair(uint32_t hp, float f, float c)
+{
+    const h2 h = bitcast<h2>(hp);
+    return pack_bf16(__builtin_fmaf((float)h[0], f, c), __builtin_fmaf((float)h[1], f, c));
+}
+
+// One private-layout word as eight bfloat16 values t * (q - z) in k order.
+__device__ __forceinline__ b8 mix_word(uint32_t w, const mix_t& m)
+{
+    const uint32_t magic = kMagic2;
+    const uint32_t w8 = w >> 8;
+    const float f1 = m.t * 0.0625f;
+    u4 o;
+    o[0] = mix_pair(and_or(w, 0x000F000Fu, magic), m.t, m.c0);
+    o[1] = mix_pair(and_or(w, 0x00F000F0u, magic), f1, m.c1);
+    o[2] = mix_pair(and_or(w8, 0x000F000Fu, magic), m.t, m.c0);
+    o[3] = mix_pair(and_or(w8, 0x00F000F0u, magic), f1, m.c1);
+    return bitcast<b8>(o);
+}
+
 // ---- raw buffer loads ------------------------------------------------------
 // A raw buffer descriptor carries the byte size of the tensor; a load whose
 // per-lane offset lies at or beyond it returns zeros without touching memory.
@@ -164,6 +225,16 @@ __device__ __forceinline__ f16x mfma32(h8 a, h8 b, f16x c)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f4 mfma16(b8 a, b8 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x mfma32(b8 a, b8 b, f16x c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
 {
     return bitcast<uint16_t>(static_cast<_Float16>(v));
@@ -172,6 +243,31 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b)
 {
     return static_cast<float>(bitcast<_Float16>(b));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v)
+{
+    return bitcast<uint16_t>(static_cast<__bf16>(v));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
+{
+    return bitcast<float>((uint32_t)b << 16);
+}
+
+// Activation-format traits: BF selects bfloat16 activations, bias and output.
+template <bool BF>
+__device__ __forceinline__ float act_to_f32(uint16_t b)
+{
+    if constexpr (BF) return bf16_bits_to_f32(b);
+    else return f16_bits_to_f32(b);
+}
+
+template <bool BF>
+__device__ __forceinline__ uint16_t f32_to_act(float v)
+{
+    if constexpr (BF) return f32_to_bf16_bits(v);
+    else return f32_to_f16_bits(v);
 }
 
 }  // namespace q4dev

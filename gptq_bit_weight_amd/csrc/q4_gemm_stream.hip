@@ -24,6 +24,10 @@
 //  * One barrier per k-tile: after it, every wave has finished the previous
 //    tile, so the stage that tile used is refilled (tile kt + 1) while tile
 //    kt is multiplied.
+//  * BF: bfloat16 activations, bias and output (the activation dtype is kept;
+//    GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row). The
+//    matrix pipe then takes bfloat16 operands: each weight s * (q - z) is
+//    formed exactly in fp32 and rounded once to bfloat16.
 #include <type_traits>
 
 #include "q4_device.h"
@@ -125,8 +129,9 @@ __device__ __forceinline__ void load_b(BRegs<NG>& R, const Ctx& c, const GemmArg
 // KT: K is not a multiple of 64, so the last k-tile skips its sub-steps past
 // K (a separate instantiation, so that the common kernel has no branch
 // around the multiply: the accumulators stay in the same registers).
-template <int NG, bool KT>
-__global__ __launch_bounds__(NT) void q4_gemm_stream_kernel(GemmArgs p)
+// (Two workgroups per CU: the register budget is 256 per lane.)
+template <int NG, bool KT, bool BF>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_stream_kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
@@ -198,26 +203,43 @@ __global__ __launch_bounds__(NT) void q4_gemm_stream_kernel(GemmArgs p)
     auto mma = [&](const char* A, const BRegs<NG>& R, int kt) {
         zero_t hz[NG][NJ];
         h2 s2[NG][NJ];
+        mix_t mz[NJ];   // BF: the constants of the current group only (registers)
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                hz[gi][j] = zero_pair((R.z[gi][j] >> c.z_shift[j]) & 0xFu);
-                s2[gi][j] = scale_pair(R.s[gi][j]);
+                if constexpr (!BF) {
+                    hz[gi][j] = zero_pair((R.z[gi][j] >> c.z_shift[j]) & 0xFu);
+                    s2[gi][j] = scale_pair(R.s[gi][j]);
+                }
             }
         const int k0 = kt * BK;
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
-            if (!KT || k0 + 16 * sub < p.K) {
-                const int gi = NG == 2 ? (sub >> 1) : 0;
-                h8 b[NJ];
+            const int gi = NG == 2 ? (sub >> 1) : 0;
+            if constexpr (BF) {
+                if (sub % (4 / NG) == 0)
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) b[j] = dequant_word(R.w[j][sub & 1][sub >> 1], hz[gi][j], s2[gi][j]);
+                    for (int j = 0; j < NJ; ++j)
+                        mz[j] = mix_consts((R.z[gi][j] >> c.z_shift[j]) & 0xFu,
+                                           f16_bits_to_f32((uint16_t)R.s[gi][j]));
+            }
+            if (!KT || k0 + 16 * sub < p.K) {
+                u4 b[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const uint32_t w = R.w[j][sub & 1][sub >> 1];
+                    if constexpr (BF) b[j] = bitcast<u4>(mix_word(w, mz[j]));
+                    else b[j] = bitcast<u4>(dequant_word(w, hz[gi][j], s2[gi][j]));
+                }
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
-                    const h8 a = *reinterpret_cast<const h8*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
+                    const u4 a = *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a, b[j], acc[i][j]);
+                    for (int j = 0; j < NJ; ++j) {
+                        if constexpr (BF) acc[i][j] = mfma32(bitcast<b8>(a), bitcast<b8>(b[j]), acc[i][j]);
+                        else acc[i][j] = mfma32(bitcast<h8>(a), bitcast<h8>(b[j]), acc[i][j]);
+                    }
                 }
             }
         }
@@ -259,15 +281,29 @@ __global__ __launch_bounds__(NT) void q4_gemm_stream_kernel(GemmArgs p)
     for (int j = 0; j < NJ; ++j) {
         const int n = lane_cols[j];
         if (n >= p.N) continue;
-        const float bv = p.bias ? f16_bits_to_f32(p.bias[n]) : 0.f;
+        const float bv = p.bias ? act_to_f32<BF>(p.bias[n]) : 0.f;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_f16_bits(acc[i][j][r] + bv);
+                if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_act<BF>(acc[i][j][r] + bv);
             }
     }
+}
+
+template <bool BF>
+hipError_t launch_stream(const GemmArgs& p, int tiles, bool g32, bool kt, hipStream_t stream)
+{
+    if (g32 && kt)
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+    else if (g32)
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+    else if (kt)
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -275,7 +311,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_stream_kernel(GemmArgs p)
 namespace q4 {
 
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, hipStream_t stream)
+                              int M, bool bf16, hipStream_t stream)
 {
     GemmArgs p;
     p.qweight = h->qweight;
@@ -292,15 +328,7 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;
-    if (g32 && kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true>), dim3(tiles), dim3(NT), 0, stream, p);
-    else if (g32)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false>), dim3(tiles), dim3(NT), 0, stream, p);
-    else if (kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true>), dim3(tiles), dim3(NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false>), dim3(tiles), dim3(NT), 0, stream, p);
-    return hipGetLastError();
+    return bf16 ? launch_stream<true>(p, tiles, g32, kt, stream) : launch_stream<false>(p, tiles, g32, kt, stream);
 }
 
 }  // namespace q4

@@ -168,23 +168,24 @@ __device__ __forceinline__ u4 row_shl(u4 v)
 // from lane group i % XS of the load that holds step i, shifted down the row.
 // (i is a constant after unrolling, so the switch folds away.)
 template <int XS>
-__device__ __forceinline__ h8 a_operand(const u4 a[4], int i)
+__device__ __forceinline__ u4 a_operand(const u4 a[4], int i)
 {
     constexpr int R = 16 / XS;
     const u4 v = a[i / XS];
     switch (R * (i % XS)) {
-    case 4: return bitcast<h8>(row_shl<4>(v));
-    case 8: return bitcast<h8>(row_shl<8>(v));
-    case 12: return bitcast<h8>(row_shl<12>(v));
-    default: return bitcast<h8>(v);
+    case 4: return row_shl<4>(v);
+    case 8: return row_shl<8>(v);
+    case 12: return row_shl<12>(v);
+    default: return v;
     }
 }
 
 // Multiply one block into the totals: per group, the MFMA sums of x * (q - z)
-// over its k-steps, then tot += s * sum in fp32.
+// over its k-steps, then tot += s * sum in fp32. BF: bfloat16 activations and
+// the exact q - z as bfloat16 (both operands bfloat16 on the matrix pipe).
 // XL: block b's activations are read from the LDS copy (xl = this lane's
 // address in it for the first block of the workgroup's range, bs0).
-template <int NGB, int CT, int XS, bool XL>
+template <int NGB, int CT, int XS, bool XL, bool BF>
 __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT], uint32_t zshift,
                                               const char* xl, int b, int bs0)
 {
@@ -201,20 +202,32 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
         zero_t zp[CT];
+        mix_t mz[CT];
         float sf[CT];
+        // (1 kept opaque, so that f * h + c stays one v_fma_mix_f32 instead
+        // of a conversion and an add)
+        float one = 1.0f;
+        if constexpr (BF) asm("" : "+v"(one));
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-            zp[j] = zero_pair((B.z[gi][j] >> zshift) & 0xFu);
+            const uint32_t z = (B.z[gi][j] >> zshift) & 0xFu;
+            if constexpr (BF) mz[j] = mix_consts(z, one);
+            else zp[j] = zero_pair(z);
             sf[j] = f16_bits_to_f32((uint16_t)B.s[gi][j]);
         }
         f4 acc[CT];
 #pragma unroll
         for (int ii = 0; ii < SPG; ++ii) {
             const int i = gi * SPG + ii;
-            const h8 a = a_operand<XS>(av, i);
+            const u4 a = a_operand<XS>(av, i);
+            const f4 c0 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < CT; ++j)
-                acc[j] = mfma16(a, sub_zero_word(B.w[j][i], zp[j]), ii == 0 ? f4{0.f, 0.f, 0.f, 0.f} : acc[j]);
+            for (int j = 0; j < CT; ++j) {
+                if constexpr (BF)
+                    acc[j] = mfma16(bitcast<b8>(a), mix_word(B.w[j][i], mz[j]), ii == 0 ? c0 : acc[j]);
+                else
+                    acc[j] = mfma16(bitcast<h8>(a), sub_zero_word(B.w[j][i], zp[j]), ii == 0 ? c0 : acc[j]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < CT; ++j)
@@ -256,7 +269,7 @@ __device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR]
         }
 }
 
-template <int NGB, int CT, int XS, bool TAIL, bool XL>
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF>
 __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 {
     constexpr int COLS = 16 * CT;
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS, XL>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
+                compute_block<NGB, CT, XS, XL, BF>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
                 load_block<NGB, CT, XS, TAIL, XL>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS, XL>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
+            if (d < last) compute_block<NGB, CT, XS, XL, BF>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -399,8 +412,8 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
             float y = red[0][m][c];
 #pragma unroll
             for (int w = 1; w < WV; ++w) y += red[w][m][c];
-            if (p.bias) y += f16_bits_to_f32(p.bias[n]);
-            p.out[(size_t)m * p.N + n] = f32_to_f16_bits(y);
+            if (p.bias) y += act_to_f32<BF>(p.bias[n]);
+            p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
         }
         return;
     }
@@ -437,22 +450,22 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int s = 0; s < p.splits; ++s)
             y += __hip_atomic_load(&p.partials[((size_t)s * 16 + m) * p.N + n], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (p.bias) y += f16_bits_to_f32(p.bias[n]);
-        p.out[(size_t)m * p.N + n] = f32_to_f16_bits(y);
+        if (p.bias) y += act_to_f32<BF>(p.bias[n]);
+        p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
     }
     if (tid == 0)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NGB, int XS, bool TAIL, bool XL>
+template <int NGB, int XS, bool TAIL, bool XL, bool BF>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
     const dim3 block(NT);
     const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL>), dim3((p.N + 63) / 64, splits), block, lds, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF>), dim3((p.N + 63) / 64, splits), block, lds, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -462,25 +475,25 @@ hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 // per k-step. A K that is not a multiple of 128 (one partial block) takes the
 // one-per-step form, whose past-K steps are masked per load.
 // (Staged act-order activations come with M <= 2 only.)
-template <int NGB, bool XL>
+template <int NGB, bool XL, bool BF>
 hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
-    if (p.K % 128) return launch_ct<NGB, 1, true, XL>(p, ct, splits, stream);
-    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL>(p, ct, splits, stream);
+    if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF>(p, ct, splits, stream);
+    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF>(p, ct, splits, stream);
     if constexpr (!XL) {
-        if (p.M <= 8) return launch_ct<NGB, 2, false, XL>(p, ct, splits, stream);
-        return launch_ct<NGB, 1, false, XL>(p, ct, splits, stream);
+        if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF>(p, ct, splits, stream);
+        return launch_ct<NGB, 1, false, XL, BF>(p, ct, splits, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <bool XL>
+template <bool XL, bool BF>
 hipError_t launch_xl(const GemvArgs& p, int ngb, int ct, int splits, hipStream_t stream)
 {
     switch (ngb) {
-    case 1: return launch_ngb<1, XL>(p, ct, splits, stream);
-    case 2: return launch_ngb<2, XL>(p, ct, splits, stream);
-    case 4: return launch_ngb<4, XL>(p, ct, splits, stream);
+    case 1: return launch_ngb<1, XL, BF>(p, ct, splits, stream);
+    case 2: return launch_ngb<2, XL, BF>(p, ct, splits, stream);
+    case 4: return launch_ngb<4, XL, BF>(p, ct, splits, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -490,7 +503,7 @@ hipError_t launch_xl(const GemvArgs& p, int ngb, int ct, int splits, hipStream_t
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, bool gather_x, hipStream_t stream)
+                       int M, int col_tiles, int splits, bool gather_x, bool bf16, hipStream_t stream)
 {
     if (M < 1 || M > 16 || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
     if (gather_x && (!h->inv16 || !gemv_gathers_x(M, h->K, splits))) return hipErrorInvalidValue;
@@ -522,8 +535,11 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     // groups per 128-row block: groups of 32 or 64 rows split a block; larger
     // groups (and one group over K) cover it whole
     const int ngb = (h->G == h->K || h->G >= 128) ? 1 : 128 / h->G;
-    return gather_x ? launch_xl<true>(p, ngb, col_tiles, splits, stream)
-                    : launch_xl<false>(p, ngb, col_tiles, splits, stream);
+    if (bf16)
+        return gather_x ? launch_xl<true, true>(p, ngb, col_tiles, splits, stream)
+                        : launch_xl<false, true>(p, ngb, col_tiles, splits, stream);
+    return gather_x ? launch_xl<true, false>(p, ngb, col_tiles, splits, stream)
+                    : launch_xl<false, false>(p, ngb, col_tiles, splits, stream);
 }
 
 }  // namespace q4

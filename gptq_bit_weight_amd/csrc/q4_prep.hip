@@ -108,7 +108,10 @@ __global__ __launch_bounds__(256) void q4_permute_rows_kernel(const uint16_t* __
 // kernel's own (q - z) from sub_zero_word times the fp32 scale, which is the
 // exact weight the kernel applies, then one RNE rounding. Otherwise (GEMM):
 // the fp16 value dequant_word feeds to the MFMA.
-template <bool FACTORED>
+// BF: bfloat16 values of the bfloat16 forms -- FACTORED: the kernel's exact
+// q - z as bfloat16 times the fp32 scale, rounded once to bfloat16;
+// otherwise the bfloat16 weight mix_word feeds to the bfloat16 MFMA.
+template <bool FACTORED, bool BF>
 __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict__ qweight,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint32_t* __restrict__ qzeros,
@@ -125,7 +128,15 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const uint32_t word = qweight[private_word(kk, n, N, &e)];
         const uint32_t z = (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
         const uint16_t sb = scales[(size_t)g * N + n];
-        if (FACTORED) {
+        if constexpr (BF) {
+            float t = FACTORED ? 1.0f : f16_bits_to_f32(sb);
+            asm("" : "+v"(t));    // as in the kernels: one fused multiply-add per value
+            const b8 v = mix_word(word, mix_consts(z, t));
+            if (FACTORED)
+                w[idx] = f32_to_bf16_bits(f16_bits_to_f32(sb) * static_cast<float>(v[e]));
+            else
+                w[idx] = bitcast<uint16_t>(v[e]);
+        } else if (FACTORED) {
             const h8 d = sub_zero_word(word, zero_pair(z));
             w[idx] = f32_to_f16_bits(f16_bits_to_f32(sb) * static_cast<float>(d[e]));
         } else {
@@ -171,14 +182,21 @@ hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp
     return hipGetLastError();
 }
 
-hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream)
+hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream)
 {
     const dim3 grid(grid_for((size_t)h->K * h->N));
-    if (path == Q4_PATH_GEMV)
-        hipLaunchKernelGGL(q4_dump_kernel<true>, grid, dim3(256), 0, stream, h->qweight, h->scales,
+    const bool f = path == Q4_PATH_GEMV;
+    if (f && bf16)
+        hipLaunchKernelGGL((q4_dump_kernel<true, true>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+    else if (f)
+        hipLaunchKernelGGL((q4_dump_kernel<true, false>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+    else if (bf16)
+        hipLaunchKernelGGL((q4_dump_kernel<false, true>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     else
-        hipLaunchKernelGGL(q4_dump_kernel<false>, grid, dim3(256), 0, stream, h->qweight, h->scales,
+        hipLaunchKernelGGL((q4_dump_kernel<false, false>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     return hipGetLastError();
 }

@@ -162,6 +162,31 @@ q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
                        uint16_t* out, int M, int path, int variant, int splits,
                        hipStream_t stream);
 
+/*
+ * q4_matmul_bf16 -- q4_matmul_bias with bfloat16 activations, bias and output
+ * (GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row: the
+ * activation dtype -- FP16, BF16 or FP32 -- is kept, with FP16 scales and
+ * FP32 accumulation). x is bfloat16 [M][K], bias bfloat16 [N] or NULL, out
+ * bfloat16 [M][N]; the handle (fp16 scales) is the same as for fp16 calls.
+ * Accumulation is fp32 and the only rounding of the result is the final
+ * round-to-nearest-even cast to bfloat16. The skinny kernel applies the
+ * exact weights s * (q - z) (as the fp16 path); the GEMM multiplies the
+ * weights rounded once to bfloat16, RNE_bf16(s * (q - z)), since its matrix
+ * operands are bfloat16. Same arguments, ownership, errors, concurrency and
+ * graph-capture rules as q4_matmul.
+ */
+q4_status q4_matmul_bf16(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
+                         uint16_t* out, int M, hipStream_t stream);
+
+/*
+ * q4_matmul_ex_bf16 -- q4_matmul_bf16 with an explicit kernel, as
+ * q4_matmul_ex; the GEMM takes variant 0 or 3 only (other variants:
+ * Q4_ERR_UNSUPPORTED).
+ */
+q4_status q4_matmul_ex_bf16(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
+                            uint16_t* out, int M, int path, int variant, int splits,
+                            hipStream_t stream);
+
 /* q4_free -- release a handle (NULL is allowed). The caller must have
  * synchronized every stream that used it. */
 void q4_free(q4_matrix* h);
@@ -209,6 +234,15 @@ int q4_path_for(const q4_matrix* h, int M);
  * round-to-nearest-even of s * (q - z). Not on the hot path.
  */
 q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
+
+/*
+ * q4_dequant_dump_bf16 -- as q4_dequant_dump for the bfloat16 kernels: w is
+ * bfloat16 [K][N]. Q4_PATH_GEMV: the skinny kernel's q - z in bfloat16 times
+ * the fp32 scale, rounded once to bfloat16; Q4_PATH_MFMA: the bfloat16
+ * weights the GEMM feeds its MFMA. Each value is round-to-nearest-even of
+ * s * (q - z) to bfloat16.
+ */
+q4_status q4_dequant_dump_bf16(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
 
 /*
  * q4_gemv_gather -- 1 when, for this act-order handle, M and K splits
