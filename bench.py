@@ -27,9 +27,10 @@ Also reported on the same JSON line:
   secondary     the same block with q/k/v and gate/up fused into one call each
                 (4 launches a step); the 70B-shaped MLP layers at M = 1, 2, 4,
                 8, 16 and the act-order 7B MLP layers at M = 1, 4 (GB/s, each
-                layer over >= 1 GiB of copies); the prefill GEMM at M = 2048 on
-                the 7B MLP shapes, groupsize 128 and 32 and act-order
-                (TFLOPS against the dense fp16 MFMA peak).
+                layer over >= 1 GiB of copies); the seven-layer block with
+                bfloat16 activations; the prefill GEMM at M = 2048 on the 7B
+                MLP shapes, groupsize 128 and 32, act-order and bfloat16
+                (TFLOPS against the dense fp16/bf16 MFMA peak).
 """
 from __future__ import annotations
 
@@ -41,6 +42,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -84,9 +87,12 @@ class Layer:
                     torch.from_numpy(L.g_idx).to(dev) if L.g_idx is not None else None)
         self.name, self.K, self.N, self.G, self.M = name, L.K, L.N, L.G, L.M
         self.mats = [self._make() for _ in range(copies)]
-        self.x = torch.from_numpy(L.x).to(dev)
-        self.bias = torch.from_numpy(L.bias).to(dev) if L.bias is not None else None
-        self.out = torch.empty((L.M, L.N), dtype=torch.float16, device=dev)
+        self.bf16 = L.xfmt == "bf16"
+        act = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)) if self.bf16 \
+            else torch.from_numpy
+        self.x = act(L.x).to(dev)
+        self.bias = act(L.bias).to(dev) if L.bias is not None else None
+        self.out = torch.empty((L.M, L.N), dtype=self.x.dtype, device=dev)
         self.bytes = L.metric_bytes()
         self.flops = 2 * L.M * L.K * L.N
         self.xp = ctypes.c_void_p(self.x.data_ptr())
@@ -107,9 +113,10 @@ class Layer:
             self.mats.pop().close()
 
     def launch(self, lib, copy, stream_ptr):
-        st = lib.q4_matmul_bias(self.mats[copy]._h, self.xp, self.bp, self.op, self.M, stream_ptr)
+        fn = lib.q4_matmul_bf16 if self.bf16 else lib.q4_matmul_bias
+        st = fn(self.mats[copy]._h, self.xp, self.bp, self.op, self.M, stream_ptr)
         if st:
-            raise RuntimeError(f"q4_matmul_bias({self.name}) failed: {lib.q4_last_error()}")
+            raise RuntimeError(f"q4_matmul({self.name}) failed: {lib.q4_last_error()}")
 
     def close(self):
         for m in self.mats:
@@ -117,10 +124,10 @@ class Layer:
         self.mats = []
 
 
-def build_layers(q4, torch, synth, specs, G, M, workload, copies):
+def build_layers(q4, torch, synth, specs, G, M, workload, copies, xfmt="f16"):
     layers = []
     for name, K, N, bias in specs:
-        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed(workload, name, M), bias=bias)
+        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed(workload, name, M), bias=bias, xfmt=xfmt)
         layers.append(Layer(q4, torch, name, L, copies))
     return layers
 
@@ -316,6 +323,25 @@ def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=F
     return out
 
 
+def bf16_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500):
+    """The seven-layer block with bfloat16 activations, bias and outputs:
+    the same weights' shapes, copies rotated and graphs replayed as in the
+    main figure."""
+    layers = build_layers(q4, torch, synth, synth.LLAMA7B_BLOCK, G, M, workload + "_bf16", copies,
+                          xfmt="bf16")
+    step_bytes = sum(ly.bytes for ly in layers)
+    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 50, stream, use_graph=True)
+    del graphs
+    lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
+    for ly in layers:
+        ly.close()
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (elapsed / steps) / 1e9
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_step": round(elapsed / steps * 1e6, 2),
+            "per_layer_us": {ly.name: round(t * 1e6, 3) for ly, t in zip(layers, lt)}}
+
+
 def prefill_rates(q4, torch, synth, lib, stream, M=2048):
     """TFLOP/s of the prefill GEMM on the 7B MLP shapes: groupsize 128 and 32,
     and act-order at 128 (the weights are 23-26 MB; compute, not memory,
@@ -323,9 +349,12 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
     three times after a warm-up replay; the median replay gives the time."""
     out = {}
     reps = 20
-    for K, N, G, act in ((4096, 11008, 128, False), (11008, 4096, 128, False), (4096, 11008, 32, False),
-                         (11008, 4096, 32, False), (4096, 11008, 128, True)):
-        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("prefill", K, N, G, act), act_order=act)
+    for K, N, G, act, xfmt in ((4096, 11008, 128, False, "f16"), (11008, 4096, 128, False, "f16"),
+                               (4096, 11008, 32, False, "f16"), (11008, 4096, 32, False, "f16"),
+                               (4096, 11008, 128, True, "f16"), (4096, 11008, 128, False, "bf16"),
+                               (11008, 4096, 128, False, "bf16")):
+        L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("prefill", K, N, G, act), act_order=act,
+                             xfmt=xfmt)
         ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
         with torch.cuda.stream(stream):
             ly.launch(lib, 0, ctypes.c_void_p(stream.cuda_stream))   # sizes the act-order workspace
@@ -348,7 +377,7 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
                 times.append(a.elapsed_time(b) * 1e-3 / reps)
         t = sorted(times)[1]
         tf = ly.flops / t / 1e12
-        out[f"{K}x{N}_g{G}{'_act' if act else ''}_m{M}"] = {
+        out[f"{K}x{N}_g{G}{'_act' if act else ''}{'_bf16' if xfmt == 'bf16' else ''}_m{M}"] = {
             "TFLOP/s": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)}
         del g
         ly.close()
@@ -358,13 +387,15 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
 
 
 def secondary(q4, torch, synth, lib, stream):
-    """Figures on the other workloads: the 7B block with projection fusion,
-    the 70B MLP layers at M = 1, 2, 4, 8, 16 (where the skinny kernel stops
+    """Figures on the other workloads: the 7B block with projection fusion
+    and with bfloat16 activations, the 70B MLP layers at M = 1, 2, 4, 8, 16 (where the skinny kernel stops
     being bandwidth-bound), the act-order 7B MLP layers at M = 1 and 4, and
     the prefill GEMM at M = 2048."""
     out = {}
     out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
                                                 "llama7b_block_decode", 10)
+    out["llama7b_block_bf16_m1"] = bf16_block(q4, torch, synth, lib, stream, 128, 1,
+                                              "llama7b_block_decode", 10)
     out["llama70b_mlp_decode"] = decode_sweep(q4, torch, synth, lib, stream, "llama70b_mlp_decode",
                                               synth.LLAMA70B_MLP, (1, 2, 4, 8, 16))
     out["llama7b_actorder_decode"] = decode_sweep(
