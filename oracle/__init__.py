@@ -15,6 +15,7 @@ Functions:
   double_to_bf16(values)       float64 -> bfloat16 bits, round to nearest even
   unpack_qweight(qweight, K)   uint8 [K, N] codes
   unpack_qzeros(qzeros, N)     uint8 [ng, N] zero points
+  (every function taking packed tensors has bits=4 (default) or 8)
   dequant32(...)               float32 [K, N], W = s * (q - z) (exact)
   dequant16(...)               uint16 [K, N], binary16 bits of RNE(W)
   dequant_bf16(...)            uint16 [K, N], bfloat16 bits of RNE(W)
@@ -55,21 +56,21 @@ def _load():
     lib.q4o_double_to_half_array.argtypes = [_I, _P, _P]
     lib.q4o_num_groups.argtypes = [_I, _I]
     lib.q4o_num_groups.restype = ctypes.c_int
-    lib.q4o_unpack_qweight.argtypes = [_P, _I, _I, _P]
-    lib.q4o_unpack_qzeros.argtypes = [_P, _I, _I, _P]
-    lib.q4o_dequant32.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
-    lib.q4o_dequant16.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
+    _F = ctypes.c_int
+    lib.q4o_unpack_qweight_ex.argtypes = [_P, _I, _I, _F, _P]
+    lib.q4o_unpack_qzeros_ex.argtypes = [_P, _I, _I, _F, _P]
+    lib.q4o_dequant32_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _F, _P]
+    lib.q4o_dequant16_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _F, _P]
     lib.q4o_bf16_to_double_array.argtypes = [_I, _P, _P]
     lib.q4o_double_to_bf16_array.argtypes = [_I, _P, _P]
-    lib.q4o_dequant_bf16.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
-    _F = ctypes.c_int
-    lib.q4o_matmul_fused_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
-    lib.q4o_matmul_fallback_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]
-    lib.q4o_matmul_fused_at_fmt.argtypes = [_F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                            _I, _P, _P, _P, _P]
-    for f in ("q4o_unpack_qweight", "q4o_unpack_qzeros", "q4o_dequant32", "q4o_dequant16",
-              "q4o_dequant_bf16", "q4o_matmul_fused_fmt", "q4o_matmul_fallback_fmt",
-              "q4o_matmul_fused_at_fmt"):
+    lib.q4o_dequant_bf16_ex.argtypes = [_P, _P, _P, _P, _I, _I, _I, _F, _P]
+    lib.q4o_matmul_fused_ex.argtypes = [_F, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]
+    lib.q4o_matmul_fallback_ex.argtypes = [_F, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]
+    lib.q4o_matmul_fused_at_ex.argtypes = [_F, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                           _I, _P, _P, _P, _P]
+    for f in ("q4o_unpack_qweight_ex", "q4o_unpack_qzeros_ex", "q4o_dequant32_ex",
+              "q4o_dequant16_ex", "q4o_dequant_bf16_ex", "q4o_matmul_fused_ex",
+              "q4o_matmul_fallback_ex", "q4o_matmul_fused_at_ex"):
         getattr(lib, f).restype = ctypes.c_int
     lib.q4o_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -156,19 +157,19 @@ def _xfmt(xfmt: str) -> int:
     return _XFMT[xfmt]
 
 
-def unpack_qweight(qweight, K: int) -> np.ndarray:
+def unpack_qweight(qweight, K: int, bits: int = 4) -> np.ndarray:
     qw = _c(qweight, np.int32)
     N = qw.shape[1]
     q = np.empty((K, N), dtype=np.uint8)
-    _check(_load().q4o_unpack_qweight(_ptr(qw), K, N, _ptr(q)), "unpack_qweight")
+    _check(_load().q4o_unpack_qweight_ex(_ptr(qw), K, N, bits, _ptr(q)), "unpack_qweight")
     return q
 
 
-def unpack_qzeros(qzeros, N: int) -> np.ndarray:
+def unpack_qzeros(qzeros, N: int, bits: int = 4) -> np.ndarray:
     qz = _c(qzeros, np.int32)
     ng = qz.shape[0]
     z = np.empty((ng, N), dtype=np.uint8)
-    _check(_load().q4o_unpack_qzeros(_ptr(qz), ng, N, _ptr(z)), "unpack_qzeros")
+    _check(_load().q4o_unpack_qzeros_ex(_ptr(qz), ng, N, bits, _ptr(z)), "unpack_qzeros")
     return z
 
 
@@ -176,34 +177,35 @@ def _weights(qweight, qzeros, scales, g_idx):
     return _c(qweight, np.int32), _c(qzeros, np.int32), _bits16(scales), _c(g_idx, np.int32)
 
 
-def dequant32(qweight, qzeros, scales, g_idx, K: int, N: int, G: int) -> np.ndarray:
+def dequant32(qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bits: int = 4) -> np.ndarray:
     qw, qz, s, gi = _weights(qweight, qzeros, scales, g_idx)
     W = np.empty((K, N), dtype=np.float32)
-    _check(_load().q4o_dequant32(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, _ptr(W)),
+    _check(_load().q4o_dequant32_ex(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, bits, _ptr(W)),
            "dequant32")
     return W
 
 
-def dequant16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int) -> np.ndarray:
+def dequant16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bits: int = 4) -> np.ndarray:
     """binary16 bit patterns (uint16) of RNE(s * (q - z))."""
     qw, qz, s, gi = _weights(qweight, qzeros, scales, g_idx)
     dq = np.empty((K, N), dtype=np.uint16)
-    _check(_load().q4o_dequant16(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, _ptr(dq)),
-           "dequant16")
+    _check(_load().q4o_dequant16_ex(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, bits,
+                                    _ptr(dq)), "dequant16")
     return dq
 
 
-def dequant_bf16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int) -> np.ndarray:
+def dequant_bf16(qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bits: int = 4) -> np.ndarray:
     """bfloat16 bit patterns (uint16) of RNE(s * (q - z))."""
     qw, qz, s, gi = _weights(qweight, qzeros, scales, g_idx)
     dq = np.empty((K, N), dtype=np.uint16)
-    _check(_load().q4o_dequant_bf16(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, _ptr(dq)),
-           "dequant_bf16")
+    _check(_load().q4o_dequant_bf16_ex(_ptr(qw), _ptr(qz), _ptr(s), _ptr(gi), K, N, G, bits,
+                                       _ptr(dq)), "dequant_bf16")
     return dq
 
 
 def matmul(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bias=None,
-           route: str = "fused", xfmt: str = "f16") -> Tuple[np.ndarray, Optional[np.ndarray]]:
+           route: str = "fused", xfmt: str = "f16", bits: int = 4
+           ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """y = x @ W (+ bias) in float64. Returns (y, A) for the fused route, where
     A[m, n] = sum_k |x[m,k] * W[k,n]|, and (y, None) for the fallback route.
     x and bias are bit patterns in format xfmt ("f16" or "bf16")."""
@@ -218,18 +220,18 @@ def matmul(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, bias=None,
     lib = _load()
     if route == "fused":
         A = np.empty((M, N), dtype=np.float64)
-        _check(lib.q4o_matmul_fused_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
-                                        _ptr(b), M, K, N, G, _ptr(y), _ptr(A)), "matmul_fused")
+        _check(lib.q4o_matmul_fused_ex(fmt, bits, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
+                                       _ptr(b), M, K, N, G, _ptr(y), _ptr(A)), "matmul_fused")
         return y, A
     if route == "fallback":
-        _check(lib.q4o_matmul_fallback_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
-                                           _ptr(b), M, K, N, G, _ptr(y)), "matmul_fallback")
+        _check(lib.q4o_matmul_fallback_ex(fmt, bits, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s),
+                                          _ptr(gi), _ptr(b), M, K, N, G, _ptr(y)), "matmul_fallback")
         return y, None
     raise OracleError(f"unknown route {route!r}")
 
 
 def matmul_at(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, ms, ns,
-              bias=None, xfmt: str = "f16") -> Tuple[np.ndarray, np.ndarray]:
+              bias=None, xfmt: str = "f16", bits: int = 4) -> Tuple[np.ndarray, np.ndarray]:
     """Fused-route y and A at output elements (ms[i], ns[i])."""
     fmt = _xfmt(xfmt)
     xb = _bits16(x)
@@ -240,9 +242,9 @@ def matmul_at(x, qweight, qzeros, scales, g_idx, K: int, N: int, G: int, ms, ns,
     ns = _c(ns, np.int64)
     y = np.empty(ms.shape, dtype=np.float64)
     A = np.empty(ms.shape, dtype=np.float64)
-    _check(_load().q4o_matmul_fused_at_fmt(fmt, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s), _ptr(gi),
-                                           _ptr(b), M, K, N, G, ms.size, _ptr(ms), _ptr(ns),
-                                           _ptr(y), _ptr(A)),
+    _check(_load().q4o_matmul_fused_at_ex(fmt, bits, _ptr(xb), _ptr(qw), _ptr(qz), _ptr(s),
+                                          _ptr(gi), _ptr(b), M, K, N, G, ms.size, _ptr(ms),
+                                          _ptr(ns), _ptr(y), _ptr(A)),
            "matmul_fused_at")
     return y, A
 

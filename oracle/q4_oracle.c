@@ -42,6 +42,13 @@
  *    Its fp16 form dq16 is one round-to-nearest-even of that exact product.
  *  - Accumulation is in double, in increasing k; the bias (if any) is added
  *    in double after the sum.
+ *  - Bit width: 4 (eight codes a word) or 8 (four codes a word), packed the
+ *    same way (code i of a word in bits i*bits ..; qweight along K, qzeros
+ *    along N). GPTQModel wiki "Inference Backends": GPTQ kernels declare 4-
+ *    and 8-bit weights (backend catalogue), and the native 8-bit GPTQ path
+ *    keeps the same checkpoint tensors, qweight, qzeros, scales and g_idx
+ *    (section "Runtime cache lifetime"). A symmetric 8-bit layer's zero
+ *    point is 2^(8-1) = 128 (the "Missing zeros" row, as for 4-bit).
  *  - Activation format: GPTQModel wiki "Inference Backends", hardware table
  *    (ExLlama v2 row), keeps the activation dtype (FP16, BF16 or FP32) with
  *    FP16 scales and FP32 accumulation. The matmul entry points with a format
@@ -188,35 +195,49 @@ void q4o_double_to_half_array(int64_t n, const double* in, uint16_t* out)
 }
 
 /* ---------------------------------------------------------------------------
- * Unpacking and group lookup.
+ * Unpacking and group lookup. A layer has bits = 4 (eight codes a word) or
+ * 8 (four codes a word), packed the same way: code i of a word sits in bits
+ * i*bits .. i*bits + bits - 1, qweight along K, qzeros along N.
  * ------------------------------------------------------------------------- */
 
-static inline unsigned nibble(int32_t word, int i)
+typedef struct {
+    const int32_t* qweight;
+    const int32_t* qzeros;     /* NULL: symmetric, zero point 2^(bits-1) */
+    const uint16_t* scales;
+    const int32_t* g_idx;
+    int64_t N, G;
+    int bits;
+} layer_t;
+
+static inline unsigned field(int32_t word, int i, int bits)
 {
-    return ((uint32_t)word >> (4 * i)) & 0xFu;
+    return ((uint32_t)word >> (bits * i)) & ((1u << bits) - 1u);
 }
 
-/* q[k][n]: 4-bit code of input row k, output column n. */
-static inline unsigned code_q(const int32_t* qweight, int64_t N, int64_t k, int64_t n)
+/* q[k][n]: code of input row k, output column n. */
+static inline unsigned code_q(const layer_t* L, int64_t k, int64_t n)
 {
-    return nibble(qweight[(k / 8) * N + n], (int)(k % 8));
+    const int per = 32 / L->bits;
+    return field(L->qweight[(k / per) * L->N + n], (int)(k % per), L->bits);
 }
 
-/* z[g][n]: 4-bit zero point of group g, column n; 8 for a symmetric layer
+/* z[g][n]: zero point of group g, column n; 2^(bits-1) for a symmetric layer
  * stored without zeros (qzeros NULL). */
-static inline unsigned code_z(const int32_t* qzeros, int64_t N, int64_t g, int64_t n)
+static inline unsigned code_z(const layer_t* L, int64_t g, int64_t n)
 {
-    if (!qzeros) return 8u;
-    return nibble(qzeros[g * (N / 8) + n / 8], (int)(n % 8));
+    if (!L->qzeros) return 1u << (L->bits - 1);
+    const int per = 32 / L->bits;
+    return field(L->qzeros[g * (L->N / per) + n / per], (int)(n % per), L->bits);
 }
 
-static inline int64_t group_of(const int32_t* g_idx, int64_t G, int64_t k)
+static inline int64_t group_of(const layer_t* L, int64_t k)
 {
-    return g_idx ? (int64_t)g_idx[k] : k / G;
+    return L->g_idx ? (int64_t)L->g_idx[k] : k / L->G;
 }
 
-static int check_args(int64_t M, int64_t K, int64_t N, int64_t* G, const int32_t* g_idx)
+static int check_args(int64_t M, int64_t K, int64_t N, int64_t* G, const int32_t* g_idx, int bits)
 {
+    if (bits != 4 && bits != 8) return 1;
     if (M < 0 || K <= 0 || N <= 0 || K % 8 || N % 8) return 1;
     if (*G <= 0) *G = K;
     int64_t ng = (K + *G - 1) / *G;
@@ -226,76 +247,113 @@ static int check_args(int64_t M, int64_t K, int64_t N, int64_t* G, const int32_t
     return 0;
 }
 
+static layer_t make_layer(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                          const int32_t* g_idx, int64_t N, int64_t G, int bits)
+{
+    layer_t L = {qweight, qzeros, scales, g_idx, N, G, bits};
+    return L;
+}
+
 int q4o_num_groups(int64_t K, int64_t G)
 {
     if (G <= 0) G = K;
     return (int)((K + G - 1) / G);
 }
 
-int q4o_unpack_qweight(const int32_t* qweight, int64_t K, int64_t N, uint8_t* q)
+int q4o_unpack_qweight_ex(const int32_t* qweight, int64_t K, int64_t N, int bits, uint8_t* q)
 {
-    if (K <= 0 || N <= 0 || K % 8) return 1;
+    if ((bits != 4 && bits != 8) || K <= 0 || N <= 0 || K % (32 / bits)) return 1;
+    layer_t L = make_layer(qweight, NULL, NULL, NULL, N, K, bits);
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n)
-            q[k * N + n] = (uint8_t)code_q(qweight, N, k, n);
+            q[k * N + n] = (uint8_t)code_q(&L, k, n);
     return 0;
+}
+
+int q4o_unpack_qzeros_ex(const int32_t* qzeros, int64_t ng, int64_t N, int bits, uint8_t* z)
+{
+    if ((bits != 4 && bits != 8) || ng <= 0 || N <= 0 || N % (32 / bits)) return 1;
+    layer_t L = make_layer(NULL, qzeros, NULL, NULL, N, 1, bits);
+    for (int64_t g = 0; g < ng; ++g)
+        for (int64_t n = 0; n < N; ++n)
+            z[g * N + n] = (uint8_t)code_z(&L, g, n);
+    return 0;
+}
+
+int q4o_unpack_qweight(const int32_t* qweight, int64_t K, int64_t N, uint8_t* q)
+{
+    return q4o_unpack_qweight_ex(qweight, K, N, 4, q);
 }
 
 int q4o_unpack_qzeros(const int32_t* qzeros, int64_t ng, int64_t N, uint8_t* z)
 {
-    if (ng <= 0 || N <= 0 || N % 8) return 1;
-    for (int64_t g = 0; g < ng; ++g)
-        for (int64_t n = 0; n < N; ++n)
-            z[g * N + n] = (uint8_t)code_z(qzeros, N, g, n);
+    return q4o_unpack_qzeros_ex(qzeros, ng, N, 4, z);
+}
+
+/* W[k][n] = s * (q - z) in fp32 (exact, see the header; with 8-bit codes
+ * |q - z| <= 255, an 11-bit significand times an 8-bit integer). */
+static inline float dequant_one(const layer_t* L, int64_t k, int64_t n)
+{
+    int64_t g = group_of(L, k);
+    float s = (float)q4o_half_to_double(L->scales[g * L->N + n]);
+    float d = (float)((int)code_q(L, k, n) - (int)code_z(L, g, n));
+    return s * d;
+}
+
+/* out: 0 fp32 W, 1 binary16 RNE(W), 2 bfloat16 RNE(W). */
+static int dequant_any(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                       const int32_t* g_idx, int64_t K, int64_t N, int64_t G, int bits, int out,
+                       void* dst)
+{
+    int rc = check_args(0, K, N, &G, g_idx, bits);
+    if (rc) return rc;
+    layer_t L = make_layer(qweight, qzeros, scales, g_idx, N, G, bits);
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            float w = dequant_one(&L, k, n);
+            if (out == 0) ((float*)dst)[k * N + n] = w;
+            else if (out == 1) ((uint16_t*)dst)[k * N + n] = q4o_double_to_half_rne((double)w);
+            else ((uint16_t*)dst)[k * N + n] = q4o_double_to_bf16_rne((double)w);
+        }
     return 0;
 }
 
-/* W[k][n] = s * (q - z) in fp32 (exact, see the header). */
-static inline float dequant_one(const int32_t* qweight, const int32_t* qzeros,
-                                const uint16_t* scales, const int32_t* g_idx,
-                                int64_t N, int64_t G, int64_t k, int64_t n)
+int q4o_dequant32_ex(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                     const int32_t* g_idx, int64_t K, int64_t N, int64_t G, int bits, float* W)
 {
-    int64_t g = group_of(g_idx, G, k);
-    float s = (float)q4o_half_to_double(scales[g * N + n]);
-    float d = (float)((int)code_q(qweight, N, k, n) - (int)code_z(qzeros, N, g, n));
-    return s * d;
+    return dequant_any(qweight, qzeros, scales, g_idx, K, N, G, bits, 0, W);
+}
+
+/* dq16[k][n] = RNE_fp16(s * (q - z)), binary16 bit patterns. */
+int q4o_dequant16_ex(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                     const int32_t* g_idx, int64_t K, int64_t N, int64_t G, int bits, uint16_t* dq)
+{
+    return dequant_any(qweight, qzeros, scales, g_idx, K, N, G, bits, 1, dq);
+}
+
+/* dqb[k][n] = RNE_bf16(s * (q - z)), bfloat16 bit patterns. */
+int q4o_dequant_bf16_ex(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                        const int32_t* g_idx, int64_t K, int64_t N, int64_t G, int bits, uint16_t* dq)
+{
+    return dequant_any(qweight, qzeros, scales, g_idx, K, N, G, bits, 2, dq);
 }
 
 int q4o_dequant32(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                   const int32_t* g_idx, int64_t K, int64_t N, int64_t G, float* W)
 {
-    int rc = check_args(0, K, N, &G, g_idx);
-    if (rc) return rc;
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n)
-            W[k * N + n] = dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
-    return 0;
+    return q4o_dequant32_ex(qweight, qzeros, scales, g_idx, K, N, G, 4, W);
 }
 
-/* dq16[k][n] = RNE_fp16(s * (q - z)), binary16 bit patterns. */
 int q4o_dequant16(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                   const int32_t* g_idx, int64_t K, int64_t N, int64_t G, uint16_t* dq)
 {
-    int rc = check_args(0, K, N, &G, g_idx);
-    if (rc) return rc;
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n)
-            dq[k * N + n] = q4o_double_to_half_rne(
-                (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n));
-    return 0;
+    return q4o_dequant16_ex(qweight, qzeros, scales, g_idx, K, N, G, 4, dq);
 }
 
-/* dqb[k][n] = RNE_bf16(s * (q - z)), bfloat16 bit patterns. */
 int q4o_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                      const int32_t* g_idx, int64_t K, int64_t N, int64_t G, uint16_t* dq)
 {
-    int rc = check_args(0, K, N, &G, g_idx);
-    if (rc) return rc;
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n)
-            dq[k * N + n] = q4o_double_to_bf16_rne(
-                (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n));
-    return 0;
+    return q4o_dequant_bf16_ex(qweight, qzeros, scales, g_idx, K, N, G, 4, dq);
 }
 
 /* ---------------------------------------------------------------------------
@@ -305,20 +363,22 @@ int q4o_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const uint16
  * ------------------------------------------------------------------------- */
 
 /* Fused route: dequantize each weight inside the k loop, never store W. */
-int q4o_matmul_fused_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                         const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                         int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
+int q4o_matmul_fused_ex(int xfmt, int bits, const uint16_t* x, const int32_t* qweight,
+                        const int32_t* qzeros, const uint16_t* scales, const int32_t* g_idx,
+                        const uint16_t* bias, int64_t M, int64_t K, int64_t N, int64_t G,
+                        double* y, double* A)
 {
     to_double_fn to_d = format_of(xfmt);
     if (!to_d) return 1;
-    int rc = check_args(M, K, N, &G, g_idx);
+    int rc = check_args(M, K, N, &G, g_idx, bits);
     if (rc) return rc;
+    layer_t L = make_layer(qweight, qzeros, scales, g_idx, N, G, bits);
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, aabs = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
+                double w = (double)dequant_one(&L, k, n);
                 double p = to_d(x[m * K + k]) * w;
                 acc += p;
                 aabs += fabs(p);
@@ -330,25 +390,19 @@ int q4o_matmul_fused_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, co
     return 0;
 }
 
-int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                     const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                     int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
-{
-    return q4o_matmul_fused_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y, A);
-}
-
 /* Fallback route: materialize the dequantized W[K][N], then a plain matmul. */
-int q4o_matmul_fallback_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                            const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                            int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+int q4o_matmul_fallback_ex(int xfmt, int bits, const uint16_t* x, const int32_t* qweight,
+                           const int32_t* qzeros, const uint16_t* scales, const int32_t* g_idx,
+                           const uint16_t* bias, int64_t M, int64_t K, int64_t N, int64_t G,
+                           double* y)
 {
     to_double_fn to_d = format_of(xfmt);
     if (!to_d) return 1;
-    int rc = check_args(M, K, N, &G, g_idx);
+    int rc = check_args(M, K, N, &G, g_idx, bits);
     if (rc) return rc;
     float* W = (float*)malloc((size_t)K * (size_t)N * sizeof(float));
     if (!W) return 1;
-    q4o_dequant32(qweight, qzeros, scales, g_idx, K, N, G, W);
+    q4o_dequant32_ex(qweight, qzeros, scales, g_idx, K, N, G, bits, W);
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
@@ -362,33 +416,27 @@ int q4o_matmul_fallback_fmt(int xfmt, const uint16_t* x, const int32_t* qweight,
     return 0;
 }
 
-int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                        int64_t M, int64_t K, int64_t N, int64_t G, double* y)
-{
-    return q4o_matmul_fallback_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y);
-}
-
 /* Fused route at selected output elements (m[i], n[i]), i < count. Used for
  * full-size layers where the whole product would take the CPU too long. */
-int q4o_matmul_fused_at_fmt(int xfmt, const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                            const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
-                            int64_t M, int64_t K, int64_t N, int64_t G,
-                            int64_t count, const int64_t* ms, const int64_t* ns,
-                            double* y, double* A)
+int q4o_matmul_fused_at_ex(int xfmt, int bits, const uint16_t* x, const int32_t* qweight,
+                           const int32_t* qzeros, const uint16_t* scales, const int32_t* g_idx,
+                           const uint16_t* bias, int64_t M, int64_t K, int64_t N, int64_t G,
+                           int64_t count, const int64_t* ms, const int64_t* ns,
+                           double* y, double* A)
 {
     to_double_fn to_d = format_of(xfmt);
     if (!to_d) return 1;
-    int rc = check_args(M, K, N, &G, g_idx);
+    int rc = check_args(M, K, N, &G, g_idx, bits);
     if (rc) return rc;
     for (int64_t i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return 1;
+    layer_t L = make_layer(qweight, qzeros, scales, g_idx, N, G, bits);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i) {
         int64_t m = ms[i], n = ns[i];
         double acc = 0.0, aabs = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double w = (double)dequant_one(qweight, qzeros, scales, g_idx, N, G, k, n);
+            double w = (double)dequant_one(&L, k, n);
             double p = to_d(x[m * K + k]) * w;
             acc += p;
             aabs += fabs(p);
@@ -400,14 +448,29 @@ int q4o_matmul_fused_at_fmt(int xfmt, const uint16_t* x, const int32_t* qweight,
     return 0;
 }
 
+/* binary16 activations, 4-bit weights (the original entry points). */
+int q4o_matmul_fused(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                     const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                     int64_t M, int64_t K, int64_t N, int64_t G, double* y, double* A)
+{
+    return q4o_matmul_fused_ex(0, 4, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y, A);
+}
+
+int q4o_matmul_fallback(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                        const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
+                        int64_t M, int64_t K, int64_t N, int64_t G, double* y)
+{
+    return q4o_matmul_fallback_ex(0, 4, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G, y);
+}
+
 int q4o_matmul_fused_at(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                         const uint16_t* scales, const int32_t* g_idx, const uint16_t* bias,
                         int64_t M, int64_t K, int64_t N, int64_t G,
                         int64_t count, const int64_t* ms, const int64_t* ns,
                         double* y, double* A)
 {
-    return q4o_matmul_fused_at_fmt(0, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G,
-                                   count, ms, ns, y, A);
+    return q4o_matmul_fused_at_ex(0, 4, x, qweight, qzeros, scales, g_idx, bias, M, K, N, G,
+                                  count, ms, ns, y, A);
 }
 
 int q4o_num_threads(void)

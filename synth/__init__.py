@@ -22,7 +22,9 @@ contract table of "Implementation: Predibase Lorax GPTQ Exllama V1"):
 
 Uniform 4-bit codes are drawn as uniform 32-bit words: the eight nibbles of
 a uniformly random 32-bit word are independent and uniform on {0..15}, which
-is exactly "q ~ U{0..15}, then packed" without any packing code here.
+is exactly "q ~ U{0..15}, then packed" without any packing code here. With
+``bits=8`` the words hold four 8-bit codes (qweight ``[K/4, N]``, qzeros
+``[ceil(K/G), N/4]``), again uniform.
 
 Draw order per layer (fixed so that a seed names one tensor set): qweight
 words, qzeros words, scales, x, bias (if asked), act-order permutation (if
@@ -66,6 +68,7 @@ class Layer:
     bias: Optional[np.ndarray]    # float16 [N] or None (xfmt "bf16": uint16 bits)
     seed: int
     xfmt: str = "f16"
+    bits: int = 4                 # 4 or 8 (qweight [K*bits/32, N], qzeros [ng, N*bits/32])
 
     @property
     def M(self) -> int:
@@ -100,18 +103,21 @@ def to_bf16_bits(values) -> np.ndarray:
 
 def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = False,
                bias: bool = False, scale_lo: float = 0.005, scale_hi: float = 0.02,
-               xfmt: str = "f16") -> Layer:
+               xfmt: str = "f16", bits: int = 4) -> Layer:
     """Draw one layer with the value distributions described in the module doc."""
     if xfmt not in ("f16", "bf16"):
         raise ValueError(f"unknown activation format {xfmt!r}")
+    if bits not in (4, 8):
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
     if K % 8 or N % 8:
         raise ValueError("K and N must be multiples of 8")
     if G <= 0:
         G = K
     ng = -(-K // G)
     rng = np.random.Generator(np.random.PCG64(seed))
-    qweight = _words(rng, (K // 8, N))
-    qzeros = _words(rng, (ng, N // 8))
+    per = 32 // bits
+    qweight = _words(rng, (K // per, N))
+    qzeros = _words(rng, (ng, N // per))
     scales = rng.uniform(scale_lo, scale_hi, size=(ng, N)).astype(np.float16)
     if xfmt == "f16":
         x = rng.standard_normal((M, K)).astype(np.float16)
@@ -126,7 +132,7 @@ def make_layer(K: int, N: int, G: int, M: int, seed: int, *, act_order: bool = F
         pos[pi] = np.arange(K)
         g_idx = (pos // G).astype(np.int32)
     return Layer(K=K, N=N, G=G, qweight=qweight, qzeros=qzeros, scales=scales,
-                 g_idx=g_idx, x=x, bias=b, seed=seed, xfmt=xfmt)
+                 g_idx=g_idx, x=x, bias=b, seed=seed, xfmt=xfmt, bits=bits)
 
 
 def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
@@ -139,8 +145,8 @@ def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
     for p in parts[1:]:
         if p.K != p0.K or p.G != p0.G:
             raise ValueError("parts must share K and G")
-        if p.xfmt != p0.xfmt:
-            raise ValueError("parts must share the activation format")
+        if p.xfmt != p0.xfmt or p.bits != p0.bits:
+            raise ValueError("parts must share the activation format and bit width")
         if (p.g_idx is None) != (p0.g_idx is None) or (
                 p.g_idx is not None and not np.array_equal(p.g_idx, p0.g_idx)):
             raise ValueError("parts must share g_idx")
@@ -154,7 +160,7 @@ def concat_layers(parts, x: Optional[np.ndarray] = None) -> Layer:
                  qzeros=np.ascontiguousarray(np.concatenate([p.qzeros for p in parts], axis=1)),
                  scales=np.ascontiguousarray(np.concatenate([p.scales for p in parts], axis=1)),
                  g_idx=p0.g_idx, x=p0.x if x is None else x, bias=bias, seed=p0.seed,
-                 xfmt=p0.xfmt)
+                 xfmt=p0.xfmt, bits=p0.bits)
 
 
 def make_x(M: int, K: int, seed: int) -> np.ndarray:

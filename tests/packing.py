@@ -1,5 +1,5 @@
-"""Test-side packer for 4-bit codes (pure Python/numpy, written independently
-of the oracle and of the GPU library).
+"""Test-side packer for 4-bit and 8-bit codes (pure Python/numpy, written
+independently of the oracle and of the GPU library).
 
 It builds GPTQ words from known codes so that tests can start from the codes
 themselves rather than from an unpacking routine. Layout: qweight word (r, n)
@@ -13,25 +13,30 @@ from __future__ import annotations
 import numpy as np
 
 
-def pack_rows(codes: np.ndarray) -> np.ndarray:
-    """codes uint [K, N] (values 0..15) -> int32 [K/8, N], packed along K."""
+def pack_rows(codes: np.ndarray, bits: int = 4) -> np.ndarray:
+    """codes uint [K, N] (values below 2^bits) -> int32 [K*bits/32, N],
+    packed along K: word r holds rows r*per .. r*per + per - 1, per = 32/bits,
+    the first in the lowest bits."""
+    per = 32 // bits
     codes = np.asarray(codes, dtype=np.uint32)
     K, N = codes.shape
-    assert K % 8 == 0
-    out = np.zeros((K // 8, N), dtype=np.uint32)
-    for i in range(8):
-        out |= (codes[i::8, :] & 0xF) << np.uint32(4 * i)
+    assert K % per == 0
+    out = np.zeros((K // per, N), dtype=np.uint32)
+    for i in range(per):
+        out |= (codes[i::per, :] & np.uint32((1 << bits) - 1)) << np.uint32(bits * i)
     return out.view(np.int32)
 
 
-def pack_cols(codes: np.ndarray) -> np.ndarray:
-    """codes uint [R, N] (values 0..15) -> int32 [R, N/8], packed along N."""
+def pack_cols(codes: np.ndarray, bits: int = 4) -> np.ndarray:
+    """codes uint [R, N] (values below 2^bits) -> int32 [R, N*bits/32], packed
+    along N in the same order."""
+    per = 32 // bits
     codes = np.asarray(codes, dtype=np.uint32)
     R, N = codes.shape
-    assert N % 8 == 0
-    out = np.zeros((R, N // 8), dtype=np.uint32)
-    for j in range(8):
-        out |= (codes[:, j::8] & 0xF) << np.uint32(4 * j)
+    assert N % per == 0
+    out = np.zeros((R, N // per), dtype=np.uint32)
+    for j in range(per):
+        out |= (codes[:, j::per] & np.uint32((1 << bits) - 1)) << np.uint32(bits * j)
     return out.view(np.int32)
 
 

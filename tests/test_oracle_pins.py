@@ -541,3 +541,96 @@ def test_bf16_activations_beyond_binary16_range(oracle_mod):
     assert np.array_equal(yb[2], 1 + np.arange(N) * 2.0 ** -7)
     with pytest.raises(ValueError):
         oracle_mod.matmul(x, L.qweight, L.qzeros, L.scales, None, K, N, G, xfmt="f32")
+
+
+# ---------------------------------------------------------------- 8-bit -----
+# GPTQModel wiki "Inference Backends": GPTQ kernels declare 4- and 8-bit
+# weights (backend catalogue); the native 8-bit path keeps the checkpoint's
+# qweight, qzeros, scales and g_idx ("Runtime cache lifetime"). Reading: four
+# 8-bit codes a word, packed as the 4-bit ones (code i in bits 8i..8i+7,
+# qweight along K, qzeros along N); symmetric zero point 2^(8-1) = 128.
+
+def test_hand_words_8bit(oracle_mod):
+    qw = np.array([[0x04030201, np.uint32(0xFFFEFDFC).view(np.int32)]], dtype=np.int64).astype(np.int32)
+    q = oracle_mod.unpack_qweight(qw, 4, bits=8)
+    assert q[:, 0].tolist() == [1, 2, 3, 4] and q[:, 1].tolist() == [252, 253, 254, 255]
+    qz = np.array([[0x04030201, 0x08070605]], dtype=np.int32)
+    assert oracle_mod.unpack_qzeros(qz, 8, bits=8)[0].tolist() == [1, 2, 3, 4, 5, 6, 7, 8]
+
+
+@pytest.mark.parametrize("K,N", [(8, 8), (64, 24), (512, 136)])
+def test_pack_unpack_round_trip_8bit(oracle_mod, K, N):
+    rng = np.random.default_rng(K * 7 + N)
+    q = rng.integers(0, 256, size=(K, N), dtype=np.uint8)
+    assert np.array_equal(oracle_mod.unpack_qweight(pack_rows(q, 8), K, bits=8), q)
+    z = rng.integers(0, 256, size=(K // 8, N), dtype=np.uint8)
+    assert np.array_equal(oracle_mod.unpack_qzeros(pack_cols(z, 8), N, bits=8), z)
+
+
+def test_dequant_8bit_brute_force_fractions(oracle_mod):
+    rng = np.random.default_rng(17)
+    K, N, G = 64, 16, 32
+    q = rng.integers(0, 256, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 256, size=(K // G, N), dtype=np.uint8)
+    s = rng.uniform(0.0005, 0.002, size=(K // G, N)).astype(np.float16)
+    s[0, 0] = np.float16(-0.00107)
+    s[1, 3] = np.float16(6.0e-6)            # subnormal
+    W = oracle_mod.dequant32(pack_rows(q, 8), pack_cols(z, 8), s, None, K, N, G, bits=8)
+    for k in range(K):
+        for n in range(N):
+            g = k // G
+            exact = Fraction(float(s[g, n])) * (int(q[k, n]) - int(z[g, n]))
+            assert Fraction(float(W[k, n])) == exact, (k, n)
+    dq = oracle_mod.dequant16(pack_rows(q, 8), pack_cols(z, 8), s, None, K, N, G, bits=8)
+    ref = W.astype(np.float16).view(np.uint16)
+    assert np.array_equal(dq, ref)
+    db = oracle_mod.dequant_bf16(pack_rows(q, 8), pack_cols(z, 8), s, None, K, N, G, bits=8)
+    assert np.array_equal(db, _torch_bf16_bits(W))
+
+
+def test_matmul_8bit_exact_brute_force(oracle_mod):
+    rng = np.random.default_rng(18)
+    M, K, N, G = 2, 64, 16, 32
+    q = rng.integers(0, 256, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 256, size=(K // G, N), dtype=np.uint8)
+    s = rng.uniform(0.0005, 0.002, size=(K // G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    b = rng.normal(0, 0.1, size=N).astype(np.float16)
+    y, _ = oracle_mod.matmul(x, pack_rows(q, 8), pack_cols(z, 8), s, None, K, N, G, bias=b, bits=8)
+    ex = _exact_product(x, q, z, s, G, bias=b)
+    for m in range(M):
+        for n in range(N):
+            # every product is exact in double, the 64-term sum may round
+            # (up to ~55 significant bits): 64 * 2^-53 relative at most, far
+            # below any wrong code, zero or index (at least min|s x| ~ 1e-7)
+            assert abs(Fraction(y[m, n]) - ex[m][n]) <= Fraction(1, 1 << 40) * (1 + abs(ex[m][n])), (m, n)
+
+
+def test_8bit_equals_4bit_on_small_codes(oracle_mod):
+    """Codes and zeros below 16 packed as 8-bit words give exactly the 4-bit
+    layer's results (two different unpackers, the same layer)."""
+    rng = np.random.default_rng(19)
+    M, K, N, G = 3, 256, 40, 64
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    s = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    gi = synth.make_layer(K, N, G, 1, seed=3, act_order=True).g_idx
+    y4, A4 = oracle_mod.matmul(x, pack_rows(q), pack_cols(z), s, gi, K, N, G)
+    y8, A8 = oracle_mod.matmul(x, pack_rows(q, 8), pack_cols(z, 8), s, gi, K, N, G, bits=8)
+    assert np.array_equal(y4, y8) and np.array_equal(A4, A8)
+    y8f, _ = oracle_mod.matmul(x, pack_rows(q, 8), pack_cols(z, 8), s, gi, K, N, G, bits=8,
+                               route="fallback")
+    assert np.array_equal(y8f, y8)
+    ms, ns = np.array([0, 2, 1]), np.array([0, 39, 7])
+    ya, _ = oracle_mod.matmul_at(x, pack_rows(q, 8), pack_cols(z, 8), s, gi, K, N, G, ms, ns, bits=8)
+    assert np.array_equal(ya, y8[ms, ns])
+
+
+def test_8bit_missing_zeros_mean_128(oracle_mod):
+    K, N, G = 16, 8, 16
+    q = (np.arange(K * N, dtype=np.int64).reshape(K, N) * 37) % 256
+    W = oracle_mod.dequant32(pack_rows(q, 8), None, np.ones((1, N), np.float16), None, K, N, G, bits=8)
+    assert np.array_equal(W, (q - 128).astype(np.float32))
+    with pytest.raises(ValueError):
+        oracle_mod.dequant32(pack_rows(q, 8), None, np.ones((1, N), np.float16), None, K, N, G, bits=6)
