@@ -36,7 +36,8 @@ EXPORTED_SYMBOLS = (
     "q4_make", "q4_make_cat", "q4_matmul", "q4_matmul_bias", "q4_matmul_ex", "q4_free", "q4_last_status",
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
-    "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16",
+    "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16", "q4_make_bits", "q4_make_cat_bits",
+    "q4_handle_bits", "q4_check_shape_bits",
 )
 
 _lib = None
@@ -66,6 +67,14 @@ def load_library():
     lib.q4_make.restype = P
     lib.q4_make_cat.argtypes = [I, P, P, P, P, I, P, I]
     lib.q4_make_cat.restype = P
+    lib.q4_make_bits.argtypes = [P, P, P, P, I, I, I, I]
+    lib.q4_make_bits.restype = P
+    lib.q4_make_cat_bits.argtypes = [I, P, P, P, P, I, P, I, I]
+    lib.q4_make_cat_bits.restype = P
+    lib.q4_handle_bits.argtypes = [P]
+    lib.q4_handle_bits.restype = I
+    lib.q4_check_shape_bits.argtypes = [I, I, I, I]
+    lib.q4_check_shape_bits.restype = I
     lib.q4_matmul.argtypes = [P, P, P, I, P]
     lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
     lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, I, P]
@@ -120,9 +129,12 @@ def _check(status: int, what: str):
 
 # ---------------------------------------------------------------- host only ---
 
-def check_shape(K: int, N: int, groupsize: int) -> None:
-    """Raise if (K, N, groupsize) is not accepted by q4_make."""
-    _check(load_library().q4_check_shape(K, N, groupsize), "q4_check_shape")
+def check_shape(K: int, N: int, groupsize: int, bits: int = 4) -> None:
+    """Raise if (K, N, groupsize) is not accepted by q4_make (q4_make_bits)."""
+    if bits == 4:
+        _check(load_library().q4_check_shape(K, N, groupsize), "q4_check_shape")
+    else:
+        _check(load_library().q4_check_shape_bits(K, N, groupsize, bits), "q4_check_shape_bits")
 
 
 def plan_actorder(g_idx, K: int, groupsize: int):
@@ -196,42 +208,45 @@ class Q4Matrix:
     not reach it.
     """
 
-    def __init__(self, qweight, qzeros, scales, g_idx=None, groupsize: int = 128):
-        self._build([(qweight, qzeros, scales)], g_idx, groupsize)
+    def __init__(self, qweight, qzeros, scales, g_idx=None, groupsize: int = 128, bits: int = 4):
+        self._build([(qweight, qzeros, scales)], g_idx, groupsize, bits)
 
     @classmethod
-    def concat(cls, parts, g_idx=None, groupsize: int = 128):
+    def concat(cls, parts, g_idx=None, groupsize: int = 128, bits: int = 4):
         """One matrix over the column concatenation of layers that share the
         input (QKV or gate/up fusion; q4_make_cat). parts: sequence of
         (qweight, qzeros, scales) with equal K; g_idx shared by all parts.
         Output columns follow part order; split() cuts an output into parts."""
         self = cls.__new__(cls)
-        self._build(list(parts), g_idx, groupsize)
+        self._build(list(parts), g_idx, groupsize, bits)
         return self
 
-    def _build(self, parts, g_idx, groupsize):
+    def _build(self, parts, g_idx, groupsize, bits=4):
         torch = _torch()
         lib = load_library()
         if not parts:
             raise ValueError("at least one part is needed")
+        if bits not in (4, 8):
+            raise NotImplementedError(f"bits must be 4 or 8, got {bits}")
+        per = 32 // bits                # codes per int32 word
         K = None
         ns = []
         for i, (qweight, qzeros, scales) in enumerate(parts):
             _dev_tensor(qweight, torch.int32, f"qweight[{i}]")
             if qweight.dim() != 2:
-                raise ValueError("qweight must be 2-D [K/8, N]")
-            k_i, n_i = int(qweight.shape[0]) * 8, int(qweight.shape[1])
+                raise ValueError(f"qweight must be 2-D [K/{per}, N]")
+            k_i, n_i = int(qweight.shape[0]) * per, int(qweight.shape[1])
             if K is not None and k_i != K:
                 raise ValueError(f"part {i} has K={k_i}, part 0 has K={K}")
             K = k_i
-            check_shape(K, n_i, groupsize)
+            check_shape(K, n_i, groupsize, bits)
             G = K if groupsize == -1 else groupsize
             ng = -(-K // G) if G > 0 else 0
-            if qzeros is not None:      # None: symmetric, every zero point is 8
-                _dev_tensor(qzeros, torch.int32, f"qzeros[{i}]", (ng, n_i // 8))
+            if qzeros is not None:      # None: symmetric, every zero point is 2^(bits-1)
+                _dev_tensor(qzeros, torch.int32, f"qzeros[{i}]", (ng, n_i // per))
             _dev_tensor(scales, torch.float16, f"scales[{i}]", (ng, n_i))
             ns.append(n_i)
-        check_shape(K, sum(ns), groupsize)
+        check_shape(K, sum(ns), groupsize, bits)
         if g_idx is not None:
             _dev_tensor(g_idx, torch.int32, "g_idx", (K,))
         dev = parts[0][0].device
@@ -245,16 +260,16 @@ class Q4Matrix:
         with torch.cuda.device(dev):
             if len(parts) == 1:
                 qw, qz, sc = parts[0]
-                h = lib.q4_make(qw.data_ptr(), qz.data_ptr() if qz is not None else None, sc.data_ptr(),
-                                gp, K, ns[0], groupsize)
-                what = "q4_make"
+                h = lib.q4_make_bits(qw.data_ptr(), qz.data_ptr() if qz is not None else None,
+                                     sc.data_ptr(), gp, K, ns[0], groupsize, bits)
+                what = "q4_make_bits"
             else:
                 arr = lambda vals: (ctypes.c_void_p * len(vals))(*vals)
-                h = lib.q4_make_cat(len(parts), arr([p[0].data_ptr() for p in parts]),
-                                    arr([p[1].data_ptr() if p[1] is not None else None for p in parts]),
-                                    arr([p[2].data_ptr() for p in parts]), gp, K,
-                                    (ctypes.c_int * len(ns))(*ns), groupsize)
-                what = "q4_make_cat"
+                h = lib.q4_make_cat_bits(len(parts), arr([p[0].data_ptr() for p in parts]),
+                                         arr([p[1].data_ptr() if p[1] is not None else None for p in parts]),
+                                         arr([p[2].data_ptr() for p in parts]), gp, K,
+                                         (ctypes.c_int * len(ns))(*ns), groupsize, bits)
+                what = "q4_make_cat_bits"
         if not h:
             _raise(lib.q4_last_status(), what)
         self._h = ctypes.c_void_p(h)
@@ -264,6 +279,7 @@ class Q4Matrix:
         lib.q4_handle_info(self._h, None, None, ctypes.byref(gs), ctypes.byref(act))
         self.groupsize = int(gs.value)
         self.act_order = bool(act.value)
+        self.bits = int(lib.q4_handle_bits(self._h))
 
     def split(self, out):
         """Views of an output [M, N] as one [M, N_i] per part (column order)."""

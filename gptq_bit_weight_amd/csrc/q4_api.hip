@@ -18,7 +18,7 @@ hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                               int M, bool bf16, hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
-                         int n_total, int col_off, hipStream_t stream);
+                         int n_total, int col_off, int bits, hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
 hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream);
@@ -71,8 +71,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // result, in part order). q4_make is the one-part case.
 q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
                     const uint16_t* const* scales, const int32_t* g_idx, int K, const int* Np,
-                    int groupsize, const char* who, q4_matrix** out)
+                    int groupsize, int bits, const char* who, q4_matrix** out)
 {
+    if (bits != 4 && bits != 8) return fail(Q4_ERR_UNSUPPORTED, "%s: bits=%d is not 4 or 8", who, bits);
     if (parts < 1 || parts > kMaxParts)
         return fail(Q4_ERR_INVALID_ARG, "%s: parts=%d outside [1, %d]", who, parts, kMaxParts);
     if (!qweight || !scales || !Np)
@@ -91,7 +92,7 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     if (ntot > INT_MAX) return fail(Q4_ERR_UNSUPPORTED, "%s: %lld columns in total", who, ntot);
     const int N = (int)ntot;
     int G = 0;
-    q4_status st = check_shape(K, N, groupsize, &G);
+    q4_status st = check_shape(K, N, groupsize, &G, bits);
     if (st != Q4_OK) return st;
     int dev = -1, num_cu = 0;
     st = check_device(&dev, &num_cu);
@@ -119,6 +120,7 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     h->G = G;
     h->ng = ng;
     h->act_order = act;
+    h->bits = bits;
     h->device = dev;
     h->num_cu = num_cu;
     auto bail = [&](q4_status s) {
@@ -126,10 +128,11 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
         return s;
     };
     hipError_t e;
-    const size_t words = packed_words(K, N);
+    const size_t words = packed_words(K, N, bits);
     if ((e = hipMalloc(&h->qweight, words * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qweight"));
     if ((e = hipMalloc(&h->scales, (size_t)ng * N * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
-    if ((e = hipMalloc(&h->qzeros, (size_t)ng * (N / 8) * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
+    const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
+    if ((e = hipMalloc(&h->qzeros, (size_t)ng * zrow)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
     if ((e = hipMalloc(&h->partials, (size_t)kMaxSplits * 16 * N * 4)) != hipSuccess)
         return bail(hip_fail(e, "q4_make: workspace"));
     const int col_tiles = (N + 15) / 16;
@@ -161,18 +164,21 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
                              (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: scales"));
         // A part without zeros is symmetric: every zero point is
-        // 2^(bits-1) = 8 (GPTQModel wiki "Inference Backends", section
+        // 2^(bits-1) (GPTQModel wiki "Inference Backends", section
         // "Packing, conversion, and runtime initialization", row "Missing
-        // zeros"), i.e. zero words 0x88888888.
+        // zeros"): 8, zero words 0x88888888, or 128, zero bytes 0x80. The
+        // part's zeros occupy bytes off * bits / 8 .. of each row (off and
+        // N[i] are multiples of 8, so no word is shared between parts).
         const int32_t* qz = qzeros ? qzeros[i] : nullptr;
+        char* zdst = reinterpret_cast<char*>(h->qzeros) + (size_t)off * bits / 8;
+        const size_t zpart = (size_t)Np[i] * bits / 8;
         if (qz)
-            e = hipMemcpy2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, qz, (size_t)(Np[i] / 8) * 4,
-                            (size_t)(Np[i] / 8) * 4, (size_t)ng, hipMemcpyDeviceToDevice);
+            e = hipMemcpy2D(zdst, zrow, qz, zpart, zpart, (size_t)ng, hipMemcpyDeviceToDevice);
         else
-            e = hipMemset2D(h->qzeros + off / 8, (size_t)(N / 8) * 4, 0x88, (size_t)(Np[i] / 8) * 4, (size_t)ng);
+            e = hipMemset2D(zdst, zrow, bits == 8 ? 0x80 : 0x88, zpart, (size_t)ng);
         if (e != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
         if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight[i]), h->perm, h->qweight, K, Np[i], N,
-                               off, 0)) != hipSuccess)
+                               off, bits, 0)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: repack launch"));
         off += Np[i];
     }
@@ -240,6 +246,8 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
         if (variant != 0 && variant != 1 && variant != 2 && variant != 4)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: skinny-kernel tiles %d not 0, 1, 2 or 4", variant);
+        if (h->bits == 8 && variant == 4)
+            return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights take at most 2 column tiles");
     } else {
         if (splits != 0)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the GEMM takes no K splits (got %d)", splits);
@@ -248,12 +256,15 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (bf16 && variant != 0 && variant != 3)
             return fail(Q4_ERR_UNSUPPORTED,
                         "q4_matmul: bfloat16 activations run on GEMM variant 3 only (got %d)", variant);
+        if (h->bits == 8 && variant != 0 && variant != 3)
+            return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights run on GEMM variant 3 only (got %d)",
+                        variant);
     }
 
     int ct = 0, s = 0;
     bool gather = false;
     if (kind == Q4_PATH_GEMV) {
-        plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
+        plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s, h->bits);
         if (variant) ct = variant;
         if (splits) s = splits;
         // act-order: without K splits, the skinny kernel stages x[:, perm]
@@ -296,7 +307,17 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
                    const int32_t* g_idx, int K, int N, int groupsize)
 {
     q4_matrix* h = nullptr;
-    return q4::make_impl(1, &qweight, &qzeros, &scales, g_idx, K, &N, groupsize, "q4_make", &h) == Q4_OK
+    return q4::make_impl(1, &qweight, &qzeros, &scales, g_idx, K, &N, groupsize, 4, "q4_make", &h) == Q4_OK
+               ? h
+               : nullptr;
+}
+
+q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                        const int32_t* g_idx, int K, int N, int groupsize, int bits)
+{
+    q4_matrix* h = nullptr;
+    return q4::make_impl(1, &qweight, &qzeros, &scales, g_idx, K, &N, groupsize, bits, "q4_make_bits",
+                         &h) == Q4_OK
                ? h
                : nullptr;
 }
@@ -306,7 +327,18 @@ q4_matrix* q4_make_cat(int parts, const int32_t* const* qweight, const int32_t* 
                        int groupsize)
 {
     q4_matrix* h = nullptr;
-    return q4::make_impl(parts, qweight, qzeros, scales, g_idx, K, N, groupsize, "q4_make_cat", &h) == Q4_OK
+    return q4::make_impl(parts, qweight, qzeros, scales, g_idx, K, N, groupsize, 4, "q4_make_cat", &h) == Q4_OK
+               ? h
+               : nullptr;
+}
+
+q4_matrix* q4_make_cat_bits(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
+                            const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
+                            int groupsize, int bits)
+{
+    q4_matrix* h = nullptr;
+    return q4::make_impl(parts, qweight, qzeros, scales, g_idx, K, N, groupsize, bits, "q4_make_cat_bits",
+                         &h) == Q4_OK
                ? h
                : nullptr;
 }
@@ -357,9 +389,11 @@ int q4_gemv_gather(const q4_matrix* h, int M, int splits)
     if (!h || M < 1 || M > Q4_GEMV_MAX_M || splits < 0 || splits > q4::kMaxSplits) return -1;
     if (!h->act_order || !h->inv16) return 0;
     int ct = 0, s = 0;
-    q4::plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s);
+    q4::plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s, h->bits);
     return q4::gemv_gathers_x(M, h->K, splits ? splits : s) ? 1 : 0;
 }
+
+int q4_handle_bits(const q4_matrix* h) { return h ? h->bits : -1; }
 
 int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order)
 {

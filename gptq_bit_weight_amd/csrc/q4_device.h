@@ -107,6 +107,36 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, zero_t z, h2 s2)
     return d * s8;
 }
 
+// ---- 8-bit codes -------------------------------------------------------------
+// A k-step's eight 8-bit codes are two words, one byte each in k order. One
+// v_perm_b32 per pair puts codes k, k + 1 into the low bytes of two fp16
+// halves whose high bytes are 0x64: 1024 + q exactly (q <= 255 fits the
+// 10-bit fraction). (1024 + q) - (1024 + z) is exact (|q - z| <= 255), so the
+// 4-bit forms carry over: the exact q - z, or its one rounding with s.
+__device__ __forceinline__ uint32_t byte_pair(uint32_t w, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(0x64646464u, w, sel);
+}
+
+constexpr uint32_t kPairLo = 0x04010400u;   // bytes 0, 1 of w under 0x64
+constexpr uint32_t kPairHi = 0x04030402u;   // bytes 2, 3
+
+__device__ __forceinline__ h8 sub_zero_word8(uint32_t w0, uint32_t w1, zero_t z)
+{
+    const h2 v0 = bitcast<h2>(byte_pair(w0, kPairLo)) - z.hz;
+    const h2 v1 = bitcast<h2>(byte_pair(w0, kPairHi)) - z.hz;
+    const h2 v2 = bitcast<h2>(byte_pair(w1, kPairLo)) - z.hz;
+    const h2 v3 = bitcast<h2>(byte_pair(w1, kPairHi)) - z.hz;
+    return h8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+__device__ __forceinline__ h8 dequant_word8(uint32_t w0, uint32_t w1, zero_t z, h2 s2)
+{
+    const h8 d = sub_zero_word8(w0, w1, z);
+    const h8 s8 = h8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]};
+    return d * s8;
+}
+
 // ---- bfloat16 activations ---------------------------------------------------
 // The activation dtype is kept (GPTQModel wiki "Inference Backends", hardware
 // table, ExLlama v2 row: FP16/BF16 activations, FP16 scales, FP32
@@ -152,6 +182,19 @@ __device__ __forceinline__ uint32_t mix_pair(uint32_t hp, float f, float c)
 {
     const h2 h = bitcast<h2>(hp);
     return pack_bf16(__builtin_fmaf((float)h[0], f, c), __builtin_fmaf((float)h[1], f, c));
+}
+
+// One k-step of 8-bit codes (two words) as eight bfloat16 values t * (q - z):
+// every half is 1024 + q, so each pair takes f = t, c = -(1024 + z) t
+// (exact: 11-bit products and |t (q - z)| needs at most 19 bits).
+__device__ __forceinline__ b8 mix_word8(uint32_t w0, uint32_t w1, const mix_t& m)
+{
+    u4 o;
+    o[0] = mix_pair(byte_pair(w0, kPairLo), m.t, m.c0);
+    o[1] = mix_pair(byte_pair(w0, kPairHi), m.t, m.c0);
+    o[2] = mix_pair(byte_pair(w1, kPairLo), m.t, m.c0);
+    o[3] = mix_pair(byte_pair(w1, kPairHi), m.t, m.c0);
+    return bitcast<b8>(o);
 }
 
 // One private-layout word as eight bfloat16 values t * (q - z) in k order.

@@ -24,6 +24,9 @@
 //  * One barrier per k-tile: after it, every wave has finished the previous
 //    tile, so the stage that tile used is refilled (tile kt + 1) while tile
 //    kt is multiplied.
+//  * W8: 8-bit codes. A chunk is 32 bytes (two words per k-step), so a
+//    column's k-tile is 16 contiguous bytes of chunks (b, kb) and (b, kb + 2):
+//    two 16-byte loads instead of two 8-byte ones.
 //  * BF: bfloat16 activations, bias and output (the activation dtype is kept;
 //    GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row). The
 //    matrix pipe then takes bfloat16 operands: each weight s * (q - z) is
@@ -59,6 +62,7 @@ struct GemmArgs {
     const uint16_t* bias;
     uint16_t* out;
     int M, K, N, G;
+    int zrow;               // bytes per row of packed zeros (N * bits / 8)
 };
 
 __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
@@ -74,9 +78,9 @@ __device__ __forceinline__ void lds_barrier()
 // (b, kb, n_j) -- sub-steps 0 and 2 -- and w[j][1] those of chunk
 // (b, kb + 2, n_j) -- sub-steps 1 and 3; scale and zero words of the tile's
 // NG groups (two for groups of 32 rows).
-template <int NG>
+template <int NG, bool W8>
 struct BRegs {
-    u2 w[NJ][2];
+    std::conditional_t<W8, u4, u2> w[NJ][2];
     uint32_t s[NG][NJ];
     uint32_t z[NG][NJ];
 };
@@ -106,14 +110,18 @@ __device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* st
     }
 }
 
-template <int NG>
-__device__ __forceinline__ void load_b(BRegs<NG>& R, const Ctx& c, const GemmArgs& p, int kt)
+template <int NG, bool W8>
+__device__ __forceinline__ void load_b(BRegs<NG, W8>& R, const Ctx& c, const GemmArgs& p, int kt)
 {
-    const uint32_t tile = (uint32_t)(kt >> 1) * (uint32_t)p.N * 64u + 8u * (uint32_t)(kt & 1);
+    constexpr uint32_t CB = W8 ? 32 : 16;   // chunk bytes
+    const uint32_t tile = (uint32_t)(kt >> 1) * (uint32_t)p.N * 4u * CB + (CB / 2) * (uint32_t)(kt & 1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 2; ++v) R.w[j][v] = buf_load8(c.rw, c.w_off[j][v], tile);
+        for (int v = 0; v < 2; ++v) {
+            if constexpr (W8) R.w[j][v] = buf_load16(c.rw, c.w_off[j][v], tile);
+            else R.w[j][v] = buf_load8(c.rw, c.w_off[j][v], tile);
+        }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         const int k = min(kt * BK + 32 * gi, p.K - 1);
@@ -121,7 +129,7 @@ __device__ __forceinline__ void load_b(BRegs<NG>& R, const Ctx& c, const GemmArg
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             R.s[gi][j] = buf_load2(c.rs, c.s_off[j], g * (uint32_t)p.N * 2u);
-            R.z[gi][j] = buf_load4(c.rz, c.z_off[j], g * (uint32_t)(p.N >> 3) * 4u);
+            R.z[gi][j] = buf_load4(c.rz, c.z_off[j], g * (uint32_t)p.zrow);
         }
     }
 }
@@ -130,7 +138,7 @@ __device__ __forceinline__ void load_b(BRegs<NG>& R, const Ctx& c, const GemmArg
 // K (a separate instantiation, so that the common kernel has no branch
 // around the multiply: the accumulators stay in the same registers).
 // (Two workgroups per CU: the register budget is 256 per lane.)
-template <int NG, bool KT, bool BF>
+template <int NG, bool KT, bool BF, bool W8>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_stream_kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
@@ -161,9 +169,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     Ctx c;
     const int ng = p.K / p.G;
     c.rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    c.rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * 64u);
+    c.rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * (W8 ? 128u : 64u));
     c.rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
-    c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)(p.N >> 3) * 4u);
+    c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)p.zrow);
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) {
         // instruction e of wave w fills rows 8 * (4e + w) .. +7 of the stage;
@@ -180,10 +188,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         lane_cols[j] = n0 + wn * WTN + 32 * j + l32;
         const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
 #pragma unroll
-        for (int v = 0; v < 2; ++v) c.w_off[j][v] = ((uint32_t)(lhi + 2 * v) * (uint32_t)p.N + n) * 16u;
+        for (int v = 0; v < 2; ++v) c.w_off[j][v] = ((uint32_t)(lhi + 2 * v) * (uint32_t)p.N + n) * (W8 ? 32u : 16u);
         c.s_off[j] = n * 2u;
-        c.z_off[j] = (n >> 3) * 4u;
-        c.z_shift[j] = 4u * (n & 7u);
+        c.z_off[j] = (n >> (W8 ? 2 : 3)) * 4u;
+        c.z_shift[j] = W8 ? 8u * (n & 3u) : 4u * (n & 7u);
     }
 
     f16x acc[MI][NJ];
@@ -195,12 +203,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int ktiles = (p.K + BK - 1) / BK;
-    BRegs<NG> R0, R1;
+    BRegs<NG, W8> R0, R1;
 
     // Multiply k-tile kt: activations from `A`, weights from register set R.
     // With KT, sub-steps past K (zero activations) are skipped so that their
     // weights (code 0, any scale) add nothing.
-    auto mma = [&](const char* A, const BRegs<NG>& R, int kt) {
+    auto mma = [&](const char* A, const BRegs<NG, W8>& R, int kt) {
         zero_t hz[NG][NJ];
         h2 s2[NG][NJ];
         mix_t mz[NJ];   // BF: the constants of the current group only (registers)
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 if constexpr (!BF) {
-                    hz[gi][j] = zero_pair((R.z[gi][j] >> c.z_shift[j]) & 0xFu);
+                    hz[gi][j] = zero_pair((R.z[gi][j] >> c.z_shift[j]) & (W8 ? 0xFFu : 0xFu));
                     s2[gi][j] = scale_pair(R.s[gi][j]);
                 }
             }
@@ -221,16 +229,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 if (sub % (4 / NG) == 0)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        mz[j] = mix_consts((R.z[gi][j] >> c.z_shift[j]) & 0xFu,
+                        mz[j] = mix_consts((R.z[gi][j] >> c.z_shift[j]) & (W8 ? 0xFFu : 0xFu),
                                            f16_bits_to_f32((uint16_t)R.s[gi][j]));
             }
             if (!KT || k0 + 16 * sub < p.K) {
                 u4 b[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const uint32_t w = R.w[j][sub & 1][sub >> 1];
-                    if constexpr (BF) b[j] = bitcast<u4>(mix_word(w, mz[j]));
-                    else b[j] = bitcast<u4>(dequant_word(w, hz[gi][j], s2[gi][j]));
+                    if constexpr (W8) {
+                        // sub-step s: words 2 (s / 2), 2 (s / 2) + 1 of the 16 bytes from chunk s % 2
+                        const uint32_t w0 = R.w[j][sub & 1][2 * (sub >> 1)], w1 = R.w[j][sub & 1][2 * (sub >> 1) + 1];
+                        if constexpr (BF) b[j] = bitcast<u4>(mix_word8(w0, w1, mz[j]));
+                        else b[j] = bitcast<u4>(dequant_word8(w0, w1, hz[gi][j], s2[gi][j]));
+                    } else {
+                        const uint32_t w = R.w[j][sub & 1][sub >> 1];
+                        if constexpr (BF) b[j] = bitcast<u4>(mix_word(w, mz[j]));
+                        else b[j] = bitcast<u4>(dequant_word(w, hz[gi][j], s2[gi][j]));
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     // One k-tile on stage S with register set Rc, prefetching tile kt + 1
     // (clamped: past the end it reloads the last tile, into buffers nobody
     // reads again) into the other stage and set Rn.
-    auto step = [&](auto S_tag, int kt, BRegs<NG>& Rc, BRegs<NG>& Rn) {
+    auto step = [&](auto S_tag, int kt, BRegs<NG, W8>& Rc, BRegs<NG, W8>& Rn) {
         constexpr int S = decltype(S_tag)::value;
         char* cur = S == 0 ? lds_a0 : lds_a1;
         char* nxt = S == 0 ? lds_a1 : lds_a0;
@@ -292,17 +307,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     }
 }
 
-template <bool BF>
+template <bool BF, bool W8>
 hipError_t launch_stream(const GemmArgs& p, int tiles, bool g32, bool kt, hipStream_t stream)
 {
     if (g32 && kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
     else if (g32)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
     else if (kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -328,7 +343,12 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;
-    return bf16 ? launch_stream<true>(p, tiles, g32, kt, stream) : launch_stream<false>(p, tiles, g32, kt, stream);
+    p.zrow = h->N * h->bits / 8;
+    if (h->bits == 8)
+        return bf16 ? launch_stream<true, true>(p, tiles, g32, kt, stream)
+                    : launch_stream<false, true>(p, tiles, g32, kt, stream);
+    return bf16 ? launch_stream<true, false>(p, tiles, g32, kt, stream)
+                : launch_stream<false, false>(p, tiles, g32, kt, stream);
 }
 
 }  // namespace q4

@@ -86,13 +86,18 @@ struct GemvArgs {
     int blocks_per_wave;
     int splits;
     int ldx;                // XL: halfs per LDS activation row (kblocks * 128 + pad)
+    int zrow;               // bytes per row of packed zeros (N * bits / 8)
 };
 
 // One k-block of loads for one lane. NGB = groups per block: 4 (groups of 32
-// rows), 2 (64) or 1 (128, 256, or one group over K).
-template <int NGB, int CT>
+// rows), 2 (64) or 1 (128, 256, or one group over K). W8: 8-bit codes, whose
+// block takes two 16-byte loads per column (WL = 2).
+template <bool W8>
+constexpr int wl() { return W8 ? 2 : 1; }
+
+template <int NGB, int CT, bool W8>
 struct Block {
-    u4 w[CT];
+    u4 w[CT][wl<W8>()];
     u4 a[4];
     uint32_t s[NGB][CT];
     uint32_t z[NGB][CT];
@@ -104,11 +109,11 @@ struct Block {
 // end of x and read zeros.
 template <int CT>
 struct Lane {
-    uint32_t w[CT];          // (kb * N + n_j) * 16
+    uint32_t w[CT];          // (kb * N + n_j) * 16 (8-bit: * 32)
     uint32_t s[CT];          // n_j * 2
-    uint32_t z[CT];          // (n_j / 8) * 4
+    uint32_t z[CT];          // (n_j / 8) * 4 (8-bit: (n_j / 4) * 4)
     uint32_t x;              // ((l % R) * K + 8 * kb + 32 * ((l % 16) / R)) * 2
-    uint32_t zshift;         // 4 * (n_j % 8), equal for every j
+    uint32_t zshift;         // 4 * (n_j % 8) (8-bit: 8 * (n_j % 4)), equal for every j
 };
 
 // Descriptors of the four tensors, and one of size 0: a load through it
@@ -124,13 +129,15 @@ struct Rsrc {
 // XS = k-steps per activation load (1, 2 or 4); B.a[0 .. 4/XS - 1] are loaded.
 // XL: the activations come from the workgroup's LDS copy instead; they are
 // read when the block is multiplied.
-template <int NGB, int CT, int XS, bool TAIL, bool XL>
-__device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p, const Rsrc& r,
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool W8>
+__device__ __forceinline__ void load_block(Block<NGB, CT, W8>& B, const GemvArgs& p, const Rsrc& r,
                                            const Lane<CT>& ln, int b)
 {
-    const uint32_t wso = (uint32_t)b * (uint32_t)p.N * 64u;
+    const uint32_t wso = (uint32_t)b * (uint32_t)p.N * 64u * wl<W8>();
 #pragma unroll
-    for (int j = 0; j < CT; ++j) B.w[j] = buf_load16_nt(r.w, ln.w[j], wso);
+    for (int j = 0; j < CT; ++j)
+#pragma unroll
+        for (int v = 0; v < wl<W8>(); ++v) B.w[j][v] = buf_load16_nt(r.w, ln.w[j] + 16u * v, wso);
     const int ksteps = p.K >> 5;
     if constexpr (!XL) {
 #pragma unroll
@@ -148,7 +155,7 @@ __device__ __forceinline__ void load_block(Block<NGB, CT>& B, const GemvArgs& p,
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
             B.s[gi][j] = buf_load2(rs, ln.s[j], (uint32_t)g * (uint32_t)p.N * 2u);
-            B.z[gi][j] = buf_load4(rz, ln.z[j], (uint32_t)g * (uint32_t)(p.N >> 3) * 4u);
+            B.z[gi][j] = buf_load4(rz, ln.z[j], (uint32_t)g * (uint32_t)p.zrow);
         }
     }
 }
@@ -185,8 +192,8 @@ __device__ __forceinline__ u4 a_operand(const u4 a[4], int i)
 // the exact q - z as bfloat16 (both operands bfloat16 on the matrix pipe).
 // XL: block b's activations are read from the LDS copy (xl = this lane's
 // address in it for the first block of the workgroup's range, bs0).
-template <int NGB, int CT, int XS, bool XL, bool BF>
-__device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT], uint32_t zshift,
+template <int NGB, int CT, int XS, bool XL, bool BF, bool W8>
+__device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 tot[CT], uint32_t zshift,
                                               const char* xl, int b, int bs0)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
@@ -210,7 +217,7 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT
         if constexpr (BF) asm("" : "+v"(one));
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-            const uint32_t z = (B.z[gi][j] >> zshift) & 0xFu;
+            const uint32_t z = (B.z[gi][j] >> zshift) & (W8 ? 0xFFu : 0xFu);
             if constexpr (BF) mz[j] = mix_consts(z, one);
             else zp[j] = zero_pair(z);
             sf[j] = f16_bits_to_f32((uint16_t)B.s[gi][j]);
@@ -223,10 +230,18 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT>& B, f4 tot[CT
             const f4 c0 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < CT; ++j) {
-                if constexpr (BF)
-                    acc[j] = mfma16(bitcast<b8>(a), mix_word(B.w[j][i], mz[j]), ii == 0 ? c0 : acc[j]);
-                else
-                    acc[j] = mfma16(bitcast<h8>(a), sub_zero_word(B.w[j][i], zp[j]), ii == 0 ? c0 : acc[j]);
+                if constexpr (W8) {
+                    // k-step i: words 2i, 2i + 1 of the lane's 32-byte chunk
+                    const uint32_t w0 = B.w[j][i >> 1][2 * (i & 1)], w1 = B.w[j][i >> 1][2 * (i & 1) + 1];
+                    if constexpr (BF)
+                        acc[j] = mfma16(bitcast<b8>(a), mix_word8(w0, w1, mz[j]), ii == 0 ? c0 : acc[j]);
+                    else
+                        acc[j] = mfma16(bitcast<h8>(a), sub_zero_word8(w0, w1, zp[j]), ii == 0 ? c0 : acc[j]);
+                } else if constexpr (BF) {
+                    acc[j] = mfma16(bitcast<b8>(a), mix_word(B.w[j][0][i], mz[j]), ii == 0 ? c0 : acc[j]);
+                } else {
+                    acc[j] = mfma16(bitcast<h8>(a), sub_zero_word(B.w[j][0][i], zp[j]), ii == 0 ? c0 : acc[j]);
+                }
             }
         }
 #pragma unroll
@@ -269,7 +284,7 @@ __device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR]
         }
 }
 
-template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF>
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8>
 __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 {
     constexpr int COLS = 16 * CT;
@@ -293,26 +308,26 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     const int n0 = tile * COLS;
 
     Rsrc r;
-    r.w = make_rsrc(p.qweight, (uint32_t)p.kblocks * (uint32_t)p.N * 64u);
+    r.w = make_rsrc(p.qweight, (uint32_t)p.kblocks * (uint32_t)p.N * 64u * wl<W8>());
     r.x = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
     r.s = make_rsrc(p.scales, (uint32_t)p.ng * (uint32_t)p.N * 2u);
-    r.z = make_rsrc(p.qzeros, (uint32_t)p.ng * (uint32_t)(p.N >> 3) * 4u);
+    r.z = make_rsrc(p.qzeros, (uint32_t)p.ng * (uint32_t)p.zrow);
     r.none = make_rsrc(p.qweight, 0u);   // (used by TAIL only)
     if constexpr (XL) r.inv = make_rsrc(p.inv, (uint32_t)p.K * 2u);
     Lane<CT> ln;
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
         const int n = min(n0 + 16 * j + c16, p.N - 1);
-        ln.w[j] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u;
+        ln.w[j] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u * wl<W8>();
         ln.s[j] = (uint32_t)n * 2u;
-        ln.z[j] = (uint32_t)(n >> 3) * 4u;
+        ln.z[j] = (uint32_t)(n >> (W8 ? 2 : 3)) * 4u;
     }
     constexpr int R = 16 / XS;
     {
         // rows m >= M fall past the end of x and read zeros
         ln.x = ((uint32_t)(c16 % R) * (uint32_t)p.K + 8u * (uint32_t)kb + 32u * (uint32_t)(c16 / R)) * 2u;
     }
-    ln.zshift = 4u * (uint32_t)(c16 & 7);
+    ln.zshift = W8 ? 8u * (uint32_t)(c16 & 3) : 4u * (uint32_t)(c16 & 7);
 
     const int split = blockIdx.y;
     const int bs0 = split * p.blocks_per_split;
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     // worse of two orders), and no work of a later block (which would
     // wait for its loads) is hoisted into an earlier one.
     const int bl = b0 + nb - 1;
-    Block<NGB, CT> buf[D];
+    Block<NGB, CT, W8> buf[D];
     // XL: the first XR activation rows and the sorted positions go out
     // before the weights, so storing them waits for them alone.
     constexpr int XJ = XL ? q4::kGemvXUnits : 1;
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     if (XL || nb > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            load_block<NGB, CT, XS, TAIL, XL>(buf[d], p, r, ln, min(b0 + d, bl));
+            load_block<NGB, CT, XS, TAIL, XL, W8>(buf[d], p, r, ln, min(b0 + d, bl));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -382,15 +397,15 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS, XL, BF>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
-                load_block<NGB, CT, XS, TAIL, XL>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
+                compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
+                load_block<NGB, CT, XS, TAIL, XL, W8>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS, XL, BF>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
+            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -457,15 +472,19 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NGB, int XS, bool TAIL, bool XL, bool BF>
+template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
     const dim3 block(NT);
     const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF>), dim3((p.N + 63) / 64, splits), block, lds, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 4:
+        // (8-bit blocks are twice the registers: at most two tiles)
+        if constexpr (W8) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -475,27 +494,38 @@ hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 // per k-step. A K that is not a multiple of 128 (one partial block) takes the
 // one-per-step form, whose past-K steps are masked per load.
 // (Staged act-order activations come with M <= 2 only.)
-template <int NGB, bool XL, bool BF>
+template <int NGB, bool XL, bool BF, bool W8>
 hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
-    if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF>(p, ct, splits, stream);
-    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF>(p, ct, splits, stream);
+    if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF, W8>(p, ct, splits, stream);
+    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF, W8>(p, ct, splits, stream);
     if constexpr (!XL) {
-        if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF>(p, ct, splits, stream);
-        return launch_ct<NGB, 1, false, XL, BF>(p, ct, splits, stream);
+        if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF, W8>(p, ct, splits, stream);
+        return launch_ct<NGB, 1, false, XL, BF, W8>(p, ct, splits, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <bool XL, bool BF>
+template <bool XL, bool BF, bool W8>
 hipError_t launch_xl(const GemvArgs& p, int ngb, int ct, int splits, hipStream_t stream)
 {
     switch (ngb) {
-    case 1: return launch_ngb<1, XL, BF>(p, ct, splits, stream);
-    case 2: return launch_ngb<2, XL, BF>(p, ct, splits, stream);
-    case 4: return launch_ngb<4, XL, BF>(p, ct, splits, stream);
+    case 1: return launch_ngb<1, XL, BF, W8>(p, ct, splits, stream);
+    case 2: return launch_ngb<2, XL, BF, W8>(p, ct, splits, stream);
+    case 4: return launch_ngb<4, XL, BF, W8>(p, ct, splits, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <bool W8>
+hipError_t launch_w(const GemvArgs& p, int ngb, int ct, int splits, bool gather_x, bool bf16,
+                    hipStream_t stream)
+{
+    if (bf16)
+        return gather_x ? launch_xl<true, true, W8>(p, ngb, ct, splits, stream)
+                        : launch_xl<false, true, W8>(p, ngb, ct, splits, stream);
+    return gather_x ? launch_xl<true, false, W8>(p, ngb, ct, splits, stream)
+                    : launch_xl<false, false, W8>(p, ngb, ct, splits, stream);
 }
 
 }  // namespace
@@ -535,11 +565,9 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     // groups per 128-row block: groups of 32 or 64 rows split a block; larger
     // groups (and one group over K) cover it whole
     const int ngb = (h->G == h->K || h->G >= 128) ? 1 : 128 / h->G;
-    if (bf16)
-        return gather_x ? launch_xl<true, true>(p, ngb, col_tiles, splits, stream)
-                        : launch_xl<false, true>(p, ngb, col_tiles, splits, stream);
-    return gather_x ? launch_xl<true, false>(p, ngb, col_tiles, splits, stream)
-                    : launch_xl<false, false>(p, ngb, col_tiles, splits, stream);
+    p.zrow = h->N * h->bits / 8;
+    return h->bits == 8 ? launch_w<true>(p, ngb, col_tiles, splits, gather_x, bf16, stream)
+                        : launch_w<false>(p, ngb, col_tiles, splits, gather_x, bf16, stream);
 }
 
 }  // namespace q4

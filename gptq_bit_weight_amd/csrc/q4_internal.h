@@ -17,9 +17,18 @@ namespace q4 {
 // MFMA lane in each of four consecutive 32-row k-steps, and the 64 rows a
 // prefill k-tile needs are 8 contiguous bytes of every chunk. K is padded to
 // a whole block with code 0 (the kernels give those rows zero activations).
+//
+// 8-bit weights use the same blocks with 32-byte chunks: word 2i + h of chunk
+// (b, kb, n) holds rows 32 * (4b + i) + 8 * kb + 4h .. +3, one byte each in k
+// order. A skinny-kernel lane then loads its block with two 16-byte loads,
+// and a prefill k-tile (k-steps 2t, 2t + 1 of a block) is 16 contiguous bytes
+// of a chunk.
 constexpr int kBlockK = 128;
 constexpr int num_kblocks(int K) { return (K + kBlockK - 1) / kBlockK; }
-constexpr size_t packed_words(int K, int N) { return (size_t)num_kblocks(K) * (kBlockK / 8) * (size_t)N; }
+constexpr size_t packed_words(int K, int N, int bits = 4)
+{
+    return (size_t)num_kblocks(K) * (kBlockK * bits / 32) * (size_t)N;
+}
 
 // ---- skinny (M <= 16) kernel geometry ------------------------------------
 constexpr int kGemvWaves = 8;        // waves per workgroup (they split its K range)
@@ -51,11 +60,11 @@ q4_status fail(q4_status st, const char* fmt, ...) __attribute__((format(printf,
 q4_status last_status();
 const char* last_message();
 
-q4_status check_shape(int K, int N, int groupsize, int* G_out);
+q4_status check_shape(int K, int N, int groupsize, int* G_out, int bits = 4);
 q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* trivial);
 // Skinny-kernel launch plan: 16-column tiles per wave (1, 2 or 4) and K
 // splits across workgroups (1..kMaxSplits) for a chip of num_cu CUs.
-void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits);
+void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits, int bits = 4);
 // Whether the skinny kernel stages act-order activations itself for this
 // M, K and number of K splits.
 bool gemv_gathers_x(int M, int K, int splits);
@@ -67,11 +76,12 @@ bool gemv_gathers_x(int M, int K, int splits);
 struct q4_matrix {
     int K = 0, N = 0, G = 0, ng = 0;
     int act_order = 0;
+    int bits = 4;                  // 4 or 8
     int device = -1;
     int num_cu = 256;
-    uint32_t* qweight = nullptr;   // packed_words(K, N): private block layout (above)
+    uint32_t* qweight = nullptr;   // packed_words(K, N, bits): private block layout (above)
     uint16_t* scales = nullptr;    // [ng][N] fp16
-    uint32_t* qzeros = nullptr;    // [ng][N/8]
+    uint32_t* qzeros = nullptr;    // [ng][N * bits / 32]
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
     uint16_t* inv16 = nullptr;     // the same in 16 bits, when K <= kGemvXRows

@@ -30,7 +30,7 @@ const char* last_message() { return t_message; }
 // Shape rules of the GPU path. The checkpoint format only needs K % 8 and
 // N % 8 (whole packed words along K for qweight and along N for qzeros); the
 // kernels also walk K in steps of 32 (one MFMA k-block), hence K % 32.
-q4_status check_shape(int K, int N, int groupsize, int* G_out)
+q4_status check_shape(int K, int N, int groupsize, int* G_out, int bits)
 {
     if (K <= 0 || N <= 0)
         return fail(Q4_ERR_INVALID_ARG, "K and N must be positive (got K=%d, N=%d)", K, N);
@@ -50,7 +50,8 @@ q4_status check_shape(int K, int N, int groupsize, int* G_out)
     // Byte offsets inside the packed weights (K padded to whole 128-row
     // blocks) stay below 2^31: the kernels mark out-of-range lanes by setting
     // bit 31 of the offset.
-    const long long packed = (long long)num_kblocks(K) * (kBlockK / 2) * (long long)N;
+    if (bits != 4 && bits != 8) return fail(Q4_ERR_UNSUPPORTED, "bits=%d is not 4 or 8", bits);
+    const long long packed = (long long)num_kblocks(K) * (kBlockK * bits / 8) * (long long)N;
     if (packed > (1LL << 31) - 1)
         return fail(Q4_ERR_UNSUPPORTED, "%lld bytes of packed weights exceed 2^31 - 1", packed);
     if (G_out) *G_out = G;
@@ -94,15 +95,16 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 //    cannot give every CU a workgroup, and only while every wave of every
 //    split keeps a k-block. Each split adds a round of fp32 partials and a
 //    last-arriver reduction to the critical path.
-void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits)
+void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits, int bits)
 {
     if (num_cu <= 0) num_cu = 256;
     // gain x 100 for 1, 2, 4 tiles: M <= 4, M <= 8, M <= 16
     static const int gain[3][3] = {{100, 110, 120}, {100, 140, 150}, {100, 160, 190}};
     const int mi = M <= 4 ? 0 : M <= 8 ? 1 : 2;
-    // (groups of 32 rows carry four scale/zero sets per block; four tiles of
-    // them do not fit the register file)
-    const int max_ct = G == 32 ? 2 : kMaxColTiles;
+    // (groups of 32 rows carry four scale/zero sets per block, and 8-bit
+    // blocks are twice the words; four tiles of either do not fit the
+    // register file)
+    const int max_ct = (G == 32 || bits == 8) ? 2 : kMaxColTiles;
     int ct = 1;
     long long best = -1;
     for (int c = 1, ci = 0; c <= max_ct; c *= 2, ++ci) {
@@ -140,6 +142,12 @@ q4_status q4_check_shape(int K, int N, int groupsize)
 {
     int G;
     return q4::check_shape(K, N, groupsize, &G);
+}
+
+q4_status q4_check_shape_bits(int K, int N, int groupsize, int bits)
+{
+    int G;
+    return q4::check_shape(K, N, groupsize, &G, bits);
 }
 
 q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int32_t* perm,

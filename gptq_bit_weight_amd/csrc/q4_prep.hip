@@ -21,12 +21,14 @@ namespace {
 
 using namespace q4dev;
 
-// Row k' of the private layout: its chunk (b, kb), the word i inside the
-// chunk and the element e inside the word.
-__device__ __forceinline__ size_t private_word(int kk, int n, int N, int* e)
+// Row k' of the private layout: its chunk (b, kb), the word inside the chunk
+// and the element e inside the k-step's eight rows (4-bit: word i; 8-bit:
+// word 2i + e / 4).
+__device__ __forceinline__ size_t private_word(int kk, int n, int N, int* e, int bits)
 {
     const int b = kk >> 7, i = (kk >> 5) & 3, kb = (kk >> 3) & 3;
     *e = kk & 7;
+    if (bits == 8) return ((size_t)(4 * b + kb) * N + n) * 8 + 2 * i + (*e >> 2);
     return ((size_t)(4 * b + kb) * N + n) * 4 + i;
 }
 
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restri
                                                         uint32_t* __restrict__ dst, int K, int N,
                                                         int n_total, int col_off)
 {
-    const size_t total = q4::packed_words(K, N);
+    const size_t total = q4::packed_words(K, N, 4);
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
         const int i = (int)(idx & 3);
@@ -57,6 +59,36 @@ __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restri
             w |= code << (4 * slot_of(e));
         }
         dst[((size_t)q * n_total + col_off + n) * 4 + i] = w;
+    }
+}
+
+// 8-bit codes: one thread per output word, word 2i + h of chunk (b, kb) =
+// the four codes of (sorted) rows 32 * (4b + i) + 8 * kb + 4h + e, e = 0..3,
+// in k order, gathered from original rows perm[k'] (code of row k in byte
+// k % 4 of source word k / 4). Rows past K get code 0.
+__global__ __launch_bounds__(256) void q4_repack8_kernel(const uint32_t* __restrict__ src,
+                                                         const int32_t* __restrict__ perm,
+                                                         uint32_t* __restrict__ dst, int K, int N,
+                                                         int n_total, int col_off)
+{
+    const size_t total = q4::packed_words(K, N, 8);
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int wi = (int)(idx & 7);
+        const size_t chunk = idx >> 3;
+        const int n = (int)(chunk % N);
+        const int q = (int)(chunk / N);                  // 4 * b + kb
+        const int k0 = 32 * (4 * (q >> 2) + (wi >> 1)) + 8 * (q & 3) + 4 * (wi & 1);
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kk = k0 + e;
+            if (kk >= K) break;
+            const int k = perm ? perm[kk] : kk;
+            const uint32_t code = (src[(size_t)(k >> 2) * N + n] >> (8 * (k & 3))) & 0xFFu;
+            w |= code << (8 * e);
+        }
+        dst[((size_t)q * n_total + col_off + n) * 8 + wi] = w;
     }
 }
 
@@ -111,7 +143,7 @@ __global__ __launch_bounds__(256) void q4_permute_rows_kernel(const uint16_t* __
 // BF: bfloat16 values of the bfloat16 forms -- FACTORED: the kernel's exact
 // q - z as bfloat16 times the fp32 scale, rounded once to bfloat16;
 // otherwise the bfloat16 weight mix_word feeds to the bfloat16 MFMA.
-template <bool FACTORED, bool BF>
+template <bool FACTORED, bool BF, bool W8>
 __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict__ qweight,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint32_t* __restrict__ qzeros,
@@ -125,22 +157,27 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const int kk = inv_perm ? inv_perm[k] : k;       // sorted position of row k
         const int g = kk / G;
         int e;
-        const uint32_t word = qweight[private_word(kk, n, N, &e)];
-        const uint32_t z = (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
+        const size_t wp = private_word(kk, n, N, &e, W8 ? 8 : 4);
+        const uint32_t z = W8 ? (qzeros[(size_t)g * (N >> 2) + (n >> 2)] >> (8 * (n & 3))) & 0xFFu
+                              : (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
+        // the two words of the k-step (8-bit) or its one word (4-bit)
+        const uint32_t word = qweight[wp];
+        const uint32_t w0 = W8 ? qweight[wp - (e >> 2)] : word, w1 = W8 ? qweight[wp - (e >> 2) + 1] : word;
         const uint16_t sb = scales[(size_t)g * N + n];
         if constexpr (BF) {
             float t = FACTORED ? 1.0f : f16_bits_to_f32(sb);
             asm("" : "+v"(t));    // as in the kernels: one fused multiply-add per value
-            const b8 v = mix_word(word, mix_consts(z, t));
+            const b8 v = W8 ? mix_word8(w0, w1, mix_consts(z, t)) : mix_word(word, mix_consts(z, t));
             if (FACTORED)
                 w[idx] = f32_to_bf16_bits(f16_bits_to_f32(sb) * static_cast<float>(v[e]));
             else
                 w[idx] = bitcast<uint16_t>(v[e]);
         } else if (FACTORED) {
-            const h8 d = sub_zero_word(word, zero_pair(z));
+            const h8 d = W8 ? sub_zero_word8(w0, w1, zero_pair(z)) : sub_zero_word(word, zero_pair(z));
             w[idx] = f32_to_f16_bits(f16_bits_to_f32(sb) * static_cast<float>(d[e]));
         } else {
-            const h8 v = dequant_word(word, zero_pair(z), scale_pair(sb));
+            const h8 v = W8 ? dequant_word8(w0, w1, zero_pair(z), scale_pair(sb))
+                            : dequant_word(word, zero_pair(z), scale_pair(sb));
             w[idx] = bitcast<uint16_t>(v[e]);
         }
     }
@@ -159,10 +196,14 @@ int grid_for(size_t total)
 namespace q4 {
 
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
-                         int n_total, int col_off, hipStream_t stream)
+                         int n_total, int col_off, int bits, hipStream_t stream)
 {
-    hipLaunchKernelGGL(q4_repack_kernel, dim3(grid_for(packed_words(K, N))), dim3(256), 0, stream,
-                       src, perm, dst, K, N, n_total, col_off);
+    if (bits == 8)
+        hipLaunchKernelGGL(q4_repack8_kernel, dim3(grid_for(packed_words(K, N, 8))), dim3(256), 0, stream,
+                           src, perm, dst, K, N, n_total, col_off);
+    else
+        hipLaunchKernelGGL(q4_repack_kernel, dim3(grid_for(packed_words(K, N, 4))), dim3(256), 0, stream,
+                           src, perm, dst, K, N, n_total, col_off);
     return hipGetLastError();
 }
 
@@ -182,23 +223,30 @@ hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp
     return hipGetLastError();
 }
 
-hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream)
+template <bool W8>
+hipError_t launch_dump_w(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream)
 {
     const dim3 grid(grid_for((size_t)h->K * h->N));
     const bool f = path == Q4_PATH_GEMV;
     if (f && bf16)
-        hipLaunchKernelGGL((q4_dump_kernel<true, true>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+        hipLaunchKernelGGL((q4_dump_kernel<true, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     else if (f)
-        hipLaunchKernelGGL((q4_dump_kernel<true, false>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+        hipLaunchKernelGGL((q4_dump_kernel<true, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     else if (bf16)
-        hipLaunchKernelGGL((q4_dump_kernel<false, true>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+        hipLaunchKernelGGL((q4_dump_kernel<false, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     else
-        hipLaunchKernelGGL((q4_dump_kernel<false, false>), grid, dim3(256), 0, stream, h->qweight, h->scales,
+        hipLaunchKernelGGL((q4_dump_kernel<false, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
                            h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
     return hipGetLastError();
+}
+
+hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream)
+{
+    return h->bits == 8 ? launch_dump_w<true>(h, path, w, bf16, stream)
+                        : launch_dump_w<false>(h, path, w, bf16, stream);
 }
 
 }  // namespace q4

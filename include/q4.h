@@ -104,6 +104,23 @@ q4_matrix* q4_make(const int32_t* qweight, const int32_t* qzeros, const uint16_t
                    const int32_t* g_idx, int K, int N, int groupsize);
 
 /*
+ * q4_make_bits -- q4_make for 4- or 8-bit codes (bits = 4 or 8). GPTQModel
+ * wiki "Inference Backends": GPTQ kernels declare 4- and 8-bit weights
+ * (backend catalogue) and the native 8-bit GPTQ path keeps the same
+ * checkpoint tensors (section "Runtime cache lifetime"). With bits = 8 a word
+ * holds four codes packed the same way (code i in bits 8i .. 8i + 7):
+ * qweight [K/4][N] (row k = 4r + i in byte i of word (r, n)), qzeros
+ * [K/groupsize][N/4] (column n = 4c + j in byte j of word (g, c)); a NULL
+ * qzeros means the symmetric zero point 2^(8-1) = 128. bits = 4 is q4_make.
+ * Every other argument, the ownership and the errors are as in q4_make
+ * (Q4_ERR_UNSUPPORTED for other bit widths). The matmul calls are the same;
+ * 8-bit handles take at most two skinny-kernel column tiles and GEMM
+ * variant 0 or 3 only.
+ */
+q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                        const int32_t* g_idx, int K, int N, int groupsize, int bits);
+
+/*
  * q4_matmul -- out[M][N] = fp16(x[M][K] @ W) (Lorax page, Description: x @ q4
  * producing (batch, width)). Accumulation is in fp32 (GPTQModel wiki,
  * hardware table, ExLlama v2 row: FP32 accumulation, FP16 scales); the only
@@ -217,6 +234,12 @@ q4_matrix* q4_make_cat(int parts, const int32_t* const* qweight, const int32_t* 
                        const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
                        int groupsize);
 
+/* q4_make_cat_bits -- q4_make_cat for 4- or 8-bit parts (all parts the
+ * same width; layouts as in q4_make_bits). */
+q4_matrix* q4_make_cat_bits(int parts, const int32_t* const* qweight, const int32_t* const* qzeros,
+                            const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
+                            int groupsize, int bits);
+
 const char* q4_last_error(void);
 
 /*
@@ -257,6 +280,9 @@ int q4_gemv_gather(const q4_matrix* h, int M, int splits);
  * non-trivial g_idx was given). Returns 0, or -1 for a NULL handle. */
 int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_order);
 
+/* The handle's code width (4 or 8), or -1 for a NULL handle. */
+int q4_handle_bits(const q4_matrix* h);
+
 /* ------------------------------------------------------------------------
  * Host-only planning helpers (no HIP calls; usable without a GPU).
  * ---------------------------------------------------------------------- */
@@ -267,6 +293,10 @@ int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_
  * Q4_ERR_UNSUPPORTED (message in q4_last_error).
  */
 q4_status q4_check_shape(int K, int N, int groupsize);
+
+/* q4_check_shape for q4_make_bits (bits = 4 or 8; other widths give
+ * Q4_ERR_UNSUPPORTED). */
+q4_status q4_check_shape_bits(int K, int N, int groupsize, int bits);
 
 /*
  * q4_plan_actorder -- host act-order plan for a host copy of g_idx[K]:

@@ -73,7 +73,8 @@ def make_matrix(L, t=None, g_idx="layer"):
     import gptq_bit_weight_amd as q4
     t = t or device_tensors(L)
     gi = t["g_idx"] if g_idx == "layer" else g_idx
-    return q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], gi, groupsize=L.G if L.G != L.K else -1)
+    return q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], gi, groupsize=L.G if L.G != L.K else -1,
+                       bits=L.bits)
 
 
 def run(L, *, path=0, variant=0, splits=0, W=None, t=None, x=None, bias="layer"):
@@ -106,12 +107,12 @@ def compare(y16: np.ndarray, y_ref: np.ndarray, A: np.ndarray, what: str = "",
 
 def oracle_full(L):
     return oracle.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G, bias=L.bias,
-                         xfmt=L.xfmt)
+                         xfmt=L.xfmt, bits=L.bits)
 
 
 def oracle_sampled(L, ms, ns):
     return oracle.matmul_at(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G, ms, ns,
-                            bias=L.bias, xfmt=L.xfmt)
+                            bias=L.bias, xfmt=L.xfmt, bits=L.bits)
 
 
 def sample_indices(M: int, N: int, count: int, seed: int):
