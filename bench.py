@@ -27,10 +27,11 @@ Also reported on the same JSON line:
   secondary     the same block with q/k/v and gate/up fused into one call each
                 (4 launches a step); the 70B-shaped MLP layers at M = 1, 2, 4,
                 8, 16 and the act-order 7B MLP layers at M = 1, 4 (GB/s, each
-                layer over >= 1 GiB of copies); the seven-layer block with
-                bfloat16 activations; the prefill GEMM at M = 2048 on the 7B
-                MLP shapes, groupsize 128 and 32, act-order and bfloat16
-                (TFLOPS against the dense fp16/bf16 MFMA peak).
+                layer over >= 1 GiB of copies); the 7B MLP layers with 8-bit
+                weights at M = 1, 4; the seven-layer block with bfloat16
+                activations; the prefill GEMM at M = 2048 on the 7B MLP
+                shapes, groupsize 128 and 32, act-order, bfloat16 and 8-bit
+                weights (TFLOPS against the dense fp16/bf16 MFMA peak).
 """
 from __future__ import annotations
 
@@ -86,6 +87,7 @@ class Layer:
                     torch.from_numpy(L.scales).to(dev),
                     torch.from_numpy(L.g_idx).to(dev) if L.g_idx is not None else None)
         self.name, self.K, self.N, self.G, self.M = name, L.K, L.N, L.G, L.M
+        self.bits = L.bits
         self.mats = [self._make() for _ in range(copies)]
         self.bf16 = L.xfmt == "bf16"
         act = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)) if self.bf16 \
@@ -101,7 +103,7 @@ class Layer:
 
     def _make(self):
         qw, qz, sc, gi = self.src
-        return self.q4.Q4Matrix(qw, qz, sc, gi, groupsize=self.G)
+        return self.q4.Q4Matrix(qw, qz, sc, gi, groupsize=self.G, bits=self.bits)
 
     def grow(self, copies):
         """Make handle copies until there are `copies` of them."""
@@ -297,14 +299,14 @@ def fused_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500
             "per_layer_us": {ly.name: round(t * 1e6, 3) for ly, t in zip(layers, lt)}}
 
 
-def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=False):
+def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=False, bits=4):
     """GB/s of each layer in `specs` ((name, K, N)) at each M: one layer's
     handles rotate over >= 1 GiB of copies (per_launch_times), the same
     handles serve every M (only the activations change)."""
     out = {}
     for name, K, N in specs:
         L = synth.make_layer(K, N, 128, max(Ms), seed=synth.layer_seed(workload, name, act_order),
-                             act_order=act_order)
+                             act_order=act_order, bits=bits)
         ly = Layer(q4, torch, name, L, 1)
         x_all = ly.x
         for M in Ms:
@@ -349,12 +351,13 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
     three times after a warm-up replay; the median replay gives the time."""
     out = {}
     reps = 20
-    for K, N, G, act, xfmt in ((4096, 11008, 128, False, "f16"), (11008, 4096, 128, False, "f16"),
-                               (4096, 11008, 32, False, "f16"), (11008, 4096, 32, False, "f16"),
-                               (4096, 11008, 128, True, "f16"), (4096, 11008, 128, False, "bf16"),
-                               (11008, 4096, 128, False, "bf16")):
+    for K, N, G, act, xfmt, bits in ((4096, 11008, 128, False, "f16", 4), (11008, 4096, 128, False, "f16", 4),
+                                     (4096, 11008, 32, False, "f16", 4), (11008, 4096, 32, False, "f16", 4),
+                                     (4096, 11008, 128, True, "f16", 4), (4096, 11008, 128, False, "bf16", 4),
+                                     (11008, 4096, 128, False, "bf16", 4), (4096, 11008, 128, False, "f16", 8),
+                                     (11008, 4096, 128, False, "f16", 8)):
         L = synth.make_layer(K, N, G, M, seed=synth.layer_seed("prefill", K, N, G, act), act_order=act,
-                             xfmt=xfmt)
+                             xfmt=xfmt, bits=bits)
         ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
         with torch.cuda.stream(stream):
             ly.launch(lib, 0, ctypes.c_void_p(stream.cuda_stream))   # sizes the act-order workspace
@@ -377,7 +380,8 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
                 times.append(a.elapsed_time(b) * 1e-3 / reps)
         t = sorted(times)[1]
         tf = ly.flops / t / 1e12
-        out[f"{K}x{N}_g{G}{'_act' if act else ''}{'_bf16' if xfmt == 'bf16' else ''}_m{M}"] = {
+        out[f"{K}x{N}_g{G}{'_act' if act else ''}{'_bf16' if xfmt == 'bf16' else ''}"
+            f"{'_w8' if bits == 8 else ''}_m{M}"] = {
             "TFLOP/s": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)}
         del g
         ly.close()
@@ -398,6 +402,9 @@ def secondary(q4, torch, synth, lib, stream):
                                               "llama7b_block_decode", 10)
     out["llama70b_mlp_decode"] = decode_sweep(q4, torch, synth, lib, stream, "llama70b_mlp_decode",
                                               synth.LLAMA70B_MLP, (1, 2, 4, 8, 16))
+    out["llama7b_mlp_w8_decode"] = decode_sweep(
+        q4, torch, synth, lib, stream, "llama7b_mlp_w8_decode",
+        (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (1, 4), bits=8)
     out["llama7b_actorder_decode"] = decode_sweep(
         q4, torch, synth, lib, stream, "llama7b_actorder_decode",
         (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (1, 4), act_order=True)
