@@ -1,5 +1,9 @@
-// Prefill fused W4A16 GEMM (M > 16) on the matrix cores: activations staged
+// Prefill fused GPTQ GEMM (M > 16) on the matrix cores: activations staged
 // in LDS, weights streamed into registers.
+//
+// q4_gemm_stream_kernel<NG, KT, BF, W8>: NG groups per 64-row k-tile (2 for
+// groups of 32), KT (K not a multiple of 64), BF (bfloat16 activations and
+// output), W8 (8-bit codes).
 //
 // The multiply runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation
 // (GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row: FP32

@@ -1,4 +1,9 @@
-// Skinny fused W4A16 kernel for 1 <= M <= 16 (decode).
+// Skinny fused GPTQ kernel for 1 <= M <= 16 (decode).
+//
+// q4_gemv_kernel<NGB, CT, XS, TAIL, XL, BF, W8>: NGB groups per 128-row block,
+// CT 16-column tiles per wave, XS k-steps per activation load, TAIL (K not a
+// multiple of 128), XL (act-order activations staged in LDS), BF (bfloat16
+// activations and output), W8 (8-bit codes; 4-bit otherwise).
 //
 // Weight-bound decoding is limited by memory bandwidth ("GPTQ's 'Exllama
 // Kernel Not Installed' Warning", section "What the fallback actually
@@ -12,7 +17,8 @@
 //    gives it the eight rows 32 * (4b + i) + 8 * kb .. +7 for each of the
 //    four k-steps i of block b, which is exactly the B operand of four
 //    v_mfma_f32_16x16x32_f16 (lane l: rows 8 * (l / 16) .. +7 of column
-//    l % 16). A is the activations (row m = l % 16), shared by the CT tiles.
+//    l % 16). (8-bit codes: the chunk is 32 bytes, two 16-byte loads.)
+//    A is the activations (row m = l % 16), shared by the CT tiles.
 //    M is padded to 16 on the matrix pipe, which has the capacity to spare:
 //    output rows m >= M are never stored, so what A holds in those rows does
 //    not matter. That lets one 16-byte load serve XS = 16 / R k-steps when
@@ -24,7 +30,8 @@
 //    sum_k x * s * (q - z) = s * sum_k x * (q - z). The weight s * (q - z) is
 //    exact in fp32, so this is the product with the exact dequantized weight,
 //    accumulated in fp32, and the vector ALU does one unpack and one packed
-//    subtract per two weights.
+//    subtract per two weights. (BF: the same exact q - z as bfloat16, formed
+//    by one fused multiply-add per value; the MFMA takes bfloat16.)
 //  * the weights are read exactly once, with the non-temporal hint (5-7%
 //    faster on the 7B layers than default caching);
 //  * each wave keeps D k-blocks of loads in flight (a ring of register
