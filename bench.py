@@ -41,6 +41,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -63,17 +64,25 @@ def log(*a):
 # The sources that decide what the skinny kernel does and how it is launched
 # (its code, the shared device helpers and geometry, the weight layout the
 # repack writes, the launch plan and the dispatch): counter figures taken for
-# it stay valid while these are unchanged.
+# it stay valid while their code (comments aside) is unchanged.
 GEMV_SOURCES = ("q4_gemv.hip", "q4_device.h", "q4_internal.h", "q4_prep.hip", "q4_plan.cpp",
                 "q4_api.hip")
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and blank-line or trailing-space changes,
+    so that editing a comment does not invalidate recorded counters."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gptq_bit_weight_amd", "csrc")
     for name in GEMV_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
