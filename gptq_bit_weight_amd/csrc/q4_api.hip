@@ -22,6 +22,7 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
 hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream);
+hipError_t launch_make_sz(q4_matrix* h, hipStream_t stream);
 
 namespace {
 
@@ -43,6 +44,7 @@ void destroy(q4_matrix* h)
     (void)hipFree(h->qweight);
     (void)hipFree(h->scales);
     (void)hipFree(h->qzeros);
+    (void)hipFree(h->sz);
     (void)hipFree(h->perm);
     (void)hipFree(h->inv_perm);
     (void)hipFree(h->inv16);
@@ -133,6 +135,7 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     if ((e = hipMalloc(&h->scales, (size_t)ng * N * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
     const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
     if ((e = hipMalloc(&h->qzeros, (size_t)ng * zrow)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
+    if ((e = hipMalloc(&h->sz, (size_t)ng * N * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
     if ((e = hipMalloc(&h->partials, (size_t)kMaxSplits * 16 * N * 4)) != hipSuccess)
         return bail(hip_fail(e, "q4_make: workspace"));
     const int col_tiles = (N + 15) / 16;
@@ -182,6 +185,7 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
             return bail(hip_fail(e, "q4_make: repack launch"));
         off += Np[i];
     }
+    if ((e = launch_make_sz(h, 0)) != hipSuccess) return bail(hip_fail(e, "q4_make: group parameters"));
     if ((e = hipDeviceSynchronize()) != hipSuccess) return bail(hip_fail(e, "q4_make: repack"));
     *out = h;
     return Q4_OK;

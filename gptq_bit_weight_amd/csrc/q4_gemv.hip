@@ -77,8 +77,7 @@ constexpr int depth() { return CT >= 2 ? q4::kGemvDepth / 2 : q4::kGemvDepth; }
 
 struct GemvArgs {
     const uint32_t* qweight;
-    const uint16_t* scales;
-    const uint32_t* qzeros;
+    const uint32_t* sz;     // [ng][N]: scale bits | zero << 16
     const uint16_t* x;
     const uint16_t* inv;    // act-order: original row -> sorted position (XL)
     const uint16_t* bias;
@@ -93,7 +92,6 @@ struct GemvArgs {
     int blocks_per_wave;
     int splits;
     int ldx;                // XL: halfs per LDS activation row (kblocks * 128 + pad)
-    int zrow;               // bytes per row of packed zeros (N * bits / 8)
 };
 
 // One k-block of loads for one lane. NGB = groups per block: 4 (groups of 32
@@ -106,8 +104,7 @@ template <int NGB, int CT, bool W8>
 struct Block {
     u4 w[CT][wl<W8>()];
     u4 a[4];
-    uint32_t s[NGB][CT];
-    uint32_t z[NGB][CT];
+    uint32_t sz[NGB][CT];   // scale bits | zero << 16
 };
 
 // Per-lane byte offsets, fixed for the whole kernel; each block adds a
@@ -117,17 +114,15 @@ struct Block {
 template <int CT>
 struct Lane {
     uint32_t w[CT];          // (kb * N + n_j) * 16 (8-bit: * 32)
-    uint32_t s[CT];          // n_j * 2
-    uint32_t z[CT];          // (n_j / 8) * 4 (8-bit: (n_j / 4) * 4)
+    uint32_t sz[CT];         // n_j * 4
     uint32_t x;              // ((l % R) * K + 8 * kb + 32 * ((l % 16) / R)) * 2
-    uint32_t zshift;         // 4 * (n_j % 8) (8-bit: 8 * (n_j % 4)), equal for every j
 };
 
-// Descriptors of the four tensors, and one of size 0: a load through it
+// Descriptors of the tensors, and one of size 0: a load through it
 // returns zeros and moves no data. Only the last k-block of a K that is not a
 // multiple of 128 needs it (TAIL): its k-steps past K and its groups past K / G.
 struct Rsrc {
-    rsrc_t w, x, s, z, none, inv;
+    rsrc_t w, x, sz, none, inv;
 };
 
 // Load k-block b (0 <= b < kblocks). The per-block offsets are wave-uniform
@@ -157,13 +152,9 @@ __device__ __forceinline__ void load_block(Block<NGB, CT, W8>& B, const GemvArgs
     for (int gi = 0; gi < NGB; ++gi) {
         const int g = (4 * b + gi * (4 / NGB)) >> p.gshift;
         const bool ok = !TAIL || g < p.ng;
-        const rsrc_t rs = ok ? r.s : r.none;
-        const rsrc_t rz = ok ? r.z : r.none;
+        const rsrc_t rsz = ok ? r.sz : r.none;
 #pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            B.s[gi][j] = buf_load2(rs, ln.s[j], (uint32_t)g * (uint32_t)p.N * 2u);
-            B.z[gi][j] = buf_load4(rz, ln.z[j], (uint32_t)g * (uint32_t)p.zrow);
-        }
+        for (int j = 0; j < CT; ++j) B.sz[gi][j] = buf_load4(rsz, ln.sz[j], (uint32_t)g * (uint32_t)p.N * 4u);
     }
 }
 
@@ -200,8 +191,8 @@ __device__ __forceinline__ u4 a_operand(const u4 a[4], int i)
 // XL: block b's activations are read from the LDS copy (xl = this lane's
 // address in it for the first block of the workgroup's range, bs0).
 template <int NGB, int CT, int XS, bool XL, bool BF, bool W8>
-__device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 tot[CT], uint32_t zshift,
-                                              const char* xl, int b, int bs0)
+__device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 tot[CT], const char* xl,
+                                              int b, int bs0)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
     u4 av[4];
@@ -224,10 +215,10 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 to
         if constexpr (BF) asm("" : "+v"(one));
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-            const uint32_t z = (B.z[gi][j] >> zshift) & (W8 ? 0xFFu : 0xFu);
+            const uint32_t z = B.sz[gi][j] >> 16;
             if constexpr (BF) mz[j] = mix_consts(z, one);
             else zp[j] = zero_pair(z);
-            sf[j] = f16_bits_to_f32((uint16_t)B.s[gi][j]);
+            sf[j] = f16_bits_to_f32((uint16_t)B.sz[gi][j]);
         }
         f4 acc[CT];
 #pragma unroll
@@ -317,8 +308,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     Rsrc r;
     r.w = make_rsrc(p.qweight, (uint32_t)p.kblocks * (uint32_t)p.N * 64u * wl<W8>());
     r.x = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
-    r.s = make_rsrc(p.scales, (uint32_t)p.ng * (uint32_t)p.N * 2u);
-    r.z = make_rsrc(p.qzeros, (uint32_t)p.ng * (uint32_t)p.zrow);
+    r.sz = make_rsrc(p.sz, (uint32_t)p.ng * (uint32_t)p.N * 4u);
     r.none = make_rsrc(p.qweight, 0u);   // (used by TAIL only)
     if constexpr (XL) r.inv = make_rsrc(p.inv, (uint32_t)p.K * 2u);
     Lane<CT> ln;
@@ -326,15 +316,13 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     for (int j = 0; j < CT; ++j) {
         const int n = min(n0 + 16 * j + c16, p.N - 1);
         ln.w[j] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u * wl<W8>();
-        ln.s[j] = (uint32_t)n * 2u;
-        ln.z[j] = (uint32_t)(n >> (W8 ? 2 : 3)) * 4u;
+        ln.sz[j] = (uint32_t)n * 4u;
     }
     constexpr int R = 16 / XS;
     {
         // rows m >= M fall past the end of x and read zeros
         ln.x = ((uint32_t)(c16 % R) * (uint32_t)p.K + 8u * (uint32_t)kb + 32u * (uint32_t)(c16 / R)) * 2u;
     }
-    ln.zshift = W8 ? 8u * (uint32_t)(c16 & 3) : 4u * (uint32_t)(c16 & 7);
 
     const int split = blockIdx.y;
     const int bs0 = split * p.blocks_per_split;
@@ -404,7 +392,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, ln.zshift, xl, b0 + D * (rd - 1) + d, bs0);
+                compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, xl, b0 + D * (rd - 1) + d, bs0);
                 load_block<NGB, CT, XS, TAIL, XL, W8>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -412,7 +400,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, ln.zshift, xl, b0 + D * (rounds - 1) + d, bs0);
+            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, xl, b0 + D * (rounds - 1) + d, bs0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -546,8 +534,7 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     if (gather_x && (!h->inv16 || !gemv_gathers_x(M, h->K, splits))) return hipErrorInvalidValue;
     GemvArgs p;
     p.qweight = h->qweight;
-    p.scales = h->scales;
-    p.qzeros = h->qzeros;
+    p.sz = h->sz;
     p.x = x;
     p.inv = gather_x ? h->inv16 : nullptr;
     p.bias = bias;
@@ -572,7 +559,6 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     // groups per 128-row block: groups of 32 or 64 rows split a block; larger
     // groups (and one group over K) cover it whole
     const int ngb = (h->G == h->K || h->G >= 128) ? 1 : 128 / h->G;
-    p.zrow = h->N * h->bits / 8;
     return h->bits == 8 ? launch_w<true>(p, ngb, col_tiles, splits, gather_x, bf16, stream)
                         : launch_w<false>(p, ngb, col_tiles, splits, gather_x, bf16, stream);
 }

@@ -82,6 +82,9 @@ struct q4_matrix {
     uint32_t* qweight = nullptr;   // packed_words(K, N, bits): private block layout (above)
     uint16_t* scales = nullptr;    // [ng][N] fp16
     uint32_t* qzeros = nullptr;    // [ng][N * bits / 32]
+    // the skinny kernel's group parameters, one word per (group, column):
+    // scale bits | zero point << 16 (one load instead of two per block)
+    uint32_t* sz = nullptr;        // [ng][N]
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
     uint16_t* inv16 = nullptr;     // the same in 16 bits, when K <= kGemvXRows

@@ -135,6 +135,23 @@ __global__ __launch_bounds__(256) void q4_permute_rows_kernel(const uint16_t* __
     }
 }
 
+// sz[g][n] = scale bits | zero point << 16, from the handle's scales and
+// packed zeros (bits-wide codes, packed along N).
+__global__ __launch_bounds__(256) void q4_make_sz_kernel(const uint16_t* __restrict__ scales,
+                                                         const uint32_t* __restrict__ qzeros,
+                                                         uint32_t* __restrict__ sz, int ng, int N, int bits)
+{
+    const size_t total = (size_t)ng * N;
+    const int per = 32 / bits;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const size_t g = idx / N;
+        const int n = (int)(idx % N);
+        const uint32_t z = (qzeros[g * (N / per) + n / per] >> (bits * (n % per))) & ((1u << bits) - 1u);
+        sz[idx] = (uint32_t)scales[idx] | (z << 16);
+    }
+}
+
 // Debug dump: w[k][n] (original row order) = the dequantized weight (k, n) as
 // each kernel forms it, rounded to fp16. FACTORED (skinny kernel): the
 // kernel's own (q - z) from sub_zero_word times the fp32 scale, which is the
@@ -147,6 +164,7 @@ template <bool FACTORED, bool BF, bool W8>
 __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict__ qweight,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint32_t* __restrict__ qzeros,
+                                                      const uint32_t* __restrict__ sz,
                                                       const int32_t* __restrict__ inv_perm,
                                                       uint16_t* __restrict__ w, int K, int N, int G)
 {
@@ -158,12 +176,15 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const int g = kk / G;
         int e;
         const size_t wp = private_word(kk, n, N, &e, W8 ? 8 : 4);
-        const uint32_t z = W8 ? (qzeros[(size_t)g * (N >> 2) + (n >> 2)] >> (8 * (n & 3))) & 0xFFu
+        // the skinny kernel reads its scale and zero from sz, the GEMM from
+        // scales and qzeros
+        const uint32_t z = FACTORED ? sz[(size_t)g * N + n] >> 16
+                         : W8 ? (qzeros[(size_t)g * (N >> 2) + (n >> 2)] >> (8 * (n & 3))) & 0xFFu
                               : (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
         // the two words of the k-step (8-bit) or its one word (4-bit)
         const uint32_t word = qweight[wp];
         const uint32_t w0 = W8 ? qweight[wp - (e >> 2)] : word, w1 = W8 ? qweight[wp - (e >> 2) + 1] : word;
-        const uint16_t sb = scales[(size_t)g * N + n];
+        const uint16_t sb = FACTORED ? (uint16_t)sz[(size_t)g * N + n] : scales[(size_t)g * N + n];
         if constexpr (BF) {
             float t = FACTORED ? 1.0f : f16_bits_to_f32(sb);
             asm("" : "+v"(t));    // as in the kernels: one fused multiply-add per value
@@ -207,6 +228,13 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
     return hipGetLastError();
 }
 
+hipError_t launch_make_sz(q4_matrix* h, hipStream_t stream)
+{
+    hipLaunchKernelGGL(q4_make_sz_kernel, dim3(grid_for((size_t)h->ng * h->N)), dim3(256), 0, stream,
+                       h->scales, h->qzeros, h->sz, h->ng, h->N, h->bits);
+    return hipGetLastError();
+}
+
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream)
 {
@@ -230,16 +258,16 @@ hipError_t launch_dump_w(const q4_matrix* h, int path, uint16_t* w, bool bf16, h
     const bool f = path == Q4_PATH_GEMV;
     if (f && bf16)
         hipLaunchKernelGGL((q4_dump_kernel<true, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
     else if (f)
         hipLaunchKernelGGL((q4_dump_kernel<true, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
     else if (bf16)
         hipLaunchKernelGGL((q4_dump_kernel<false, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
     else
         hipLaunchKernelGGL((q4_dump_kernel<false, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->inv_perm, w, h->K, h->N, h->G);
+                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
     return hipGetLastError();
 }
 
