@@ -20,7 +20,7 @@ from typing import Optional
 
 __all__ = [
     "Q4Matrix", "Q4Error", "load_library", "library_path", "check_shape", "plan_actorder",
-    "plan_gemv", "plan_gemv_gather", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
+    "plan_gemv", "plan_gemv_gather", "plan_gemm", "PATH_NONE", "PATH_GEMV", "PATH_MFMA", "GEMV_MAX_M", "EXPORTED_SYMBOLS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +28,7 @@ _LIB_PATH = os.path.join(HERE, "libq4.so")
 
 PATH_NONE, PATH_GEMV, PATH_MFMA = 0, 1, 2
 GEMV_MAX_M = 16
+GEMM_MAX_WORKERS = 1024
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
 
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
     "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16", "q4_make_bits", "q4_make_cat_bits",
-    "q4_handle_bits", "q4_check_shape_bits",
+    "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm",
 )
 
 _lib = None
@@ -108,6 +109,8 @@ def load_library():
     lib.q4_gemv_gather.restype = I
     lib.q4_plan_gemv_gather.argtypes = [I, I, I]
     lib.q4_plan_gemv_gather.restype = I
+    lib.q4_plan_gemm.argtypes = [I, I, I, I]
+    lib.q4_plan_gemm.restype = I
     _lib = lib
     return lib
 
@@ -158,6 +161,15 @@ def plan_gemv(M: int, K: int, N: int, groupsize: int, num_cu: int = 256) -> tupl
     _check(lib.q4_plan_gemv(M, K, N, groupsize, num_cu, ctypes.byref(ct), ctypes.byref(sp)),
            "q4_plan_gemv")
     return int(ct.value), int(sp.value)
+
+
+def plan_gemm(M: int, N: int, K: int, num_cu: int = 256) -> int:
+    """Workgroups of the streaming GEMM for an M x N output with K rows:
+    the number of 256 x 128 output tiles (one each) or a stream-K count."""
+    r = int(load_library().q4_plan_gemm(M, N, K, num_cu))
+    if r < 0:
+        raise ValueError(f"q4_plan_gemm: bad arguments M={M} N={N} K={K}")
+    return r
 
 
 def plan_gemv_gather(M: int, K: int, splits: int) -> bool:
@@ -316,8 +328,9 @@ class Q4Matrix:
         16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 automatic,
         1 register-staged, 2 direct-to-LDS, 3 weights streamed into
         registers (the automatic choice; the only one for bfloat16).
-        splits: skinny kernel K splits (0 planned, 1..16); must be 0 for the
-        GEMM."""
+        splits: skinny kernel K splits (0 planned, 1..16); GEMM variant 3
+        workgroups (0 planned, 1 one per output tile, 2..GEMM_MAX_WORKERS
+        sharing the tiles' k-steps: stream-K); variants 1 and 2 take 0 or 1."""
         torch = _torch()
         h = self._handle()
         if getattr(x, "dtype", None) not in (torch.float16, torch.bfloat16):

@@ -1,8 +1,11 @@
 // C ABI of libq4: handle construction, dispatch and debug entry points.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstring>
+#include <map>
+#include <utility>
 #include <vector>
 
 #include "q4_internal.h"
@@ -16,7 +19,8 @@ hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t
 hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                             int M, hipStream_t stream);
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, bool bf16, hipStream_t stream);
+                              int M, bool bf16, int workers, float* partials, uint32_t* counters,
+                              hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          int n_total, int col_off, int bits, hipStream_t stream);
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
@@ -51,6 +55,7 @@ void destroy(q4_matrix* h)
     (void)hipFree(h->partials);
     (void)hipFree(h->counters);
     (void)hipFree(h->xperm);
+    for (uint16_t* p : h->xperm_retired) (void)hipFree(p);
     delete h;
 }
 
@@ -206,21 +211,68 @@ q4_status ensure_xperm(const q4_matrix* h, int M, hipStream_t stream)
     const size_t need = (size_t)M * h->K;
     std::lock_guard<std::mutex> lock(h->ws_mutex);
     if (h->xperm_elems >= need) return Q4_OK;
-    // Growing synchronizes the device and allocates, which a stream under
-    // graph capture cannot do: say so instead of breaking the capture.
+    // Growing allocates, which a stream under graph capture cannot do: say
+    // so instead of breaking the capture.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
     if (cap != hipStreamCaptureStatusNone)
         return fail(Q4_ERR_INVALID_ARG,
                     "q4_matmul: the act-order workspace must grow to M=%d under stream capture; "
                     "make one uncaptured call with this M (or larger) first", M);
-    // Earlier calls may still read the old buffer: wait for them first.
-    Q4_HIP(hipDeviceSynchronize(), "q4_matmul: workspace grow");
-    (void)hipFree(h->xperm);
-    h->xperm = nullptr;
-    h->xperm_elems = 0;
-    Q4_HIP(hipMalloc(&h->xperm, need * 2), "q4_matmul: act-order workspace");
+    // Earlier launches, and graphs captured from them, may still use the old
+    // buffer: retire it (freed with the handle) instead of freeing it now.
+    uint16_t* fresh = nullptr;
+    Q4_HIP(hipMalloc(&fresh, need * 2), "q4_matmul: act-order workspace");
+    if (h->xperm) h->xperm_retired.push_back(h->xperm);
+    h->xperm = fresh;
     h->xperm_elems = need;
+    return Q4_OK;
+}
+
+// Stream-K workspace of the streaming GEMM, one per (device, stream): two
+// 256 x 128 fp32 partial slots and one arrival counter per workgroup, for
+// max(workers, 2 x CUs) workgroups rounded up to a power of two (128 MiB on
+// 256 CUs). Calls on one stream run in order, so they can share it whatever
+// handle they use; calls on different streams get different buffers. A
+// workspace that is outgrown is replaced but never freed (a captured graph
+// may still name it); all are kept until the process ends.
+struct SkSpace {
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    int workers = 0;
+};
+std::mutex g_sk_mutex;
+auto* g_sk = new std::map<std::pair<int, hipStream_t>, SkSpace>;
+
+// Fills *ws for `workers` workgroups on (device, stream). Under stream
+// capture a missing or small workspace cannot be allocated: *ws is then left
+// empty (workers = 0).
+q4_status sk_workspace(int device, int num_cu, hipStream_t stream, int workers, SkSpace* ws)
+{
+    std::lock_guard<std::mutex> lock(g_sk_mutex);
+    SkSpace& sp = (*g_sk)[{device, stream}];
+    if (sp.workers >= workers) {
+        *ws = sp;
+        return Q4_OK;
+    }
+    *ws = SkSpace{};
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
+    if (cap != hipStreamCaptureStatusNone) return Q4_OK;
+    int n = 2 * std::max(num_cu, 1);
+    while (n < workers) n *= 2;
+    const size_t slot = (size_t)kGemmBM * kGemmBN * sizeof(float);
+    SkSpace fresh;
+    Q4_HIP(hipMalloc(&fresh.partials, 2 * (size_t)n * slot), "q4_matmul: stream-K partials");
+    if (hipMalloc(&fresh.counters, (size_t)n * sizeof(uint32_t)) != hipSuccess) {
+        (void)hipFree(fresh.partials);
+        return fail(Q4_ERR_OOM, "q4_matmul: stream-K counters");
+    }
+    Q4_HIP(hipMemsetAsync(fresh.counters, 0, (size_t)n * sizeof(uint32_t), stream),
+           "q4_matmul: stream-K counters");
+    fresh.workers = n;
+    sp = fresh;
+    *ws = sp;
     return Q4_OK;
 }
 
@@ -253,10 +305,15 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (h->bits == 8 && variant == 4)
             return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights take at most 2 column tiles");
     } else {
-        if (splits != 0)
-            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the GEMM takes no K splits (got %d)", splits);
         if (variant < 0 || variant > 3)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1, 2 or 3", variant);
+        if (splits < 0 || splits > Q4_GEMM_MAX_WORKERS)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM workgroups %d outside [0, %d]", splits,
+                        Q4_GEMM_MAX_WORKERS);
+        if (splits > 1 && variant != 0 && variant != 3)
+            return fail(Q4_ERR_UNSUPPORTED,
+                        "q4_matmul: GEMM variant %d runs one workgroup per tile (splits 0 or 1, got %d)",
+                        variant, splits);
         if (bf16 && variant != 0 && variant != 3)
             return fail(Q4_ERR_UNSUPPORTED,
                         "q4_matmul: bfloat16 activations run on GEMM variant 3 only (got %d)", variant);
@@ -294,8 +351,29 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (variant == 0) variant = 3;
         if (variant == 1)
             Q4_HIP(launch_gemm_regs(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
-        else if (variant == 3)
-            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, stream), "q4_matmul: gemm launch");
+        else if (variant == 3) {
+            // splits: 0 planned, 1 one workgroup per output tile, P >= 2
+            // workgroups sharing the tiles' k-iterations (stream-K)
+            const int tiles = gemm_tiles(M, h->N);
+            int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu) : splits == 1 ? tiles : splits;
+            // every workgroup must get at least one (tile, k-step) iteration:
+            // a split tile counts its contributors as a range of workgroups
+            workers = (int)std::min<long long>(workers, (long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK));
+            SkSpace ws;
+            if (workers != tiles) {
+                q4_status st = sk_workspace(h->device, h->num_cu, stream, workers, &ws);
+                if (st != Q4_OK) return st;
+                if (!ws.partials) {
+                    if (splits != 0)
+                        return fail(Q4_ERR_INVALID_ARG,
+                                    "q4_matmul: the stream-K workspace for %d workgroups must be made "
+                                    "under no stream capture; make one uncaptured call first", workers);
+                    workers = tiles;   // planned call under capture: one workgroup per tile
+                }
+            }
+            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, workers, ws.partials, ws.counters, stream),
+                   "q4_matmul: gemm launch");
+        }
         else
             Q4_HIP(launch_gemm_dma(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
     }

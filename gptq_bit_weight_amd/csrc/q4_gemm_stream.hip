@@ -67,6 +67,17 @@ struct GemmArgs {
     uint16_t* out;
     int M, K, N, G;
     int zrow;               // bytes per row of packed zeros (N * bits / 8)
+    // Schedule: `workers` workgroups share the (output tile, k-tile)
+    // iterations evenly, in contiguous ranges, each at least one iteration
+    // long (workers <= iterations). workers = tiles is one tile per
+    // workgroup; fewer or more split some tiles' K ranges between workgroups
+    // (stream-K), whose fp32 partial sums go through `partials` (two
+    // 256 x 128 slots per workgroup) and an arrival counter per split tile
+    // (zero between launches).
+    float* partials;
+    uint32_t* counters;
+    int workers;
+    int xcd;                // 1: each XCD takes the row tiles r with r % 8 == XCD (row tiles % 8 == 0)
 };
 
 __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
@@ -147,28 +158,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 {
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
+    __shared__ int s_last;
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, lhi = lane >> 5;
+    // per-lane indices, recomputed for every segment (below) so that values
+    // derived from them are not kept live across the k-loop
+    int tid = 0, lane = 0, l32 = 0, lhi = 0;
 
-    // Workgroup order: when the row tiles divide evenly over the 8 XCDs
-    // (workgroup i runs on XCD i % 8), every XCD works on its own row tiles
-    // and keeps their activations in its L2; otherwise row-major order.
+    // Iteration space. With `xcd`, workgroup i runs on XCD i % 8 and works on
+    // that XCD's own row tiles (row tile r with r % 8 == XCD), which keeps
+    // their activations in its L2; otherwise one space in row-major tile
+    // order. A space of T tiles holds T * ktiles iterations (tile-major);
+    // worker r of Ps takes iterations [r * I / Ps, (r + 1) * I / Ps).
     const int nt = (p.N + BN - 1) / BN, mt = (p.M + BM - 1) / BM;
+    const int ktiles = (p.K + BK - 1) / BK;
     const int id = blockIdx.x;
-    int mtile, ntile;
-    if (mt % 8 == 0) {
-        const int xcd = id & 7, r = id >> 3;
-        mtile = (r / nt) * 8 + xcd;
-        ntile = r % nt;
-    } else {
-        mtile = id / nt;
-        ntile = id % nt;
-    }
-    const int m0 = mtile * BM, n0 = ntile * BN;
+    const int space = p.xcd ? (id & 7) : 0;
+    const int rk = p.xcd ? (id >> 3) : id;
+    const int Ps = p.xcd ? p.workers >> 3 : p.workers;
+    const long long I = (long long)(p.xcd ? (mt >> 3) * nt : mt * nt) * ktiles;
+    const long long it_begin = (long long)rk * I / Ps, it_end = (long long)(rk + 1) * I / Ps;
+    // worker of iteration i: the largest r with r * I / Ps <= i
+    auto owner = [&](long long i) { return (int)(((i + 1) * Ps + I - 1) / I - 1); };
+    auto worker_id = [&](int r) { return p.xcd ? r * 8 + space : r; };
 
     Ctx c;
     const int ng = p.K / p.G;
@@ -176,38 +189,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     c.rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * (W8 ? 128u : 64u));
     c.rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
     c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)p.zrow);
-#pragma unroll
-    for (int e = 0; e < A_LOADS; ++e) {
-        // instruction e of wave w fills rows 8 * (4e + w) .. +7 of the stage;
-        // lane i lands in slot i % 8 of row i / 8, which holds chunk
-        // slot ^ ((row >> 1) & 7)
-        const int row = 8 * (4 * e + wave) + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        c.a_k[e] = 8u * (uint32_t)chunk;
-        c.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + c.a_k[e]) * 2u;
-    }
-    int lane_cols[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        lane_cols[j] = n0 + wn * WTN + 32 * j + l32;
-        const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
-#pragma unroll
-        for (int v = 0; v < 2; ++v) c.w_off[j][v] = ((uint32_t)(lhi + 2 * v) * (uint32_t)p.N + n) * (W8 ? 32u : 16u);
-        c.s_off[j] = n * 2u;
-        c.z_off[j] = (n >> (W8 ? 2 : 3)) * 4u;
-        c.z_shift[j] = W8 ? 8u * (n & 3u) : 4u * (n & 7u);
-    }
 
     f16x acc[MI][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int ktiles = (p.K + BK - 1) / BK;
     BRegs<NG, W8> R0, R1;
+    int m0 = 0, seg_end = 0;
+    int lane_cols[NJ];
 
     // Multiply k-tile kt: activations from `A`, weights from register set R.
     // With KT, sub-steps past K (zero activations) are skipped so that their
@@ -265,8 +251,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     };
 
     // One k-tile on stage S with register set Rc, prefetching tile kt + 1
-    // (clamped: past the end it reloads the last tile, into buffers nobody
-    // reads again) into the other stage and set Rn.
+    // (clamped: past the segment's end it reloads its last tile, into
+    // buffers nobody reads again) into the other stage and set Rn.
     auto step = [&](auto S_tag, int kt, BRegs<NG, W8>& Rc, BRegs<NG, W8>& Rn) {
         constexpr int S = decltype(S_tag)::value;
         char* cur = S == 0 ? lds_a0 : lds_a1;
@@ -277,51 +263,187 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         // compiler issued the two kinds of loads in.
         Q4S_VMCNT(0);
         lds_barrier();
-        const int kn = min(kt + 1, ktiles - 1);
+        const int kn = min(kt + 1, seg_end - 1);
         load_a<KT>(c, p, nxt, wave, kn);
         load_b(Rn, c, p, kn);
         mma(cur, Rc, kt);
     };
 
-    load_a<KT>(c, p, lds_a0, wave, 0);
-    load_b(R0, c, p, 0);
-    int kt = 0;
-    for (; kt + 1 < ktiles; kt += 2) {
-        step(std::integral_constant<int, 0>{}, kt, R0, R1);
-        step(std::integral_constant<int, 1>{}, kt + 1, R1, R0);
-    }
-    if (kt < ktiles) step(std::integral_constant<int, 0>{}, kt, R0, R1);
-    // Drain the last (unused) prefetch before the workgroup's LDS is reused.
-    Q4S_VMCNT(0);
-
-    // Epilogue: fp32 bias, one round-to-nearest-even cast, store. Lane l holds
-    // rows 8*(r/4) + 4*(l/32) + r%4 of column l%32 of each 32 x 32 tile.
+    // The range [a, b) is the tail of a split tile [a, lo), whole tiles
+    // [lo, hi) and the head of a split tile [hi, b). The two split segments
+    // go first: the neighbouring workgroups also start with theirs, so both
+    // halves of a split tile finish early and its fix-up overlaps the whole
+    // tiles of this workgroup and of the one sharing its CU, instead of all
+    // fix-ups landing at the end of the kernel.
+    const long long lo = min(it_end, (it_begin + ktiles - 1) / ktiles * ktiles);
+    const long long hi = max(lo, it_end / ktiles * ktiles);
+    const int nfull = (int)((hi - lo) / ktiles);
+    bool first_seg = true;
+    for (int sg = -2; sg < nfull; ++sg) {
+        const long long sb = sg == -2 ? it_begin : sg == -1 ? hi : lo + (long long)sg * ktiles;
+        const long long se = sg == -2 ? lo : sg == -1 ? it_end : sb + ktiles;
+        if (sb >= se) continue;
+        const int lt = (int)(sb / ktiles);
+        const int kb = (int)(sb - (long long)lt * ktiles);
+        const int ke = kb + (int)(se - sb);
+        const int mtile = p.xcd ? (lt / nt) * 8 + space : lt / nt;
+        const int n0 = (lt % nt) * BN;
+        m0 = mtile * BM;
+        seg_end = ke;
+        tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        lane = tid & 63;
+        l32 = lane & 31;
+        lhi = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int n = lane_cols[j];
-        if (n >= p.N) continue;
-        const float bv = p.bias ? act_to_f32<BF>(p.bias[n]) : 0.f;
+        for (int e = 0; e < A_LOADS; ++e) {
+            // instruction e of wave w fills rows 8 * (4e + w) .. +7 of the stage;
+            // lane i lands in slot i % 8 of row i / 8, which holds chunk
+            // slot ^ ((row >> 1) & 7)
+            const int row = 8 * (4 * e + wave) + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            c.a_k[e] = 8u * (uint32_t)chunk;
+            c.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + c.a_k[e]) * 2u;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            lane_cols[j] = n0 + wn * WTN + 32 * j + l32;
+            const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
+#pragma unroll
+            for (int v = 0; v < 2; ++v) c.w_off[j][v] = ((uint32_t)(lhi + 2 * v) * (uint32_t)p.N + n) * (W8 ? 32u : 16u);
+            c.s_off[j] = n * 2u;
+            c.z_off[j] = (n >> (W8 ? 2 : 3)) * 4u;
+            c.z_shift[j] = W8 ? 8u * (n & 3u) : 4u * (n & 7u);
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_act<BF>(acc[i][j][r] + bv);
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        // Every wave has finished reading the stages (previous segment)
+        // before they are refilled.
+        if (!first_seg) lds_barrier();
+        first_seg = false;
+        load_a<KT>(c, p, lds_a0, wave, kb);
+        load_b(R0, c, p, kb);
+        int kt = kb;
+        for (; kt + 1 < ke; kt += 2) {
+            step(std::integral_constant<int, 0>{}, kt, R0, R1);
+            step(std::integral_constant<int, 1>{}, kt + 1, R1, R0);
+        }
+        if (kt < ke) step(std::integral_constant<int, 0>{}, kt, R0, R1);
+        // Drain the last (unused) prefetch before the LDS is reused.
+        Q4S_VMCNT(0);
+
+        if (kb != 0 || ke != ktiles) {
+            // A split tile, whose workers wf .. wl each hold one k-segment.
+            // The last of them to arrive adds the fp32 sums in k order,
+            // p_wf + p_wf+1 + ... + p_wl (the same bits whichever worker that
+            // is), and stores. The others publish their sums first: agent-
+            // scope atomic stores and loads go to the device-coherent level
+            // (a full fence would write back and invalidate the XCD's L2),
+            // and every wave's stores are complete before the arrival count
+            // is bumped. A worker that finds all the others already counted
+            // is last without publishing its own.
+            // Slots: a segment that starts inside its tile is its worker's
+            // first (slot 2 id), one that starts the tile is its worker's
+            // last (slot 2 id + 1).
+            const long long t0 = (long long)lt * ktiles;
+            const int wf = owner(t0), wl = owner(t0 + ktiles - 1);
+            const uint32_t others = (uint32_t)(wl - wf);
+            auto slot_of = [&](int r) {
+                return p.partials + (size_t)(r == wf ? 2 * worker_id(r) + 1 : 2 * worker_id(r)) * (BM * BN);
+            };
+            uint32_t* counter = p.counters + worker_id(wf);
+            if (tid == 0)
+                s_last = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == others;
+            __syncthreads();
+            if (!s_last) {
+                float* mine = slot_of(rk);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            __hip_atomic_store(&mine[((i * NJ + j) * 16 + r) * NT + tid], acc[i][j][r],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (tid == 0)
+                    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                             others;
+                __syncthreads();
+                if (!s_last) continue;
             }
+            // Ordered sum, 32 values per lane at a time.
+#pragma unroll
+            for (int q = 0; q < MI * NJ; q += 2) {
+#define Q4S_ACC(e) acc[(q + (e) / 16) / NJ][(q + (e) / 16) % NJ][(e) % 16]
+                if (rk > wf) {
+                    // p_wf + ... + p_(rk-1), then + this worker's sums
+                    float t[32];
+                    const float* src = slot_of(wf) + (size_t)q * 16 * NT + tid;
+#pragma unroll
+                    for (int e = 0; e < 32; ++e)
+                        t[e] = __hip_atomic_load(&src[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int r = wf + 1; r < rk; ++r) {
+                        const float* sr = slot_of(r) + (size_t)q * 16 * NT + tid;
+                        float v[32];
+#pragma unroll
+                        for (int e = 0; e < 32; ++e)
+                            v[e] = __hip_atomic_load(&sr[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                        for (int e = 0; e < 32; ++e) t[e] += v[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) Q4S_ACC(e) = t[e] + Q4S_ACC(e);
+                }
+                for (int r = rk + 1; r <= wl; ++r) {
+                    const float* sr = slot_of(r) + (size_t)q * 16 * NT + tid;
+                    float v[32];
+#pragma unroll
+                    for (int e = 0; e < 32; ++e)
+                        v[e] = __hip_atomic_load(&sr[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) Q4S_ACC(e) += v[e];
+                }
+#undef Q4S_ACC
+            }
+            if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // Epilogue: fp32 bias, one round-to-nearest-even cast, store. Lane l
+        // holds rows 8*(r/4) + 4*(l/32) + r%4 of column l%32 of each 32 x 32 tile.
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int n = lane_cols[j];
+            if (n >= p.N) continue;
+            const float bv = p.bias ? act_to_f32<BF>(p.bias[n]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
+                    if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_act<BF>(acc[i][j][r] + bv);
+                }
+        }
     }
 }
 
 template <bool BF, bool W8>
-hipError_t launch_stream(const GemmArgs& p, int tiles, bool g32, bool kt, hipStream_t stream)
+hipError_t launch_stream(const GemmArgs& p, int grid, bool g32, bool kt, hipStream_t stream)
 {
     if (g32 && kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else if (g32)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else if (kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF, W8>), dim3(tiles), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -330,7 +452,8 @@ hipError_t launch_stream(const GemmArgs& p, int tiles, bool g32, bool kt, hipStr
 namespace q4 {
 
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, bool bf16, hipStream_t stream)
+                              int M, bool bf16, int workers, float* partials, uint32_t* counters,
+                              hipStream_t stream)
 {
     GemmArgs p;
     p.qweight = h->qweight;
@@ -343,7 +466,12 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     p.K = h->K;
     p.N = h->N;
     p.G = h->G;
-    const int tiles = ((h->N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    p.partials = partials;
+    p.counters = counters;
+    p.workers = workers;
+    // XCD spaces need whole row tiles and workers per XCD
+    p.xcd = ((M + BM - 1) / BM) % 8 == 0 && workers % 8 == 0;
+    const int tiles = workers;
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;

@@ -4,6 +4,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "q4.h"
 
@@ -54,6 +55,7 @@ constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 256;
+inline int gemm_tiles(int M, int N) { return ((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN); }
 
 // Error reporting (thread-local status + message).
 q4_status fail(q4_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -68,6 +70,10 @@ void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* spli
 // Whether the skinny kernel stages act-order activations itself for this
 // M, K and number of K splits.
 bool gemv_gathers_x(int M, int K, int splits);
+// Workgroups of the streaming GEMM for an M x N output and K rows on a chip
+// of num_cu CUs: gemm_tiles(M, N) (one per output tile) when the tiles fill
+// whole rounds of two workgroups per CU, otherwise a stream-K split.
+int plan_gemm_workers(int M, int N, int K, int num_cu);
 
 }  // namespace q4
 
@@ -95,4 +101,5 @@ struct q4_matrix {
     mutable std::mutex ws_mutex;
     mutable uint16_t* xperm = nullptr;
     mutable size_t xperm_elems = 0;
+    mutable std::vector<uint16_t*> xperm_retired;   // outgrown buffers, freed with the handle
 };

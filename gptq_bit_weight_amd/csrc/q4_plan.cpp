@@ -131,6 +131,30 @@ bool gemv_gathers_x(int M, int K, int splits)
            (long long)M * (rows + kGemvXPad) <= kGemvXLdsHalfs;
 }
 
+// Streaming-GEMM schedule. Two workgroups share a CU (64 KiB of LDS and
+// 256 VGPRs each), and a CU that holds only one runs a tile at about 0.7
+// times the rate of two (one wave per SIMD leaves the matrix pipe idle while
+// that wave dequantizes). With one workgroup per output tile, tile counts
+// that are not whole rounds of 2 x CUs leave CUs idle or half-used (256
+// tiles: every CU at one; 688: a third round on a third of the chip).
+// Stream-K gives every workgroup the same number of (tile, k-tile)
+// iterations instead, at the price of fp32 partials for the tiles that
+// straddle two workgroups. It is planned when one-per-tile would waste more
+// than a tenth of the rounds; at most two workgroups per tile, so that a
+// split tile has two or three contributors.
+int plan_gemm_workers(int M, int N, int K, int num_cu)
+{
+    if (num_cu <= 0) num_cu = 256;
+    const long long tiles = gemm_tiles(M, N);
+    const long long cap = 2LL * num_cu;
+    const long long rounds = (tiles + cap - 1) / cap;
+    if (tiles * 10 >= rounds * cap * 9) return (int)tiles;
+    const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
+    long long w = std::min(cap, 2 * tiles);
+    w = std::min(w, tiles * ktiles);
+    return (int)std::min<long long>(w, Q4_GEMM_MAX_WORKERS);
+}
+
 }  // namespace q4
 
 extern "C" {
@@ -168,6 +192,12 @@ int q4_plan_gemv_gather(int M, int K, int splits)
 {
     if (M < 1 || M > Q4_GEMV_MAX_M || K < 1 || splits < 1 || splits > q4::kMaxSplits) return -1;
     return q4::gemv_gathers_x(M, K, splits) ? 1 : 0;
+}
+
+int q4_plan_gemm(int M, int N, int K, int num_cu)
+{
+    if (M < 1 || N < 1 || K < 1) return -1;
+    return q4::plan_gemm_workers(M, N, K, num_cu);
 }
 
 q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles, int* splits)

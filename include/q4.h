@@ -67,6 +67,8 @@ enum {
 };
 
 #define Q4_GEMV_MAX_M 16
+/* Most workgroups one streaming-GEMM launch may be given (q4_matmul_ex). */
+#define Q4_GEMM_MAX_WORKERS 1024
 
 /*
  * q4_make -- build a handle from GPTQ tensors (Lorax page, Description: a
@@ -133,7 +135,11 @@ q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uin
  *
  * Concurrency: the handle's workspace is shared by its calls, so calls on one
  * handle must be ordered on one stream (or synchronized); different handles
- * are independent.
+ * are independent. The GEMM's stream-K partial sums (tiles whose K range is
+ * split between two workgroups) go to a workspace per (device, stream) that
+ * the library allocates on the first call on that stream that needs it
+ * (2 x 128 KiB + 4 bytes per workgroup: 128 MiB for 512 workgroups) and
+ * keeps until the process ends; calls on one stream share it in order.
  *
  * Act-order (non-trivial g_idx): the weights are stored in sorted-group
  * order, so the product needs the activations x[:, perm] (the Lorax GPTQ
@@ -145,10 +151,15 @@ q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uin
  *
  * Graph capture: a call may be captured into a HIP graph and replayed; it
  * enqueues kernels only (no memset or copy nodes; the skinny kernel's split-K
- * counters are reset by the kernel). An act-order handle grows its
- * activation workspace on the first call with a larger M that needs the
- * separate permute, which cannot happen under capture: such a call returns
- * Q4_ERR_INVALID_ARG, so make one uncaptured call with the largest M first.
+ * counters, and the GEMM's stream-K counters, are reset by the kernels). A
+ * GEMM call captured on a stream that has no stream-K workspace yet runs one
+ * workgroup per output tile instead (the same result up to fp32 rounding).
+ * An act-order handle grows its activation workspace on the first call with
+ * a larger M that needs the separate permute, which cannot happen under
+ * capture: such a call returns Q4_ERR_INVALID_ARG, so make one uncaptured
+ * call with the largest M first. Outgrown workspaces are not freed before
+ * the handle (act-order buffer) or the process (stream-K buffers), so graphs
+ * captured earlier stay valid.
  */
 q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M,
                     hipStream_t stream);
@@ -171,7 +182,15 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
  *                  1..16;
  *   GEMM:          variant = 0 (automatic: 3), 1 (register-staged tiles),
  *                  2 (direct-to-LDS pipeline) or 3 (activations in LDS,
- *                  weights streamed into registers); splits must be 0.
+ *                  weights streamed into registers); splits = workgroups
+ *                  of variant 3: 0 (planned, q4_plan_gemm), 1 (one per
+ *                  256 x 128 output tile) or 2..Q4_GEMM_MAX_WORKERS (the
+ *                  tiles' 64-row k-steps shared evenly, stream-K; a count
+ *                  above the number of (tile, k-step) pairs is reduced to
+ *                  it; under
+ *                  stream capture only once the stream has a workspace that
+ *                  large, else Q4_ERR_INVALID_ARG). Variants 1 and 2 take
+ *                  splits 0 or 1 (else Q4_ERR_UNSUPPORTED).
  * Anything else is Q4_ERR_INVALID_ARG. Results differ between paths,
  * variants and split counts only by fp32 rounding.
  */
@@ -307,6 +326,15 @@ q4_status q4_check_shape_bits(int K, int N, int groupsize, int bits);
  */
 q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int32_t* perm,
                            int* trivial);
+
+/*
+ * q4_plan_gemm -- the streaming GEMM's planned workgroup count for an
+ * M x N output with K rows on a chip of num_cu compute units (<= 0: 256):
+ * one per 256 x 128 output tile when those fill whole rounds of two per CU
+ * (to within a tenth), else min(2 num_cu, 2 tiles) sharing the k-steps
+ * (stream-K). Host-only; -1 for M, N or K < 1.
+ */
+int q4_plan_gemm(int M, int N, int K, int num_cu);
 
 /*
  * q4_plan_gemv -- the skinny kernel's launch plan for (M, K, N, groupsize) on

@@ -113,8 +113,9 @@ def test_gemm_parity(K, N, G, M, act, bias, variant):
 
 
 def test_gemm_variants_bit_identical():
-    """Both GEMM variants accumulate each output over k in the same order with
-    the same MFMA shape, so their results must agree bit for bit."""
+    """The three GEMM variants, one workgroup per output tile, accumulate each
+    output over k in the same order with the same MFMA shape, so their
+    results must agree bit for bit."""
     import gptq_bit_weight_amd as q4
     torch = torch_mod()
     L = _layer(1024, 520, 128, 300, 21, bias=True)
@@ -123,7 +124,7 @@ def test_gemm_variants_bit_identical():
     W = make_matrix(L, t)
     a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=1)
     b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=2)
-    c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=3)
+    c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=3, splits=1)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
 
@@ -280,7 +281,9 @@ def test_m_zero_and_argument_errors():
     with pytest.raises(ValueError):
         W.matmul(t["x"], splits=17)
     with pytest.raises(ValueError):
-        W.matmul(t["x"], path=q4.PATH_MFMA, splits=3)
+        W.matmul(t["x"], path=q4.PATH_MFMA, splits=q4.GEMM_MAX_WORKERS + 1)
+    with pytest.raises(NotImplementedError):
+        W.matmul(t["x"], path=q4.PATH_MFMA, variant=1, splits=3)
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_MFMA, variant=4)
     with pytest.raises(ValueError):

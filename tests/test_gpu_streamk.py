@@ -1,0 +1,145 @@
+"""GPU parity of the streaming GEMM's stream-K schedule (needs an MI355X).
+
+The workgroups of a stream-K launch share the (output tile, 64-row k-step)
+iterations evenly, so a tile's K range can be split between two or more
+workgroups; the last to arrive adds the fp32 partial sums in k order. Every
+output must stay within the acceptance rule of tests/gpu_util against the
+oracle for any number of workgroups: fewer than the tiles, more, one per
+k-step (every tile split between all of its k-steps' workgroups) and more
+than there are iterations (reduced to one each). The reduction order depends only
+on the schedule, so a repeated call gives the same bits, and one workgroup
+per tile gives exactly the one-tile-per-workgroup result.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import (BF16_GEMM_REL_A, BF16_REL_Y, REL_A, REL_Y, announce, compare,
+                            device_tensors, make_matrix, oracle_full, to_float64, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gptq_bit_weight_amd as q4
+    q4.load_library()            # must load on a GPU machine: no fallback
+    yield
+
+
+def _layer(K, N, G, M, seed, **kw):
+    return synth.make_layer(K, N, G, M, seed=synth.layer_seed("streamk", K, N, G, M, seed), **kw)
+
+
+def _tiles(M, N):
+    return -(-M // 256) * -(-N // 128)
+
+
+SK_CASES = [
+    # K, N, G, M, act, bias, xfmt, bits, workgroup counts
+    # 10 tiles of 16 k-steps (160 iterations): 2..37 workgroups split tiles
+    # into 2..5 segments, 160 gives every k-step its own workgroup, and 200
+    # (more workgroups than iterations) is reduced to 160
+    (1024, 520, 128, 300, False, True, "f16", 4, (2, 3, 7, 10, 13, 20, 37, 160, 200)),
+    # groups of 32 and a K tail inside the last k-step: 4 tiles of 2 k-steps
+    (96, 136, 32, 300, False, False, "f16", 4, (3, 5, 8)),
+    # 8 row tiles: XCD-ordered spaces when the count divides by 8 (8, 16, 40, 96)
+    (256, 264, 128, 2048, False, True, "f16", 4, (8, 12, 16, 24, 40, 96)),
+    # act-order (permuted activations): 2 tiles of 16 k-steps
+    (1024, 256, 128, 256, True, True, "f16", 4, (3, 5)),
+    # bfloat16 activations and 8-bit weights
+    (512, 264, 128, 300, False, True, "bf16", 4, (5, 11)),
+    (512, 264, 64, 300, False, True, "f16", 8, (5, 11)),
+]
+
+
+@pytest.mark.parametrize("K,N,G,M,act,bias,xfmt,bits,workers", SK_CASES)
+def test_stream_k_parity(K, N, G, M, act, bias, xfmt, bits, workers):
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(K, N, G, M, 0, act_order=act, bias=bias, xfmt=xfmt, bits=bits)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    yD, A = oracle_full(L)
+    tol = (dict(rel_a=BF16_GEMM_REL_A, rel_y=BF16_REL_Y) if xfmt == "bf16"
+           else dict(rel_a=REL_A, rel_y=REL_Y))
+    announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} one-per-tile")
+    one = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=1)
+    torch.cuda.synchronize()
+    compare(to_float64(one), yD, A, f"one per tile K={K} N={N} M={M}", **tol)
+    for P in workers:
+        announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} workers={P}")
+        a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
+        b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
+        torch.cuda.synchronize()
+        compare(to_float64(a), yD, A, f"stream-k K={K} N={N} M={M} workers={P}", **tol)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"workers={P}: not repeatable"
+        if P == _tiles(M, N):
+            assert torch.equal(a.view(torch.int16), one.view(torch.int16)), \
+                f"workers={P}: one workgroup per tile should match splits=1"
+        iters = _tiles(M, N) * -(-K // 64)
+        if P > iters:
+            c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=iters)
+            torch.cuda.synchronize()
+            assert torch.equal(a.view(torch.int16), c.view(torch.int16)), \
+                f"workers={P} should run as {iters}"
+
+
+def test_stream_k_planned_matches_explicit():
+    """The planned schedule (splits=0) is the one q4_plan_gemm names."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(1024, 520, 128, 300, 1, bias=True)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    P = q4.plan_gemm(300, 520, 1024, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert P != _tiles(300, 520)
+    announce(f"stream-k planned workers={P}")
+    a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA)
+    b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stream_k_graph_replay():
+    """Captured stream-K launches replay with the eager result every time
+    (the arrival counters are reset by the kernel), with other eager calls on
+    the same handle in between; an explicit count whose workspace does not
+    exist yet is refused under capture instead of allocating."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    L = _layer(1024, 520, 128, 300, 2, bias=True)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    s = torch.cuda.Stream()
+    announce("stream-k graph eager reference")
+    with torch.cuda.stream(s):
+        ref = W.matmul(t["x"], t["bias"], splits=13, stream=s).clone()
+    s.synchronize()
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        W.matmul(t["x"], t["bias"], out=out, splits=13, stream=torch.cuda.current_stream())
+    for r in range(4):
+        announce(f"stream-k graph replay {r}")
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        W.matmul(t["x"], splits=7)
+        torch.cuda.synchronize()
+    # 2048 rows: 40 tiles of 16 k-steps, so 1024 workgroups run as 640, more
+    # than the stream's workspace was made for (2 x CUs)
+    announce("stream-k capture refusal")
+    x2 = torch.zeros((2048, 1024), dtype=torch.float16, device="cuda")
+    out2 = torch.empty((2048, 520), dtype=torch.float16, device="cuda")
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        with pytest.raises(ValueError, match="stream capture"):
+            W.matmul(x2, out=out2, splits=q4.GEMM_MAX_WORKERS, stream=torch.cuda.current_stream())
+    yD, A = oracle_full(L)
+    compare(out.cpu().numpy(), yD, A, "stream-k graph")
