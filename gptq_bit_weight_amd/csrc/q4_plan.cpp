@@ -139,16 +139,20 @@ bool gemv_gathers_x(int M, int K, int splits)
 // tiles: every CU at one; 688: a third round on a third of the chip).
 // Stream-K gives every workgroup the same number of (tile, k-tile)
 // iterations instead, at the price of fp32 partials for the tiles that
-// straddle two workgroups. It is planned when one-per-tile would waste more
-// than a tenth of the rounds; at most two workgroups per tile, so that a
-// split tile has two or three contributors.
+// straddle two workgroups (measured: 11-13 us a launch at 2048 rows) and of
+// more, shorter segments. It is planned below 1.5 rounds of tiles, when
+// one-per-tile would also waste more than a tenth of the rounds (256 tiles:
+// 735 -> 970 TFLOP/s; 688: 869 -> 913); from 1.5 rounds on, the lone
+// workgroups of a last half round run fast enough that stream-K measured
+// no better (768 tiles: equal; 1792: 1.5% slower). At most two workgroups
+// per tile, so that a split tile has two or three contributors.
 int plan_gemm_workers(int M, int N, int K, int num_cu)
 {
     if (num_cu <= 0) num_cu = 256;
     const long long tiles = gemm_tiles(M, N);
     const long long cap = 2LL * num_cu;
     const long long rounds = (tiles + cap - 1) / cap;
-    if (tiles * 10 >= rounds * cap * 9) return (int)tiles;
+    if (tiles * 10 >= rounds * cap * 9 || tiles * 2 >= cap * 3) return (int)tiles;
     const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
     long long w = std::min(cap, 2 * tiles);
     w = std::min(w, tiles * ktiles);

@@ -331,8 +331,9 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
  * q4_plan_gemm -- the streaming GEMM's planned workgroup count for an
  * M x N output with K rows on a chip of num_cu compute units (<= 0: 256):
  * one per 256 x 128 output tile when those fill whole rounds of two per CU
- * (to within a tenth), else min(2 num_cu, 2 tiles) sharing the k-steps
- * (stream-K). Host-only; -1 for M, N or K < 1.
+ * (to within a tenth) or make at least 1.5 such rounds, else
+ * min(2 num_cu, 2 tiles) sharing the k-steps (stream-K). Host-only; -1 for
+ * M, N or K < 1.
  */
 int q4_plan_gemm(int M, int N, int K, int num_cu);
 

@@ -147,21 +147,21 @@ def test_plan_gemv():
 
 def test_plan_gemm():
     """One workgroup per 256 x 128 output tile when the tiles fill whole
-    rounds of two per CU (to within a tenth); otherwise min(2 CUs, 2 tiles)
-    workgroups share the k-steps (stream-K), never more than there are
-    (tile, 64-row k-step) iterations."""
+    rounds of two per CU (to within a tenth) or make 1.5 rounds or more;
+    otherwise min(2 CUs, 2 tiles) workgroups share the k-steps (stream-K),
+    never more than there are (tile, 64-row k-step) iterations."""
     p = q4.plan_gemm
     assert p(2048, 4096, 11008, 256) == 512      # 256 tiles: every CU at one
     assert p(2048, 11008, 4096, 256) == 512      # 688 tiles: 1.34 rounds
-    assert p(2048, 12288, 4096, 256) == 512      # fused q/k/v: 768 tiles
+    assert p(2048, 12288, 4096, 256) == 768      # fused q/k/v: 768 tiles, 1.5 rounds
     assert p(4096, 4096, 4096, 256) == 512       # 512 tiles: one whole round
     assert p(16384, 28672, 8192, 256) == 14336   # 28 whole rounds
-    assert p(2048, 28672, 8192, 256) == 512      # 1792 tiles: 3.5 rounds
+    assert p(2048, 28672, 8192, 256) == 1792     # 3.5 rounds
     assert p(17, 4096, 4096, 256) == 64          # 32 tiles: two workgroups each
     assert p(300, 136, 96, 256) == 8             # 4 tiles of 2 k-steps: 8 iterations
     assert p(300, 136, 32, 256) == 4             # 4 tiles of 1 k-step: one each
     assert p(2048, 4096, 11008, 64) == 256       # a smaller chip: two whole rounds
-    assert p(2048, 11008, 4096, 64) == 128       # 688 tiles in 6 rounds of 128: 0.896
+    assert p(2048, 11008, 4096, 64) == 688       # 688 tiles: 5.4 rounds of 128
     for bad in ((0, 8, 32), (1, 0, 32), (1, 8, 0)):
         with pytest.raises(ValueError):
             p(*bad)
