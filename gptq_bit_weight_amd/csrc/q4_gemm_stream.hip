@@ -196,12 +196,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     int lane_cols[NJ];
 
     // Multiply k-tile kt: activations from `A`, weights from register set R.
+    // Software-pipelined over the four 16-row sub-steps: the weights of
+    // sub-step s + 1 are dequantized while the eight MFMAs of sub-step s run,
+    // and the scheduling groups below interleave those vector instructions
+    // with the MFMAs (the matrix pipe takes 32 cycles per MFMA, during which
+    // the wave can issue independent vector instructions) instead of leaving
+    // a burst of dequantization ahead of each sub-step's MFMAs.
     // With KT, sub-steps past K (zero activations) are skipped so that their
     // weights (code 0, any scale) add nothing.
     auto mma = [&](const char* A, const BRegs<NG, W8>& R, int kt) {
         zero_t hz[NG][NJ];
         h2 s2[NG][NJ];
-        mix_t mz[NJ];   // BF: the constants of the current group only (registers)
+        mix_t mz[NJ];   // BF: the constants of the group being dequantized (registers)
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
@@ -211,9 +217,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                     s2[gi][j] = scale_pair(R.s[gi][j]);
                 }
             }
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int sub = 0; sub < BK / 16; ++sub) {
+        // dequantize sub-step `sub` of this k-tile into b
+        auto deq = [&](int sub, u4 (&b)[NJ]) {
             const int gi = NG == 2 ? (sub >> 1) : 0;
             if constexpr (BF) {
                 if (sub % (4 / NG) == 0)
@@ -222,31 +227,51 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                         mz[j] = mix_consts((R.z[gi][j] >> c.z_shift[j]) & (W8 ? 0xFFu : 0xFu),
                                            f16_bits_to_f32((uint16_t)R.s[gi][j]));
             }
-            if (!KT || k0 + 16 * sub < p.K) {
-                u4 b[NJ];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    if constexpr (W8) {
-                        // sub-step s: words 2 (s / 2), 2 (s / 2) + 1 of the 16 bytes from chunk s % 2
-                        const uint32_t w0 = R.w[j][sub & 1][2 * (sub >> 1)], w1 = R.w[j][sub & 1][2 * (sub >> 1) + 1];
-                        if constexpr (BF) b[j] = bitcast<u4>(mix_word8(w0, w1, mz[j]));
-                        else b[j] = bitcast<u4>(dequant_word8(w0, w1, hz[gi][j], s2[gi][j]));
-                    } else {
-                        const uint32_t w = R.w[j][sub & 1][sub >> 1];
-                        if constexpr (BF) b[j] = bitcast<u4>(mix_word(w, mz[j]));
-                        else b[j] = bitcast<u4>(dequant_word(w, hz[gi][j], s2[gi][j]));
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const u4 a = *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        if constexpr (BF) acc[i][j] = mfma32(bitcast<b8>(a), bitcast<b8>(b[j]), acc[i][j]);
-                        else acc[i][j] = mfma32(bitcast<h8>(a), bitcast<h8>(b[j]), acc[i][j]);
-                    }
+            for (int j = 0; j < NJ; ++j) {
+                if constexpr (W8) {
+                    // sub-step s: words 2 (s / 2), 2 (s / 2) + 1 of the 16 bytes from chunk s % 2
+                    const uint32_t w0 = R.w[j][sub & 1][2 * (sub >> 1)], w1 = R.w[j][sub & 1][2 * (sub >> 1) + 1];
+                    if constexpr (BF) b[j] = bitcast<u4>(mix_word8(w0, w1, mz[j]));
+                    else b[j] = bitcast<u4>(dequant_word8(w0, w1, hz[gi][j], s2[gi][j]));
+                } else {
+                    const uint32_t w = R.w[j][sub & 1][sub >> 1];
+                    if constexpr (BF) b[j] = bitcast<u4>(mix_word(w, mz[j]));
+                    else b[j] = bitcast<u4>(dequant_word(w, hz[gi][j], s2[gi][j]));
                 }
             }
+        };
+        const int k0 = kt * BK;
+        u4 bc[NJ], bn[NJ];
+        deq(0, bc);
+#pragma unroll
+        for (int sub = 0; sub < BK / 16; ++sub) {
+            u4 a[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                a[i] = *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
+            if (sub + 1 < BK / 16) deq(sub + 1, bn);
+            if (!KT || k0 + 16 * sub < p.K) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        if constexpr (BF) acc[i][j] = mfma32(bitcast<b8>(a[i]), bitcast<b8>(bc[j]), acc[i][j]);
+                        else acc[i][j] = mfma32(bitcast<h8>(a[i]), bitcast<h8>(bc[j]), acc[i][j]);
+                    }
+            }
+            if (sub + 1 < BK / 16) {
+                // the sub-step's activation reads, then each MFMA followed
+                // by up to three vector instructions of the next dequantization
+                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+#pragma unroll
+                for (int q = 0; q < MI * NJ; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) bc[j] = bn[j];
         }
     };
 
