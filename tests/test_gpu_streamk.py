@@ -53,6 +53,9 @@ SK_CASES = [
     # bfloat16 activations and 8-bit weights
     (512, 264, 128, 300, False, True, "bf16", 4, (5, 11)),
     (512, 264, 64, 300, False, True, "f16", 8, (5, 11)),
+    # groups of 32 and a K tail with bfloat16, and with 8-bit weights
+    (480, 136, 32, 260, False, True, "bf16", 4, (3, 7)),
+    (480, 136, 32, 260, True, True, "f16", 8, (3, 7)),
 ]
 
 
