@@ -276,10 +276,23 @@ q4_status sk_workspace(int device, int num_cu, hipStream_t stream, int workers, 
     return Q4_OK;
 }
 
+// The handle's buffers live on the device it was made on, which must be
+// the current one (kernels run on the current device).
+q4_status check_current(const q4_matrix* h, const char* who)
+{
+    int cur = -1;
+    Q4_HIP(hipGetDevice(&cur), "hipGetDevice");
+    if (cur != h->device)
+        return fail(Q4_ERR_INVALID_ARG, "%s: the handle was made on device %d, the current device is %d", who,
+                    h->device, cur);
+    return Q4_OK;
+}
+
 q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                       int M, int path, int variant, int splits, bool bf16, hipStream_t stream)
 {
     if (!h) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: null handle");
+    if (q4_status st = check_current(h, "q4_matmul"); st != Q4_OK) return st;
     if (M < 0) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: M=%d is negative", M);
     if (M == 0) return Q4_OK;
     if (!x || !out) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: x and out must be non-null");
@@ -491,6 +504,7 @@ static q4_status dump_impl(const q4_matrix* h, int path, uint16_t* w, bool bf16,
                            const char* who)
 {
     if (!h || !w) return q4::fail(Q4_ERR_INVALID_ARG, "%s: null argument", who);
+    if (q4_status st = q4::check_current(h, who); st != Q4_OK) return st;
     if (path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
         return q4::fail(Q4_ERR_INVALID_ARG, "%s: unknown path %d", who, path);
     hipError_t e = q4::launch_dump(h, path, w, bf16, stream);

@@ -14,7 +14,10 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers passed to q4_make / q4_matmul* / q4_dequant_dump are
- *    DEVICE pointers on the current HIP device, to dense row-major data.
+ *    DEVICE pointers on the current HIP device, to dense row-major data. A
+ *    handle is used on the device it was made on: q4_matmul* and
+ *    q4_dequant_dump return Q4_ERR_INVALID_ARG when another device is
+ *    current.
  *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *  - A failing call returns NULL or a non-zero q4_status, enqueues nothing and
  *    leaves every output untouched; q4_last_error() then holds the reason
