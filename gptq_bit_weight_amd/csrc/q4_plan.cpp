@@ -90,7 +90,15 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 //    columns, which pays more the more rows M has (the activation loads grow
 //    with M); gain(ct, M) below is that benefit as measured on MI355X over
 //    the Llama-7B/70B layer shapes. The plan takes the widest tile with the
-//    best balance x gain.
+//    best balance x gain. For M > 4 the balance counts the K splits that
+//    tile width would get while every wave keeps at least 4 k-blocks: a
+//    narrow layer then takes wide tiles split in K rather than narrow ones
+//    unsplit (M = 16: 28672x8192 35.1 -> 27.9 us with 4 tiles x 2 splits,
+//    11008x4096 14.1 -> 11.2 us with 2 x 2). For M <= 4 the partial round
+//    trip of a split costs more than the reuse gains (28672x8192, M = 1:
+//    2 tiles unsplit 21.4 us, 4 tiles x 2 splits 23.4 us), and with fewer
+//    blocks per wave it costs more than the balance gains (4096x4096, M = 8:
+//    5.0 us unsplit, 6.5 us with 2 x 2).
 //  * splits: K ranges across workgroups, only when the column tiles alone
 //    cannot give every CU a workgroup, and only while every wave of every
 //    split keeps a k-block. Each split adds a round of fp32 partials and a
@@ -105,23 +113,28 @@ void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* spli
     // blocks are twice the words; four tiles of either do not fit the
     // register file)
     const int max_ct = (G == 32 || bits == 8) ? 2 : kMaxColTiles;
+    const int kb = num_kblocks(K);
+    // K splits for `tiles` column tiles keeping >= min_blocks k-blocks a wave
+    auto splits_for = [&](long long tiles, int min_blocks) {
+        int s = 1;
+        while (2 * s <= kMaxSplits && tiles * 2 * s <= num_cu && kb >= 2 * s * kGemvWaves * min_blocks) s *= 2;
+        return s;
+    };
     int ct = 1;
     long long best = -1;
     for (int c = 1, ci = 0; c <= max_ct; c *= 2, ++ci) {
         const long long tiles = (N + 16 * c - 1) / (16 * c);
         const long long rounds = (tiles + num_cu - 1) / num_cu;
-        const long long score = tiles * 1000 * gain[mi][ci] / (rounds * num_cu);
+        const long long s = M > 4 ? splits_for(tiles, 4) : 1;
+        const long long score = tiles * s * 1000 * gain[mi][ci] / (rounds * num_cu);
         if (score >= best) {
             best = score;
             ct = c;
         }
     }
     const int tiles = (N + 16 * ct - 1) / (16 * ct);
-    const int kb = num_kblocks(K);
-    int s = 1;
-    while (2 * s <= kMaxSplits && tiles * 2 * s <= num_cu && kb >= 2 * s * kGemvWaves) s *= 2;
     *col_tiles = ct;
-    *splits = s;
+    *splits = splits_for(tiles, 1);
 }
 
 bool gemv_gathers_x(int M, int K, int splits)

@@ -136,6 +136,13 @@ def test_plan_gemv():
     assert q4.plan_gemv(1, 8192, 28672, 128, num_cu=256) == (4, 1)
     assert q4.plan_gemv(16, 8192, 28672, 32, num_cu=256)[0] == 2        # groups of 32: at most 2
     assert q4.plan_gemv(1, 4096, 1024, 128, num_cu=256) == (1, 4)       # 64 tiles, 32 blocks
+    # M > 4 on narrow layers: wide tiles split in K while waves keep 4 blocks
+    assert q4.plan_gemv(16, 28672, 8192, 128, num_cu=256) == (4, 2)
+    assert q4.plan_gemv(8, 28672, 8192, 128, num_cu=256) == (4, 2)
+    assert q4.plan_gemv(16, 11008, 4096, 128, num_cu=256) == (2, 2)
+    assert q4.plan_gemv(8, 11008, 4096, 128, num_cu=256) == (2, 2)
+    assert q4.plan_gemv(8, 4096, 4096, 128, num_cu=256) == (1, 1)       # 32 blocks: no split
+    assert q4.plan_gemv(4, 28672, 8192, 128, num_cu=256) == (2, 1)      # M <= 4: splits cost more
     assert q4.plan_gemv(1, 512, 512, 128, num_cu=256) == (1, 1)         # 4 blocks: too few to split
     with pytest.raises(ValueError):
         q4.plan_gemv(0, 4096, 4096, 128)
