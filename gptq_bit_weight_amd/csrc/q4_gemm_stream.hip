@@ -1,9 +1,10 @@
 // Prefill fused GPTQ GEMM (M > 16) on the matrix cores: activations staged
 // in LDS, weights streamed into registers.
 //
-// q4_gemm_stream_kernel<NG, KT, BF, W8>: NG groups per 64-row k-tile (2 for
-// groups of 32), KT (K not a multiple of 64), BF (bfloat16 activations and
-// output), W8 (8-bit codes).
+// q4_gemm_stream_kernel<BM, NG, KT, BF, W8>: BM rows per output tile (256,
+// or 64 when M <= 64), NG groups per 64-row k-tile (2 for groups of 32), KT
+// (K not a multiple of 64), BF (bfloat16 activations and output), W8 (8-bit
+// codes).
 //
 // The multiply runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation
 // (GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row: FP32
@@ -44,17 +45,25 @@ namespace {
 
 using namespace q4dev;
 
-constexpr int BM = q4::kGemmBM;      // 256
 constexpr int BN = q4::kGemmBN;      // 128
 constexpr int BK = q4::kGemmBK;      // 64
 constexpr int NT = q4::kGemmThreads; // 256
-constexpr int WTM = BM / 2;          // wave tile rows
 constexpr int WTN = BN / 2;          // wave tile columns
-constexpr int MI = WTM / 32;
 constexpr int NJ = WTN / 32;
-constexpr int A_TILE_BYTES = BM * BK * 2;          // 32 KiB
-constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);  // 8 direct loads per thread
 static_assert(BK == 64 && BN == 128 && NT == 256 && NJ == 2, "index arithmetic below assumes these");
+
+// Geometry that depends on the tile height BM (256, or 64 for few rows): a
+// 2 x 2 grid of waves, each WTM x WTN (MI x NJ MFMA tiles of 32 x 32); the
+// activation stage is BM x BK halfs, filled by A_LOADS 16-byte direct loads
+// per thread (8 at BM = 256: 32 KiB a stage; 2 at BM = 64: 8 KiB).
+template <int BM>
+struct Geo {
+    static constexpr int WTM = BM / 2;
+    static constexpr int MI = WTM / 32;
+    static constexpr int A_TILE_BYTES = BM * BK * 2;
+    static constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);
+    static_assert(MI >= 1 && A_LOADS >= 1 && A_TILE_BYTES == A_LOADS * NT * 16, "tile height");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -100,10 +109,12 @@ struct BRegs {
     uint32_t z[NG][NJ];
 };
 
+constexpr int kMaxALoads = Geo<256>::A_LOADS;
 struct Ctx {
     rsrc_t rx, rw, rs, rz;
-    uint32_t a_off[A_LOADS];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
-    uint32_t a_k[A_LOADS];     // k of each chunk for k0 = 0
+    // (the first A_LOADS entries are used)
+    uint32_t a_off[kMaxALoads];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
+    uint32_t a_k[kMaxALoads];     // k of each chunk for k0 = 0
     uint32_t w_off[NJ][2];     // weight byte offsets of the two chunks per column (k-tile 0)
     uint32_t s_off[NJ];        // scale byte offsets (group 0)
     uint32_t z_off[NJ];        // zero-word byte offsets (group 0)
@@ -113,7 +124,7 @@ struct Ctx {
 // The k offset of the tile is wave-uniform (a scalar register); rows past M
 // lie past the end of x through the per-lane offset alone. Only with KT can a
 // chunk lie past K (in the last tile); its lanes are pushed out of range.
-template <bool KT>
+template <bool KT, int A_LOADS>
 __device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* stage, int wave, int kt)
 {
     const uint32_t k0 = (uint32_t)kt * BK;
@@ -153,9 +164,11 @@ __device__ __forceinline__ void load_b(BRegs<NG, W8>& R, const Ctx& c, const Gem
 // K (a separate instantiation, so that the common kernel has no branch
 // around the multiply: the accumulators stay in the same registers).
 // (Two workgroups per CU: the register budget is 256 per lane.)
-template <int NG, bool KT, bool BF, bool W8>
+template <int BM, int NG, bool KT, bool BF, bool W8>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_stream_kernel(GemmArgs p)
 {
+    constexpr int WTM = Geo<BM>::WTM, MI = Geo<BM>::MI;
+    constexpr int A_TILE_BYTES = Geo<BM>::A_TILE_BYTES, A_LOADS = Geo<BM>::A_LOADS;
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
     __shared__ int s_last;
@@ -289,7 +302,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         Q4S_VMCNT(0);
         lds_barrier();
         const int kn = min(kt + 1, seg_end - 1);
-        load_a<KT>(c, p, nxt, wave, kn);
+        load_a<KT, A_LOADS>(c, p, nxt, wave, kn);
         load_b(Rn, c, p, kn);
         mma(cur, Rc, kt);
     };
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         // before they are refilled.
         if (!first_seg) lds_barrier();
         first_seg = false;
-        load_a<KT>(c, p, lds_a0, wave, kb);
+        load_a<KT, A_LOADS>(c, p, lds_a0, wave, kb);
         load_b(R0, c, p, kb);
         int kt = kb;
         for (; kt + 1 < ke; kt += 2) {
@@ -403,23 +416,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 __syncthreads();
                 if (!s_last) continue;
             }
-            // Ordered sum, 32 values per lane at a time.
+            // Ordered sum, 32 values per lane at a time: p_wf + ... + p_wl,
+            // this worker's own sums taken from its registers.
+            auto load32 = [&](float (&v)[32], int r, int q) {
+                const float* src = slot_of(r) + (size_t)q * 16 * NT + tid;
+#pragma unroll
+                for (int e = 0; e < 32; ++e)
+                    v[e] = __hip_atomic_load(&src[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
 #pragma unroll
             for (int q = 0; q < MI * NJ; q += 2) {
 #define Q4S_ACC(e) acc[(q + (e) / 16) / NJ][(q + (e) / 16) % NJ][(e) % 16]
                 if (rk > wf) {
                     // p_wf + ... + p_(rk-1), then + this worker's sums
                     float t[32];
-                    const float* src = slot_of(wf) + (size_t)q * 16 * NT + tid;
-#pragma unroll
-                    for (int e = 0; e < 32; ++e)
-                        t[e] = __hip_atomic_load(&src[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    load32(t, wf, q);
                     for (int r = wf + 1; r < rk; ++r) {
-                        const float* sr = slot_of(r) + (size_t)q * 16 * NT + tid;
                         float v[32];
-#pragma unroll
-                        for (int e = 0; e < 32; ++e)
-                            v[e] = __hip_atomic_load(&sr[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        load32(v, r, q);
 #pragma unroll
                         for (int e = 0; e < 32; ++e) t[e] += v[e];
                     }
@@ -427,11 +441,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                     for (int e = 0; e < 32; ++e) Q4S_ACC(e) = t[e] + Q4S_ACC(e);
                 }
                 for (int r = rk + 1; r <= wl; ++r) {
-                    const float* sr = slot_of(r) + (size_t)q * 16 * NT + tid;
                     float v[32];
-#pragma unroll
-                    for (int e = 0; e < 32; ++e)
-                        v[e] = __hip_atomic_load(&sr[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    load32(v, r, q);
 #pragma unroll
                     for (int e = 0; e < 32; ++e) Q4S_ACC(e) += v[e];
                 }
@@ -458,18 +469,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     }
 }
 
-template <bool BF, bool W8>
+template <int BM, bool BF, bool W8>
 hipError_t launch_stream(const GemmArgs& p, int grid, bool g32, bool kt, hipStream_t stream)
 {
     if (g32 && kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 2, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else if (g32)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<2, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 2, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else if (kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 1, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<1, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 1, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int BM>
+hipError_t launch_bm(const GemmArgs& p, int grid, bool g32, bool kt, bool bf16, bool w8, hipStream_t stream)
+{
+    if (w8)
+        return bf16 ? launch_stream<BM, true, true>(p, grid, g32, kt, stream)
+                    : launch_stream<BM, false, true>(p, grid, g32, kt, stream);
+    return bf16 ? launch_stream<BM, true, false>(p, grid, g32, kt, stream)
+                : launch_stream<BM, false, false>(p, grid, g32, kt, stream);
 }
 
 }  // namespace
@@ -494,18 +515,16 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     p.partials = partials;
     p.counters = counters;
     p.workers = workers;
+    // tile height: 64 rows when that covers M (few rows), else 256
+    const int bm = gemm_bm(M);
     // XCD spaces need whole row tiles and workers per XCD
-    p.xcd = ((M + BM - 1) / BM) % 8 == 0 && workers % 8 == 0;
-    const int tiles = workers;
+    p.xcd = ((M + bm - 1) / bm) % 8 == 0 && workers % 8 == 0;
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;
     p.zrow = h->N * h->bits / 8;
-    if (h->bits == 8)
-        return bf16 ? launch_stream<true, true>(p, tiles, g32, kt, stream)
-                    : launch_stream<false, true>(p, tiles, g32, kt, stream);
-    return bf16 ? launch_stream<true, false>(p, tiles, g32, kt, stream)
-                : launch_stream<false, false>(p, tiles, g32, kt, stream);
+    return bm == 64 ? launch_bm<64>(p, workers, g32, kt, bf16, h->bits == 8, stream)
+                    : launch_bm<kGemmBM>(p, workers, g32, kt, bf16, h->bits == 8, stream);
 }
 
 }  // namespace q4

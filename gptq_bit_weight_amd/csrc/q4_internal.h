@@ -55,7 +55,16 @@ constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 256;
-inline int gemm_tiles(int M, int N) { return ((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN); }
+// The streaming GEMM takes 64-row output tiles when M <= kGemmSmallM (few
+// rows: a 256-row tile would leave most CUs idle and multiply padding), else
+// 256-row tiles.
+constexpr int kGemmSmallM = 64;
+inline int gemm_bm(int M) { return M <= kGemmSmallM ? 64 : kGemmBM; }
+inline int gemm_tiles(int M, int N)
+{
+    const int bm = gemm_bm(M);
+    return ((M + bm - 1) / bm) * ((N + kGemmBN - 1) / kGemmBN);
+}
 
 // Error reporting (thread-local status + message).
 q4_status fail(q4_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -144,21 +144,28 @@ bool gemv_gathers_x(int M, int K, int splits)
            (long long)M * (rows + kGemvXPad) <= kGemvXLdsHalfs;
 }
 
-// Streaming-GEMM schedule. Two workgroups share a CU (64 KiB of LDS and
-// 256 VGPRs each), and a CU that holds only one runs a tile at about 0.7
-// times the rate of two (one wave per SIMD leaves the matrix pipe idle while
-// that wave dequantizes). With one workgroup per output tile, tile counts
-// that are not whole rounds of 2 x CUs leave CUs idle or half-used (256
-// tiles: every CU at one; 688: a third round on a third of the chip).
-// Stream-K gives every workgroup the same number of (tile, k-tile)
-// iterations instead, at the price of fp32 partials for the tiles that
-// straddle two workgroups (measured: 11-13 us a launch at 2048 rows) and of
-// more, shorter segments. It is planned below 1.5 rounds of tiles, when
-// one-per-tile would also waste more than a tenth of the rounds (256 tiles:
-// 735 -> 970 TFLOP/s; 688: 869 -> 913); from 1.5 rounds on, the lone
-// workgroups of a last half round run fast enough that stream-K measured
-// no better (768 tiles: equal; 1792: 1.5% slower). At most two workgroups
-// per tile, so that a split tile has two or three contributors.
+// Streaming-GEMM schedule. Two 256-row workgroups share a CU (64 KiB of LDS
+// and about 240 VGPRs each), and a CU that holds only one runs a tile at
+// about 0.7 times the rate of two (one wave per SIMD leaves the matrix pipe
+// idle while that wave dequantizes). With one workgroup per output tile,
+// tile counts that are not whole rounds of 2 x CUs leave CUs idle or
+// half-used (256 tiles: every CU at one; 688: a third round on a third of
+// the chip). Stream-K gives every workgroup the same number of (tile,
+// k-tile) iterations instead, at the price of fp32 partials for the tiles
+// that straddle two workgroups (measured: 11-13 us a launch at 2048 rows)
+// and of more, shorter segments. It is planned below 1.5 rounds of tiles,
+// when one-per-tile would also waste more than a tenth of the rounds (256
+// tiles: 735 -> 970 TFLOP/s; 688: 869 -> 913); from 1.5 rounds on, the lone
+// workgroups of a last half round run fast enough that stream-K measured no
+// better (768 tiles: equal; 1792: 1.5% slower).
+//  * 256-row tiles: 2 x tiles workgroups (a split tile has two or three
+//    contributors), but at least one per CU: with few rows the tiles are
+//    few (11008x4096 at M <= 256: 32), and 64 workgroups left three CUs in
+//    four idle (97 us against 54 us with 256).
+//  * 64-row tiles (M <= 64): few rows make the product bound by the weight
+//    stream, and 2 x CUs workgroups measured best on every 7B and 70B
+//    shape (4096x11008: 29.5 us against 33.5 at 256 and 38 at 1024;
+//    28672x8192: 77 us against 114 at 256); their partials are 32 KiB.
 int plan_gemm_workers(int M, int N, int K, int num_cu)
 {
     if (num_cu <= 0) num_cu = 256;
@@ -167,7 +174,7 @@ int plan_gemm_workers(int M, int N, int K, int num_cu)
     const long long rounds = (tiles + cap - 1) / cap;
     if (tiles * 10 >= rounds * cap * 9 || tiles * 2 >= cap * 3) return (int)tiles;
     const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
-    long long w = std::min(cap, 2 * tiles);
+    long long w = gemm_bm(M) == 64 ? cap : std::min(cap, std::max<long long>(2 * tiles, num_cu));
     w = std::min(w, tiles * ktiles);
     return (int)std::min<long long>(w, Q4_GEMM_MAX_WORKERS);
 }
