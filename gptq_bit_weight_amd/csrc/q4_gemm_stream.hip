@@ -2,7 +2,7 @@
 // in LDS, weights streamed into registers.
 //
 // q4_gemm_stream_kernel<BM, NG, KT, BF, W8>: BM rows per output tile (256,
-// or 64 when M <= 64), NG groups per 64-row k-tile (2 for groups of 32), KT
+// or 64 when M <= 256), NG groups per 64-row k-tile (2 for groups of 32), KT
 // (K not a multiple of 64), BF (bfloat16 activations and output), W8 (8-bit
 // codes).
 //
@@ -169,8 +169,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 {
     constexpr int WTM = Geo<BM>::WTM, MI = Geo<BM>::MI;
     constexpr int A_TILE_BYTES = Geo<BM>::A_TILE_BYTES, A_LOADS = Geo<BM>::A_LOADS;
+    // Ring depth: activation stages in LDS and weight register sets, both
+    // D - 1 k-tiles ahead. 64-row tiles (few rows) are bound by the weight
+    // stream, so they keep two tiles in flight; 256-row tiles one.
+    constexpr int D = BM == 64 ? 3 : 2;
+    // vector-memory loads one step issues per thread (activation DMA, packed
+    // weights, scale and zero words)
+    constexpr int LPS = A_LOADS + 2 * NJ + 2 * NG * NJ;
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_a2[A_TILE_BYTES];   // (D = 3 only)
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)p.zrow);
 
     f16x acc[MI][NJ];
-    BRegs<NG, W8> R0, R1;
+    BRegs<NG, W8> R[D];
     int m0 = 0, seg_end = 0;
     int lane_cols[NJ];
 
@@ -288,23 +296,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         }
     };
 
-    // One k-tile on stage S with register set Rc, prefetching tile kt + 1
-    // (clamped: past the segment's end it reloads its last tile, into
-    // buffers nobody reads again) into the other stage and set Rn.
-    auto step = [&](auto S_tag, int kt, BRegs<NG, W8>& Rc, BRegs<NG, W8>& Rn) {
+    auto stage = [&](int st) -> char* { return st == 0 ? lds_a0 : st == 1 ? lds_a1 : lds_a2; };
+
+    // One k-tile on stage and register set S = (kt - segment start) % D,
+    // prefetching tile kt + D - 1 (clamped: past the segment's end it
+    // reloads its last tile, into buffers nobody reads again) into the stage
+    // and set tile kt - 1 has just finished with.
+    auto step = [&](auto S_tag, int kt) {
         constexpr int S = decltype(S_tag)::value;
-        char* cur = S == 0 ? lds_a0 : lds_a1;
-        char* nxt = S == 0 ? lds_a1 : lds_a0;
-        // Tile kt's activations and weight registers, the only loads in
-        // flight, must have landed (the activations in every thread's part of
-        // the stage). The wait names no count, so it holds whatever order the
-        // compiler issued the two kinds of loads in.
-        Q4S_VMCNT(0);
+        constexpr int SN = (S + D - 1) % D;
+        // Tile kt's activations and weight registers must have landed (the
+        // activations in every thread's part of the stage). The D - 2 steps
+        // since its loads each issued LPS loads, and scheduling barriers keep
+        // every step's loads inside that step, so the count holds whatever
+        // order a step issues its own loads in (D = 2: no count at all).
+        Q4S_VMCNT((D - 2) * LPS);
         lds_barrier();
-        const int kn = min(kt + 1, seg_end - 1);
-        load_a<KT, A_LOADS>(c, p, nxt, wave, kn);
-        load_b(Rn, c, p, kn);
-        mma(cur, Rc, kt);
+        const int kn = min(kt + D - 1, seg_end - 1);
+        if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
+        load_a<KT, A_LOADS>(c, p, stage(SN), wave, kn);
+        load_b(R[SN], c, p, kn);
+        // (with D = 2 the wait above counts nothing, and leaving the loads
+        // free to move measured 1-2% faster)
+        if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
+        mma(stage(S), R[S], kt);
     };
 
     // The range [a, b) is the tail of a split tile [a, lo), whole tiles
@@ -364,14 +379,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         // before they are refilled.
         if (!first_seg) lds_barrier();
         first_seg = false;
-        load_a<KT, A_LOADS>(c, p, lds_a0, wave, kb);
-        load_b(R0, c, p, kb);
-        int kt = kb;
-        for (; kt + 1 < ke; kt += 2) {
-            step(std::integral_constant<int, 0>{}, kt, R0, R1);
-            step(std::integral_constant<int, 1>{}, kt + 1, R1, R0);
+#pragma unroll
+        for (int d = 0; d + 1 < D; ++d) {
+            const int kd = min(kb + d, ke - 1);
+            load_a<KT, A_LOADS>(c, p, stage(d), wave, kd);
+            load_b(R[d], c, p, kd);
+            if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt < ke) step(std::integral_constant<int, 0>{}, kt, R0, R1);
+        int kt = kb;
+        for (; kt + D - 1 < ke; kt += D) {
+            step(std::integral_constant<int, 0>{}, kt);
+            step(std::integral_constant<int, 1>{}, kt + 1);
+            if constexpr (D == 3) step(std::integral_constant<int, D - 1>{}, kt + 2);
+        }
+        if (kt < ke) step(std::integral_constant<int, 0>{}, kt);
+        if constexpr (D == 3)
+            if (kt + 1 < ke) step(std::integral_constant<int, 1>{}, kt + 1);
         // Drain the last (unused) prefetch before the LDS is reused.
         Q4S_VMCNT(0);
 

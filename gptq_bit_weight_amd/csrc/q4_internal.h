@@ -56,9 +56,10 @@ constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 256;
 // The streaming GEMM takes 64-row output tiles when M <= kGemmSmallM (few
-// rows: a 256-row tile would leave most CUs idle and multiply padding), else
-// 256-row tiles.
-constexpr int kGemmSmallM = 64;
+// rows: 256-row tiles leave most CUs idle and multiply padding; measured on
+// the 7B MLP shapes, 64-row tiles are faster up to M = 256, even at 384 and
+// slower from 512 on), else 256-row tiles.
+constexpr int kGemmSmallM = 256;
 inline int gemm_bm(int M) { return M <= kGemmSmallM ? 64 : kGemmBM; }
 inline int gemm_tiles(int M, int N)
 {

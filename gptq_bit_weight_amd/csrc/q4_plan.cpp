@@ -160,12 +160,15 @@ bool gemv_gathers_x(int M, int K, int splits)
 // better (768 tiles: equal; 1792: 1.5% slower).
 //  * 256-row tiles: 2 x tiles workgroups (a split tile has two or three
 //    contributors), but at least one per CU: with few rows the tiles are
-//    few (11008x4096 at M <= 256: 32), and 64 workgroups left three CUs in
-//    four idle (97 us against 54 us with 256).
-//  * 64-row tiles (M <= 64): few rows make the product bound by the weight
-//    stream, and 2 x CUs workgroups measured best on every 7B and 70B
-//    shape (4096x11008: 29.5 us against 33.5 at 256 and 38 at 1024;
-//    28672x8192: 77 us against 114 at 256); their partials are 32 KiB.
+//    few (11008x4096 at M = 257 .. 512: 64), and too few workgroups leave
+//    CUs idle (at M <= 256, before the 64-row tiles: 97 us with 64
+//    workgroups against 54 us with 256).
+//  * 64-row tiles (M <= 256): few rows make the product bound by the weight
+//    stream (their kernel keeps two k-tiles in flight). About 24 k-tiles a
+//    workgroup measured best, between one and two workgroups per CU: the 7B
+//    MLP shapes (5504 iterations) 22-24 us at 256 workgroups against
+//    25-30 us at 512; the 70B ones (28672) 58-62 us at 512 against 63-70 us
+//    at 256 or 1024. Their partials are 32 KiB.
 int plan_gemm_workers(int M, int N, int K, int num_cu)
 {
     if (num_cu <= 0) num_cu = 256;
@@ -174,8 +177,10 @@ int plan_gemm_workers(int M, int N, int K, int num_cu)
     const long long rounds = (tiles + cap - 1) / cap;
     if (tiles * 10 >= rounds * cap * 9 || tiles * 2 >= cap * 3) return (int)tiles;
     const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
-    long long w = gemm_bm(M) == 64 ? cap : std::min(cap, std::max<long long>(2 * tiles, num_cu));
-    w = std::min(w, tiles * ktiles);
+    const long long iters = tiles * ktiles;
+    long long w = gemm_bm(M) < kGemmBM ? std::min(cap, std::max<long long>(num_cu, iters / 24))
+                                   : std::min(cap, std::max<long long>(2 * tiles, num_cu));
+    w = std::min(w, iters);
     return (int)std::min<long long>(w, Q4_GEMM_MAX_WORKERS);
 }
 

@@ -11,7 +11,7 @@ at M = 1 (q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096, bias on
 q), its act-order variant (4096x11008 and 11008x4096, M in {1, 4}), the
 Llama-70B-shaped MLP (8192x28672 and 28672x8192, M in {1, 2, 4, 8, 16}),
 prefill at M = 2048 (4096x11008 and 11008x4096, groupsize 128 and 32, plus
-act-order) and small batches past the skinny kernel (M in {17, 64, 200}).
+act-order) and small batches past the skinny kernel (M in {17, 64, 200, 400}).
 """
 import numpy as np
 import pytest
@@ -85,9 +85,9 @@ def test_prefill(K, N, G, act):
 
 
 @pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (28672, 8192)])
-@pytest.mark.parametrize("M", [17, 64, 200])
+@pytest.mark.parametrize("M", [17, 64, 200, 400])
 def test_small_batch_gemm(K, N, M):
-    """Batches just past the skinny kernel's 16 rows: 64-row output tiles
-    (M <= 64) or few 256-row tiles, both with stream-K across the CUs."""
+    """Batches past the skinny kernel's 16 rows: 64-row output tiles
+    (M <= 256), with stream-K across the CUs; and 400 rows: two 256-row tiles."""
     L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("small_batch", K, N, M), bias=True)
     _check_layer(L, f"small batch {K}x{N}")

@@ -35,7 +35,7 @@ def _layer(K, N, G, M, seed, **kw):
 
 
 def _tiles(M, N):
-    bm = 64 if M <= 64 else 256      # the tile height the library takes for M rows
+    bm = 64 if M <= 256 else 256     # the tile height the library takes for M rows
     return -(-M // bm) * -(-N // 128)
 
 
@@ -57,7 +57,7 @@ SK_CASES = [
     # groups of 32 and a K tail with bfloat16, and with 8-bit weights
     (480, 136, 32, 260, False, True, "bf16", 4, (3, 7)),
     (480, 136, 32, 260, True, True, "f16", 8, (3, 7)),
-    # 64-row tiles (M <= 64): 5 tiles of 16 k-steps; 80 = one k-step each
+    # 64-row tiles (M <= 256): 5 tiles of 16 k-steps; 80 = one k-step each
     (1024, 520, 128, 40, False, True, "f16", 4, (2, 5, 9, 40, 80, 100)),
     (1024, 520, 128, 64, True, True, "f16", 4, (3, 13)),
     (480, 136, 32, 17, False, True, "bf16", 4, (3, 7)),

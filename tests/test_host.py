@@ -153,12 +153,12 @@ def test_plan_gemv():
 
 
 def test_plan_gemm():
-    """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 64)
+    """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 256)
     when the tiles fill whole rounds of two per CU (to within a tenth) or make
     1.5 rounds or more; otherwise the workgroups share the k-steps
-    (stream-K): 2 x CUs of them for 64-row tiles, min(2 CUs, max(2 tiles,
-    CUs)) for 256-row ones, never more than there are (tile, 64-row k-step)
-    iterations."""
+    (stream-K): about 24 k-steps each between CUs and 2 x CUs workgroups for
+    64-row tiles, min(2 CUs, max(2 tiles, CUs)) for 256-row ones, never more
+    than there are (tile, 64-row k-step) iterations."""
     p = q4.plan_gemm
     assert p(2048, 4096, 11008, 256) == 512      # 256 tiles: every CU at one
     assert p(2048, 11008, 4096, 256) == 512      # 688 tiles: 1.34 rounds
@@ -166,10 +166,14 @@ def test_plan_gemm():
     assert p(4096, 4096, 4096, 256) == 512       # 512 tiles: one whole round
     assert p(16384, 28672, 8192, 256) == 14336   # 28 whole rounds
     assert p(2048, 28672, 8192, 256) == 1792     # 3.5 rounds
-    assert p(17, 4096, 4096, 256) == 512         # 64-row tiles: 2 x CUs workgroups
-    assert p(64, 4096, 11008, 256) == 512
-    assert p(128, 11008, 4096, 256) == 256       # 86 tiles of 256 rows: one workgroup per CU
-    assert p(256, 4096, 11008, 256) == 256       # 32 tiles: at least one per CU
+    assert p(17, 4096, 4096, 256) == 256         # 64-row tiles: about 24 k-tiles a workgroup,
+    assert p(64, 4096, 11008, 256) == 256        # between CUs and 2 x CUs workgroups
+    assert p(32, 28672, 8192, 256) == 512
+    assert p(64, 11008, 4096, 256) == 256
+    assert p(128, 11008, 4096, 256) == 458       # 2 x 86 tiles of 64 rows x 64 k-steps / 24
+    assert p(256, 4096, 11008, 256) == 512       # 4 x 32 tiles x 172 k-steps: at most 2 x CUs
+    assert p(300, 11008, 4096, 256) == 344       # 2 x 86 tiles of 256 rows: 2 x tiles
+    assert p(512, 4096, 11008, 256) == 256       # 2 x 32 tiles of 256 rows: at least one per CU
     assert p(300, 136, 96, 256) == 8             # 4 tiles of 2 k-steps: 8 iterations
     assert p(300, 136, 32, 256) == 4             # 4 tiles of 1 k-step: one each
     assert p(2048, 4096, 11008, 64) == 256       # a smaller chip: two whole rounds
