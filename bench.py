@@ -327,7 +327,7 @@ def decode_sweep(q4, torch, synth, lib, stream, workload, specs, Ms, act_order=F
             t = per_launch_times(lib, torch, [ly], min_launches=200, stream=stream)[0]
             gbs = ly.bytes / t / 1e9
             out[f"{name}_m{M}"] = {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                   "us": round(t * 1e6, 2)}
+                                   "us": round(t * 1e6, 2), "TFLOP/s": round(2 * M * K * N / t / 1e12, 1)}
         ly.close()
         del ly
         torch.cuda.empty_cache()
@@ -402,8 +402,9 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
 def secondary(q4, torch, synth, lib, stream):
     """Figures on the other workloads: the 7B block with projection fusion
     and with bfloat16 activations, the 70B MLP layers at M = 1, 2, 4, 8, 16 (where the skinny kernel stops
-    being bandwidth-bound), the act-order 7B MLP layers at M = 1 and 4, and
-    the prefill GEMM at M = 2048."""
+    being bandwidth-bound), the 7B MLP layers at M = 17 .. 256 (small
+    batches on the GEMM), the 8-bit and act-order 7B MLP layers at M = 1
+    and 4, and the prefill GEMM at M = 2048."""
     out = {}
     out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
                                                 "llama7b_block_decode", 10)
@@ -411,6 +412,10 @@ def secondary(q4, torch, synth, lib, stream):
                                               "llama7b_block_decode", 10)
     out["llama70b_mlp_decode"] = decode_sweep(q4, torch, synth, lib, stream, "llama70b_mlp_decode",
                                               synth.LLAMA70B_MLP, (1, 2, 4, 8, 16))
+    # batches past the skinny kernel's 16 rows (the GEMM's 64-row tiles)
+    out["llama7b_mlp_small_batch"] = decode_sweep(
+        q4, torch, synth, lib, stream, "llama7b_mlp_small_batch",
+        (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (17, 32, 64, 128, 256))
     out["llama7b_mlp_w8_decode"] = decode_sweep(
         q4, torch, synth, lib, stream, "llama7b_mlp_w8_decode",
         (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (1, 4), bits=8)
