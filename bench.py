@@ -55,6 +55,7 @@ METRIC = "W4A16 GEMV effective HBM GB/s (% peak) at M=1; TFLOPS (% MFMA peak) at
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 MALL_DEFEAT_BYTES = 1 << 30     # rotate at least this much distinct weight memory
+WARM_S = 0.05                   # seconds of replays before a per-launch timing
 
 
 def log(*a):
@@ -147,10 +148,13 @@ def per_launch_times(lib, torch, layers, min_launches, stream):
     """Mean kernel duration of each layer, with its weights coming from HBM:
     the layer's launches rotate over ceil(1 GiB / layer bytes) handle copies
     (made for this measurement and freed after it), at least `min_launches`
-    of them, captured in one HIP graph on the launch stream and replayed
-    between two events. Consecutive kernels of a graph start back to back, so
-    elapsed / launches is the mean launch duration (the figure the kernel
-    trace of rocprofv3 reports for the same launches)."""
+    of them, captured in one HIP graph on the launch stream. The graph is
+    replayed for about WARM_S seconds first (clocks ramp up over some
+    milliseconds after the host-side set-up left the GPU idle), then three
+    times between two events each; the median replay gives the time.
+    Consecutive kernels of a graph start back to back, so elapsed / launches
+    is the mean launch duration (the figure the kernel trace of rocprofv3
+    reports for the same launches)."""
     out = []
     for ly in layers:
         base = len(ly.mats)
@@ -167,15 +171,22 @@ def per_launch_times(lib, torch, layers, min_launches, stream):
             cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for r in range(n):
                 ly.launch(lib, r % copies, cap)
+        def timed_replay():
+            with torch.cuda.stream(stream):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+            stream.synchronize()
+            return a.elapsed_time(b) * 1e-3
+
+        first = timed_replay()
         with torch.cuda.stream(stream):
-            g.replay()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
+            for _ in range(max(1, math.ceil(WARM_S / first))):
+                g.replay()
         stream.synchronize()
-        out.append(a.elapsed_time(b) * 1e-3 / n)
+        out.append(sorted(timed_replay() for _ in range(3))[1] / n)
         del g
         ly.shrink(base)
         torch.cuda.empty_cache()
@@ -296,7 +307,7 @@ def fused_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500
                                   bias=specs[n][2]) for n in names]
         layers.append(Layer(q4, torch, gname, synth.concat_layers(parts), copies))
     step_bytes = sum(ly.bytes for ly in layers)
-    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 50, stream, use_graph=True)
+    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 1000, stream, use_graph=True)
     del graphs
     lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
     for ly in layers:
@@ -341,7 +352,7 @@ def bf16_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500)
     layers = build_layers(q4, torch, synth, synth.LLAMA7B_BLOCK, G, M, workload + "_bf16", copies,
                           xfmt="bf16")
     step_bytes = sum(ly.bytes for ly in layers)
-    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 50, stream, use_graph=True)
+    elapsed, _, graphs = time_steps(lib, torch, layers, copies, steps, 1000, stream, use_graph=True)
     del graphs
     lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
     for ly in layers:
@@ -430,7 +441,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--eager", action="store_true", help="launch each step directly (no graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")

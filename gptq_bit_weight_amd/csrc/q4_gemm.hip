@@ -112,6 +112,7 @@ struct Ctx {
     uint32_t a_off[A_LOADS];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
     uint32_t a_k[A_LOADS];     // k of each chunk for k0 = 0
     uint32_t bp_off;           // packed-weight byte offset of this lane's word in k-tile 0, kb = 0
+    uint32_t bp_kbs;           // bytes from chunk (kb, n) to chunk (kb + 1, n): 16 * tile width
     uint32_t bp_kill;          // kOOB for a column past N
     uint32_t sz_off;           // scale or zero-word byte offset of this lane (row 0, kill folded in)
     bool sz_is_zero;           // this wave loads zero words (else scales)
@@ -142,7 +143,7 @@ __device__ __forceinline__ void load_b(const Ctx& c, const GemmArgs& p, char* ba
     for (int kb = 0; kb < BP_LOADS; ++kb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             c.rw, (lds_void*)(base + (kb * 4 + wave) * 256), 4,
-            (int)((c.bp_off + (uint32_t)kb * (uint32_t)p.N * 16u + tile_off) | c.bp_kill), 0, 0, 0);
+            (int)((c.bp_off + (uint32_t)kb * c.bp_kbs + tile_off) | c.bp_kill), 0, 0, 0);
     const int k = kt * BK + 32 * c.sz_group;
     const uint32_t kill = k < p.K ? 0u : kOOB;
     const uint32_t g = (uint32_t)(min(k, p.K - 1) / p.G);
@@ -250,7 +251,9 @@ __global__ __launch_bounds__(NT) void q4_gemm_dma_kernel(GemmArgs p)
         // packed tile: lane pair (2i, 2i + 1) of wave w takes the two words of
         // column n0 + 32w + i
         const int col = n0 + 32 * wave + (lane >> 1);
-        c.bp_off = (uint32_t)col * 16u + 4u * (uint32_t)(lane & 1);
+        const int cn = min(col, p.N - 1);
+        c.bp_off = q4::chunk_in_block(0, cn, p.N) * 16u + 4u * (uint32_t)(lane & 1);
+        c.bp_kbs = (q4::chunk_in_block(1, cn, p.N) - q4::chunk_in_block(0, cn, p.N)) * 16u;
         c.bp_kill = col < p.N ? 0u : kOOB;
     }
     {

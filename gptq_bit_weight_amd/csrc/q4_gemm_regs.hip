@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NT) void q4_gemm_regs_kernel(GemmArgs p)
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
         const int kb = tid >> 6, n = n0 + 2 * (tid & 63) + v;
-        ln.b_off[v] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u;
+        ln.b_off[v] = q4::chunk_in_block(kb, min(n, p.N - 1), p.N) * 16u;
         ln.b_kill[v] = n < p.N ? 0u : kOOB;
     }
     int lane_cols[NJ];

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             lane_cols[j] = n0 + wn * WTN + 32 * j + l32;
             const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
 #pragma unroll
-            for (int v = 0; v < 2; ++v) c.w_off[j][v] = ((uint32_t)(lhi + 2 * v) * (uint32_t)p.N + n) * (W8 ? 32u : 16u);
+            for (int v = 0; v < 2; ++v) c.w_off[j][v] = q4::chunk_in_block(lhi + 2 * v, (int)n, p.N) * (W8 ? 32u : 16u);
             c.s_off[j] = n * 2u;
             c.z_off[j] = (n >> (W8 ? 2 : 3)) * 4u;
             c.z_shift[j] = W8 ? 8u * (n & 3u) : 4u * (n & 7u);

@@ -113,7 +113,7 @@ struct Block {
 // end of x and read zeros.
 template <int CT>
 struct Lane {
-    uint32_t w[CT];          // (kb * N + n_j) * 16 (8-bit: * 32)
+    uint32_t w[CT];          // chunk (kb, n_j) of a block * 16 (8-bit: * 32)
     uint32_t sz[CT];         // n_j * 4
     uint32_t x;              // ((l % R) * K + 8 * kb + 32 * ((l % 16) / R)) * 2
 };
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
         const int n = min(n0 + 16 * j + c16, p.N - 1);
-        ln.w[j] = ((uint32_t)kb * (uint32_t)p.N + (uint32_t)n) * 16u * wl<W8>();
+        ln.w[j] = q4::chunk_in_block(kb, n, p.N) * 16u * wl<W8>();
         ln.sz[j] = (uint32_t)n * 4u;
     }
     constexpr int R = 16 / XS;

@@ -13,11 +13,16 @@ namespace q4 {
 // ---- private weight layout -------------------------------------------------
 // The packed weights are stored in k-blocks of 128 rows. Inside block b, the
 // 16-byte chunk (b, kb, n) (kb = 0..3) holds four words of column n; word i of
-// it packs rows 32 * (4b + i) + 8 * kb .. +7. Chunks are ordered
-// [b][kb][n], so one 16-byte load gives a lane the eight rows it feeds to an
-// MFMA lane in each of four consecutive 32-row k-steps, and the 64 rows a
-// prefill k-tile needs are 8 contiguous bytes of every chunk. K is padded to
-// a whole block with code 0 (the kernels give those rows zero activations).
+// it packs rows 32 * (4b + i) + 8 * kb .. +7. One 16-byte load gives a lane
+// the eight rows it feeds to an MFMA lane in each of four consecutive 32-row
+// k-steps, and the 64 rows a prefill k-tile needs are 8 contiguous bytes of
+// every chunk. Block b holds 4N chunks; inside it the columns go in tiles of
+// 16, each tile's chunks ordered [kb][column] (chunk_in_block), so the 64
+// lanes of a skinny-kernel wave (16 columns x 4 kb) read 1 KiB of contiguous
+// memory with one instruction. (Ordering the block [kb][n] instead makes that
+// read four 256-byte pieces N * 16 bytes apart; a read-only probe of the
+// 7B- and 70B-shaped layers streamed 8-11% slower that way.) K is padded to a
+// whole block with code 0 (the kernels give those rows zero activations).
 //
 // 8-bit weights use the same blocks with 32-byte chunks: word 2i + h of chunk
 // (b, kb, n) holds rows 32 * (4b + i) + 8 * kb + 4h .. +3, one byte each in k
@@ -29,6 +34,15 @@ constexpr int num_kblocks(int K) { return (K + kBlockK - 1) / kBlockK; }
 constexpr size_t packed_words(int K, int N, int bits = 4)
 {
     return (size_t)num_kblocks(K) * (kBlockK * bits / 32) * (size_t)N;
+}
+
+// Chunk (b, kb, n) counted from the start of block b, for a layout of N
+// columns (0 <= n < N): the tile of 16 columns holding n starts at chunk
+// 4 * (n - n % 16) and is tw = min(16, N - (n - n % 16)) columns wide (the last
+// tile of an N that is not a multiple of 16 is narrower).
+__host__ __device__ constexpr uint32_t chunk_in_block(int kb, int n, int N)
+{
+    return (uint32_t)(4 * (n & ~15) + kb * ((N - (n & ~15)) < 16 ? (N - (n & ~15)) : 16) + (n & 15));
 }
 
 // ---- skinny (M <= 16) kernel geometry ------------------------------------

@@ -4,8 +4,8 @@
 // scales/zeros", GPTQModel wiki "Inference Backends", section "Packing,
 // conversion, and runtime initialization"): qweight is rewritten once into
 // the kernels' private layout -- 128-row k-blocks of 16-byte chunks, word i
-// of chunk (b, kb, n) packing rows 32 * (4b + i) + 8 * kb .. +7 of column n
-// (q4_internal.h), each word in the nibble slot order of q4_device.h -- and,
+// of chunk (b, kb, n) packing rows 32 * (4b + i) + 8 * kb .. +7 of column n,
+// chunks in 16-column tiles (q4_internal.h), each word in the nibble slot order of q4_device.h -- and,
 // for act-order, with its rows in the order of one stable argsort of g_idx
 // (same page, section "Runtime cache lifetime"), so that every group becomes
 // a contiguous run of groupsize rows. Rows past K (up to the next multiple of
@@ -28,8 +28,9 @@ __device__ __forceinline__ size_t private_word(int kk, int n, int N, int* e, int
 {
     const int b = kk >> 7, i = (kk >> 5) & 3, kb = (kk >> 3) & 3;
     *e = kk & 7;
-    if (bits == 8) return ((size_t)(4 * b + kb) * N + n) * 8 + 2 * i + (*e >> 2);
-    return ((size_t)(4 * b + kb) * N + n) * 4 + i;
+    const size_t chunk = (size_t)b * 4 * N + q4::chunk_in_block(kb, n, N);
+    if (bits == 8) return chunk * 8 + 2 * i + (*e >> 2);
+    return chunk * 4 + i;
 }
 
 // One thread per output word of one part (N columns of a handle with n_total,
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t* __restri
             const uint32_t code = (src[(size_t)(k >> 3) * N + n] >> (4 * (k & 7))) & 0xFu;
             w |= code << (4 * slot_of(e));
         }
-        dst[((size_t)q * n_total + col_off + n) * 4 + i] = w;
+        dst[((size_t)(q >> 2) * 4 * n_total + q4::chunk_in_block(q & 3, col_off + n, n_total)) * 4 + i] = w;
     }
 }
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void q4_repack8_kernel(const uint32_t* __restr
             const uint32_t code = (src[(size_t)(k >> 2) * N + n] >> (8 * (k & 3))) & 0xFFu;
             w |= code << (8 * e);
         }
-        dst[((size_t)q * n_total + col_off + n) * 8 + wi] = w;
+        dst[((size_t)(q >> 2) * 4 * n_total + q4::chunk_in_block(q & 3, col_off + n, n_total)) * 8 + wi] = w;
     }
 }
 
