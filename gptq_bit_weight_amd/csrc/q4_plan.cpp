@@ -106,9 +106,12 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits, int bits)
 {
     if (num_cu <= 0) num_cu = 256;
-    // gain x 100 for 1, 2, 4 tiles: M <= 4, M <= 8, M <= 16
-    static const int gain[3][3] = {{100, 110, 120}, {100, 140, 150}, {100, 160, 190}};
-    const int mi = M <= 4 ? 0 : M <= 8 ? 1 : 2;
+    // gain x 100 for 1, 2, 4 tiles: M <= 2, M <= 4, M <= 8, M <= 16. (At
+    // M = 1 a wider tile saves little: 8192x28672 ran 21.2 us with one tile
+    // a wave against 21.8 us with four, 28672x8192 20.5 us with two against
+    // 21.1 us with one, the tiles then filling one round of CUs exactly.)
+    static const int gain[4][3] = {{100, 104, 104}, {100, 110, 120}, {100, 140, 150}, {100, 160, 190}};
+    const int mi = M <= 2 ? 0 : M <= 4 ? 1 : M <= 8 ? 2 : 3;
     // (groups of 32 rows carry four scale/zero sets per block, and 8-bit
     // blocks are twice the words; four tiles of either do not fit the
     // register file)
