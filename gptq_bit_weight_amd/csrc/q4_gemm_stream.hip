@@ -14,15 +14,15 @@
 // exists anywhere but in registers ("GPTQ's 'Exllama Kernel Not Installed'
 // Warning", section "What the fallback actually does").
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a 256 x 128 output tile;
-// each wave owns 128 x 64 (4 x 2 MFMA tiles of 32 x 32). K advances in
-// 64-row tiles.
+// Tiling: a workgroup of 4 waves computes a BM x 128 output tile; each wave
+// owns BM x 32 (BM / 32 MFMA tiles of 32 x 32, one column tile). K advances
+// in 64-row tiles.
 //  * Activations: a 2-stage LDS ring (32 KiB a stage, 16-byte chunks of the
 //    128-byte rows XOR-swizzled by (row / 2) % 8) filled by direct-to-LDS
 //    buffer loads. 64 KiB of LDS lets two workgroups share a CU.
-//  * Weights: for its two columns a lane needs, per k-tile, words 2h and
+//  * Weights: for its column (lane % 32 of the wave's 32) a lane needs, per k-tile, words 2h and
 //    2h + 1 of chunks (b, kb) and (b, kb + 2) of the private block layout
-//    (k-tile 2b + h, kb = lane / 32): two 8-byte loads per column. With the
+//    (k-tile 2b + h, kb = lane / 32): two 8-byte loads. With the
 //    scale and zero words of the tile's group(s), these go to one of two
 //    register sets; the k-loop is unrolled by two so that the set a step
 //    multiplies is never a set a load is filling.
@@ -48,17 +48,25 @@ using namespace q4dev;
 constexpr int BN = q4::kGemmBN;      // 128
 constexpr int BK = q4::kGemmBK;      // 64
 constexpr int NT = q4::kGemmThreads; // 256
-constexpr int WTN = BN / 2;          // wave tile columns
+// The four waves sit side by side along N (1 x 4): each owns all BM rows of
+// 32 columns, so every packed word is dequantized by exactly one wave and each
+// wave reads the whole activation stage from LDS. (A 2 x 2 grid reads half the
+// activations per wave but dequantizes every word twice; measured slower:
+// M = 2048 948 -> 969 TFLOP/s on 4096x11008, M = 256 453 -> 601, M = 64
+// 264 -> 291. LDS reads stay under a third of the LDS bandwidth.)
+constexpr int WGN = 4;               // waves along N (the rest along M)
+constexpr int WGM = 4 / WGN;
+constexpr int WTN = BN / WGN;        // wave tile columns
 constexpr int NJ = WTN / 32;
-static_assert(BK == 64 && BN == 128 && NT == 256 && NJ == 2, "index arithmetic below assumes these");
+static_assert(BK == 64 && BN == 128 && NT == 256 && NJ >= 1 && WGM * WGN == 4, "index arithmetic below assumes these");
 
 // Geometry that depends on the tile height BM (256, or 64 for few rows): a
-// 2 x 2 grid of waves, each WTM x WTN (MI x NJ MFMA tiles of 32 x 32); the
+// WGM x WGN grid of waves, each WTM x WTN (MI x NJ MFMA tiles of 32 x 32); the
 // activation stage is BM x BK halfs, filled by A_LOADS 16-byte direct loads
 // per thread (8 at BM = 256: 32 KiB a stage; 2 at BM = 64: 8 KiB).
 template <int BM>
 struct Geo {
-    static constexpr int WTM = BM / 2;
+    static constexpr int WTM = BM / WGM;
     static constexpr int MI = WTM / 32;
     static constexpr int A_TILE_BYTES = BM * BK * 2;
     static constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     // per-lane indices, recomputed for every segment (below) so that values
     // derived from them are not kept live across the k-loop
     int tid = 0, lane = 0, l32 = 0, lhi = 0;
