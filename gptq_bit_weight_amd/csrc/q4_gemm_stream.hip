@@ -272,31 +272,38 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         };
         const int k0 = kt * BK;
         u4 bc[NJ], bn[NJ];
+        u4 a[MI];
+        auto read_a = [&](int sub, int i) {
+            return *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
+        };
+#pragma unroll
+        for (int i = 0; i < MI; ++i) a[i] = read_a(0, i);
         deq(0, bc);
 #pragma unroll
         for (int sub = 0; sub < BK / 16; ++sub) {
-            u4 a[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                a[i] = *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
             if (sub + 1 < BK / 16) deq(sub + 1, bn);
-            if (!KT || k0 + 16 * sub < p.K) {
+            const bool live = !KT || k0 + 16 * sub < p.K;
+            // row tile i's MFMAs, then its activations for the next
+            // sub-step into the same registers
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MI; ++i) {
+                if (live) {
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) {
                         if constexpr (BF) acc[i][j] = mfma32(bitcast<b8>(a[i]), bitcast<b8>(bc[j]), acc[i][j]);
                         else acc[i][j] = mfma32(bitcast<h8>(a[i]), bitcast<h8>(bc[j]), acc[i][j]);
                     }
+                }
+                if (sub + 1 < BK / 16) a[i] = read_a(sub + 1, i);
             }
             if (sub + 1 < BK / 16) {
-                // the sub-step's activation reads, then each MFMA followed
-                // by up to three vector instructions of the next dequantization
-                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+                // each MFMA followed by one activation read and up to two
+                // vector instructions of the next sub-step
 #pragma unroll
                 for (int q = 0; q < MI * NJ; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                    if (q < MI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
                 }
             }
 #pragma unroll
