@@ -2,7 +2,7 @@
 // in LDS, weights streamed into registers.
 //
 // q4_gemm_stream_kernel<BM, NG, KT, BF, W8>: BM rows per output tile (256,
-// or 64 when M <= 256), NG groups per 64-row k-tile (2 for groups of 32), KT
+// or 64 when M <= 512), NG groups per 64-row k-tile (2 for groups of 32), KT
 // (K not a multiple of 64), BF (bfloat16 activations and output), W8 (8-bit
 // codes).
 //

@@ -71,9 +71,9 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmThreads = 256;
 // The streaming GEMM takes 64-row output tiles when M <= kGemmSmallM (few
 // rows: 256-row tiles leave most CUs idle and multiply padding; measured on
-// the 7B MLP shapes, 64-row tiles are faster up to M = 256, even at 384 and
-// slower from 512 on), else 256-row tiles.
-constexpr int kGemmSmallM = 256;
+// the 7B MLP shapes, 64-row tiles are faster up to M = 384 (22-26% there),
+// within -2 .. +7% at 512 and 5-12% slower from 768 on), else 256-row tiles.
+constexpr int kGemmSmallM = 512;
 inline int gemm_bm(int M) { return M <= kGemmSmallM ? 64 : kGemmBM; }
 inline int gemm_tiles(int M, int N)
 {

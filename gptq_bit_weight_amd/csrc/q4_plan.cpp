@@ -163,10 +163,10 @@ bool gemv_gathers_x(int M, int K, int splits)
 // better (768 tiles: equal; 1792: 1.5% slower).
 //  * 256-row tiles: 2 x tiles workgroups (a split tile has two or three
 //    contributors), but at least one per CU: with few rows the tiles are
-//    few (11008x4096 at M = 257 .. 512: 64), and too few workgroups leave
+//    few (11008x4096 at M = 513 .. 768: 96), and too few workgroups leave
 //    CUs idle (at M <= 256, before the 64-row tiles: 97 us with 64
 //    workgroups against 54 us with 256).
-//  * 64-row tiles (M <= 256): few rows make the product bound by the weight
+//  * 64-row tiles (M <= 512): few rows make the product bound by the weight
 //    stream (their kernel keeps two k-tiles in flight). About 24 k-tiles a
 //    workgroup measured best, between one and two workgroups per CU: the 7B
 //    MLP shapes (5504 iterations) 22-24 us at 256 workgroups against

@@ -85,9 +85,9 @@ def test_prefill(K, N, G, act):
 
 
 @pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (28672, 8192)])
-@pytest.mark.parametrize("M", [17, 64, 200, 400])
+@pytest.mark.parametrize("M", [17, 64, 200, 400, 600])
 def test_small_batch_gemm(K, N, M):
     """Batches past the skinny kernel's 16 rows: 64-row output tiles
-    (M <= 256), with stream-K across the CUs; and 400 rows: two 256-row tiles."""
+    (M <= 512), with stream-K across the CUs; and 600 rows: three 256-row tiles."""
     L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("small_batch", K, N, M), bias=True)
     _check_layer(L, f"small batch {K}x{N}")

@@ -35,29 +35,30 @@ def _layer(K, N, G, M, seed, **kw):
 
 
 def _tiles(M, N):
-    bm = 64 if M <= 256 else 256     # the tile height the library takes for M rows
+    bm = 64 if M <= 512 else 256     # the tile height the library takes for M rows
     return -(-M // bm) * -(-N // 128)
 
 
 SK_CASES = [
     # K, N, G, M, act, bias, xfmt, bits, workgroup counts
-    # 10 tiles of 16 k-steps (160 iterations): 2..37 workgroups split tiles
-    # into 2..5 segments, 160 gives every k-step its own workgroup, and 200
-    # (more workgroups than iterations) is reduced to 160
-    (1024, 520, 128, 300, False, True, "f16", 4, (2, 3, 7, 10, 13, 20, 37, 160, 200)),
-    # groups of 32 and a K tail inside the last k-step: 4 tiles of 2 k-steps
-    (96, 136, 32, 300, False, False, "f16", 4, (3, 5, 8)),
+    # 256-row tiles: 15 tiles of 16 k-steps (240 iterations; the last row
+    # tile holds 8 rows): 2..37 workgroups split tiles into 2..9 segments, 15
+    # is one per tile, 240 gives every k-step its own workgroup, and 300
+    # (more workgroups than iterations) is reduced to 240
+    (1024, 520, 128, 520, False, True, "f16", 4, (2, 3, 7, 13, 15, 20, 37, 240, 300)),
+    # groups of 32 and a K tail inside the last k-step: 6 tiles of 2 k-steps
+    (96, 136, 32, 520, False, False, "f16", 4, (3, 5, 8)),
     # 8 row tiles: XCD-ordered spaces when the count divides by 8 (8, 16, 40, 96)
     (256, 264, 128, 2048, False, True, "f16", 4, (8, 12, 16, 24, 40, 96)),
-    # act-order (permuted activations): 2 tiles of 16 k-steps
+    # act-order (permuted activations), 64-row tiles: 8 tiles of 16 k-steps
     (1024, 256, 128, 256, True, True, "f16", 4, (3, 5)),
     # bfloat16 activations and 8-bit weights
-    (512, 264, 128, 300, False, True, "bf16", 4, (5, 11)),
-    (512, 264, 64, 300, False, True, "f16", 8, (5, 11)),
+    (512, 264, 128, 520, False, True, "bf16", 4, (5, 11)),
+    (512, 264, 64, 520, False, True, "f16", 8, (5, 11)),
     # groups of 32 and a K tail with bfloat16, and with 8-bit weights
-    (480, 136, 32, 260, False, True, "bf16", 4, (3, 7)),
-    (480, 136, 32, 260, True, True, "f16", 8, (3, 7)),
-    # 64-row tiles (M <= 256): 5 tiles of 16 k-steps; 80 = one k-step each
+    (480, 136, 32, 516, False, True, "bf16", 4, (3, 7)),
+    (480, 136, 32, 516, True, True, "f16", 8, (3, 7)),
+    # 64-row tiles (M <= 512): 5 tiles of 16 k-steps; 80 = one k-step each
     (1024, 520, 128, 40, False, True, "f16", 4, (2, 5, 9, 40, 80, 100)),
     (1024, 520, 128, 64, True, True, "f16", 4, (3, 13)),
     (480, 136, 32, 17, False, True, "bf16", 4, (3, 7)),

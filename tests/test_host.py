@@ -154,7 +154,7 @@ def test_plan_gemv():
 
 
 def test_plan_gemm():
-    """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 256)
+    """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 512)
     when the tiles fill whole rounds of two per CU (to within a tenth) or make
     1.5 rounds or more; otherwise the workgroups share the k-steps
     (stream-K): about 24 k-steps each between CUs and 2 x CUs workgroups for
@@ -173,10 +173,11 @@ def test_plan_gemm():
     assert p(64, 11008, 4096, 256) == 256
     assert p(128, 11008, 4096, 256) == 458       # 2 x 86 tiles of 64 rows x 64 k-steps / 24
     assert p(256, 4096, 11008, 256) == 512       # 4 x 32 tiles x 172 k-steps: at most 2 x CUs
-    assert p(300, 11008, 4096, 256) == 344       # 2 x 86 tiles of 256 rows: 2 x tiles
-    assert p(512, 4096, 11008, 256) == 256       # 2 x 32 tiles of 256 rows: at least one per CU
-    assert p(300, 136, 96, 256) == 8             # 4 tiles of 2 k-steps: 8 iterations
-    assert p(300, 136, 32, 256) == 4             # 4 tiles of 1 k-step: one each
+    assert p(512, 4096, 11008, 256) == 512       # 8 x 32 tiles of 64 rows x 172 k-steps: 2 x CUs
+    assert p(520, 6144, 4096, 256) == 288        # 3 x 48 tiles of 256 rows: 2 x tiles
+    assert p(520, 4096, 11008, 256) == 256       # 3 x 32 tiles of 256 rows: at least one per CU
+    assert p(520, 136, 96, 256) == 12            # 6 tiles of 2 k-steps: 12 iterations
+    assert p(520, 136, 32, 256) == 6             # 6 tiles of 1 k-step: one each
     assert p(2048, 4096, 11008, 64) == 256       # a smaller chip: two whole rounds
     assert p(2048, 11008, 4096, 64) == 688       # 688 tiles: 5.4 rounds of 128
     for bad in ((0, 8, 32), (1, 0, 32), (1, 8, 0)):
