@@ -83,6 +83,7 @@ struct GemmArgs {
     const uint16_t* bias;
     uint16_t* out;
     int M, K, N, G;
+    int gshift;             // group of row k = k >> gshift (31: one group over K)
     int zrow;               // bytes per row of packed zeros (N * bits / 8)
     // Schedule: `workers` workgroups share the (output tile, k-tile)
     // iterations evenly, in contiguous ranges, each at least one iteration
@@ -159,7 +160,7 @@ __device__ __forceinline__ void load_b(BRegs<NG, W8>& R, const Ctx& c, const Gem
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         const int k = min(kt * BK + 32 * gi, p.K - 1);
-        const uint32_t g = (uint32_t)(k / p.G);
+        const uint32_t g = (uint32_t)k >> p.gshift;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             R.s[gi][j] = buf_load2(c.rs, c.s_off[j], g * (uint32_t)p.N * 2u);
@@ -550,6 +551,11 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     p.K = h->K;
     p.N = h->N;
     p.G = h->G;
+    // groups are 32, 64, 128 or 256 rows, or one group over K
+    p.gshift = 31;
+    if (h->G != h->K)
+        for (int sh = 5; sh <= 8; ++sh)
+            if ((1 << sh) == h->G) p.gshift = sh;
     p.partials = partials;
     p.counters = counters;
     p.workers = workers;

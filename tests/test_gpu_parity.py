@@ -94,6 +94,7 @@ GEMM_CASES = [
     (1024, 256, 128, 256, True, True),     # act-order, whole tiles
     (768, 264, 256, 70, True, False),      # act-order, groups of 256
     (320, 72, -1, 33, False, False),       # one group over K
+    (640, 200, 64, 90, False, True),       # groups of 64: one group per k-tile
 ]
 
 
