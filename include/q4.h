@@ -187,7 +187,7 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
  *                  2 (direct-to-LDS pipeline) or 3 (activations in LDS,
  *                  weights streamed into registers); splits = workgroups
  *                  of variant 3: 0 (planned, q4_plan_gemm), 1 (one per
- *                  output tile: 256 x 128, or 64 x 128 when M <= 256) or
+ *                  output tile: 256 x 128, or 64 x 128 when M <= 512) or
  *                  2..Q4_GEMM_MAX_WORKERS (the
  *                  tiles' 64-row k-steps shared evenly, stream-K; a count
  *                  above the number of (tile, k-step) pairs is reduced to
@@ -334,7 +334,7 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
 /*
  * q4_plan_gemm -- the streaming GEMM's planned workgroup count for an
  * M x N output with K rows on a chip of num_cu compute units (<= 0: 256).
- * Output tiles are 64 x 128 when M <= 256, else 256 x 128. One workgroup per
+ * Output tiles are 64 x 128 when M <= 512, else 256 x 128. One workgroup per
  * tile when the tiles fill whole rounds of two per CU (to within a tenth) or
  * make at least 1.5 such rounds; otherwise the tiles' 64-row k-steps are
  * shared evenly (stream-K) by about one workgroup per 24 k-steps, between
