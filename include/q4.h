@@ -268,7 +268,8 @@ const char* q4_last_error(void);
 /*
  * q4_path_for -- the kernel q4_matmul would launch for this M (Q4_PATH_*),
  * or -1 for a NULL handle or M < 0. Lets a caller check which kernel runs
- * (the first page's advice: verify the kernel, not the absence of a warning).
+ * ("GPTQ's 'Exllama Kernel Not Installed' Warning": check which kernel runs
+ * rather than relying on the absence of a warning).
  */
 int q4_path_for(const q4_matrix* h, int M);
 

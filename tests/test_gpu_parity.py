@@ -31,7 +31,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import gptq_bit_weight_amd as q4
-    q4.load_library()            # must load on a GPU machine: no fallback
+    q4.load_library()            # must load where a GPU is present: no fallback
     yield
 
 
