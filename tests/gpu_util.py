@@ -115,6 +115,54 @@ def oracle_sampled(L, ms, ns):
                             bias=L.bias, xfmt=L.xfmt, bits=L.bits)
 
 
+def tile_lines(extent: int, window: int, per_window: int, seed: int, first: bool = False) -> np.ndarray:
+    """Indices along one output axis that hit every `window`-wide stretch:
+    the last index of each stretch, `per_window` random ones inside it and,
+    with `first`, its first index (sorted, without repeats)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for lo in range(0, extent, window):
+        hi = min(extent, lo + window)
+        out.append(hi - 1)
+        if first:
+            out.append(lo)
+        out += list(rng.integers(lo, hi, per_window))
+    return np.unique(np.array(out, dtype=np.int64))
+
+
+def check_rows_cols(L, y, what: str, seed: int = 0, **tol) -> int:
+    """Every element of whole output rows and whole output columns against the
+    oracle. Rows: the first, the last and one random row of each row tile of
+    the GEMM (64 rows up to M = 512, else 256); columns: column 0 and, of each
+    128-column tile, the last and one random column. The rows cover every
+    column of their tiles and the columns every row, so each output tile and
+    each stream-K split of it has whole checked rows and columns. Returns the
+    number of elements compared."""
+    y = np.asarray(y)
+    rows = tile_lines(L.M, 64 if L.M <= 512 else 256, 1, seed + 1, first=True)
+    cols = np.unique(np.concatenate([[0], tile_lines(L.N, 128, 1, seed + 2)]))
+    rm, rn = np.meshgrid(rows, np.arange(L.N, dtype=np.int64), indexing="ij")
+    cm, cn = np.meshgrid(np.arange(L.M, dtype=np.int64), cols, indexing="ij")
+    ms = np.concatenate([rm.ravel(), cm.ravel()])
+    ns = np.concatenate([rn.ravel(), cn.ravel()])
+    yD, A = oracle_sampled(L, ms, ns)
+    compare(y[ms, ns], yD, A, what, **tol)
+    return int(ms.size)
+
+
+def check_output(L, y, what: str, seed: int = 0, full_max_m: int = 16, **tol) -> int:
+    """The acceptance rule on a whole GPU output: every element for
+    M <= full_max_m (the oracle computes the whole product), else whole rows
+    and columns through check_rows_cols. Returns the number of elements
+    compared."""
+    y = np.asarray(y)
+    if L.M <= full_max_m:
+        yD, A = oracle_full(L)
+        compare(y, yD, A, what, **tol)
+        return int(y.size)
+    return check_rows_cols(L, y, what, seed, **tol)
+
+
 def sample_indices(M: int, N: int, count: int, seed: int):
     """Sampled output elements: corners, the last row/column, random ones."""
     rng = np.random.default_rng(seed)
