@@ -55,7 +55,7 @@ METRIC = "W4A16 GEMV effective HBM GB/s (% peak) at M=1; TFLOPS (% MFMA peak) at
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 MALL_DEFEAT_BYTES = 1 << 30     # rotate at least this much distinct weight memory
-WARM_S = 0.05                   # seconds of replays before a per-launch timing
+WARM_S = 0.1                    # seconds of replays before a timed region
 
 
 def log(*a):
@@ -240,6 +240,13 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
                 s += 1
 
     with torch.cuda.stream(stream):
+        # Clocks ramp over milliseconds after the host-side set-up left the
+        # GPU idle: replay for at least WARM_S seconds whatever `warmup` is,
+        # then the `warmup` steps themselves.
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < WARM_S:
+            run(0, copies)
+            stream.synchronize()
         run(0, warmup)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -253,11 +260,37 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
     return t0.elapsed_time(t1) * 1e-3, wall, graphs
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(oracle, L, budget_s):
+    """Whole-layer oracle runs of L (fused route) repeated for about budget_s
+    seconds (at least once): (GB/s of metric bytes, GFLOP/s, runs, seconds)."""
+    runs, elapsed = 0, 0.0
+    while runs == 0 or elapsed < budget_s:
+        t = time.perf_counter()
+        oracle.matmul(L.x, L.qweight, L.qzeros, L.scales, L.g_idx, L.K, L.N, L.G, bias=L.bias)
+        elapsed += time.perf_counter() - t
+        runs += 1
+    return (L.metric_bytes() * runs / elapsed / 1e9, 2.0 * L.M * L.K * L.N * runs / elapsed / 1e9,
+            runs, elapsed)
+
+
 def cpu_baseline(synth, oracle, specs, G, workload, budget_s):
     """The oracle's fused route on whole layers of the block at M = 1, layers
     in block order and repeated (at least one whole block), until budget_s of
-    CPU time has passed."""
-    done_bytes, elapsed, layers_done = 0, 0.0, 0
+    CPU time has passed, on all the threads the oracle is given; then single
+    threaded on one layer of each decode workload (tiny 512x512; the block's
+    q projection 4096x4096; the act-order 4096x11008 layer at M = 1)."""
+    done_bytes, done_flops, elapsed, layers_done = 0, 0, 0.0, 0
     cache = {}
     i = 0
     while elapsed < budget_s or layers_done < len(specs):
@@ -270,16 +303,113 @@ def cpu_baseline(synth, oracle, specs, G, workload, budget_s):
         oracle.matmul(L.x, L.qweight, L.qzeros, L.scales, None, K, N, G, bias=L.bias)
         elapsed += time.perf_counter() - t
         done_bytes += L.metric_bytes()
+        done_flops += 2 * L.K * L.N
         layers_done += 1
         i += 1
+    threads = oracle.num_threads()
+    single = {}
+    prev = oracle.set_num_threads(1)
+    try:
+        for label, L in (
+                ("tiny_512x512_m1", synth.make_layer(512, 512, 128, 1, seed=synth.layer_seed("tiny", 1))),
+                ("llama7b_q_proj_4096x4096_m1", cache.get("q_proj") or synth.make_layer(
+                    4096, 4096, G, 1, seed=synth.layer_seed(workload, "q_proj", 1), bias=True)),
+                ("llama7b_actorder_4096x11008_m1", synth.make_layer(
+                    4096, 11008, 128, 1, seed=synth.layer_seed("llama7b_actorder", 4096, 11008, 1),
+                    act_order=True))):
+            gbs, gfl, runs, secs = _oracle_rate(oracle, L, 1.0)
+            single[label] = {"GB/s": round(gbs, 4), "GFLOP/s": round(gfl, 3), "runs": runs,
+                             "seconds": round(secs, 2)}
+    finally:
+        oracle.set_num_threads(prev)
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{layers_done} whole M=1 layers of the block in order (fused route, double "
-                  f"accumulation), {elapsed:.1f} s",
+                  f"accumulation), {elapsed:.1f} s on {threads} threads",
+        "GFLOP/s": round(done_flops / elapsed / 1e9, 3),
+        "cpu_model": cpu_model(),
+        "single_thread": single,
     }
+
+
+def gpu_environment(torch):
+    """Clocks and software versions of the run (best effort: missing tools
+    give null)."""
+    env = {"rocm": None, "torch_hip": getattr(torch.version, "hip", None), "sclk_mhz": None,
+           "mclk_mhz": None, "device": torch.cuda.get_device_name(0)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+        card = next(iter(data.values()), {}) if data else {}
+        env["smi_clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or None
+        for key, val in card.items():
+            m = re.search(r"\(?(\d+)\s*Mhz", str(val), re.I)
+            if not m:
+                continue
+            k = key.lower()
+            if k.startswith("sclk") and env["sclk_mhz"] is None:
+                env["sclk_mhz"] = int(m.group(1))
+            elif k.startswith("mclk") and env["mclk_mhz"] is None:
+                env["mclk_mhz"] = int(m.group(1))
+    except Exception:   # noqa: BLE001 -- a missing or odd tool leaves nulls
+        pass
+    return env
+
+
+def read_ceiling(lib, torch, stream, sizes):
+    """Achievable read rate of one launch of each size in `sizes` (bytes,
+    rounded down to a multiple of 16 KiB): q4_read_probe launches, captured
+    in a graph that rotates over at least 1 GiB of distinct memory (so the
+    bytes come from HBM, as the weights do), replayed for WARM_S seconds and
+    then three times between events; the median replay gives the mean launch
+    time. Returns {size: {"GB/s", "us"}}."""
+    pool_bytes = max(MALL_DEFEAT_BYTES, max(sizes)) + (16 << 20)
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    out = {}
+    for size in sizes:
+        size = size - size % 16384
+        copies = max(1, min(pool_bytes // size, math.ceil(MALL_DEFEAT_BYTES / size)))
+        offs = [(c * size) - (c * size) % 256 for c in range(copies)]
+        n = copies * max(1, math.ceil(200 / copies)) if size < (256 << 20) else max(copies, 10)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for r in range(n):
+                st = lib.q4_read_probe(ctypes.c_void_p(pool.data_ptr() + offs[r % copies]), size,
+                                       ctypes.c_void_p(sink.data_ptr()), cap)
+                if st:
+                    raise RuntimeError(f"q4_read_probe failed: {lib.q4_last_error()}")
+        with torch.cuda.stream(stream):
+            w0 = time.perf_counter()
+            while time.perf_counter() - w0 < WARM_S:
+                g.replay()
+                stream.synchronize()
+            times = []
+            for _ in range(3):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                stream.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3 / n)
+        t = sorted(times)[1]
+        out[size] = {"GB/s": round(size / t / 1e9, 1), "us": round(t * 1e6, 3)}
+        del g
+    del pool, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def traffic_for(kernel: str, src_hash: str):
@@ -503,6 +633,7 @@ def main():
     log("[bench] per-launch event timing")
     lt = per_launch_times(lib, torch, layers, min_launches=200, stream=stream)
     kern_bytes = sum(ly.bytes for ly in layers)
+    layer_bytes = [ly.bytes for ly in layers]
     n_layers = len(layers)
     kern_time = sum(lt)
     achieved = kern_bytes / kern_time / 1e9
@@ -526,6 +657,16 @@ def main():
 
     sec = {} if args.no_secondary else secondary(q4, torch, synth, lib, stream)
 
+    log("[bench] read ceiling")
+    sizes = sorted({ly_bytes for ly_bytes in (8716288, 23425024, 122028032)} | {2 << 30})
+    ceiling = read_ceiling(lib, torch, stream, sizes)
+
+    def probe_us(nbytes):
+        """Read-probe time for nbytes, from the probe of the nearest size."""
+        size = min(ceiling, key=lambda k: abs(k - nbytes))
+        return ceiling[size]["us"] * nbytes / size
+
+    block_read_us = sum(probe_us(b) for b in layer_bytes)
     src_hash = kernel_source_hash()
     traffic = traffic_for("q4_gemv_kernel", src_hash)
     result = {
@@ -563,6 +704,15 @@ def main():
                              for (ly_name, _, _, _), t in zip(synth.LLAMA7B_BLOCK, lt)},
             "source_hash": src_hash,
         },
+        "read_ceiling": {
+            "what": "one q4_read_probe launch of each size (16-byte non-temporal loads, nothing "
+                    "else), rotating over >= 1 GiB, mean launch time",
+            "by_bytes": {str(k): v for k, v in ceiling.items()},
+            "block_us": round(block_read_us, 2),
+            "block_GB/s": round(block_bytes / block_read_us / 1e3, 1),
+            "value_frac_of_ceiling": round(block_read_us / (ms_per_step * 1e3), 4),
+        },
+        "environment": gpu_environment(torch),
         "secondary": sec,
     }
     if not args.no_cpu_baseline:

@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
     "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16", "q4_make_bits", "q4_make_cat_bits",
-    "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm",
+    "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm", "q4_read_probe",
 )
 
 _lib = None
@@ -111,6 +111,8 @@ def load_library():
     lib.q4_plan_gemv_gather.restype = I
     lib.q4_plan_gemm.argtypes = [I, I, I, I]
     lib.q4_plan_gemm.restype = I
+    lib.q4_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.q4_read_probe.restype = I
     _lib = lib
     return lib
 
@@ -325,12 +327,11 @@ class Q4Matrix:
         then bfloat16 too; the weights and fp16 scales are the same).
 
         path: 0 automatic, PATH_GEMV or PATH_MFMA. variant: skinny kernel --
-        16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 automatic,
-        1 register-staged, 2 direct-to-LDS, 3 weights streamed into
-        registers (the automatic choice; the only one for bfloat16).
-        splits: skinny kernel K splits (0 planned, 1..16); GEMM variant 3
-        workgroups (0 planned, 1 one per output tile, 2..GEMM_MAX_WORKERS
-        sharing the tiles' k-steps: stream-K); variants 1 and 2 take 0 or 1."""
+        16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 or 3 (one
+        kernel: activations in LDS, weights streamed into registers).
+        splits: skinny kernel K splits (0 planned, 1..16); GEMM workgroups
+        (0 planned, 1 one per output tile, 2..GEMM_MAX_WORKERS sharing the
+        tiles' k-steps: stream-K)."""
         torch = _torch()
         h = self._handle()
         if getattr(x, "dtype", None) not in (torch.float16, torch.bfloat16):

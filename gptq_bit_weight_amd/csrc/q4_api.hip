@@ -13,11 +13,8 @@
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, bool gather_x, bool bf16, hipStream_t stream);
-hipError_t launch_gemm_dma(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                           int M, hipStream_t stream);
-hipError_t launch_gemm_regs(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                            int M, hipStream_t stream);
+                       int M, int col_tiles, int splits, bool gather_x, bool bf16, float* partials,
+                       uint32_t* counters, hipStream_t stream);
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
                               int M, bool bf16, int workers, float* partials, uint32_t* counters,
                               hipStream_t stream);
@@ -53,6 +50,7 @@ void destroy(q4_matrix* h)
     (void)hipFree(h->inv_perm);
     (void)hipFree(h->inv16);
     (void)hipFree(h->partials);
+    for (float* p : h->partials_retired) (void)hipFree(p);
     (void)hipFree(h->counters);
     (void)hipFree(h->xperm);
     for (uint16_t* p : h->xperm_retired) (void)hipFree(p);
@@ -141,8 +139,19 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
     if ((e = hipMalloc(&h->qzeros, (size_t)ng * zrow)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
     if ((e = hipMalloc(&h->sz, (size_t)ng * N * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
-    if ((e = hipMalloc(&h->partials, (size_t)kMaxSplits * 16 * N * 4)) != hipSuccess)
-        return bail(hip_fail(e, "q4_make: workspace"));
+    // Split-K partials for the largest K split the plan takes at any M the
+    // skinny kernel serves (1 for most layers: then none).
+    int max_splits = 1;
+    for (int m = 1; m <= Q4_GEMV_MAX_M; ++m) {
+        int ct = 0, sp = 0;
+        plan_gemv(m, K, N, G, num_cu, &ct, &sp, bits);
+        max_splits = std::max(max_splits, sp);
+    }
+    if (max_splits > 1) {
+        if ((e = hipMalloc(&h->partials, (size_t)max_splits * 16 * N * 4)) != hipSuccess)
+            return bail(hip_fail(e, "q4_make: workspace"));
+        h->partial_splits = max_splits;
+    }
     const int col_tiles = (N + 15) / 16;
     if ((e = hipMalloc(&h->counters, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
     if ((e = hipMemset(h->counters, 0, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
@@ -226,6 +235,28 @@ q4_status ensure_xperm(const q4_matrix* h, int M, hipStream_t stream)
     if (h->xperm) h->xperm_retired.push_back(h->xperm);
     h->xperm = fresh;
     h->xperm_elems = need;
+    return Q4_OK;
+}
+
+// Grow the skinny kernel's split-K partials to hold `splits` splits (an
+// explicit split count above the planned ones).
+q4_status ensure_partials(const q4_matrix* h, int splits, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lock(h->ws_mutex);
+    if (h->partial_splits >= splits) return Q4_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(Q4_ERR_INVALID_ARG,
+                    "q4_matmul: the split-K workspace must grow to %d splits under stream capture; "
+                    "make one uncaptured call with this split count first", splits);
+    float* fresh = nullptr;
+    Q4_HIP(hipMalloc(&fresh, (size_t)splits * 16 * h->N * 4), "q4_matmul: split-K workspace");
+    // earlier launches (and graphs captured from them) may still use the old
+    // buffer: retire it, freed with the handle
+    if (h->partials) h->partials_retired.push_back(h->partials);
+    h->partials = fresh;
+    h->partial_splits = splits;
     return Q4_OK;
 }
 
@@ -318,21 +349,11 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (h->bits == 8 && variant == 4)
             return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights take at most 2 column tiles");
     } else {
-        if (variant < 0 || variant > 3)
-            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 1, 2 or 3", variant);
+        if (variant != 0 && variant != 3)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0 or 3", variant);
         if (splits < 0 || splits > Q4_GEMM_MAX_WORKERS)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM workgroups %d outside [0, %d]", splits,
                         Q4_GEMM_MAX_WORKERS);
-        if (splits > 1 && variant != 0 && variant != 3)
-            return fail(Q4_ERR_UNSUPPORTED,
-                        "q4_matmul: GEMM variant %d runs one workgroup per tile (splits 0 or 1, got %d)",
-                        variant, splits);
-        if (bf16 && variant != 0 && variant != 3)
-            return fail(Q4_ERR_UNSUPPORTED,
-                        "q4_matmul: bfloat16 activations run on GEMM variant 3 only (got %d)", variant);
-        if (h->bits == 8 && variant != 0 && variant != 3)
-            return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights run on GEMM variant 3 only (got %d)",
-                        variant);
     }
 
     int ct = 0, s = 0;
@@ -353,42 +374,34 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         xe = h->xperm;
     }
     if (kind == Q4_PATH_GEMV) {
-        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, bf16, stream), "q4_matmul: gemv launch");
-    } else {
-        // Three GEMM variants share tile shape and accumulation order: the
-        // automatic choice streams the weights into registers (activations
-        // in a 2-stage LDS ring, two workgroups per CU), which measured
-        // fastest on every prefill shape; `variant` 1 (register-staged
-        // tiles) and 2 (direct-to-LDS pipeline with one dequantization per
-        // workgroup) select the others.
-        if (variant == 0) variant = 3;
-        if (variant == 1)
-            Q4_HIP(launch_gemm_regs(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
-        else if (variant == 3) {
-            // splits: 0 planned, 1 one workgroup per output tile, P >= 2
-            // workgroups sharing the tiles' k-iterations (stream-K)
-            const int tiles = gemm_tiles(M, h->N);
-            int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu) : splits == 1 ? tiles : splits;
-            // every workgroup must get at least one (tile, k-step) iteration:
-            // a split tile counts its contributors as a range of workgroups
-            workers = (int)std::min<long long>(workers, (long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK));
-            SkSpace ws;
-            if (workers != tiles) {
-                q4_status st = sk_workspace(h->device, h->num_cu, stream, workers, &ws);
-                if (st != Q4_OK) return st;
-                if (!ws.partials) {
-                    if (splits != 0)
-                        return fail(Q4_ERR_INVALID_ARG,
-                                    "q4_matmul: the stream-K workspace for %d workgroups must be made "
-                                    "under no stream capture; make one uncaptured call first", workers);
-                    workers = tiles;   // planned call under capture: one workgroup per tile
-                }
-            }
-            Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, workers, ws.partials, ws.counters, stream),
-                   "q4_matmul: gemm launch");
+        if (s > 1) {
+            q4_status st = ensure_partials(h, s, stream);
+            if (st != Q4_OK) return st;
         }
-        else
-            Q4_HIP(launch_gemm_dma(h, xe, bias, out, M, stream), "q4_matmul: gemm launch");
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, bf16, h->partials, h->counters, stream),
+               "q4_matmul: gemv launch");
+    } else {
+        // splits: 0 planned, 1 one workgroup per output tile, P >= 2
+        // workgroups sharing the tiles' k-iterations (stream-K)
+        const int tiles = gemm_tiles(M, h->N);
+        int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu) : splits == 1 ? tiles : splits;
+        // every workgroup must get at least one (tile, k-step) iteration:
+        // a split tile counts its contributors as a range of workgroups
+        workers = (int)std::min<long long>(workers, (long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK));
+        SkSpace ws;
+        if (workers != tiles) {
+            q4_status st = sk_workspace(h->device, h->num_cu, stream, workers, &ws);
+            if (st != Q4_OK) return st;
+            if (!ws.partials) {
+                if (splits != 0)
+                    return fail(Q4_ERR_INVALID_ARG,
+                                "q4_matmul: the stream-K workspace for %d workgroups must be made "
+                                "under no stream capture; make one uncaptured call first", workers);
+                workers = tiles;   // planned call under capture: one workgroup per tile
+            }
+        }
+        Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, workers, ws.partials, ws.counters, stream),
+               "q4_matmul: gemm launch");
     }
     return Q4_OK;
 }

@@ -5,10 +5,11 @@
 // multiple of 128), XL (act-order activations staged in LDS), BF (bfloat16
 // activations and output), W8 (8-bit codes; 4-bit otherwise).
 //
-// Weight-bound decoding is limited by memory bandwidth ("GPTQ's 'Exllama
-// Kernel Not Installed' Warning", section "What the fallback actually
-// does"), so the kernel streams the packed words once with 16-byte loads,
-// dequantizes them in registers and never writes a dequantized weight.
+// When the weights dominate the bytes moved, the speed of a decode step is
+// set by HBM bandwidth, not by arithmetic ("GPTQ's 'Exllama Kernel Not
+// Installed' Warning", section "What the fallback actually does"). So the
+// kernel reads each packed word once with 16-byte loads, turns it into
+// fp16 values in registers and never stores a dequantized weight.
 //
 // Mapping. A workgroup of 8 waves owns CT 16-column tiles (16 * CT output
 // columns); its waves split its K range in whole 128-row k-blocks.
@@ -528,9 +529,11 @@ hipError_t launch_w(const GemvArgs& p, int ngb, int ct, int splits, bool gather_
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                       int M, int col_tiles, int splits, bool gather_x, bool bf16, hipStream_t stream)
+                       int M, int col_tiles, int splits, bool gather_x, bool bf16, float* partials,
+                       uint32_t* counters, hipStream_t stream)
 {
     if (M < 1 || M > 16 || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+    if (splits > 1 && (!partials || !counters)) return hipErrorInvalidValue;
     if (gather_x && (!h->inv16 || !gemv_gathers_x(M, h->K, splits))) return hipErrorInvalidValue;
     GemvArgs p;
     p.qweight = h->qweight;
@@ -539,8 +542,8 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     p.inv = gather_x ? h->inv16 : nullptr;
     p.bias = bias;
     p.out = out;
-    p.partials = h->partials;
-    p.counters = h->counters;
+    p.partials = partials;
+    p.counters = counters;
     p.M = M;
     p.K = h->K;
     p.N = h->N;

@@ -118,8 +118,13 @@ struct q4_matrix {
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
     uint16_t* inv16 = nullptr;     // the same in 16 bits, when K <= kGemvXRows
-    // skinny-kernel split-K workspace: partial sums and arrival counters
-    float* partials = nullptr;     // [kMaxSplits][16][N]
+    // skinny-kernel split-K workspace: partial sums for up to partial_splits
+    // K splits, sized at make time for the largest split count the plan
+    // gives at any M <= 16 (none for most layers), grown on demand for an
+    // explicit larger count; and arrival counters
+    mutable float* partials = nullptr;     // [partial_splits][16][N]
+    mutable int partial_splits = 0;
+    mutable std::vector<float*> partials_retired;   // outgrown buffers, freed with the handle
     uint32_t* counters = nullptr;  // [ceil(N / 16)]: one per column tile at the narrowest tiling
     // act-order activation workspace, grown on demand: x[:, perm] as fp16 [M][K]
     mutable std::mutex ws_mutex;

@@ -1,8 +1,9 @@
 // Make-time repack, act-order activation permute and the debug dequant dump.
 //
-// Repack ("runtime initialization can ... prepack tiles, shuffle
-// scales/zeros", GPTQModel wiki "Inference Backends", section "Packing,
-// conversion, and runtime initialization"): qweight is rewritten once into
+// Repack (GPTQModel wiki "Inference Backends", section "Packing, conversion,
+// and runtime initialization": a backend may rearrange the checkpoint's
+// tiles, scales and zeros into its own layout when it initializes): qweight
+// is rewritten once into
 // the kernels' private layout -- 128-row k-blocks of 16-byte chunks, word i
 // of chunk (b, kb, n) packing rows 32 * (4b + i) + 8 * kb .. +7 of column n,
 // chunks in 16-column tiles (q4_internal.h), each word in the nibble slot order of q4_device.h -- and,

@@ -28,8 +28,8 @@
  *    faults inside a kernel surface at the caller's next synchronization.
  *
  * Tensor formats (GPTQ checkpoint layout; "GPTQ's 'Exllama Kernel Not
- * Installed' Warning", section "Why the kernel is missing": 4-bit integers
- * packed into 32-bit words with a scale and a zero point per group; I/O
+ * Installed' Warning", section "Why the kernel is missing": 32-bit words
+ * carrying 4-bit codes, a scale and a zero point for each group; I/O
  * contract table of the Lorax page: qweight/qzeros int32, scales fp16, g_idx
  * int32 or absent, bits = 4):
  *  - qweight int32 [K/8][N]: word (r, n) holds the codes of input rows
@@ -44,6 +44,7 @@
 #ifndef Q4_H
 #define Q4_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -74,10 +75,10 @@ enum {
 #define Q4_GEMM_MAX_WORKERS 1024
 
 /*
- * q4_make -- build a handle from GPTQ tensors (Lorax page, Description: a
- * handle is constructed once from quantized weights, zero points, scales and
- * an optional group index; "detects whether the model uses activation
- * ordering by checking if g_idx is non-trivial").
+ * q4_make -- build a handle from GPTQ tensors (Lorax page, Description: the
+ * handle is made once from the packed weights, zero points, scales and an
+ * optional group index, and act-order is recognised from a g_idx that is not
+ * the identity grouping).
  *
  * Arguments: device pointers qweight and scales (required), qzeros (NULL for
  * a symmetric layer stored without zeros: every zero point is then
@@ -100,8 +101,11 @@ enum {
  * copied into handle-owned device memory in a private layout of the same
  * size (K rounded up to a multiple of 128 rows for the packed weights); the
  * caller keeps and may free or change its tensors afterwards; such
- * changes do not reach the handle (make a new one). The handle also owns a
- * small split-K workspace. It never holds a dequantized K x N matrix.
+ * changes do not reach the handle (make a new one). The handle also owns the
+ * skinny kernel's split-K workspace, sized for the largest K split its launch
+ * plan takes at any M <= 16 (16 x N fp32 per split; none when the plan never
+ * splits K, as for 4096-wide and wider layers on 256 CUs). It never holds a
+ * dequantized K x N matrix.
  *
  * Returns NULL on error (q4_last_status / q4_last_error tell why).
  */
@@ -142,7 +146,14 @@ q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uin
  * split between two workgroups) go to a workspace per (device, stream) that
  * the library allocates on the first call on that stream that needs it
  * (2 x 128 KiB + 4 bytes per workgroup: 128 MiB for 512 workgroups) and
- * keeps until the process ends; calls on one stream share it in order.
+ * keeps until the process ends; calls on one stream share it in order. A
+ * captured call keeps the workspace of the stream it was captured on, while
+ * a graph replays on whatever stream launches it: graphs holding GEMM calls
+ * captured on one stream (torch captures every graph on one shared side
+ * stream unless told otherwise) must not be replayed concurrently with each
+ * other or with uncaptured GEMM calls on that stream, or they race on its
+ * partial sums and arrival counters (wrong outputs, no error). Replays in
+ * stream order, one after the other, are safe.
  *
  * Act-order (non-trivial g_idx): the weights are stored in sorted-group
  * order, so the product needs the activations x[:, perm] (the Lorax GPTQ
@@ -170,8 +181,9 @@ q4_status q4_matmul(const q4_matrix* h, const uint16_t* x, uint16_t* out, int M,
 /*
  * q4_matmul_bias -- as q4_matmul, plus bias[n] added to the fp32 accumulator
  * before the single cast to fp16 (GPTQModel wiki, section "Numeric epilogues
- * and input gradients": bias joins the FP32 accumulator before the final
- * cast). bias may be NULL (then identical to q4_matmul).
+ * and input gradients": the bias is summed in FP32 with the product, and the
+ * result is rounded once at the end). bias may be NULL (then identical to
+ * q4_matmul).
  */
 q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
                          uint16_t* out, int M, hipStream_t stream);
@@ -183,20 +195,20 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
  *   skinny kernel: variant = 16-column MFMA tiles per wave, 0 (planned), 1, 2
  *                  or 4; splits = K splits across workgroups, 0 (planned) or
  *                  1..16;
- *   GEMM:          variant = 0 (automatic: 3), 1 (register-staged tiles),
- *                  2 (direct-to-LDS pipeline) or 3 (activations in LDS,
- *                  weights streamed into registers); splits = workgroups
- *                  of variant 3: 0 (planned, q4_plan_gemm), 1 (one per
- *                  output tile: 256 x 128, or 64 x 128 when M <= 512) or
- *                  2..Q4_GEMM_MAX_WORKERS (the
- *                  tiles' 64-row k-steps shared evenly, stream-K; a count
- *                  above the number of (tile, k-step) pairs is reduced to
- *                  it; under
- *                  stream capture only once the stream has a workspace that
- *                  large, else Q4_ERR_INVALID_ARG). Variants 1 and 2 take
- *                  splits 0 or 1 (else Q4_ERR_UNSUPPORTED).
+ *   GEMM:          variant = 0 or 3 (the same kernel: activations in LDS,
+ *                  weights streamed into registers); splits = workgroups:
+ *                  0 (planned, q4_plan_gemm), 1 (one per output tile:
+ *                  256 x 128, or 64 x 128 when M <= 512) or
+ *                  2..Q4_GEMM_MAX_WORKERS (the tiles' 64-row k-steps shared
+ *                  evenly, stream-K; a count above the number of (tile,
+ *                  k-step) pairs is reduced to it; under stream capture only
+ *                  once the stream has a workspace that large, else
+ *                  Q4_ERR_INVALID_ARG).
  * Anything else is Q4_ERR_INVALID_ARG. Results differ between paths,
- * variants and split counts only by fp32 rounding.
+ * tile widths and split counts only by fp32 rounding. An explicit skinny-kernel
+ * split count above the largest the plan takes for the handle grows its
+ * split-K workspace, which cannot happen under stream capture
+ * (Q4_ERR_INVALID_ARG there: make one uncaptured call with that count first).
  */
 q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
                        uint16_t* out, int M, int path, int variant, int splits,
@@ -227,12 +239,25 @@ q4_status q4_matmul_ex_bf16(const q4_matrix* h, const uint16_t* x, const uint16_
                             uint16_t* out, int M, int path, int variant, int splits,
                             hipStream_t stream);
 
-/* q4_free -- release a handle (NULL is allowed). The caller must have
- * synchronized every stream that used it. */
+/* q4_free -- release a handle and every device buffer it owns (NULL is
+ * allowed). The caller must have synchronized every stream that used it. The
+ * pages have no counterpart: their handle lives as long as the module holding
+ * it; a C ABI needs an explicit end of life. */
 void q4_free(q4_matrix* h);
 
-/* Status and message of the last failing call on this thread. */
+/*
+ * q4_last_status / q4_last_error -- the status and the reason of the last
+ * failing call on this thread (Q4_OK and "" before any failure). Every
+ * failure is returned, never replaced by a slower route: an explicitly
+ * requested backend whose checks fail raises rather than silently running
+ * another one, and the rejection keeps its specific reason (GPTQModel wiki
+ * "Inference Backends", section "Loading and selecting a backend", and the
+ * device-validation paragraph of "Hardware, dependency, and format
+ * requirements"). The message is thread-local and stays valid until the next
+ * failing call on the same thread.
+ */
 q4_status q4_last_status(void);
+const char* q4_last_error(void);
 /*
  * q4_make_cat -- one handle over the column concatenation of `parts` layers
  * (1 <= parts <= 64) that take the same input: QKV or gate/up projection
@@ -263,8 +288,6 @@ q4_matrix* q4_make_cat_bits(int parts, const int32_t* const* qweight, const int3
                             const uint16_t* const* scales, const int32_t* g_idx, int K, const int* N,
                             int groupsize, int bits);
 
-const char* q4_last_error(void);
-
 /*
  * q4_path_for -- the kernel q4_matmul would launch for this M (Q4_PATH_*),
  * or -1 for a NULL handle or M < 0. Lets a caller check which kernel runs
@@ -275,7 +298,11 @@ int q4_path_for(const q4_matrix* h, int M);
 
 /*
  * q4_dequant_dump -- debug: run the unpack + dequantize code of kernel `path`
- * (Q4_PATH_GEMV or Q4_PATH_MFMA) over the whole handle and write the fp16
+ * (the dequantized values a kernel computes, dumped in a debug mode so that
+ * the in-register unpack and dequantization of "GPTQ's 'Exllama Kernel Not
+ * Installed' Warning", section "What the fallback actually does", can be
+ * compared bit for bit with the plain definition s * (q - z)):
+ * kernel Q4_PATH_GEMV or Q4_PATH_MFMA, over the whole handle, writes the fp16
  * values that kernel feeds its multiply-accumulate to w[K][N] (device
  * buffer, caller-owned, original k order). Each value is
  * round-to-nearest-even of s * (q - z). Not on the hot path.
@@ -283,7 +310,8 @@ int q4_path_for(const q4_matrix* h, int M);
 q4_status q4_dequant_dump(const q4_matrix* h, int path, uint16_t* w, hipStream_t stream);
 
 /*
- * q4_dequant_dump_bf16 -- as q4_dequant_dump for the bfloat16 kernels: w is
+ * q4_dequant_dump_bf16 -- as q4_dequant_dump (same purpose and source) for
+ * the bfloat16 kernels: w is
  * bfloat16 [K][N]. Q4_PATH_GEMV: the skinny kernel's q - z in bfloat16 times
  * the fp32 scale, rounded once to bfloat16; Q4_PATH_MFMA: the bfloat16
  * weights the GEMM feeds its MFMA. Each value is round-to-nearest-even of
@@ -306,6 +334,22 @@ int q4_handle_info(const q4_matrix* h, int* K, int* N, int* groupsize, int* act_
 
 /* The handle's code width (4 or 8), or -1 for a NULL handle. */
 int q4_handle_bits(const q4_matrix* h);
+
+/*
+ * q4_read_probe -- measurement helper, not part of the product: enqueue one
+ * kernel on `stream` that reads `bytes` of device memory at buf with the
+ * skinny kernel's kind of load (16 bytes a lane, non-temporal) and no other
+ * work, so that timing it gives the achievable read rate of one launch of
+ * that size. Decode steps whose bytes are mostly weights run at the speed of
+ * memory, not arithmetic ("GPTQ's 'Exllama Kernel Not Installed' Warning",
+ * section "What the fallback actually does"); this is the ceiling the fused
+ * kernel's effective bandwidth is compared with. buf: device pointer, 16-byte aligned; bytes: a positive
+ * multiple of 16384; sink: device buffer of 256 uint32_t, written only when
+ * the folded data match a fixed constant (the caller ignores it). Returns
+ * Q4_ERR_INVALID_ARG for bad arguments (nothing enqueued), Q4_ERR_HIP if the
+ * launch fails.
+ */
+q4_status q4_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host-only planning helpers (no HIP calls; usable without a GPU).

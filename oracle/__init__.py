@@ -73,6 +73,8 @@ def _load():
               "q4o_matmul_fallback_ex", "q4o_matmul_fused_at_ex"):
         getattr(lib, f).restype = ctypes.c_int
     lib.q4o_num_threads.restype = ctypes.c_int
+    lib.q4o_set_num_threads.argtypes = [ctypes.c_int]
+    lib.q4o_set_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -112,6 +114,14 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(_load().q4o_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Threads for the oracle's parallel loops from now on; returns the
+    previous count. Results do not depend on it."""
+    if n < 1:
+        raise OracleError(f"thread count must be >= 1, got {n}")
+    return int(_load().q4o_set_num_threads(n))
 
 
 def num_groups(K: int, G: int) -> int:

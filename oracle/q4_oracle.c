@@ -11,12 +11,13 @@
  *
  * Sources:
  *  - "GPTQ's 'Exllama Kernel Not Installed' Warning", section "Why the kernel
- *    is missing": weights are 4-bit integers packed into 32-bit words with a
- *    scale and a zero point per group.
+ *    is missing": each 32-bit word of a checkpoint carries several 4-bit
+ *    codes, and every group of input rows has its own scale and zero point.
  *  - same page, section "What the fallback actually does": the fused kernel
  *    unpacks and dequantizes inside the multiply-accumulate; the fallback
  *    materializes the dequantized matrix and then runs an ordinary matmul;
- *    both reach the same answer. Both routes are written out below.
+ *    the two must produce identical products. Both routes are written out
+ *    below.
  *  - "Implementation: Predibase Lorax GPTQ Exllama V1", I/O contract table:
  *    qweight int32, qzeros int32, scales fp16, optional g_idx int32, bits = 4,
  *    groupsize = input features per group, output fp16.
@@ -480,4 +481,18 @@ int q4o_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* Threads the parallel loops use from now on (n >= 1); returns the previous
+ * count. Only the timing of a CPU baseline uses it: the results do not depend
+ * on it (each output element is one sequential sum over k). */
+int q4o_set_num_threads(int n)
+{
+    int prev = q4o_num_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
 }

@@ -6,8 +6,8 @@ method's arithmetic: no unpacking, no dequantization, no products. It only
 draws random tensors of the right dtype, shape and value distribution.
 
 Tensor formats (the GPTQ checkpoint layout, "GPTQ's 'Exllama Kernel Not
-Installed' Warning", section "Why the kernel is missing": 4-bit integers
-packed into 32-bit words, one scale and one zero point per group; the I/O
+Installed' Warning", section "Why the kernel is missing": 32-bit words
+carrying 4-bit codes, with a scale and a zero point for every group; the I/O
 contract table of "Implementation: Predibase Lorax GPTQ Exllama V1"):
 
 - ``qweight`` int32 ``[K/8, N]``: word (r, n) holds the 4-bit codes of rows

@@ -6,7 +6,7 @@ themselves rather than from an unpacking routine. Layout: qweight word (r, n)
 holds the code of row k = 8r+i in bits 4i..4i+3; qzeros word (g, c) holds the
 zero of column n = 8c+j in bits 4j..4j+3 (the packing stated for the tiny-layer
 workload; "GPTQ's 'Exllama Kernel Not Installed' Warning", section "Why the
-kernel is missing", says only that codes are packed into 32-bit words).
+kernel is missing", says only that 32-bit words carry the 4-bit codes).
 """
 from __future__ import annotations
 

@@ -76,14 +76,15 @@ def test_fused_columns_equal_part_handles(M, path):
     """Each column of the fused result is bit-identical to its part's own
     handle: the kernels treat columns independently and accumulate each in the
     same order (the skinny kernel is pinned to one column tile and no K split,
-    the GEMM to one variant, so both handles take the same plan)."""
+    the GEMM to one workgroup per output tile, so both handles take the same
+    plan)."""
     import gptq_bit_weight_amd as q4
     torch = torch_mod()
     parts = _parts(2048, (256, 512, 128), 128, M, 1, bias=(False,))
     announce(f"fused vs parts M={M} path={path}")
     W = _make(q4, torch, parts)
     x = _dev(torch, parts[0].x)
-    variant, splits = (1, 1) if path == 1 else (2, 0)
+    variant, splits = (1, 1) if path == 1 else (0, 1)
     y = W.matmul(x, path=path, variant=variant, splits=splits)
     singles = []
     for p in parts:

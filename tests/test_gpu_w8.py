@@ -74,7 +74,7 @@ def test_w8_dequant_dump_bit_exact(K, N, G, act, sym):
 def test_w8_small_codes_equal_4bit_layer(M, path):
     """Codes and zeros below 16: the 8-bit handle and the 4-bit handle of the
     same codes give the same output bit for bit (one column tile, no split,
-    GEMM variant 3 on both)."""
+    the GEMM on both)."""
     import gptq_bit_weight_amd as q4
     torch = torch_mod()
     rng = np.random.default_rng(M)
@@ -197,7 +197,7 @@ def test_w8_argument_errors():
     W = make_matrix(L, t)
     with pytest.raises(NotImplementedError, match="2 column tiles"):
         W.matmul(t["x"][:4].contiguous(), path=q4.PATH_GEMV, variant=4)
-    with pytest.raises(NotImplementedError, match="variant 3"):
+    with pytest.raises(ValueError, match="not 0 or 3"):
         W.matmul(t["x"], path=q4.PATH_MFMA, variant=2)
     with pytest.raises(NotImplementedError):
         q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], None, 128, bits=6)

@@ -5,9 +5,9 @@ a transposed operand in the oracle fails at least one of them.
 
 Passages:
  - "GPTQ's 'Exllama Kernel Not Installed' Warning", "Why the kernel is
-   missing": codes packed into 32-bit words, a scale and a zero per group.
+   missing": 32-bit words carrying 4-bit codes, one scale and zero per group.
  - same page, "What the fallback actually does": fused route and fallback
-   route reach the same answer.
+   route must give identical products.
  - "Implementation: Predibase Lorax GPTQ Exllama V1", Description and I/O
    contract: g_idx None or trivial means no act-order.
  - GPTQModel wiki "Inference Backends", "Runtime cache lifetime": the
