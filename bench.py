@@ -172,7 +172,11 @@ def per_launch_times(lib, torch, layers, min_launches, stream):
             for r in range(n):
                 ly.launch(lib, r % copies, cap)
         def timed_replay():
+            # one untimed replay ahead keeps the GPU busy while the timed one
+            # is enqueued, so the events do not include the host's launch
+            # latency
             with torch.cuda.stream(stream):
+                g.replay()
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -247,13 +251,19 @@ def time_steps(lib, torch, layers, copies, steps, warmup, stream, use_graph):
         while time.perf_counter() - w0 < WARM_S:
             run(0, copies)
             stream.synchronize()
-        run(0, warmup)
         torch.cuda.synchronize()
+        # The `warmup` steps (at least one graph of `copies` steps) are
+        # enqueued without waiting, so the GPU is still running them when the
+        # start event and the timed steps are enqueued: the events then time
+        # the K steps back to back on the GPU, not the host's graph launch
+        # latency in front of them (tens of microseconds, a large part of a
+        # short timed region).
+        run(0, max(warmup, copies))
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         wall0 = time.perf_counter()
         t0.record(stream)
-        run(warmup, steps)
+        run(max(warmup, copies), steps)
         t1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -397,6 +407,7 @@ def read_ceiling(lib, torch, stream, sizes):
                 stream.synchronize()
             times = []
             for _ in range(3):
+                g.replay()      # untimed, ahead of the timed replay (host launch latency)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -497,8 +508,9 @@ def bf16_block(q4, torch, synth, lib, stream, G, M, workload, copies, steps=500)
 def prefill_rates(q4, torch, synth, lib, stream, M=2048):
     """TFLOP/s of the prefill GEMM on the 7B MLP shapes: groupsize 128 and 32,
     and act-order at 128 (the weights are 23-26 MB; compute, not memory,
-    bounds these). Twenty launches are captured in one graph and replayed
-    three times after a warm-up replay; the median replay gives the time."""
+    bounds these). Twenty launches are captured in one graph, replayed for
+    WARM_S seconds, then three times (each behind an untimed replay); the
+    median replay gives the time."""
     out = {}
     reps = 20
     for K, N, G, act, xfmt, bits in ((4096, 11008, 128, False, "f16", 4), (11008, 4096, 128, False, "f16", 4),
@@ -519,8 +531,12 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
                 ly.launch(lib, 0, cap)
         times = []
         with torch.cuda.stream(stream):
-            g.replay()
+            w0 = time.perf_counter()
+            while time.perf_counter() - w0 < WARM_S:
+                g.replay()
+                stream.synchronize()
             for _ in range(3):
+                g.replay()      # untimed, ahead of the timed replay (host launch latency)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -538,6 +554,36 @@ def prefill_rates(q4, torch, synth, lib, stream, M=2048):
         del ly
     torch.cuda.empty_cache()
     return out
+
+
+def prefill_counter_run(q4, torch, synth, lib, M=2048, launches=10):
+    """Launches for counter runs (rocprofv3 --pmc): `launches` eager prefill
+    GEMMs on each 7B MLP shape (groupsize 128, the planned schedule), then 5
+    plain copies of 256 MiB as a reference of known size. Prints one JSON
+    line describing the launches to stderr."""
+    stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    meta = {"prefill_counters_run": True, "launches_per_shape": launches, "copy_bytes": 256 << 20,
+            "shapes": []}
+    for K, N in ((4096, 11008), (11008, 4096)):
+        L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("prefill", K, N, 128, False))
+        ly = Layer(q4, torch, f"prefill_{K}x{N}", L, 1)
+        with torch.cuda.stream(stream):
+            for _ in range(launches):
+                ly.launch(lib, 0, sp)
+        stream.synchronize()
+        meta["shapes"].append({"K": K, "N": N, "M": M, "flops": ly.flops, "weight_bytes": ly.bytes,
+                               "x_bytes": 2 * M * K, "out_bytes": 2 * M * N,
+                               "workers": q4.plan_gemm(M, N, K, torch.cuda.get_device_properties(0)
+                                                       .multi_processor_count)})
+        ly.close()
+    with torch.cuda.stream(stream):
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    log(json.dumps(meta))
 
 
 def secondary(q4, torch, synth, lib, stream):
@@ -581,6 +627,9 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="no timing: run 20 eager steps of the block, then 5 plain copies of "
                          "256 MiB (a reference of known size for HBM counters), for rocprofv3 --pmc")
+    ap.add_argument("--prefill-counters", action="store_true",
+                    help="no timing: 10 eager launches of the prefill GEMM at M = 2048 on each 7B MLP "
+                         "shape (groupsize 128), then 5 plain copies of 256 MiB, for rocprofv3 --pmc")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -603,6 +652,9 @@ def main():
     lib = q4.load_library()
     if args.secondary_only:
         print(json.dumps({"secondary": secondary(q4, torch, synth, lib, torch.cuda.Stream())}), flush=True)
+        return
+    if args.prefill_counters:
+        prefill_counter_run(q4, torch, synth, lib)
         return
     workload = "llama7b_block_decode"
     G, M = 128, 1
