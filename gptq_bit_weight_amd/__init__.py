@@ -29,6 +29,7 @@ _LIB_PATH = os.path.join(HERE, "libq4.so")
 PATH_NONE, PATH_GEMV, PATH_MFMA = 0, 1, 2
 GEMV_MAX_M = 16
 GEMM_MAX_WORKERS = 1024
+STATIC_SCRATCH_BYTES = 64 << 20     # Q4_STATIC_SCRATCH_BYTES: q4_matmul_static's per-GPU array
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_HIP, ERR_OOM = range(6)
 
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
     "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16", "q4_make_bits", "q4_make_cat_bits",
     "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm", "q4_read_probe",
+    "q4_matmul_static",
 )
 
 _lib = None
@@ -80,9 +82,10 @@ def load_library():
     lib.q4_matmul_bias.argtypes = [P, P, P, P, I, P]
     lib.q4_matmul_ex.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.q4_matmul_bf16.argtypes = [P, P, P, P, I, P]
+    lib.q4_matmul_static.argtypes = [P, P, P, P, I, P]
     lib.q4_matmul_ex_bf16.argtypes = [P, P, P, P, I, I, I, I, P]
     for f in (lib.q4_matmul, lib.q4_matmul_bias, lib.q4_matmul_ex, lib.q4_matmul_bf16,
-              lib.q4_matmul_ex_bf16):
+              lib.q4_matmul_ex_bf16, lib.q4_matmul_static):
         f.restype = I
     lib.q4_free.argtypes = [P]
     lib.q4_free.restype = None
@@ -360,6 +363,33 @@ class Q4Matrix:
         return out
 
     __call__ = matmul
+
+    def matmul_static(self, x, bias=None, out=None, *, stream=None):
+        """q4_matmul_static: as matmul(x, bias, out) for float16 activations
+        with the automatic launch, allocating no device memory (every
+        workspace is the library's static per-GPU array; calls that overlap
+        on one GPU race). `out` must be given by callers that cannot let
+        torch allocate."""
+        torch = _torch()
+        h = self._handle()
+        _dev_tensor(x, torch.float16, "x")
+        if x.dim() != 2 or x.shape[1] != self.K:
+            raise ValueError(f"x must be [M, {self.K}], got {tuple(x.shape)}")
+        M = int(x.shape[0])
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        else:
+            _dev_tensor(out, torch.float16, "out", (M, self.N))
+        if bias is not None:
+            _dev_tensor(bias, torch.float16, "bias", (self.N,))
+        for t, nm in ((x, "x"), (out, "out"), (bias, "bias")):
+            if t is not None and t.device != self.device:
+                raise ValueError(f"{nm} is on {t.device}, the matrix on {self.device}")
+        with torch.cuda.device(self.device):
+            st = load_library().q4_matmul_static(h, x.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                                 out.data_ptr(), M, _stream_ptr(stream))
+        _check(st, "q4_matmul_static")
+        return out
 
     def dequant_dump(self, path: int = PATH_GEMV, stream=None, dtype=None):
         """[K, N] in dtype (float16, or bfloat16 for the bfloat16 kernels): the

@@ -10,6 +10,11 @@
 
 #include "q4_internal.h"
 
+// The allocation-free entry point's workspace (q4_matmul_static): one copy
+// per GPU. Host code never passes this name to a kernel or a copy; it uses
+// the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[Q4_STATIC_SCRATCH_BYTES];
+
 namespace q4 {
 
 hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
@@ -71,6 +76,58 @@ q4_status check_device(int* dev, int* num_cu)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// ---- scratch of the allocation-free entry point (q4_matmul_static) -------
+// One array per GPU, placed in device memory when q4_make first looks it up
+// on that GPU and kept until the process ends: the first kStaticCounterBytes
+// hold arrival counters (the
+// skinny kernel's split-K or the GEMM's stream-K ones, which the kernels
+// return to zero), then an act-order call's x[:, perm], then fp32 partial
+// sums. Every q4_matmul_static call on a GPU uses that GPU's array, so calls
+// that overlap in time on one GPU race.
+constexpr size_t kStaticScratchBytes = (size_t)Q4_STATIC_SCRATCH_BYTES;
+constexpr size_t kStaticCounterBytes = 64 << 10;
+constexpr int kStaticCounters = (int)(kStaticCounterBytes / 4);
+
+__global__ void q4_zero_words_kernel(uint32_t* p, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
+}
+
+std::mutex g_static_mutex;
+auto* g_static = new std::map<int, unsigned char*>;   // device -> its copy of `scratch`
+
+// Set-up of the static scratch on `device` (the current one), once per device
+// and process, from q4_make (every handle is made on its device before any
+// call uses it): look up this device's address of `scratch` (the HIP runtime
+// places the array in device memory then) and clear its counters with a
+// small kernel on the null stream, which q4_make's closing synchronization
+// waits for. The kernels leave the counters at zero after every call.
+q4_status static_setup(int device)
+{
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    if (g_static->count(device)) return Q4_OK;
+    void* ptr = nullptr;
+    Q4_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "q4_make: static scratch address");
+    if (!ptr) return fail(Q4_ERR_HIP, "q4_make: no device address for the static scratch array");
+    hipLaunchKernelGGL(q4_zero_words_kernel, dim3((kStaticCounters + 255) / 256), dim3(256), 0, 0,
+                       static_cast<uint32_t*>(ptr), kStaticCounters);
+    Q4_HIP(hipGetLastError(), "q4_make: clear the static counters");
+    (*g_static)[device] = static_cast<unsigned char*>(ptr);
+    return Q4_OK;
+}
+
+// This device's copy of `scratch`, set up by q4_make.
+q4_status static_scratch(int device, unsigned char** base)
+{
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    auto it = g_static->find(device);
+    if (it == g_static->end())
+        return fail(Q4_ERR_INVALID_ARG, "q4_matmul_static: no handle was made on device %d", device);
+    *base = it->second;
+    return Q4_OK;
+}
+
 // One handle over the column concatenation of `parts` layers that share K,
 // groupsize and g_idx (part i supplies columns [off_i, off_i + N[i]) of the
 // result, in part order). q4_make is the one-part case.
@@ -104,6 +161,8 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     if (st != Q4_OK) return st;
     // The inputs may still be being written by work on other streams.
     Q4_HIP(hipDeviceSynchronize(), "q4_make: synchronize");
+    st = static_setup(dev);
+    if (st != Q4_OK) return st;
 
     const int ng = K / G;
     std::vector<int32_t> perm;
@@ -319,8 +378,12 @@ q4_status check_current(const q4_matrix* h, const char* who)
     return Q4_OK;
 }
 
+// `stat`: q4_matmul_static (every workspace from the device's scratch
+// array, nothing allocated); otherwise workspaces are the handle's and the
+// stream's, allocated or grown on demand.
 q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                      int M, int path, int variant, int splits, bool bf16, hipStream_t stream)
+                      int M, int path, int variant, int splits, bool bf16, hipStream_t stream,
+                      bool stat = false)
 {
     if (!h) return fail(Q4_ERR_INVALID_ARG, "q4_matmul: null handle");
     if (q4_status st = check_current(h, "q4_matmul"); st != Q4_OK) return st;
@@ -366,19 +429,56 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         // in LDS itself when all of it fits
         gather = h->act_order && h->inv16 && gemv_gathers_x(M, h->K, s);
     }
+    // Static scratch: [counters | x[:, perm] (act-order without staging) |
+    // fp32 partials]. The sizes are fixed before anything is launched.
+    unsigned char* base = nullptr;
+    size_t xp_bytes = 0, part_bytes = 0;
+    if (stat) {
+        if (h->act_order && !gather) {
+            xp_bytes = ((size_t)M * h->K * 2 + 255) & ~(size_t)255;
+            if (xp_bytes > kStaticScratchBytes - kStaticCounterBytes)
+                return fail(Q4_ERR_UNSUPPORTED,
+                            "q4_matmul_static: the act-order activations (M*K*2 = %zu bytes) exceed the "
+                            "%zu-byte static workspace; use q4_matmul_bias",
+                            (size_t)M * h->K * 2, kStaticScratchBytes - kStaticCounterBytes);
+        }
+        part_bytes = kStaticScratchBytes - kStaticCounterBytes - xp_bytes;
+        if (kind == Q4_PATH_GEMV) {
+            // fewer K splits when their partials or counters do not fit (the
+            // plan's counts are powers of two)
+            while (s > 1 && ((size_t)s * 16 * h->N * 4 > part_bytes || (h->N + 15) / 16 > kStaticCounters)) s /= 2;
+            gather = h->act_order && h->inv16 && gemv_gathers_x(M, h->K, s);
+            if (h->act_order && !gather && xp_bytes == 0)
+                return fail(Q4_ERR_UNSUPPORTED, "q4_matmul_static: no room for the act-order activations");
+        }
+        q4_status st = static_scratch(h->device, &base);
+        if (st != Q4_OK) return st;
+    }
     const uint16_t* xe = x;
     if (h->act_order && !gather) {
-        q4_status st = ensure_xperm(h, M, stream);
-        if (st != Q4_OK) return st;
-        Q4_HIP(launch_permute_x(x, h->perm, h->xperm, M, h->K, stream), "q4_matmul: permute launch");
-        xe = h->xperm;
+        uint16_t* xp = nullptr;
+        if (stat) {
+            xp = reinterpret_cast<uint16_t*>(base + kStaticCounterBytes);
+        } else {
+            q4_status st = ensure_xperm(h, M, stream);
+            if (st != Q4_OK) return st;
+            xp = h->xperm;
+        }
+        Q4_HIP(launch_permute_x(x, h->perm, xp, M, h->K, stream), "q4_matmul: permute launch");
+        xe = xp;
     }
     if (kind == Q4_PATH_GEMV) {
-        if (s > 1) {
+        float* partials = h->partials;
+        uint32_t* counters = h->counters;
+        if (stat) {
+            partials = reinterpret_cast<float*>(base + kStaticCounterBytes + xp_bytes);
+            counters = reinterpret_cast<uint32_t*>(base);
+        } else if (s > 1) {
             q4_status st = ensure_partials(h, s, stream);
             if (st != Q4_OK) return st;
+            partials = h->partials;
         }
-        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, bf16, h->partials, h->counters, stream),
+        Q4_HIP(launch_gemv(h, xe, bias, out, M, ct, s, gather, bf16, partials, counters, stream),
                "q4_matmul: gemv launch");
     } else {
         // splits: 0 planned, 1 one workgroup per output tile, P >= 2
@@ -389,7 +489,17 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         // a split tile counts its contributors as a range of workgroups
         workers = (int)std::min<long long>(workers, (long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK));
         SkSpace ws;
-        if (workers != tiles) {
+        if (stat && workers != tiles) {
+            // as many stream-K workgroups as the plan asks for and the
+            // partials region holds (two slots of bm x 128 fp32 each), else
+            // one workgroup per tile
+            const size_t per_worker = 2 * (size_t)gemm_bm(M) * kGemmBN * sizeof(float);
+            workers = (int)std::min<size_t>((size_t)workers, part_bytes / per_worker);
+            workers = std::min(workers, kStaticCounters);
+            if (workers < 2) workers = tiles;
+            ws.partials = reinterpret_cast<float*>(base + kStaticCounterBytes + xp_bytes);
+            ws.counters = reinterpret_cast<uint32_t*>(base);
+        } else if (workers != tiles) {
             q4_status st = sk_workspace(h->device, h->num_cu, stream, workers, &ws);
             if (st != Q4_OK) return st;
             if (!ws.partials) {
@@ -468,6 +578,12 @@ q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
     if (path != 0 && path != Q4_PATH_GEMV && path != Q4_PATH_MFMA)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_matmul_ex: unknown path %d", path);
     return q4::matmul_impl(h, x, bias, out, M, path, variant, splits, false, stream);
+}
+
+q4_status q4_matmul_static(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
+                           int M, hipStream_t stream)
+{
+    return q4::matmul_impl(h, x, bias, out, M, 0, 0, 0, false, stream, true);
 }
 
 q4_status q4_matmul_bf16(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,

@@ -214,6 +214,40 @@ q4_status q4_matmul_ex(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
                        uint16_t* out, int M, int path, int variant, int splits,
                        hipStream_t stream);
 
+/* Bytes of the per-GPU scratch array q4_matmul_static works in (64 MiB). */
+#define Q4_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * q4_matmul_static -- q4_matmul_bias for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It allocates nothing (no hipMalloc, hipFree or allocating
+ * library call): every workspace the call needs (the skinny kernel's split-K
+ * partial sums and arrival counters, an act-order layer's permuted
+ * activations, the GEMM's stream-K partial sums and counters) lives in one
+ * static array of Q4_STATIC_SCRATCH_BYTES per GPU. The array is set up when
+ * the first handle is made on a GPU (q4_make looks up its device address, at
+ * which point the HIP runtime places it in device memory, and clears its
+ * counters) and is kept until the process ends.
+ *
+ * Arguments, result, numerics and errors as q4_matmul_bias (fp16 x, bias,
+ * out). The launch plan is q4_matmul_bias's, except that the skinny kernel's
+ * K splits are halved, and the GEMM's stream-K workgroups reduced, until
+ * their partial sums fit the array (results then differ from q4_matmul_bias
+ * only by fp32 rounding; with the plans of the 7B and 70B layers they are the
+ * same bits). An act-order call that needs the separate permute (M > 2, or K
+ * split) stores x[:, perm] in the array too: M * K * 2 bytes must fit in
+ * Q4_STATIC_SCRATCH_BYTES - 64 KiB, else Q4_ERR_UNSUPPORTED with nothing
+ * enqueued.
+ *
+ * Concurrency: every q4_matmul_static call on a GPU shares that GPU's array,
+ * which keeps the last call's contents, so calls that overlap in time on one
+ * GPU (other streams, concurrent graph replays) race and give wrong results
+ * without an error; order them on one stream. Every call leaves the arrival
+ * counters at zero.
+ */
+q4_status q4_matmul_static(const q4_matrix* h, const uint16_t* x, const uint16_t* bias,
+                           uint16_t* out, int M, hipStream_t stream);
+
 /*
  * q4_matmul_bf16 -- q4_matmul_bias with bfloat16 activations, bias and output
  * (GPTQModel wiki "Inference Backends", hardware table, ExLlama v2 row: the
