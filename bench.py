@@ -26,8 +26,9 @@ Also reported on the same JSON line:
   cpu_baseline  the CPU oracle's fused route on whole layers of the block;
   secondary     the same block with q/k/v and gate/up fused into one call each
                 (4 launches a step); the 70B-shaped MLP layers at M = 1, 2, 4,
-                8, 16 and the act-order 7B MLP layers at M = 1, 4 (GB/s, each
-                layer over >= 1 GiB of copies); the 7B MLP layers with 8-bit
+                8, 16, the 7B MLP layers at M = 17 .. 256 and the act-order
+                7B MLP layers at M = 1, 4 (GB/s, each layer over >= 1 GiB of
+                copies); the 7B MLP layers with 8-bit
                 weights at M = 1, 4; the seven-layer block with bfloat16
                 activations; the prefill GEMM at M = 2048 on the 7B MLP
                 shapes, groupsize 128 and 32, act-order, bfloat16 and 8-bit
@@ -588,9 +589,10 @@ def prefill_counter_run(q4, torch, synth, lib, M=2048, launches=10):
 
 def secondary(q4, torch, synth, lib, stream):
     """Figures on the other workloads: the 7B block with projection fusion
-    and with bfloat16 activations, the 70B MLP layers at M = 1, 2, 4, 8, 16 (where the skinny kernel stops
-    being bandwidth-bound), the 7B MLP layers at M = 17 .. 256 (small
-    batches on the GEMM), the 8-bit and act-order 7B MLP layers at M = 1
+    and with bfloat16 activations, the 70B MLP layers at M = 1, 2, 4, 8, 16
+    (where the skinny kernel stops being bandwidth-bound), the 7B MLP layers
+    at M = 17 .. 256 (small batches: the skinny kernel's two row blocks up
+    to 32, the GEMM above), the 8-bit and act-order 7B MLP layers at M = 1
     and 4, and the prefill GEMM at M = 2048."""
     out = {}
     out["llama7b_block_fused_m1"] = fused_block(q4, torch, synth, lib, stream, 128, 1,
@@ -599,10 +601,11 @@ def secondary(q4, torch, synth, lib, stream):
                                               "llama7b_block_decode", 10)
     out["llama70b_mlp_decode"] = decode_sweep(q4, torch, synth, lib, stream, "llama70b_mlp_decode",
                                               synth.LLAMA70B_MLP, (1, 2, 4, 8, 16))
-    # batches past the skinny kernel's 16 rows (the GEMM's 64-row tiles)
+    # batches past 16 rows: the skinny kernel's two row blocks up to 32,
+    # then the GEMM's 64-row tiles
     out["llama7b_mlp_small_batch"] = decode_sweep(
         q4, torch, synth, lib, stream, "llama7b_mlp_small_batch",
-        (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (17, 32, 64, 128, 256))
+        (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (17, 24, 32, 33, 64, 128, 256))
     out["llama7b_mlp_w8_decode"] = decode_sweep(
         q4, torch, synth, lib, stream, "llama7b_mlp_w8_decode",
         (("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)), (1, 4), bits=8)

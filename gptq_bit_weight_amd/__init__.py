@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libq4.so")
 
 PATH_NONE, PATH_GEMV, PATH_MFMA = 0, 1, 2
-GEMV_MAX_M = 16
+GEMV_MAX_M = 32          # Q4_GEMV_MAX_M: most rows the skinny kernel takes
 GEMM_MAX_WORKERS = 1024
 STATIC_SCRATCH_BYTES = 64 << 20     # Q4_STATIC_SCRATCH_BYTES: q4_matmul_static's per-GPU array
 

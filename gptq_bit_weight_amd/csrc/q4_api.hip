@@ -198,18 +198,19 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
     const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
     if ((e = hipMalloc(&h->qzeros, (size_t)ng * zrow)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
     if ((e = hipMalloc(&h->sz, (size_t)ng * N * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
-    // Split-K partials for the largest K split the plan takes at any M the
-    // skinny kernel serves (1 for most layers: then none).
-    int max_splits = 1;
-    for (int m = 1; m <= Q4_GEMV_MAX_M; ++m) {
+    // Split-K partials for the largest splits x M the plan takes at any M
+    // the automatic dispatch gives the skinny kernel (none for most layers).
+    int max_rows = 0;
+    for (int m = 1; m <= kGemvMaxM; ++m) {
+        if (!gemv_serves(m, K, N, G, bits)) continue;
         int ct = 0, sp = 0;
         plan_gemv(m, K, N, G, num_cu, &ct, &sp, bits);
-        max_splits = std::max(max_splits, sp);
+        if (sp > 1) max_rows = std::max(max_rows, sp * m);
     }
-    if (max_splits > 1) {
-        if ((e = hipMalloc(&h->partials, (size_t)max_splits * 16 * N * 4)) != hipSuccess)
+    if (max_rows > 0) {
+        if ((e = hipMalloc(&h->partials, (size_t)max_rows * N * 4)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: workspace"));
-        h->partial_splits = max_splits;
+        h->partial_rows = max_rows;
     }
     const int col_tiles = (N + 15) / 16;
     if ((e = hipMalloc(&h->counters, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
@@ -266,11 +267,10 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
 
 int choose_path(const q4_matrix* h, int M, int forced)
 {
-    (void)h;
     if (M == 0) return Q4_PATH_NONE;
     if (forced == Q4_PATH_MFMA) return Q4_PATH_MFMA;
-    if (forced == Q4_PATH_GEMV) return M <= Q4_GEMV_MAX_M ? Q4_PATH_GEMV : -1;
-    return M <= Q4_GEMV_MAX_M ? Q4_PATH_GEMV : Q4_PATH_MFMA;
+    if (forced == Q4_PATH_GEMV) return M <= kGemvMaxM ? Q4_PATH_GEMV : -1;
+    return gemv_serves(M, h->K, h->N, h->G, h->bits) ? Q4_PATH_GEMV : Q4_PATH_MFMA;
 }
 
 // Grow the act-order activation workspace to hold M x K halfs.
@@ -297,25 +297,26 @@ q4_status ensure_xperm(const q4_matrix* h, int M, hipStream_t stream)
     return Q4_OK;
 }
 
-// Grow the skinny kernel's split-K partials to hold `splits` splits (an
-// explicit split count above the planned ones).
-q4_status ensure_partials(const q4_matrix* h, int splits, hipStream_t stream)
+// Grow the skinny kernel's split-K partials to hold splits x M rows (an
+// explicit split count, or explicit skinny-kernel M, above the planned ones).
+q4_status ensure_partials(const q4_matrix* h, int splits, int M, hipStream_t stream)
 {
     std::lock_guard<std::mutex> lock(h->ws_mutex);
-    if (h->partial_splits >= splits) return Q4_OK;
+    const int rows = splits * M;
+    if (h->partial_rows >= rows) return Q4_OK;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
     if (cap != hipStreamCaptureStatusNone)
         return fail(Q4_ERR_INVALID_ARG,
-                    "q4_matmul: the split-K workspace must grow to %d splits under stream capture; "
-                    "make one uncaptured call with this split count first", splits);
+                    "q4_matmul: the split-K workspace must grow to %d splits of %d rows under stream "
+                    "capture; make one uncaptured call with this split count and M first", splits, M);
     float* fresh = nullptr;
-    Q4_HIP(hipMalloc(&fresh, (size_t)splits * 16 * h->N * 4), "q4_matmul: split-K workspace");
+    Q4_HIP(hipMalloc(&fresh, (size_t)rows * h->N * 4), "q4_matmul: split-K workspace");
     // earlier launches (and graphs captured from them) may still use the old
     // buffer: retire it, freed with the handle
     if (h->partials) h->partials_retired.push_back(h->partials);
     h->partials = fresh;
-    h->partial_splits = splits;
+    h->partial_rows = rows;
     return Q4_OK;
 }
 
@@ -403,7 +404,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
     const int kind = choose_path(h, M, path);
     if (kind < 0)
         return fail(Q4_ERR_INVALID_ARG, "q4_matmul: the skinny kernel takes M <= %d (M=%d)",
-                    Q4_GEMV_MAX_M, M);
+                    kGemvMaxM, M);
     if (kind == Q4_PATH_GEMV) {
         if (splits < 0 || splits > kMaxSplits)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: splits=%d outside [0, %d]", splits, kMaxSplits);
@@ -446,7 +447,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (kind == Q4_PATH_GEMV) {
             // fewer K splits when their partials or counters do not fit (the
             // plan's counts are powers of two)
-            while (s > 1 && ((size_t)s * 16 * h->N * 4 > part_bytes || (h->N + 15) / 16 > kStaticCounters)) s /= 2;
+            while (s > 1 && ((size_t)s * M * h->N * 4 > part_bytes || (h->N + 15) / 16 > kStaticCounters)) s /= 2;
             gather = h->act_order && h->inv16 && gemv_gathers_x(M, h->K, s);
             if (h->act_order && !gather && xp_bytes == 0)
                 return fail(Q4_ERR_UNSUPPORTED, "q4_matmul_static: no room for the act-order activations");
@@ -474,7 +475,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
             partials = reinterpret_cast<float*>(base + kStaticCounterBytes + xp_bytes);
             counters = reinterpret_cast<uint32_t*>(base);
         } else if (s > 1) {
-            q4_status st = ensure_partials(h, s, stream);
+            q4_status st = ensure_partials(h, s, M, stream);
             if (st != Q4_OK) return st;
             partials = h->partials;
         }
@@ -610,7 +611,7 @@ int q4_path_for(const q4_matrix* h, int M)
 
 int q4_gemv_gather(const q4_matrix* h, int M, int splits)
 {
-    if (!h || M < 1 || M > Q4_GEMV_MAX_M || splits < 0 || splits > q4::kMaxSplits) return -1;
+    if (!h || M < 1 || M > q4::kGemvMaxM || splits < 0 || splits > q4::kMaxSplits) return -1;
     if (!h->act_order || !h->inv16) return 0;
     int ct = 0, s = 0;
     q4::plan_gemv(M, h->K, h->N, h->G, h->num_cu, &ct, &s, h->bits);

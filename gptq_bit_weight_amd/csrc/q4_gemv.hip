@@ -1,9 +1,15 @@
-// Skinny fused GPTQ kernel for 1 <= M <= 16 (decode).
+// Skinny fused GPTQ kernel for 1 <= M <= 32 (decode and small batches).
 //
-// q4_gemv_kernel<NGB, CT, XS, TAIL, XL, BF, W8>: NGB groups per 128-row block,
-// CT 16-column tiles per wave, XS k-steps per activation load, TAIL (K not a
-// multiple of 128), XL (act-order activations staged in LDS), BF (bfloat16
-// activations and output), W8 (8-bit codes; 4-bit otherwise).
+// q4_gemv_kernel<NGB, CT, XS, TAIL, XL, BF, W8, MB>: NGB groups per 128-row
+// block, CT 16-column tiles per wave, XS k-steps per activation load, TAIL (K
+// not a multiple of 128), XL (act-order activations staged in LDS), BF
+// (bfloat16 activations and output), W8 (8-bit codes; 4-bit otherwise), MB
+// blocks of 16 activation rows (1 for M <= 16; 2 for 16 < M <= 32, which
+// load one k-step per activation load and share each unpacked weight
+// fragment between the two row blocks' MFMAs). (Four row blocks, M <= 64,
+// measured 1.4-2.5x slower than the GEMM on the 7B and 70B MLP shapes: their
+// activation registers leave room for two column tiles at one workgroup per
+// CU, and the activation loads grow with every row block.)
 //
 // When the weights dominate the bytes moved, the speed of a decode step is
 // set by HBM bandwidth, not by arithmetic ("GPTQ's 'Exllama Kernel Not
@@ -71,10 +77,12 @@ using namespace q4dev;
 
 constexpr int WV = q4::kGemvWaves;     // waves per workgroup
 constexpr int NT = 64 * WV;            // threads per workgroup
-// k-blocks in flight per wave: kGemvDepth for one column tile, half that for
-// two or four (their buffers are larger; this keeps two workgroups per CU).
-template <int CT>
-constexpr int depth() { return CT >= 2 ? q4::kGemvDepth / 2 : q4::kGemvDepth; }
+// k-blocks in flight per wave: kGemvDepth for one column tile and one row
+// block, half that for wider tiles or more row blocks (their buffers are
+// larger; this keeps two workgroups per CU for M <= 16 and the register file
+// unspilled for M > 16).
+template <int CT, int MB>
+constexpr int depth() { return (CT >= 2 || MB > 1) ? q4::kGemvDepth / 2 : q4::kGemvDepth; }
 
 struct GemvArgs {
     const uint32_t* qweight;
@@ -101,10 +109,10 @@ struct GemvArgs {
 template <bool W8>
 constexpr int wl() { return W8 ? 2 : 1; }
 
-template <int NGB, int CT, bool W8>
+template <int NGB, int CT, bool W8, int MB>
 struct Block {
     u4 w[CT][wl<W8>()];
-    u4 a[4];
+    u4 a[MB][4];            // row block r: activation rows 16 r + (lane % 16)
     uint32_t sz[NGB][CT];   // scale bits | zero << 16
 };
 
@@ -132,8 +140,8 @@ struct Rsrc {
 // XS = k-steps per activation load (1, 2 or 4); B.a[0 .. 4/XS - 1] are loaded.
 // XL: the activations come from the workgroup's LDS copy instead; they are
 // read when the block is multiplied.
-template <int NGB, int CT, int XS, bool TAIL, bool XL, bool W8>
-__device__ __forceinline__ void load_block(Block<NGB, CT, W8>& B, const GemvArgs& p, const Rsrc& r,
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool W8, int MB>
+__device__ __forceinline__ void load_block(Block<NGB, CT, W8, MB>& B, const GemvArgs& p, const Rsrc& r,
                                            const Lane<CT>& ln, int b)
 {
     const uint32_t wso = (uint32_t)b * (uint32_t)p.N * 64u * wl<W8>();
@@ -143,11 +151,16 @@ __device__ __forceinline__ void load_block(Block<NGB, CT, W8>& B, const GemvArgs
         for (int v = 0; v < wl<W8>(); ++v) B.w[j][v] = buf_load16_nt(r.w, ln.w[j] + 16u * v, wso);
     const int ksteps = p.K >> 5;
     if constexpr (!XL) {
+        // (row block rb starts 16 rb rows, 32 rb K bytes, further into x;
+        // rows past M lie past its end and read zeros)
 #pragma unroll
-        for (int i = 0; i < 4 / XS; ++i) {
-            const rsrc_t rx = (!TAIL || 4 * b + i < ksteps) ? r.x : r.none;
-            B.a[i] = buf_load16(rx, ln.x + 64u * XS * i, (uint32_t)b * 256u);
-        }
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4 / XS; ++i) {
+                const rsrc_t rx = (!TAIL || 4 * b + i < ksteps) ? r.x : r.none;
+                B.a[rb][i] = buf_load16(rx, ln.x + (uint32_t)rb * 32u * (uint32_t)p.K + 64u * XS * i,
+                                        (uint32_t)b * 256u);
+            }
     }
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
@@ -191,19 +204,21 @@ __device__ __forceinline__ u4 a_operand(const u4 a[4], int i)
 // the exact q - z as bfloat16 (both operands bfloat16 on the matrix pipe).
 // XL: block b's activations are read from the LDS copy (xl = this lane's
 // address in it for the first block of the workgroup's range, bs0).
-template <int NGB, int CT, int XS, bool XL, bool BF, bool W8>
-__device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 tot[CT], const char* xl,
-                                              int b, int bs0)
+template <int NGB, int CT, int XS, bool XL, bool BF, bool W8, int MB>
+__device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f4 (&tot)[MB][CT],
+                                              const char* xl, int b, int bs0)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
-    u4 av[4];
+    u4 av[MB][4];
     if constexpr (XL) {
         const char* src = xl + (b - bs0) * 256;
 #pragma unroll
-        for (int i = 0; i < 4 / XS; ++i) av[i] = *reinterpret_cast<const u4*>(src + 64 * XS * i);
+        for (int i = 0; i < 4 / XS; ++i) av[0][i] = *reinterpret_cast<const u4*>(src + 64 * XS * i);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4 / XS; ++i) av[i] = B.a[i];
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4 / XS; ++i) av[rb][i] = B.a[rb][i];
     }
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
@@ -221,32 +236,40 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8>& B, f4 to
             else zp[j] = zero_pair(z);
             sf[j] = f16_bits_to_f32((uint16_t)B.sz[gi][j]);
         }
-        f4 acc[CT];
+        f4 acc[MB][CT];
 #pragma unroll
         for (int ii = 0; ii < SPG; ++ii) {
             const int i = gi * SPG + ii;
-            const u4 a = a_operand<XS>(av, i);
             const f4 c0 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < CT; ++j) {
+                // the B operand of tile j at k-step i, unpacked once for the
+                // MB row blocks
+                u4 bw;
                 if constexpr (W8) {
                     // k-step i: words 2i, 2i + 1 of the lane's 32-byte chunk
                     const uint32_t w0 = B.w[j][i >> 1][2 * (i & 1)], w1 = B.w[j][i >> 1][2 * (i & 1) + 1];
-                    if constexpr (BF)
-                        acc[j] = mfma16(bitcast<b8>(a), mix_word8(w0, w1, mz[j]), ii == 0 ? c0 : acc[j]);
-                    else
-                        acc[j] = mfma16(bitcast<h8>(a), sub_zero_word8(w0, w1, zp[j]), ii == 0 ? c0 : acc[j]);
+                    if constexpr (BF) bw = bitcast<u4>(mix_word8(w0, w1, mz[j]));
+                    else bw = bitcast<u4>(sub_zero_word8(w0, w1, zp[j]));
                 } else if constexpr (BF) {
-                    acc[j] = mfma16(bitcast<b8>(a), mix_word(B.w[j][0][i], mz[j]), ii == 0 ? c0 : acc[j]);
+                    bw = bitcast<u4>(mix_word(B.w[j][0][i], mz[j]));
                 } else {
-                    acc[j] = mfma16(bitcast<h8>(a), sub_zero_word(B.w[j][0][i], zp[j]), ii == 0 ? c0 : acc[j]);
+                    bw = bitcast<u4>(sub_zero_word(B.w[j][0][i], zp[j]));
+                }
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb) {
+                    const u4 a = a_operand<XS>(av[rb], i);
+                    if constexpr (BF) acc[rb][j] = mfma16(bitcast<b8>(a), bitcast<b8>(bw), ii == 0 ? c0 : acc[rb][j]);
+                    else acc[rb][j] = mfma16(bitcast<h8>(a), bitcast<h8>(bw), ii == 0 ? c0 : acc[rb][j]);
                 }
             }
         }
 #pragma unroll
-        for (int j = 0; j < CT; ++j)
+        for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tot[j][e] = __builtin_fmaf(sf[j], acc[j][e], tot[j][e]);
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tot[rb][j][e] = __builtin_fmaf(sf[j], acc[rb][j][e], tot[rb][j][e]);
     }
 }
 
@@ -283,11 +306,12 @@ __device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR]
         }
 }
 
-template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8>
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB>
 __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 {
     constexpr int COLS = 16 * CT;
-    __shared__ float red[WV][16][COLS];
+    constexpr int ROWS = 16 * MB;
+    __shared__ float red[WV][ROWS][COLS];
     __shared__ int last_flag;
     extern __shared__ u4 xs_dyn[];   // XL: the workgroup's activations, [M][ldx] halfs
 
@@ -337,11 +361,13 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     const char* xl = reinterpret_cast<const char*>(
         xs + (size_t)min(c16 % R, p.M - 1) * p.ldx + 8 * kb + 32 * (c16 / R));
 
-    f4 tot[CT];
+    f4 tot[MB][CT];
 #pragma unroll
-    for (int j = 0; j < CT; ++j) tot[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) tot[rb][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int D = depth<CT>();
+    constexpr int D = depth<CT, MB>();
     // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
     // Once a block is multiplied its buffer is refilled with the block D
     // further on. Past the wave's last block the loads repeat that block
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     // worse of two orders), and no work of a later block (which would
     // wait for its loads) is hoisted into an earlier one.
     const int bl = b0 + nb - 1;
-    Block<NGB, CT, W8> buf[D];
+    Block<NGB, CT, W8, MB> buf[D];
     // XL: the first XR activation rows and the sorted positions go out
     // before the weights, so storing them waits for them alone.
     constexpr int XJ = XL ? q4::kGemvXUnits : 1;
@@ -373,7 +399,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     if (XL || nb > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            load_block<NGB, CT, XS, TAIL, XL, W8>(buf[d], p, r, ln, min(b0 + d, bl));
+            load_block<NGB, CT, XS, TAIL, XL, W8, MB>(buf[d], p, r, ln, min(b0 + d, bl));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -393,26 +419,28 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, xl, b0 + D * (rd - 1) + d, bs0);
-                load_block<NGB, CT, XS, TAIL, XL, W8>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
+                compute_block<NGB, CT, XS, XL, BF, W8, MB>(buf[d], tot, xl, b0 + D * (rd - 1) + d, bs0);
+                load_block<NGB, CT, XS, TAIL, XL, W8, MB>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8>(buf[d], tot, xl, b0 + D * (rounds - 1) + d, bs0);
+            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8, MB>(buf[d], tot, xl, b0 + D * (rounds - 1) + d, bs0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // Cross-wave reduction. Lane l holds rows 4 * (l / 16) + i of column l % 16
-    // of each tile (16x16 MFMA output layout).
+    // Cross-wave reduction. Lane l holds rows 16 rb + 4 * (l / 16) + i of
+    // column l % 16 of each tile (16x16 MFMA output layout).
 #pragma unroll
-    for (int j = 0; j < CT; ++j)
+    for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * kb + i < p.M) red[wave][4 * kb + i][16 * j + c16] = tot[j][i];
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * rb + 4 * kb + i < p.M) red[wave][16 * rb + 4 * kb + i][16 * j + c16] = tot[rb][j][i];
     __syncthreads();
 
     const int n_elems = p.M * COLS;
@@ -442,7 +470,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         float y = red[0][m][c];
 #pragma unroll
         for (int w = 1; w < WV; ++w) y += red[w][m][c];
-        __hip_atomic_store(&p.partials[((size_t)split * 16 + m) * p.N + n], y, __ATOMIC_RELAXED,
+        __hip_atomic_store(&p.partials[((size_t)split * p.M + m) * p.N + n], y, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -459,7 +487,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         if (n >= p.N) continue;
         float y = 0.f;
         for (int s = 0; s < p.splits; ++s)
-            y += __hip_atomic_load(&p.partials[((size_t)s * 16 + m) * p.N + n], __ATOMIC_RELAXED,
+            y += __hip_atomic_load(&p.partials[((size_t)s * p.M + m) * p.N + n], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         if (p.bias) y += act_to_f32<BF>(p.bias[n]);
         p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
@@ -468,18 +496,18 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8>
+template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
     const dim3 block(NT);
     const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
     case 4:
         // (8-bit blocks are twice the registers: at most two tiles)
         if constexpr (W8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
+        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
         break;
     default: return hipErrorInvalidValue;
     }
@@ -488,16 +516,23 @@ hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 
 // Activation loads: one per 4 k-steps for M <= 4, per 2 for M <= 8, else one
 // per k-step. A K that is not a multiple of 128 (one partial block) takes the
-// one-per-step form, whose past-K steps are masked per load.
+// one-per-step form, whose past-K steps are masked per load. M > 16 takes
+// two row blocks of 16, one load per k-step each.
 // (Staged act-order activations come with M <= 2 only.)
 template <int NGB, bool XL, bool BF, bool W8>
 hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
-    if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF, W8>(p, ct, splits, stream);
-    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF, W8>(p, ct, splits, stream);
     if constexpr (!XL) {
-        if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF, W8>(p, ct, splits, stream);
-        return launch_ct<NGB, 1, false, XL, BF, W8>(p, ct, splits, stream);
+        if (p.M > 16) {
+            return p.K % 128 != 0 ? launch_ct<NGB, 1, true, false, BF, W8, 2>(p, ct, splits, stream)
+                                  : launch_ct<NGB, 1, false, false, BF, W8, 2>(p, ct, splits, stream);
+        }
+    }
+    if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF, W8, 1>(p, ct, splits, stream);
+    if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF, W8, 1>(p, ct, splits, stream);
+    if constexpr (!XL) {
+        if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF, W8, 1>(p, ct, splits, stream);
+        return launch_ct<NGB, 1, false, XL, BF, W8, 1>(p, ct, splits, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -532,8 +567,9 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
                        int M, int col_tiles, int splits, bool gather_x, bool bf16, float* partials,
                        uint32_t* counters, hipStream_t stream)
 {
-    if (M < 1 || M > 16 || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+    if (M < 1 || M > kGemvMaxM || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
     if (splits > 1 && (!partials || !counters)) return hipErrorInvalidValue;
+    if (M > 16 && gather_x) return hipErrorInvalidValue;
     if (gather_x && (!h->inv16 || !gemv_gathers_x(M, h->K, splits))) return hipErrorInvalidValue;
     GemvArgs p;
     p.qweight = h->qweight;

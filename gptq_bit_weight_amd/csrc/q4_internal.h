@@ -45,7 +45,8 @@ __host__ __device__ constexpr uint32_t chunk_in_block(int kb, int n, int N)
     return (uint32_t)(4 * (n & ~15) + kb * ((N - (n & ~15)) < 16 ? (N - (n & ~15)) : 16) + (n & 15));
 }
 
-// ---- skinny (M <= 16) kernel geometry ------------------------------------
+// ---- skinny (M <= 32) kernel geometry ------------------------------------
+constexpr int kGemvMaxM = Q4_GEMV_MAX_M;   // rows the skinny kernel takes (two blocks of 16)
 constexpr int kGemvWaves = 8;        // waves per workgroup (they split its K range)
 constexpr int kGemvDepth = 4;        // k-blocks in flight per wave
 constexpr int kMaxSplits = 16;       // K splits across workgroups (grid.y)
@@ -91,6 +92,9 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 // Skinny-kernel launch plan: 16-column tiles per wave (1, 2 or 4) and K
 // splits across workgroups (1..kMaxSplits) for a chip of num_cu CUs.
 void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits, int bits = 4);
+// Whether the automatic dispatch runs the skinny kernel for M rows (every
+// M it takes, 1 <= M <= kGemvMaxM: it measured faster than the GEMM there).
+bool gemv_serves(int M, int K, int N, int G, int bits = 4);
 // Whether the skinny kernel stages act-order activations itself for this
 // M, K and number of K splits.
 bool gemv_gathers_x(int M, int K, int splits);
@@ -118,12 +122,12 @@ struct q4_matrix {
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
     uint16_t* inv16 = nullptr;     // the same in 16 bits, when K <= kGemvXRows
-    // skinny-kernel split-K workspace: partial sums for up to partial_splits
-    // K splits, sized at make time for the largest split count the plan
-    // gives at any M <= 16 (none for most layers), grown on demand for an
-    // explicit larger count; and arrival counters
-    mutable float* partials = nullptr;     // [partial_splits][16][N]
-    mutable int partial_splits = 0;
+    // skinny-kernel split-K workspace: fp32 partial sums of splits x M rows
+    // (row stride M), sized at make time for the largest splits x M the plan
+    // gives at any M the skinny kernel serves (none for most layers), grown
+    // on demand for an explicit larger count; and arrival counters
+    mutable float* partials = nullptr;     // partial_rows x N
+    mutable int partial_rows = 0;
     mutable std::vector<float*> partials_retired;   // outgrown buffers, freed with the handle
     uint32_t* counters = nullptr;  // [ceil(N / 16)]: one per column tile at the narrowest tiling
     // act-order activation workspace, grown on demand: x[:, perm] as fp16 [M][K]

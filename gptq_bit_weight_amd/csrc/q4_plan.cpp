@@ -106,12 +106,15 @@ q4_status plan_actorder(const int32_t* g_idx, int K, int G, int32_t* perm, int* 
 void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* splits, int bits)
 {
     if (num_cu <= 0) num_cu = 256;
-    // gain x 100 for 1, 2, 4 tiles: M <= 2, M <= 4, M <= 8, M <= 16. (At
-    // M = 1 a wider tile saves little: 8192x28672 ran 21.2 us with one tile
-    // a wave against 21.8 us with four, 28672x8192 20.5 us with two against
-    // 21.1 us with one, the tiles then filling one round of CUs exactly.)
-    static const int gain[4][3] = {{100, 104, 104}, {100, 110, 120}, {100, 140, 150}, {100, 160, 190}};
-    const int mi = M <= 2 ? 0 : M <= 4 ? 1 : M <= 8 ? 2 : 3;
+    // gain x 100 for 1, 2, 4 tiles: M <= 2, M <= 4, M <= 8, M <= 16,
+    // M <= 32. (At M = 1 a wider tile saves little: 8192x28672 ran 21.2 us
+    // with one tile a wave against 21.8 us with four, 28672x8192 20.5 us
+    // with two against 21.1 us with one, the tiles then filling one round of
+    // CUs exactly.) Past 16 rows every activation load serves one k-step of
+    // one 16-row block, so wide tiles pay most.
+    static const int gain[5][3] = {{100, 104, 104}, {100, 110, 120}, {100, 140, 150}, {100, 160, 190},
+                                   {100, 180, 230}};
+    const int mi = M <= 2 ? 0 : M <= 4 ? 1 : M <= 8 ? 2 : M <= 16 ? 3 : 4;
     // (groups of 32 rows carry four scale/zero sets per block, and 8-bit
     // blocks are twice the words; four tiles of either do not fit the
     // register file)
@@ -138,6 +141,21 @@ void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* spli
     const int tiles = (N + 16 * ct - 1) / (16 * ct);
     *col_tiles = ct;
     *splits = splits_for(tiles, 1);
+}
+
+// Automatic dispatch between the skinny kernel and the GEMM: the skinny
+// kernel for every M it takes. Past 16 rows the GEMM's 64-row tiles are
+// bound by their serial k-loop (about 20 us on the 7B MLP shapes for any M
+// up to 64), while the skinny kernel with two row blocks measured (M = 17 /
+// 24 / 32, us, skinny against GEMM): 4096x11008 11.4 / 12.4 / 13.7 against
+// 19.4 / 19.5 / 19.6; 11008x4096 13.0 / 14.9 / 16.6 against 20.2;
+// 4096x4096 7.7 / 8.9 / 10.3 against 17.7; 8192x28672 33.1 / 37.6 / 43.3
+// against 44.1 / 44.8 / 45.7; 28672x8192 30.9 / 34.6 / 39.7 against
+// 44.1 / 45.3 / 46.3.
+bool gemv_serves(int M, int K, int N, int G, int bits)
+{
+    (void)K; (void)N; (void)G; (void)bits;
+    return M >= 1 && M <= kGemvMaxM;
 }
 
 bool gemv_gathers_x(int M, int K, int splits)

@@ -70,7 +70,9 @@ enum {
     Q4_PATH_MFMA = 2    /* LDS-staged MFMA GEMM for larger M                      */
 };
 
-#define Q4_GEMV_MAX_M 16
+/* Most rows the skinny kernel takes: q4_matmul runs it for 1 <= M <= 32 and
+ * the MFMA GEMM above (q4_path_for tells which). */
+#define Q4_GEMV_MAX_M 32
 /* Most workgroups one streaming-GEMM launch may be given (q4_matmul_ex). */
 #define Q4_GEMM_MAX_WORKERS 1024
 

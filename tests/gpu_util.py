@@ -150,11 +150,11 @@ def check_rows_cols(L, y, what: str, seed: int = 0, **tol) -> int:
     return int(ms.size)
 
 
-def check_output(L, y, what: str, seed: int = 0, full_max_m: int = 16, **tol) -> int:
+def check_output(L, y, what: str, seed: int = 0, full_max_m: int = 32, **tol) -> int:
     """The acceptance rule on a whole GPU output: every element for
-    M <= full_max_m (the oracle computes the whole product), else whole rows
-    and columns through check_rows_cols. Returns the number of elements
-    compared."""
+    M <= full_max_m (the oracle computes the whole product; 32 covers every M
+    the skinny kernel serves), else whole rows and columns through
+    check_rows_cols. Returns the number of elements compared."""
     y = np.asarray(y)
     if L.M <= full_max_m:
         yD, A = oracle_full(L)

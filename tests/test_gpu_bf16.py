@@ -72,6 +72,8 @@ GEMV_CASES = [
     (160, 72, -1, 5, False, False),         # one group over K
     (1024, 264, 128, 1, True, True),        # act-order staged in the kernel
     (1024, 264, 128, 4, True, True),        # act-order, separate permute
+    (1024, 1096, 128, 30, False, True),     # two row blocks
+    (1024, 264, 32, 32, True, False),       # two full row blocks, groups of 32, act-order
 ]
 
 

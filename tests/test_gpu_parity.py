@@ -85,10 +85,74 @@ def test_gemv_parity(K, N, G, M, act, bias, tiles):
     compare(y, yD, A, f"gemv K={K} N={N} G={G} M={M} tiles={tiles}")
 
 
+# Past 16 rows the skinny kernel runs two blocks of 16 activation rows over
+# each unpacked weight fragment.
+GEMV_ROWS_CASES = [
+    # K, N, G, M, act_order, bias
+    (1024, 1096, 128, 17, False, True),    # the second row block one row
+    (2048, 200, 64, 32, False, False),     # two full row blocks
+    (1024, 264, 32, 25, False, True),      # groups of 32
+    (160, 72, -1, 20, False, False),       # K tail, one group over K
+    (1024, 264, 128, 32, True, True),      # act-order (separate permute)
+    (768, 520, 256, 29, False, False),     # groups of 256
+]
+
+
+@pytest.mark.parametrize("tiles", [0, 1, 2, 4])
+@pytest.mark.parametrize("K,N,G,M,act,bias", GEMV_ROWS_CASES)
+def test_gemv_row_blocks_parity(K, N, G, M, act, bias, tiles):
+    """The skinny kernel at 17 <= M <= 32 (tiles: 16-column MFMA tiles per
+    wave, 0 planned)."""
+    import gptq_bit_weight_amd as q4
+    L = _layer(K, N, G, M, 7, act_order=act, bias=bias)
+    announce(f"gemv rows K={K} N={N} G={G} M={M} act={act} bias={bias} tiles={tiles}")
+    W = make_matrix(L)
+    assert W.path_for(M) == q4.PATH_GEMV
+    y = run(L, W=W, path=q4.PATH_GEMV, variant=tiles)
+    yD, A = oracle_full(L)
+    compare(y, yD, A, f"gemv rows K={K} N={N} G={G} M={M} tiles={tiles}")
+
+
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_row_blocks_splits_deterministic(M):
+    """K splits with row blocks: the partial sums of every split and row
+    reach the last arriver; repeated calls give the same bits."""
+    import gptq_bit_weight_amd as q4
+    L = _layer(2048, 136, 128, M, 8, bias=True)
+    announce(f"row blocks splits M={M}")
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    yD, A = oracle_full(L)
+    for splits in (2, 3, 16):
+        a = run(L, W=W, t=t, path=q4.PATH_GEMV, variant=1, splits=splits)
+        b = run(L, W=W, t=t, path=q4.PATH_GEMV, variant=1, splits=splits)
+        compare(a, yD, A, f"row blocks M={M} splits={splits}")
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_dispatch_by_m():
+    """Automatic path: the skinny kernel up to 32 rows, the GEMM above; both
+    agree with the oracle on either side of the boundary."""
+    import gptq_bit_weight_amd as q4
+    L = _layer(1024, 520, 128, 33, 9, bias=True)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    for M in (1, 16, 17, 32):
+        assert W.path_for(M) == q4.PATH_GEMV, M
+    for M in (33, 64, 65, 2048):
+        assert W.path_for(M) == q4.PATH_MFMA, M
+    yD, A = oracle_full(L)
+    for M in (32, 33):
+        announce(f"dispatch M={M}")
+        y = W.matmul(t["x"][:M].contiguous(), t["bias"])
+        torch_mod().cuda.synchronize()
+        compare(y.cpu().numpy(), yD[:M], A[:M], f"dispatch M={M}")
+
+
 # ------------------------------------------------------------ MFMA GEMM --
 
 GEMM_CASES = [
-    (512, 328, 128, 17, False, False),     # smallest M on the GEMM path, ragged N
+    (512, 328, 128, 17, False, False),     # smallest M the GEMM takes, ragged N
     (512, 328, 32, 130, False, True),      # ragged M over two row tiles, groups of 32
     (96, 136, 32, 300, False, False),      # K tail inside the 64-row k-tile
     (1024, 256, 128, 256, True, True),     # act-order, whole tiles
@@ -107,7 +171,7 @@ def test_gemm_parity(K, N, G, M, act, bias, splits):
     L = _layer(K, N, G, M, 2, act_order=act, bias=bias)
     announce(f"gemm K={K} N={N} G={G} M={M} act={act} bias={bias} splits={splits}")
     W = make_matrix(L)
-    assert W.path_for(M) == q4.PATH_MFMA
+    assert W.path_for(M) == (q4.PATH_GEMV if M <= 32 else q4.PATH_MFMA)
     y = run(L, W=W, path=q4.PATH_MFMA, splits=splits)
     yD, A = oracle_full(L)
     compare(y, yD, A, f"gemm K={K} N={N} G={G} M={M} splits={splits}")
@@ -268,7 +332,7 @@ def test_m_zero_and_argument_errors():
     t = device_tensors(L)
     W = make_matrix(L, t)
     assert W.path_for(0) == q4.PATH_NONE and W.path_for(16) == q4.PATH_GEMV
-    assert W.path_for(17) == q4.PATH_MFMA
+    assert W.path_for(32) == q4.PATH_GEMV and W.path_for(33) == q4.PATH_MFMA
     e = W.matmul(torch.empty((0, 256), dtype=torch.float16, device="cuda"))
     assert tuple(e.shape) == (0, 64)
     with pytest.raises(ValueError):
@@ -276,7 +340,8 @@ def test_m_zero_and_argument_errors():
     with pytest.raises(ValueError):
         W.matmul(torch.zeros((2, 128), dtype=torch.float16, device="cuda"))
     with pytest.raises(ValueError):
-        W.matmul(torch.zeros((17, 256), dtype=torch.float16, device="cuda"), path=q4.PATH_GEMV)
+        W.matmul(torch.zeros((q4.GEMV_MAX_M + 1, 256), dtype=torch.float16, device="cuda"),
+                 path=q4.PATH_GEMV)
     with pytest.raises(ValueError):
         W.matmul(t["x"], splits=17)
     with pytest.raises(ValueError):

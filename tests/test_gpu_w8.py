@@ -109,6 +109,8 @@ GEMV_CASES = [
     (1024, 264, 128, 4, True, True, "f16"),       # act-order, separate permute
     (1024, 1096, 128, 2, False, True, "bf16"),
     (1024, 264, 32, 9, True, False, "bf16"),
+    (1024, 1096, 128, 20, False, True, "f16"),    # two row blocks
+    (1024, 264, 64, 31, True, False, "bf16"),     # two row blocks, act-order
 ]
 
 

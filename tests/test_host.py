@@ -148,7 +148,13 @@ def test_plan_gemv():
     with pytest.raises(ValueError):
         q4.plan_gemv(0, 4096, 4096, 128)
     with pytest.raises(ValueError):
-        q4.plan_gemv(17, 4096, 4096, 128)
+        q4.plan_gemv(q4.GEMV_MAX_M + 1, 4096, 4096, 128)
+    # two row blocks (16 < M <= 32)
+    for M in (17, 32):
+        for K, N, G in ((4096, 4096, 128), (4096, 11008, 128), (11008, 4096, 128), (4096, 11008, 32)):
+            ct, s = q4.plan_gemv(M, K, N, G, num_cu=256)
+            assert ct in ((1, 2) if G == 32 else (1, 2, 4)), (M, K, N, G, ct)
+            assert s in (1, 2, 4, 8, 16)
     with pytest.raises(NotImplementedError):
         q4.plan_gemv(1, 4128, 4096, 128)      # K % groupsize != 0
 
@@ -199,7 +205,7 @@ def test_plan_gemv_gather():
     assert not g(1, 4096, 2)                            # split K
     assert not g(1, 12416, 1) and g(1, 12288, 1)        # 97 blocks exceed 12288 rows
     assert g(1, 12200, 1)                               # 96 blocks once padded
-    for bad in ((0, 4096, 1), (17, 4096, 1), (1, 4096, 0), (1, 4096, 17), (1, 0, 1)):
+    for bad in ((0, 4096, 1), (q4.GEMV_MAX_M + 1, 4096, 1), (1, 4096, 0), (1, 4096, 17), (1, 0, 1)):
         with pytest.raises(ValueError):
             g(*bad)
 
