@@ -253,6 +253,13 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off, uint32_t s
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0);
 }
 
+// A 4-byte load with the non-temporal hint.
+__device__ __forceinline__ uint32_t buf_load4_nt(rsrc_t r, uint32_t off, uint32_t soff = 0)
+{
+    constexpr int kNonTemporal = 2;
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, kNonTemporal);
+}
+
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
     return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
