@@ -28,7 +28,7 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
 hipError_t launch_permute_x(const uint16_t* x, const int32_t* perm, uint16_t* xp, int M, int K,
                             hipStream_t stream);
 hipError_t launch_dump(const q4_matrix* h, int path, uint16_t* w, bool bf16, hipStream_t stream);
-hipError_t launch_make_sz(q4_matrix* h, hipStream_t stream);
+hipError_t launch_make_sz(q4_matrix* h, const uint16_t* scales, const uint32_t* qzeros, hipStream_t stream);
 
 namespace {
 
@@ -48,15 +48,8 @@ void destroy(q4_matrix* h)
 {
     if (!h) return;
     (void)hipFree(h->qweight);
-    (void)hipFree(h->scales);
-    (void)hipFree(h->qzeros);
-    (void)hipFree(h->sz);
-    (void)hipFree(h->perm);
-    (void)hipFree(h->inv_perm);
-    (void)hipFree(h->inv16);
-    (void)hipFree(h->partials);
-    for (float* p : h->partials_retired) (void)hipFree(p);
-    (void)hipFree(h->counters);
+    (void)hipFree(h->block);
+    for (float* p : h->partials_grown) (void)hipFree(p);
     (void)hipFree(h->xperm);
     for (uint16_t* p : h->xperm_retired) (void)hipFree(p);
     delete h;
@@ -192,12 +185,6 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
         return s;
     };
     hipError_t e;
-    const size_t words = packed_words(K, N, bits);
-    if ((e = hipMalloc(&h->qweight, words * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: qweight"));
-    if ((e = hipMalloc(&h->scales, (size_t)ng * N * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
-    const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
-    if ((e = hipMalloc(&h->qzeros, (size_t)ng * zrow)) != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
-    if ((e = hipMalloc(&h->sz, (size_t)ng * N * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: scales"));
     // Split-K partials for the largest splits x M the plan takes at any M
     // the automatic dispatch gives the skinny kernel (none for most layers).
     int max_rows = 0;
@@ -207,39 +194,71 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
         plan_gemv(m, K, N, G, num_cu, &ct, &sp, bits);
         if (sp > 1) max_rows = std::max(max_rows, sp * m);
     }
+    // The handle keeps two device allocations: the packed weights, and one
+    // carved into 256-byte aligned regions for everything else (the device
+    // allocator rounds large allocations up to 2 MiB, so the small buffers
+    // share one instead of each being rounded on its own).
+    const int col_tiles = (N + 15) / 16;
+    const bool staged = act && num_kblocks(K) * kBlockK <= kGemvXRows;
+    size_t offs[6], total = 0;
+    const size_t sizes[6] = {(size_t)ng * N * 4, (size_t)col_tiles * 4, act ? (size_t)K * 4 : 0,
+                             act ? (size_t)K * 4 : 0, staged ? (size_t)K * 2 : 0, (size_t)max_rows * N * 4};
+    for (int r = 0; r < 6; ++r) {
+        offs[r] = total;
+        total += (sizes[r] + 255) & ~(size_t)255;
+    }
+    if ((e = hipMalloc(&h->qweight, packed_words(K, N, bits) * 4)) != hipSuccess)
+        return bail(hip_fail(e, "q4_make: qweight"));
+    if ((e = hipMalloc(&h->block, total)) != hipSuccess) return bail(hip_fail(e, "q4_make: device memory"));
+    h->block_bytes = total;
+    char* base = static_cast<char*>(h->block);
+    h->sz = reinterpret_cast<uint32_t*>(base + offs[0]);
+    h->counters = reinterpret_cast<uint32_t*>(base + offs[1]);
+    if (act) {
+        h->perm = reinterpret_cast<int32_t*>(base + offs[2]);
+        h->inv_perm = reinterpret_cast<int32_t*>(base + offs[3]);
+    }
+    if (staged) h->inv16 = reinterpret_cast<uint16_t*>(base + offs[4]);
     if (max_rows > 0) {
-        if ((e = hipMalloc(&h->partials, (size_t)max_rows * N * 4)) != hipSuccess)
-            return bail(hip_fail(e, "q4_make: workspace"));
+        h->partials = reinterpret_cast<float*>(base + offs[5]);
         h->partial_rows = max_rows;
     }
-    const int col_tiles = (N + 15) / 16;
-    if ((e = hipMalloc(&h->counters, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
     if ((e = hipMemset(h->counters, 0, (size_t)col_tiles * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: counters"));
     if (act) {
         std::vector<int32_t> inv(K);
         for (int k = 0; k < K; ++k) inv[perm[k]] = k;
-        if ((e = hipMalloc(&h->perm, (size_t)K * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
-        if ((e = hipMalloc(&h->inv_perm, (size_t)K * 4)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
         if ((e = hipMemcpy(h->perm, perm.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: perm"));
         if ((e = hipMemcpy(h->inv_perm, inv.data(), (size_t)K * 4, hipMemcpyHostToDevice)) != hipSuccess)
             return bail(hip_fail(e, "q4_make: perm"));
         // 16-bit copy for the skinny kernel's own activation staging, which
         // takes layers of at most kGemvXRows rows
-        if (num_kblocks(K) * kBlockK <= kGemvXRows) {
+        if (staged) {
             std::vector<uint16_t> inv16(inv.begin(), inv.end());
-            if ((e = hipMalloc(&h->inv16, (size_t)K * 2)) != hipSuccess) return bail(hip_fail(e, "q4_make: perm"));
             if ((e = hipMemcpy(h->inv16, inv16.data(), (size_t)K * 2, hipMemcpyHostToDevice)) != hipSuccess)
                 return bail(hip_fail(e, "q4_make: perm"));
         }
     }
-    // Part i's scales and zero words are columns off_i .. off_i + N_i of the
-    // handle's rows (zero words: off_i / 8 .., every offset a multiple of 8).
+    // The checkpoint's scales and packed zeros, gathered with the handle's
+    // row pitch into temporaries from which the group words are built. Part
+    // i's scales and zero words are columns off_i .. off_i + N_i of the
+    // rows (zero words: off_i / 8 .., every offset a multiple of 8).
+    uint16_t* tscales = nullptr;
+    uint32_t* tqzeros = nullptr;
+    auto bail_tmp = [&](q4_status st) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(tscales);
+        (void)hipFree(tqzeros);
+        return bail(st);
+    };
+    const size_t zrow = (size_t)N * bits / 8;   // bytes per row of packed zeros
+    if ((e = hipMalloc(&tscales, (size_t)ng * N * 2)) != hipSuccess) return bail_tmp(hip_fail(e, "q4_make: scales"));
+    if ((e = hipMalloc(&tqzeros, (size_t)ng * zrow)) != hipSuccess) return bail_tmp(hip_fail(e, "q4_make: qzeros"));
     int off = 0;
     for (int i = 0; i < parts; ++i) {
-        if ((e = hipMemcpy2D(h->scales + off, (size_t)N * 2, scales[i], (size_t)Np[i] * 2, (size_t)Np[i] * 2,
+        if ((e = hipMemcpy2D(tscales + off, (size_t)N * 2, scales[i], (size_t)Np[i] * 2, (size_t)Np[i] * 2,
                              (size_t)ng, hipMemcpyDeviceToDevice)) != hipSuccess)
-            return bail(hip_fail(e, "q4_make: scales"));
+            return bail_tmp(hip_fail(e, "q4_make: scales"));
         // A part without zeros is symmetric: every zero point is
         // 2^(bits-1) (GPTQModel wiki "Inference Backends", section
         // "Packing, conversion, and runtime initialization", row "Missing
@@ -247,20 +266,23 @@ q4_status make_impl(int parts, const int32_t* const* qweight, const int32_t* con
         // part's zeros occupy bytes off * bits / 8 .. of each row (off and
         // N[i] are multiples of 8, so no word is shared between parts).
         const int32_t* qz = qzeros ? qzeros[i] : nullptr;
-        char* zdst = reinterpret_cast<char*>(h->qzeros) + (size_t)off * bits / 8;
+        char* zdst = reinterpret_cast<char*>(tqzeros) + (size_t)off * bits / 8;
         const size_t zpart = (size_t)Np[i] * bits / 8;
         if (qz)
             e = hipMemcpy2D(zdst, zrow, qz, zpart, zpart, (size_t)ng, hipMemcpyDeviceToDevice);
         else
             e = hipMemset2D(zdst, zrow, bits == 8 ? 0x80 : 0x88, zpart, (size_t)ng);
-        if (e != hipSuccess) return bail(hip_fail(e, "q4_make: qzeros"));
+        if (e != hipSuccess) return bail_tmp(hip_fail(e, "q4_make: qzeros"));
         if ((e = launch_repack(reinterpret_cast<const uint32_t*>(qweight[i]), h->perm, h->qweight, K, Np[i], N,
                                off, bits, 0)) != hipSuccess)
-            return bail(hip_fail(e, "q4_make: repack launch"));
+            return bail_tmp(hip_fail(e, "q4_make: repack launch"));
         off += Np[i];
     }
-    if ((e = launch_make_sz(h, 0)) != hipSuccess) return bail(hip_fail(e, "q4_make: group parameters"));
-    if ((e = hipDeviceSynchronize()) != hipSuccess) return bail(hip_fail(e, "q4_make: repack"));
+    if ((e = launch_make_sz(h, tscales, tqzeros, 0)) != hipSuccess)
+        return bail_tmp(hip_fail(e, "q4_make: group parameters"));
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return bail_tmp(hip_fail(e, "q4_make: repack"));
+    (void)hipFree(tscales);
+    (void)hipFree(tqzeros);
     *out = h;
     return Q4_OK;
 }
@@ -313,8 +335,8 @@ q4_status ensure_partials(const q4_matrix* h, int splits, int M, hipStream_t str
     float* fresh = nullptr;
     Q4_HIP(hipMalloc(&fresh, (size_t)rows * h->N * 4), "q4_matmul: split-K workspace");
     // earlier launches (and graphs captured from them) may still use the old
-    // buffer: retire it, freed with the handle
-    if (h->partials) h->partials_retired.push_back(h->partials);
+    // buffer: it stays allocated until the handle is freed
+    h->partials_grown.push_back(fresh);
     h->partials = fresh;
     h->partial_rows = rows;
     return Q4_OK;

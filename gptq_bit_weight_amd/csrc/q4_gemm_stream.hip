@@ -23,9 +23,10 @@
 //  * Weights: for its column (lane % 32 of the wave's 32) a lane needs, per k-tile, words 2h and
 //    2h + 1 of chunks (b, kb) and (b, kb + 2) of the private block layout
 //    (k-tile 2b + h, kb = lane / 32): two 8-byte loads. With the
-//    scale and zero words of the tile's group(s), these go to one of two
-//    register sets; the k-loop is unrolled by two so that the set a step
-//    multiplies is never a set a load is filling.
+//    32-bit scale|zero word of each of the tile's groups (built by the make
+//    step, as for the skinny kernel), these go to one of two register sets;
+//    the k-loop is unrolled by two so that the set a step multiplies is never
+//    a set a load is filling.
 //  * One barrier per k-tile: after it, every wave has finished the previous
 //    tile, so the stage that tile used is refilled (tile kt + 1) while tile
 //    kt is multiplied.
@@ -77,14 +78,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmArgs {
     const uint32_t* qweight;
-    const uint16_t* scales;
-    const uint32_t* qzeros;
+    const uint32_t* sz;     // [ng][N]: scale bits | zero point << 16
     const uint16_t* x;
     const uint16_t* bias;
     uint16_t* out;
     int M, K, N, G;
     int gshift;             // group of row k = k >> gshift (31: one group over K)
-    int zrow;               // bytes per row of packed zeros (N * bits / 8)
     // Schedule: `workers` workgroups share the (output tile, k-tile)
     // iterations evenly, in contiguous ranges, each at least one iteration
     // long (workers <= iterations). workers = tiles is one tile per
@@ -109,25 +108,22 @@ __device__ __forceinline__ void lds_barrier()
 
 // One k-tile of a lane's weights: w[j][0] = words (2h, 2h+1) of chunk
 // (b, kb, n_j) -- sub-steps 0 and 2 -- and w[j][1] those of chunk
-// (b, kb + 2, n_j) -- sub-steps 1 and 3; scale and zero words of the tile's
+// (b, kb + 2, n_j) -- sub-steps 1 and 3; the scale|zero words of the tile's
 // NG groups (two for groups of 32 rows).
 template <int NG, bool W8>
 struct BRegs {
     std::conditional_t<W8, u4, u2> w[NJ][2];
-    uint32_t s[NG][NJ];
-    uint32_t z[NG][NJ];
+    uint32_t sz[NG][NJ];    // scale bits | zero point << 16
 };
 
 constexpr int kMaxALoads = Geo<256>::A_LOADS;
 struct Ctx {
-    rsrc_t rx, rw, rs, rz;
+    rsrc_t rx, rw, rsz;
     // (the first A_LOADS entries are used)
     uint32_t a_off[kMaxALoads];   // activation byte offsets for k0 = 0 (rows >= M fall outside x)
     uint32_t a_k[kMaxALoads];     // k of each chunk for k0 = 0
     uint32_t w_off[NJ][2];     // weight byte offsets of the two chunks per column (k-tile 0)
-    uint32_t s_off[NJ];        // scale byte offsets (group 0)
-    uint32_t z_off[NJ];        // zero-word byte offsets (group 0)
-    uint32_t z_shift[NJ];
+    uint32_t sz_off[NJ];       // group-word byte offsets (group 0)
 };
 
 // The k offset of the tile is wave-uniform (a scalar register); rows past M
@@ -163,8 +159,7 @@ __device__ __forceinline__ void load_b(BRegs<NG, W8>& R, const Ctx& c, const Gem
         const uint32_t g = (uint32_t)k >> p.gshift;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            R.s[gi][j] = buf_load2(c.rs, c.s_off[j], g * (uint32_t)p.N * 2u);
-            R.z[gi][j] = buf_load4(c.rz, c.z_off[j], g * (uint32_t)p.zrow);
+            R.sz[gi][j] = buf_load4(c.rsz, c.sz_off[j], g * (uint32_t)p.N * 4u);
         }
     }
 }
@@ -183,8 +178,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     // stream, so they keep two tiles in flight; 256-row tiles one.
     constexpr int D = BM == 64 ? 3 : 2;
     // vector-memory loads one step issues per thread (activation DMA, packed
-    // weights, scale and zero words)
-    constexpr int LPS = A_LOADS + 2 * NJ + 2 * NG * NJ;
+    // weights, scale|zero words)
+    constexpr int LPS = A_LOADS + 2 * NJ + NG * NJ;
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a2[A_TILE_BYTES];   // (D = 3 only)
@@ -217,8 +212,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     const int ng = p.K / p.G;
     c.rx = make_rsrc(p.x, (uint32_t)p.M * (uint32_t)p.K * 2u);
     c.rw = make_rsrc(p.qweight, (uint32_t)q4::num_kblocks(p.K) * (uint32_t)p.N * (W8 ? 128u : 64u));
-    c.rs = make_rsrc(p.scales, (uint32_t)ng * (uint32_t)p.N * 2u);
-    c.rz = make_rsrc(p.qzeros, (uint32_t)ng * (uint32_t)p.zrow);
+    c.rsz = make_rsrc(p.sz, (uint32_t)ng * (uint32_t)p.N * 4u);
 
     f16x acc[MI][NJ];
     BRegs<NG, W8> R[D];
@@ -243,8 +237,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 if constexpr (!BF) {
-                    hz[gi][j] = zero_pair((R.z[gi][j] >> c.z_shift[j]) & (W8 ? 0xFFu : 0xFu));
-                    s2[gi][j] = scale_pair(R.s[gi][j]);
+                    hz[gi][j] = zero_pair(R.sz[gi][j] >> 16);
+                    s2[gi][j] = scale_pair(R.sz[gi][j]);
                 }
             }
         // dequantize sub-step `sub` of this k-tile into b
@@ -254,8 +248,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 if (sub % (4 / NG) == 0)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        mz[j] = mix_consts((R.z[gi][j] >> c.z_shift[j]) & (W8 ? 0xFFu : 0xFu),
-                                           f16_bits_to_f32((uint16_t)R.s[gi][j]));
+                        mz[j] = mix_consts(R.sz[gi][j] >> 16, f16_bits_to_f32((uint16_t)R.sz[gi][j]));
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -380,9 +373,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
 #pragma unroll
             for (int v = 0; v < 2; ++v) c.w_off[j][v] = q4::chunk_in_block(lhi + 2 * v, (int)n, p.N) * (W8 ? 32u : 16u);
-            c.s_off[j] = n * 2u;
-            c.z_off[j] = (n >> (W8 ? 2 : 3)) * 4u;
-            c.z_shift[j] = W8 ? 8u * (n & 3u) : 4u * (n & 7u);
+            c.sz_off[j] = n * 4u;
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -542,8 +533,7 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
 {
     GemmArgs p;
     p.qweight = h->qweight;
-    p.scales = h->scales;
-    p.qzeros = h->qzeros;
+    p.sz = h->sz;
     p.x = x;
     p.bias = bias;
     p.out = out;
@@ -566,7 +556,6 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;
-    p.zrow = h->N * h->bits / 8;
     return bm == 64 ? launch_bm<64>(p, workers, g32, kt, bf16, h->bits == 8, stream)
                     : launch_bm<kGemmBM>(p, workers, g32, kt, bf16, h->bits == 8, stream);
 }

@@ -114,10 +114,13 @@ struct q4_matrix {
     int device = -1;
     int num_cu = 256;
     uint32_t* qweight = nullptr;   // packed_words(K, N, bits): private block layout (above)
-    uint16_t* scales = nullptr;    // [ng][N] fp16
-    uint32_t* qzeros = nullptr;    // [ng][N * bits / 32]
-    // the skinny kernel's group parameters, one word per (group, column):
-    // scale bits | zero point << 16 (one load instead of two per block)
+    // One device allocation holds every buffer below but the grown
+    // workspaces (256-byte aligned regions, in this order).
+    void* block = nullptr;
+    size_t block_bytes = 0;
+    // both kernels' group parameters, one word per (group, column): scale
+    // bits | zero point << 16, built at make time from the checkpoint's
+    // scales and packed zeros (which the handle does not keep)
     uint32_t* sz = nullptr;        // [ng][N]
     int32_t* perm = nullptr;       // [K] sorted-order -> original row, act-order only
     int32_t* inv_perm = nullptr;   // [K] original row -> sorted position, act-order only
@@ -128,7 +131,7 @@ struct q4_matrix {
     // on demand for an explicit larger count; and arrival counters
     mutable float* partials = nullptr;     // partial_rows x N
     mutable int partial_rows = 0;
-    mutable std::vector<float*> partials_retired;   // outgrown buffers, freed with the handle
+    mutable std::vector<float*> partials_grown;   // allocated on demand, freed with the handle
     uint32_t* counters = nullptr;  // [ceil(N / 16)]: one per column tile at the narrowest tiling
     // act-order activation workspace, grown on demand: x[:, perm] as fp16 [M][K]
     mutable std::mutex ws_mutex;

@@ -164,8 +164,6 @@ __global__ __launch_bounds__(256) void q4_make_sz_kernel(const uint16_t* __restr
 // otherwise the bfloat16 weight mix_word feeds to the bfloat16 MFMA.
 template <bool FACTORED, bool BF, bool W8>
 __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict__ qweight,
-                                                      const uint16_t* __restrict__ scales,
-                                                      const uint32_t* __restrict__ qzeros,
                                                       const uint32_t* __restrict__ sz,
                                                       const int32_t* __restrict__ inv_perm,
                                                       uint16_t* __restrict__ w, int K, int N, int G)
@@ -178,15 +176,12 @@ __global__ __launch_bounds__(256) void q4_dump_kernel(const uint32_t* __restrict
         const int g = kk / G;
         int e;
         const size_t wp = private_word(kk, n, N, &e, W8 ? 8 : 4);
-        // the skinny kernel reads its scale and zero from sz, the GEMM from
-        // scales and qzeros
-        const uint32_t z = FACTORED ? sz[(size_t)g * N + n] >> 16
-                         : W8 ? (qzeros[(size_t)g * (N >> 2) + (n >> 2)] >> (8 * (n & 3))) & 0xFFu
-                              : (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
+        // both kernels read the scale and the zero point from the group word
+        const uint32_t z = sz[(size_t)g * N + n] >> 16;
         // the two words of the k-step (8-bit) or its one word (4-bit)
         const uint32_t word = qweight[wp];
         const uint32_t w0 = W8 ? qweight[wp - (e >> 2)] : word, w1 = W8 ? qweight[wp - (e >> 2) + 1] : word;
-        const uint16_t sb = FACTORED ? (uint16_t)sz[(size_t)g * N + n] : scales[(size_t)g * N + n];
+        const uint16_t sb = (uint16_t)sz[(size_t)g * N + n];
         if constexpr (BF) {
             float t = FACTORED ? 1.0f : f16_bits_to_f32(sb);
             asm("" : "+v"(t));    // as in the kernels: one fused multiply-add per value
@@ -230,10 +225,10 @@ hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst
     return hipGetLastError();
 }
 
-hipError_t launch_make_sz(q4_matrix* h, hipStream_t stream)
+hipError_t launch_make_sz(q4_matrix* h, const uint16_t* scales, const uint32_t* qzeros, hipStream_t stream)
 {
     hipLaunchKernelGGL(q4_make_sz_kernel, dim3(grid_for((size_t)h->ng * h->N)), dim3(256), 0, stream,
-                       h->scales, h->qzeros, h->sz, h->ng, h->N, h->bits);
+                       scales, qzeros, h->sz, h->ng, h->N, h->bits);
     return hipGetLastError();
 }
 
@@ -259,17 +254,17 @@ hipError_t launch_dump_w(const q4_matrix* h, int path, uint16_t* w, bool bf16, h
     const dim3 grid(grid_for((size_t)h->K * h->N));
     const bool f = path == Q4_PATH_GEMV;
     if (f && bf16)
-        hipLaunchKernelGGL((q4_dump_kernel<true, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
+        hipLaunchKernelGGL((q4_dump_kernel<true, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->sz,
+                           h->inv_perm, w, h->K, h->N, h->G);
     else if (f)
-        hipLaunchKernelGGL((q4_dump_kernel<true, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
+        hipLaunchKernelGGL((q4_dump_kernel<true, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->sz,
+                           h->inv_perm, w, h->K, h->N, h->G);
     else if (bf16)
-        hipLaunchKernelGGL((q4_dump_kernel<false, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
+        hipLaunchKernelGGL((q4_dump_kernel<false, true, W8>), grid, dim3(256), 0, stream, h->qweight, h->sz,
+                           h->inv_perm, w, h->K, h->N, h->G);
     else
-        hipLaunchKernelGGL((q4_dump_kernel<false, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->scales,
-                           h->qzeros, h->sz, h->inv_perm, w, h->K, h->N, h->G);
+        hipLaunchKernelGGL((q4_dump_kernel<false, false, W8>), grid, dim3(256), 0, stream, h->qweight, h->sz,
+                           h->inv_perm, w, h->K, h->N, h->G);
     return hipGetLastError();
 }
 
