@@ -100,14 +100,17 @@ enum {
  * Q4_ERR_INVALID_ARG.
  *
  * Ownership: the inputs are read (the call synchronizes the device) and
- * copied into handle-owned device memory in a private layout of the same
- * size (K rounded up to a multiple of 128 rows for the packed weights); the
- * caller keeps and may free or change its tensors afterwards; such
- * changes do not reach the handle (make a new one). The handle also owns the
- * skinny kernel's split-K workspace, sized for the largest K split its launch
- * plan takes at any M <= 16 (16 x N fp32 per split; none when the plan never
- * splits K, as for 4096-wide and wider layers on 256 CUs). It never holds a
- * dequantized K x N matrix.
+ * copied into handle-owned device memory in private layouts: the packed
+ * weights at the same size (K rounded up to a multiple of 128 rows), and
+ * each group's scale and zero point as one 32-bit word per column (the
+ * checkpoint's scale and packed zero tensors are not kept). The caller
+ * keeps and may free or change its tensors afterwards; such changes do not
+ * reach the handle (make a new one). The handle also owns the skinny
+ * kernel's split-K workspace, sized for the largest splits x M its launch
+ * plan takes at any M <= Q4_GEMV_MAX_M (none when the plan never splits K,
+ * as for 4096-wide and wider layers on 256 CUs). It never holds a
+ * dequantized K x N matrix. Temporary device buffers for the checkpoint's
+ * group parameters are allocated and freed during the call.
  *
  * Returns NULL on error (q4_last_status / q4_last_error tell why).
  */
