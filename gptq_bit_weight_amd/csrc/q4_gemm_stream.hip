@@ -97,6 +97,18 @@ struct GemmArgs {
     int xcd;                // 1: each XCD takes the row tiles r with r % 8 == XCD (row tiles % 8 == 0)
 };
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
+
 __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4)); }
 
 #define Q4S_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -174,15 +186,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     constexpr int WTM = Geo<BM>::WTM, MI = Geo<BM>::MI;
     constexpr int A_TILE_BYTES = Geo<BM>::A_TILE_BYTES, A_LOADS = Geo<BM>::A_LOADS;
     // Ring depth: activation stages in LDS and weight register sets, both
-    // D - 1 k-tiles ahead. 64-row tiles (few rows) are bound by the weight
-    // stream, so they keep two tiles in flight; 256-row tiles one.
+    // D - 1 k-tiles ahead: two for 64-row tiles (few rows), one for 256-row
+    // tiles. (Four, six or eight 64-row stages measured 2-8% slower at
+    // M = 33 ... 512: a k-tile there costs about 0.35 us of one CU's time
+    // whatever the depth, and deeper rings only add registers and fills.)
     constexpr int D = BM == 64 ? 3 : 2;
     // vector-memory loads one step issues per thread (activation DMA, packed
     // weights, scale|zero words)
     constexpr int LPS = A_LOADS + 2 * NJ + NG * NJ;
+    // One array per stage: the compiler tells the stages apart by their
+    // variables, so reading one stage does not wait for the direct-to-LDS
+    // loads into another (with one array of stages it waits for them all).
+    static_assert(D >= 2 && D <= 8, "ring depth");
     __shared__ __attribute__((aligned(1024))) char lds_a0[A_TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[A_TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds_a2[A_TILE_BYTES];   // (D = 3 only)
+    __shared__ __attribute__((aligned(1024))) char lds_a2[D > 2 ? A_TILE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_a3[D > 3 ? A_TILE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_a4[D > 4 ? A_TILE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_a5[D > 5 ? A_TILE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_a6[D > 6 ? A_TILE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_a7[D > 7 ? A_TILE_BYTES : 1];
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -266,10 +289,46 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         };
         const int k0 = kt * BK;
         u4 bc[NJ], bn[NJ];
-        u4 a[MI];
         auto read_a = [&](int sub, int i) {
             return *reinterpret_cast<const u4*>(A + swz(wm * WTM + 32 * i + l32, 2 * sub + lhi));
         };
+        if constexpr (MI <= 2) {
+            // Few rows: one wave per SIMD, so nothing else hides a read's
+            // latency. The whole k-tile's activations are read at once, and
+            // each sub-step's MFMAs are interleaved with the dequantization
+            // of the next sub-step's weights.
+            u4 aa[BK / 16][MI];
+#pragma unroll
+            for (int sub = 0; sub < BK / 16; ++sub)
+#pragma unroll
+                for (int i = 0; i < MI; ++i) aa[sub][i] = read_a(sub, i);
+            deq(0, bc);
+#pragma unroll
+            for (int sub = 0; sub < BK / 16; ++sub) {
+                if (sub + 1 < BK / 16) deq(sub + 1, bn);
+                const bool live = !KT || k0 + 16 * sub < p.K;
+                if (live) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) {
+                            if constexpr (BF) acc[i][j] = mfma32(bitcast<b8>(aa[sub][i]), bitcast<b8>(bc[j]), acc[i][j]);
+                            else acc[i][j] = mfma32(bitcast<h8>(aa[sub][i]), bitcast<h8>(bc[j]), acc[i][j]);
+                        }
+                }
+                if (sub + 1 < BK / 16) {
+#pragma unroll
+                    for (int q = 0; q < MI * NJ; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bc[j] = bn[j];
+            }
+            return;
+        }
+        u4 a[MI];
 #pragma unroll
         for (int i = 0; i < MI; ++i) a[i] = read_a(0, i);
         deq(0, bc);
@@ -305,7 +364,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         }
     };
 
-    auto stage = [&](int st) -> char* { return st == 0 ? lds_a0 : st == 1 ? lds_a1 : lds_a2; };
+    auto stage = [&](int st) -> char* {
+        switch (st) {
+        case 0: return lds_a0;
+        case 1: return lds_a1;
+        case 2: return lds_a2;
+        case 3: return lds_a3;
+        case 4: return lds_a4;
+        case 5: return lds_a5;
+        case 6: return lds_a6;
+        default: return lds_a7;
+        }
+    };
 
     // One k-tile on stage and register set S = (kt - segment start) % D,
     // prefetching tile kt + D - 1 (clamped: past the segment's end it
@@ -394,14 +464,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
         }
         int kt = kb;
-        for (; kt + D - 1 < ke; kt += D) {
-            step(std::integral_constant<int, 0>{}, kt);
-            step(std::integral_constant<int, 1>{}, kt + 1);
-            if constexpr (D == 3) step(std::integral_constant<int, D - 1>{}, kt + 2);
-        }
-        if (kt < ke) step(std::integral_constant<int, 0>{}, kt);
-        if constexpr (D == 3)
-            if (kt + 1 < ke) step(std::integral_constant<int, 1>{}, kt + 1);
+        for (; kt + D - 1 < ke; kt += D)
+            static_for<D>([&](auto S_tag) { step(S_tag, kt + decltype(S_tag)::value); });
+        // the last 0 .. D - 1 tiles
+        static_for<D - 1>([&](auto S_tag) {
+            if (kt + decltype(S_tag)::value < ke) step(S_tag, kt + decltype(S_tag)::value);
+        });
         // Drain the last (unused) prefetch before the LDS is reused.
         Q4S_VMCNT(0);
 
