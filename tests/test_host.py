@@ -240,3 +240,17 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.q4_matmul(None, None, None, 1, None) == q4.ERR_INVALID_ARG
     assert lib.q4_dequant_dump(None, 1, None, None) == q4.ERR_INVALID_ARG
     lib.q4_free(None)
+
+
+def test_read_probe_rejects_bad_arguments():
+    # (each check runs before anything is enqueued, so no GPU is needed; the
+    # non-null pointer is never dereferenced)
+    lib = q4.load_library()
+    sink = ctypes.c_void_p(0x2000)
+    assert lib.q4_read_probe(None, 16384, sink, None) == q4.ERR_INVALID_ARG
+    assert lib.q4_read_probe(ctypes.c_void_p(0x1000), 16384, None, None) == q4.ERR_INVALID_ARG
+    assert lib.q4_read_probe(ctypes.c_void_p(0x1008), 16384, sink, None) == q4.ERR_INVALID_ARG
+    assert b"16-byte aligned" in lib.q4_last_error()
+    for bad in (0, 100, 16384 + 16):
+        assert lib.q4_read_probe(ctypes.c_void_p(0x1000), bad, sink, None) == q4.ERR_INVALID_ARG
+        assert b"multiple of 16384" in lib.q4_last_error()
