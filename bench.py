@@ -390,7 +390,10 @@ def read_ceiling(lib, torch, stream, sizes):
     out = {}
     for size in sizes:
         size = size - size % 16384
-        copies = max(1, min(pool_bytes // size, math.ceil(MALL_DEFEAT_BYTES / size)))
+        # (at most 4096 copies: the 16 KiB probe then cycles over 64 MiB,
+        # which is what a near-empty launch needs; every layer-sized probe
+        # still rotates over >= 1 GiB)
+        copies = max(1, min(pool_bytes // size, math.ceil(MALL_DEFEAT_BYTES / size), 4096))
         offs = [(c * size) - (c * size) % 256 for c in range(copies)]
         n = copies * max(1, math.ceil(200 / copies)) if size < (256 << 20) else max(copies, 10)
         g = torch.cuda.CUDAGraph()
@@ -718,12 +721,15 @@ def main():
     sec = {} if args.no_secondary else secondary(q4, torch, synth, lib, stream)
 
     log("[bench] read ceiling")
-    sizes = sorted({ly_bytes for ly_bytes in (8716288, 23425024, 122028032)} | {2 << 30})
+    # (16 KiB: one workgroup reading one chunk, the time of a launch that
+    # does almost nothing, in the same chain of dependent launches)
+    sizes = sorted({ly_bytes for ly_bytes in (8716288, 23425024, 122028032)} | {2 << 30, 16384})
     ceiling = read_ceiling(lib, torch, stream, sizes)
+    launch_floor_us = ceiling[16384]["us"]
 
     def probe_us(nbytes):
         """Read-probe time for nbytes, from the probe of the nearest size."""
-        size = min(ceiling, key=lambda k: abs(k - nbytes))
+        size = min((k for k in ceiling if k > 16384), key=lambda k: abs(k - nbytes))
         return ceiling[size]["us"] * nbytes / size
 
     block_read_us = sum(probe_us(b) for b in layer_bytes)
@@ -766,11 +772,14 @@ def main():
         },
         "read_ceiling": {
             "what": "one q4_read_probe launch of each size (16-byte non-temporal loads, nothing "
-                    "else), rotating over >= 1 GiB, mean launch time",
+                    "else), rotating over >= 1 GiB (the 16 KiB launch over 64 MiB), mean launch "
+                    "time in a chain of dependent launches; launch_floor_us is the 16 KiB one",
             "by_bytes": {str(k): v for k, v in ceiling.items()},
             "block_us": round(block_read_us, 2),
             "block_GB/s": round(block_bytes / block_read_us / 1e3, 1),
             "value_frac_of_ceiling": round(block_read_us / (ms_per_step * 1e3), 4),
+            "launch_floor_us": launch_floor_us,
+            "block_launch_floor_us": round(n_layers * launch_floor_us, 2),
         },
         "environment": gpu_environment(torch),
         "secondary": sec,
