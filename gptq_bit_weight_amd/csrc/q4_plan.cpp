@@ -184,12 +184,17 @@ bool gemv_gathers_x(int M, int K, int splits)
 //    few (11008x4096 at M = 513 .. 768: 96), and too few workgroups leave
 //    CUs idle (at M <= 256, before the 64-row tiles: 97 us with 64
 //    workgroups against 54 us with 256).
-//  * 64-row tiles (M <= 512): few rows make the product bound by the weight
-//    stream (their kernel keeps two k-tiles in flight). About 24 k-tiles a
-//    workgroup measured best, between one and two workgroups per CU: the 7B
-//    MLP shapes (5504 iterations) 22-24 us at 256 workgroups against
-//    25-30 us at 512; the 70B ones (28672) 58-62 us at 512 against 63-70 us
-//    at 256 or 1024. Their partials are 32 KiB.
+//  * 64-row tiles (M <= 512): a CU runs about one 64-row k-tile per 0.35 us
+//    whether it holds one workgroup or two, and every split tile costs a
+//    32 KiB partial round trip. So one workgroup per CU when that gives each
+//    at least 16 k-tiles, two per CU only from 32 k-tiles each, and with
+//    fewer iterations 16 k-tiles a workgroup (at least one per tile).
+//    Measured (us; 7B MLP shapes / 4096x4096; planned count first): M = 64
+//    19.1 / 19.5 at 256 (128: 24.4 / 23.5), 4096x4096 14.9 at 128 (256:
+//    17.8); M = 128 25.0 / 24.3 at 256 (512: 26.1 / 26.9); M = 256 36.9 /
+//    34.9 at 512 (256: 40.3 / 38.4), 4096x4096 19.5 at 256 (512: 20.9); the
+//    70B MLP layers at M <= 64 (28672 iterations) 58-62 us at 512 against
+//    63-70 us at 256 or 1024.
 int plan_gemm_workers(int M, int N, int K, int num_cu)
 {
     if (num_cu <= 0) num_cu = 256;
@@ -199,8 +204,11 @@ int plan_gemm_workers(int M, int N, int K, int num_cu)
     if (tiles * 10 >= rounds * cap * 9 || tiles * 2 >= cap * 3) return (int)tiles;
     const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
     const long long iters = tiles * ktiles;
-    long long w = gemm_bm(M) < kGemmBM ? std::min(cap, std::max<long long>(num_cu, iters / 24))
-                                   : std::min(cap, std::max<long long>(2 * tiles, num_cu));
+    long long w;
+    if (gemm_bm(M) < kGemmBM)
+        w = iters >= 32 * cap ? cap : iters >= 16LL * num_cu ? num_cu : std::max(tiles, iters / 16);
+    else
+        w = std::min(cap, std::max<long long>(2 * tiles, num_cu));
     w = std::min(w, iters);
     return (int)std::min<long long>(w, Q4_GEMM_MAX_WORKERS);
 }

@@ -104,10 +104,11 @@ def test_stream_k_planned_matches_explicit():
     """The planned schedule (splits=0) is the one q4_plan_gemm names."""
     import gptq_bit_weight_amd as q4
     torch = torch_mod()
-    L = _layer(1024, 520, 128, 300, 1, bias=True)
+    # (25 tiles of 64 k-steps: the plan shares them among 100 workgroups)
+    L = _layer(4096, 520, 128, 300, 1, bias=True)
     t = device_tensors(L)
     W = make_matrix(L, t)
-    P = q4.plan_gemm(300, 520, 1024, torch.cuda.get_device_properties(0).multi_processor_count)
+    P = q4.plan_gemm(300, 520, 4096, torch.cuda.get_device_properties(0).multi_processor_count)
     assert P != _tiles(300, 520)
     announce(f"stream-k planned workers={P}")
     a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA)

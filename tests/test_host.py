@@ -163,9 +163,10 @@ def test_plan_gemm():
     """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 512)
     when the tiles fill whole rounds of two per CU (to within a tenth) or make
     1.5 rounds or more; otherwise the workgroups share the k-steps
-    (stream-K): about 24 k-steps each between CUs and 2 x CUs workgroups for
-    64-row tiles, min(2 CUs, max(2 tiles, CUs)) for 256-row ones, never more
-    than there are (tile, 64-row k-step) iterations."""
+    (stream-K): for 64-row tiles 2 x CUs workgroups from 32 k-steps each, CUs
+    from 16, else 16 k-steps each (at least one per tile); for 256-row ones
+    min(2 CUs, max(2 tiles, CUs)); never more than there are (tile, 64-row
+    k-step) iterations."""
     p = q4.plan_gemm
     assert p(2048, 4096, 11008, 256) == 512      # 256 tiles: every CU at one
     assert p(2048, 11008, 4096, 256) == 512      # 688 tiles: 1.34 rounds
@@ -173,11 +174,13 @@ def test_plan_gemm():
     assert p(4096, 4096, 4096, 256) == 512       # 512 tiles: one whole round
     assert p(16384, 28672, 8192, 256) == 14336   # 28 whole rounds
     assert p(2048, 28672, 8192, 256) == 1792     # 3.5 rounds
-    assert p(17, 4096, 4096, 256) == 256         # 64-row tiles: about 24 k-tiles a workgroup,
-    assert p(64, 4096, 11008, 256) == 256        # between CUs and 2 x CUs workgroups
-    assert p(32, 28672, 8192, 256) == 512
+    assert p(17, 4096, 4096, 256) == 128         # 64-row tiles: 2048 iterations, 16 a workgroup
+    assert p(64, 4096, 11008, 256) == 256        # 5504 iterations: 21.5 each on one a CU
+    assert p(32, 28672, 8192, 256) == 512        # 28672: 56 each on two a CU
     assert p(64, 11008, 4096, 256) == 256
-    assert p(128, 11008, 4096, 256) == 458       # 2 x 86 tiles of 64 rows x 64 k-steps / 24
+    assert p(128, 11008, 4096, 256) == 256       # 2 x 86 tiles x 64 k-steps: 21.5 each at 2 a CU, too few
+    assert p(256, 4096, 4096, 256) == 256        # 8192 iterations: 32 each on one a CU, 16 at two
+    assert p(64, 1024, 1024, 256) == 8           # 8 tiles x 16 k-steps: one per tile
     assert p(256, 4096, 11008, 256) == 512       # 4 x 32 tiles x 172 k-steps: at most 2 x CUs
     assert p(512, 4096, 11008, 256) == 512       # 8 x 32 tiles of 64 rows x 172 k-steps: 2 x CUs
     assert p(520, 6144, 4096, 256) == 288        # 3 x 48 tiles of 256 rows: 2 x tiles
