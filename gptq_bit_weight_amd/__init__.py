@@ -170,7 +170,8 @@ def plan_gemv(M: int, K: int, N: int, groupsize: int, num_cu: int = 256) -> tupl
 
 def plan_gemm(M: int, N: int, K: int, num_cu: int = 256) -> int:
     """Workgroups of the streaming GEMM for an M x N output with K rows:
-    the number of 256 x 128 output tiles (one each) or a stream-K count."""
+    the number of output tiles (one each; 64 x 128 when M <= 512, else
+    256 x 128) or a stream-K count (q4_plan_gemm)."""
     r = int(load_library().q4_plan_gemm(M, N, K, num_cu))
     if r < 0:
         raise ValueError(f"q4_plan_gemm: bad arguments M={M} N={N} K={K}")

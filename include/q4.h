@@ -421,9 +421,11 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
  * Output tiles are 64 x 128 when M <= 512, else 256 x 128. One workgroup per
  * tile when the tiles fill whole rounds of two per CU (to within a tenth) or
  * make at least 1.5 such rounds; otherwise the tiles' 64-row k-steps are
- * shared evenly (stream-K) by about one workgroup per 24 k-steps, between
- * num_cu and 2 num_cu (64-row tiles), or by min(2 num_cu, max(2 tiles,
- * num_cu)) (256-row tiles), never more than there are (tile, k-step) pairs.
+ * shared evenly (stream-K): with 64-row tiles by 2 num_cu workgroups when
+ * each gets at least 32 k-steps, by num_cu when each gets at least 16, else
+ * by one per 16 k-steps (at least one per tile); with 256-row tiles by
+ * min(2 num_cu, max(2 tiles, num_cu)); never more than there are (tile,
+ * k-step) pairs.
  * Host-only; -1 for M, N or K < 1.
  */
 int q4_plan_gemm(int M, int N, int K, int num_cu);
