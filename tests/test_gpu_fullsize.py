@@ -94,3 +94,14 @@ def test_small_batch(K, N, M):
     CUs; and 600 rows: three 256-row tiles."""
     L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("small_batch", K, N, M), bias=True)
     _check_layer(L, f"small batch {K}x{N}")
+
+
+@pytest.mark.parametrize("K,N,M", [(4096, 4096, 3000), (4096, 11008, 4100), (4096, 11008, 1536)])
+def test_long_prefill(K, N, M):
+    """Longer prompts than the benchmark's: 3000 rows (11 full 256-row tiles
+    and a 184-row one: 384 tiles on 512 stream-K workgroups), 4100 rows
+    (17 x 86 tiles, one workgroup per tile, a 4-row last tile) and 1536 rows
+    (516 tiles on 512 stream-K workgroups, nearly every tile split); whole
+    rows and columns through every tile."""
+    L = synth.make_layer(K, N, 128, M, seed=synth.layer_seed("long_prefill", K, N, M), bias=True)
+    _check_layer(L, f"long prefill {K}x{N}")
