@@ -507,6 +507,9 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         // splits: 0 planned, 1 one workgroup per output tile, P >= 2
         // workgroups sharing the tiles' k-iterations (stream-K)
         const int tiles = gemm_tiles(M, h->N);
+        // (the GEMM's work split is 32-bit arithmetic)
+        if ((long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK) >= (1LL << 30))
+            return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: M=%d gives more than 2^30 GEMM (tile, k-step) pairs", M);
         int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu) : splits == 1 ? tiles : splits;
         // every workgroup must get at least one (tile, k-step) iteration:
         // a split tile counts its contributors as a range of workgroups

@@ -46,17 +46,26 @@ __device__ __forceinline__ To bitcast(const From& f)
 // and -(64 + z), each in both halves. (64 + z has binary16 exponent 6, whose
 // fraction ulp is 1/16, so its bits are 0x5400 + 16 z.)
 struct zero_t {
-    h2 hz;     // 1024 + z
-    h2 nz16;   // -(64 + z)
+    h2 hz;            // 1024 + z
+    h2 nz16;          // -(64 + z)
+    uint32_t magic;   // kMagic2, the OR constant of the unpack (a register)
 };
 
-__device__ __forceinline__ zero_t zero_pair(uint32_t z)
+// From a group word (scale bits | z << 16, z < 256): one v_perm_b32 puts z
+// (byte 2) under 0x64 (byte 1 of magic) in both halves, 1024 + z (exact for
+// z < 1024), and -(64 + z) = 960 - (1024 + z) is one exact packed subtract.
+// `magic` is kMagic2; a kernel that keeps it in a register across its loop
+// passes that register, so that neither this nor the unpack rebuilds it.
+__device__ __forceinline__ zero_t zero_pair_sz(uint32_t sz, uint32_t magic = kMagic2)
 {
     zero_t r;
-    r.hz = bitcast<h2>((z | 0x6400u) * 0x00010001u);
-    r.nz16 = bitcast<h2>((0xD400u + (z << 4)) * 0x00010001u);
+    r.hz = bitcast<h2>(__builtin_amdgcn_perm(magic, sz, 0x05020502u));
+    r.nz16 = bitcast<h2>(0x63806380u) - r.hz;   // (960, 960)
+    r.magic = magic;
     return r;
 }
+
+__device__ __forceinline__ zero_t zero_pair(uint32_t z) { return zero_pair_sz(z << 16); }
 
 // s in both halves (s given as binary16 bits).
 __device__ __forceinline__ h2 scale_pair(uint32_t s_bits)
@@ -64,15 +73,16 @@ __device__ __forceinline__ h2 scale_pair(uint32_t s_bits)
     return bitcast<h2>((s_bits & 0xFFFFu) * 0x00010001u);
 }
 
-// r = (a & mask) | orv as one v_and_or_b32. gfx9-family VOP3 encodings take
-// no literal operands and read at most one SGPR, so the compiler otherwise
-// splits this into v_and_b32 + v_or_b32; here the mask sits in an SGPR and
-// the OR constant in a VGPR.
+// r = (a & mask) | orv. gfx9-family VOP3 encodings take no literal operands
+// and read at most one SGPR, so this is one v_and_or_b32 only when orv is
+// already in a VGPR (the mask goes to an SGPR): kernels keep the OR constant
+// in a register they hide from constant folding and pass it in (an inline-asm
+// v_and_or_b32 would do the same, but the compiler does not see an asm
+// block's register writes when it spaces them from matrix instructions still
+// writing the same registers).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv)
 {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
-    return r;
+    return (a & mask) | orv;
 }
 
 // Unpack one private-layout word and subtract the zero point: eight fp16
@@ -88,7 +98,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
 //    integers), which saves the shifts that would line them up.
 __device__ __forceinline__ h8 sub_zero_word(uint32_t w, zero_t z)
 {
-    const uint32_t magic = kMagic2;
+    const uint32_t magic = z.magic;
     const uint32_t w8 = w >> 8;
     const h2 sixteenth = bitcast<h2>(0x2C002C00u);     // (1/16, 1/16)
     const h2 v0 = bitcast<h2>(and_or(w, 0x000F000Fu, magic)) - z.hz;
@@ -157,17 +167,19 @@ typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 typedef float ff2 __attribute__((ext_vector_type(2)));
 
 struct mix_t {
-    float t;     // scale of the result (1 for q - z)
-    float c0;    // -(1024 + z) t
-    float c1;    // -(64 + z) t
+    float t;          // scale of the result (1 for q - z)
+    float c0;         // -(1024 + z) t
+    float c1;         // -(64 + z) t
+    uint32_t magic;   // kMagic2, the OR constant of the unpack (a register)
 };
 
-__device__ __forceinline__ mix_t mix_consts(uint32_t z, float t)
+__device__ __forceinline__ mix_t mix_consts(uint32_t z, float t, uint32_t magic = kMagic2)
 {
     mix_t m;
     m.t = t;
     m.c0 = -(1024.0f + (float)z) * t;
     m.c1 = -(64.0f + (float)z) * t;
+    m.magic = magic;
     return m;
 }
 
@@ -200,7 +212,7 @@ __device__ __forceinline__ b8 mix_word8(uint32_t w0, uint32_t w1, const mix_t& m
 // One private-layout word as eight bfloat16 values t * (q - z) in k order.
 __device__ __forceinline__ b8 mix_word(uint32_t w, const mix_t& m)
 {
-    const uint32_t magic = kMagic2;
+    const uint32_t magic = m.magic;
     const uint32_t w8 = w >> 8;
     const float f1 = m.t * 0.0625f;
     u4 o;
@@ -263,6 +275,13 @@ __device__ __forceinline__ uint32_t buf_load4_nt(rsrc_t r, uint32_t off, uint32_
 __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
     return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
+}
+
+// A 2-byte store; like the loads, a store at or past the descriptor's size
+// is dropped.
+__device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint32_t soff, uint16_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, (int)soff, 0);
 }
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c)

@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "q4_device.h"
+#include "q4_fastdiv.h"
 #include "q4_internal.h"
 
 namespace {
@@ -95,6 +96,13 @@ struct GemmArgs {
     uint32_t* counters;
     int workers;
     int xcd;                // 1: each XCD takes the row tiles r with r % 8 == XCD (row tiles % 8 == 0)
+    // The same split in 32-bit terms, set by the host (iterations < 2^30):
+    // a space of `iters` iterations shared by `ps` workgroups, with
+    // iters = iq * ps + ir; k-tiles per output tile and column tiles; and
+    // multipliers for dividing by ps, ktiles and nt.
+    uint32_t iters, ps, iq, ir, ktiles, nt;
+    q4::FastDiv div_ps, div_kt, div_nt;
+    float ps_per_iter;      // ps / iters (the owner estimate below)
 };
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), unrolled
@@ -186,11 +194,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     constexpr int WTM = Geo<BM>::WTM, MI = Geo<BM>::MI;
     constexpr int A_TILE_BYTES = Geo<BM>::A_TILE_BYTES, A_LOADS = Geo<BM>::A_LOADS;
     // Ring depth: activation stages in LDS and weight register sets, both
-    // D - 1 k-tiles ahead: two for 64-row tiles (few rows), one for 256-row
-    // tiles. (Four, six or eight 64-row stages measured 2-8% slower at
-    // M = 33 ... 512: a k-tile there costs about 0.35 us of one CU's time
-    // whatever the depth, and deeper rings only add registers and fills.)
-    constexpr int D = BM == 64 ? 3 : 2;
+    // D - 1 k-tiles ahead: three for 64-row tiles (few rows), one for
+    // 256-row tiles. (Deeper 64-row rings first measured slower: the
+    // compiler then reused a few registers for the activation reads and
+    // waited out one LDS latency per sub-step. With all reads of a k-tile
+    // issued together (mma below), four stages beat three by 2-9% at
+    // M = 33 ... 128 on the 7B MLP shapes and 4096 x 4096.)
+    constexpr int D = BM == 64 ? 4 : 2;
     // vector-memory loads one step issues per thread (activation DMA, packed
     // weights, scale|zero words)
     constexpr int LPS = A_LOADS + 2 * NJ + NG * NJ;
@@ -219,16 +229,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     // their activations in its L2; otherwise one space in row-major tile
     // order. A space of T tiles holds T * ktiles iterations (tile-major);
     // worker r of Ps takes iterations [r * I / Ps, (r + 1) * I / Ps).
-    const int nt = (p.N + BN - 1) / BN, mt = (p.M + BM - 1) / BM;
-    const int ktiles = (p.K + BK - 1) / BK;
+    // (All of this is wave-uniform 32-bit arithmetic: 64-bit divisions here
+    // compiled to about 1200 scalar instructions, 1.1 us before the first
+    // load of every workgroup.)
+    const uint32_t ktiles = p.ktiles, nt = p.nt;
     const int id = blockIdx.x;
     const int space = p.xcd ? (id & 7) : 0;
     const int rk = p.xcd ? (id >> 3) : id;
-    const int Ps = p.xcd ? p.workers >> 3 : p.workers;
-    const long long I = (long long)(p.xcd ? (mt >> 3) * nt : mt * nt) * ktiles;
-    const long long it_begin = (long long)rk * I / Ps, it_end = (long long)(rk + 1) * I / Ps;
-    // worker of iteration i: the largest r with r * I / Ps <= i
-    auto owner = [&](long long i) { return (int)(((i + 1) * Ps + I - 1) / I - 1); };
+    // first iteration of worker r: floor(r * iters / ps) = r * iq + floor(r * ir / ps)
+    auto begin_of = [&](int r) { return (uint32_t)r * p.iq + q4::fast_div((uint32_t)r * p.ir, p.div_ps); };
+    const uint32_t it_begin = begin_of(rk), it_end = begin_of(rk + 1);
+    // worker of iteration i: the largest r with begin_of(r) <= i (a float
+    // estimate, off by at most one or two, then corrected)
+    auto owner = [&](uint32_t i) {
+        int r = min((int)((float)i * p.ps_per_iter), (int)p.ps - 1);
+        while (r > 0 && begin_of(r) > i) --r;
+        while (r + 1 < (int)p.ps && begin_of(r + 1) <= i) ++r;
+        return r;
+    };
     auto worker_id = [&](int r) { return p.xcd ? r * 8 + space : r; };
 
     Ctx c;
@@ -239,6 +257,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 
     f16x acc[MI][NJ];
     BRegs<NG, W8> R[D];
+    // the unpack's OR constant in a register (see and_or)
+    uint32_t magic = kMagic2;
+    asm volatile("" : "+v"(magic));
     int m0 = 0, seg_end = 0;
     int lane_cols[NJ];
 
@@ -260,7 +281,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 if constexpr (!BF) {
-                    hz[gi][j] = zero_pair(R.sz[gi][j] >> 16);
+                    hz[gi][j] = zero_pair_sz(R.sz[gi][j], magic);
                     s2[gi][j] = scale_pair(R.sz[gi][j]);
                 }
             }
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 if (sub % (4 / NG) == 0)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j)
-                        mz[j] = mix_consts(R.sz[gi][j] >> 16, f16_bits_to_f32((uint16_t)R.sz[gi][j]));
+                        mz[j] = mix_consts(R.sz[gi][j] >> 16, f16_bits_to_f32((uint16_t)R.sz[gi][j]), magic);
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -302,6 +323,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             for (int sub = 0; sub < BK / 16; ++sub)
 #pragma unroll
                 for (int i = 0; i < MI; ++i) aa[sub][i] = read_a(sub, i);
+            // (all of them issued before the first MFMA: otherwise the
+            // compiler reuses a few registers for them and waits out one
+            // LDS latency per sub-step)
+            __builtin_amdgcn_sched_group_barrier(0x100, BK / 16 * MI, 0);
             deq(0, bc);
 #pragma unroll
             for (int sub = 0; sub < BK / 16; ++sub) {
@@ -407,19 +432,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     // halves of a split tile finish early and its fix-up overlaps the whole
     // tiles of this workgroup and of the one sharing its CU, instead of all
     // fix-ups landing at the end of the kernel.
-    const long long lo = min(it_end, (it_begin + ktiles - 1) / ktiles * ktiles);
-    const long long hi = max(lo, it_end / ktiles * ktiles);
-    const int nfull = (int)((hi - lo) / ktiles);
+    const uint32_t lo = min(it_end, q4::fast_div(it_begin + ktiles - 1, p.div_kt) * ktiles);
+    const uint32_t hi = max(lo, q4::fast_div(it_end, p.div_kt) * ktiles);
+    const int nfull = (int)q4::fast_div(hi - lo, p.div_kt);
     bool first_seg = true;
     for (int sg = -2; sg < nfull; ++sg) {
-        const long long sb = sg == -2 ? it_begin : sg == -1 ? hi : lo + (long long)sg * ktiles;
-        const long long se = sg == -2 ? lo : sg == -1 ? it_end : sb + ktiles;
+        const uint32_t sb = sg == -2 ? it_begin : sg == -1 ? hi : lo + (uint32_t)sg * ktiles;
+        const uint32_t se = sg == -2 ? lo : sg == -1 ? it_end : sb + ktiles;
         if (sb >= se) continue;
-        const int lt = (int)(sb / ktiles);
-        const int kb = (int)(sb - (long long)lt * ktiles);
+        const uint32_t lt = q4::fast_div(sb, p.div_kt);
+        const int kb = (int)(sb - lt * ktiles);
         const int ke = kb + (int)(se - sb);
-        const int mtile = p.xcd ? (lt / nt) * 8 + space : lt / nt;
-        const int n0 = (lt % nt) * BN;
+        const uint32_t tr = q4::fast_div(lt, p.div_nt);   // row tile within the space
+        const int mtile = p.xcd ? (int)tr * 8 + space : (int)tr;
+        const int n0 = (int)(lt - tr * nt) * BN;
         m0 = mtile * BM;
         seg_end = ke;
         tid = threadIdx.x;
@@ -445,6 +471,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             for (int v = 0; v < 2; ++v) c.w_off[j][v] = q4::chunk_in_block(lhi + 2 * v, (int)n, p.N) * (W8 ? 32u : 16u);
             c.sz_off[j] = n * 4u;
         }
+        // the bias of the lane's columns, loaded before the k-loop so that
+        // its latency hides behind it (the loop's counted waits then also
+        // cover this oldest load, which only makes the first wait exact)
+        uint16_t bias_h[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bias_h[j] = p.bias ? p.bias[min(lane_cols[j], p.N - 1)] : (uint16_t)0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -473,7 +505,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         // Drain the last (unused) prefetch before the LDS is reused.
         Q4S_VMCNT(0);
 
-        if (kb != 0 || ke != ktiles) {
+        if (kb != 0 || ke != (int)ktiles) {
             // A split tile, whose workers wf .. wl each hold one k-segment.
             // The last of them to arrive adds the fp32 sums in k order,
             // p_wf + p_wf+1 + ... + p_wl (the same bits whichever worker that
@@ -486,7 +518,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             // Slots: a segment that starts inside its tile is its worker's
             // first (slot 2 id), one that starts the tile is its worker's
             // last (slot 2 id + 1).
-            const long long t0 = (long long)lt * ktiles;
+            const uint32_t t0 = lt * ktiles;
             const int wf = owner(t0), wl = owner(t0 + ktiles - 1);
             const uint32_t others = (uint32_t)(wl - wf);
             auto slot_of = [&](int r) {
@@ -515,12 +547,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 if (!s_last) continue;
             }
             // Ordered sum, 32 values per lane at a time: p_wf + ... + p_wl,
-            // this worker's own sums taken from its registers.
+            // this worker's own sums taken from its registers. With 64-row
+            // tiles (up to eight contributors on a narrow layer) the other
+            // workers' slots are read FB at a time, all loads of a batch in
+            // flight together: 1-2% faster at M = 33 ... 256 than one worker
+            // at a time (these loads are bound more by the rate at which one
+            // CU fetches device-coherent data than by their latency). 256-row
+            // tiles keep one at a time: their accumulators leave no room.
+            constexpr int FB = MI <= 2 ? 4 : 1;
             auto load32 = [&](float (&v)[32], int r, int q) {
                 const float* src = slot_of(r) + (size_t)q * 16 * NT + tid;
 #pragma unroll
                 for (int e = 0; e < 32; ++e)
                     v[e] = __hip_atomic_load(&src[e * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            // workers r0 .. r1 in batches of FB; f(v, r) consumes worker r's
+            // values, in worker order
+            auto batches = [&](int r0, int r1, int q, auto&& f) {
+                for (int rb = r0; rb <= r1; rb += FB) {
+                    float v[FB][32];
+#pragma unroll
+                    for (int b = 0; b < FB; ++b)
+                        if (rb + b <= r1) load32(v[b], rb + b, q);
+#pragma unroll
+                    for (int b = 0; b < FB; ++b)
+                        if (rb + b <= r1) f(v[b], rb + b);
+                }
             };
 #pragma unroll
             for (int q = 0; q < MI * NJ; q += 2) {
@@ -528,41 +580,55 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 if (rk > wf) {
                     // p_wf + ... + p_(rk-1), then + this worker's sums
                     float t[32];
-                    load32(t, wf, q);
-                    for (int r = wf + 1; r < rk; ++r) {
-                        float v[32];
-                        load32(v, r, q);
+                    batches(wf, rk - 1, q, [&](const float (&v)[32], int r) {
 #pragma unroll
-                        for (int e = 0; e < 32; ++e) t[e] += v[e];
-                    }
+                        for (int e = 0; e < 32; ++e) t[e] = r == wf ? v[e] : t[e] + v[e];
+                    });
 #pragma unroll
                     for (int e = 0; e < 32; ++e) Q4S_ACC(e) = t[e] + Q4S_ACC(e);
                 }
-                for (int r = rk + 1; r <= wl; ++r) {
-                    float v[32];
-                    load32(v, r, q);
+                batches(rk + 1, wl, q, [&](const float (&v)[32], int) {
 #pragma unroll
                     for (int e = 0; e < 32; ++e) Q4S_ACC(e) += v[e];
-                }
+                });
 #undef Q4S_ACC
             }
             if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
         // Epilogue: fp32 bias, one round-to-nearest-even cast, store. Lane l
-        // holds rows 8*(r/4) + 4*(l/32) + r%4 of column l%32 of each 32 x 32 tile.
+        // holds rows 8*(r/4) + 4*(l/32) + r%4 of column l%32 of each 32 x 32
+        // tile. A whole row tile stores through a buffer descriptor, the row
+        // part of each offset wave-uniform, with no per-element checks (a
+        // compare and branch per element cost about 1 us of a 64-row tile's
+        // epilogue); only the last, partial row tile checks its rows.
+        const rsrc_t ro = make_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
+        const bool whole = m0 + BM <= p.M;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int n = lane_cols[j];
             if (n >= p.N) continue;
-            const float bv = p.bias ? act_to_f32<BF>(p.bias[n]) : 0.f;
+            const float bv = p.bias ? act_to_f32<BF>(bias_h[j]) : 0.f;
+            const int mb = m0 + wm * WTM + 4 * lhi;   // the lane's first row
+            if (whole) {
+                // (m * N + n) * 2 < M * N * 2 <= 2^32 - 2: no wrap-around
+                const uint32_t voff = ((uint32_t)mb * (uint32_t)p.N + (uint32_t)n) * 2u;
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                    if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_act<BF>(acc[i][j][r] + bv);
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const uint32_t dr = (uint32_t)(32 * i + 8 * (r >> 2) + (r & 3));
+                        buf_store2(ro, voff, dr * (uint32_t)p.N * 2u, f32_to_act<BF>(acc[i][j][r] + bv));
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = mb + 32 * i + 8 * (r >> 2) + (r & 3);
+                        if (m < p.M) p.out[(size_t)m * p.N + n] = f32_to_act<BF>(acc[i][j][r] + bv);
+                    }
+            }
         }
     }
 }
@@ -620,7 +686,24 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     // tile height: 64 rows when that covers M (few rows), else 256
     const int bm = gemm_bm(M);
     // XCD spaces need whole row tiles and workers per XCD
-    p.xcd = ((M + bm - 1) / bm) % 8 == 0 && workers % 8 == 0;
+    const uint32_t mt = (uint32_t)((M + bm - 1) / bm), nt = (uint32_t)((h->N + BN - 1) / BN);
+    const uint32_t ktiles = (uint32_t)((h->K + BK - 1) / BK);
+    p.xcd = mt % 8 == 0 && workers % 8 == 0;
+    const uint64_t iters = (uint64_t)(p.xcd ? mt / 8 : mt) * nt * ktiles;
+    const uint32_t ps = (uint32_t)(p.xcd ? workers / 8 : workers);
+    // (matmul_impl rejects larger products with a message; the kernel's
+    // index arithmetic is 32-bit)
+    if (workers < 1 || iters >= (1u << 30) || ps > iters) return hipErrorInvalidValue;
+    p.iters = (uint32_t)iters;
+    p.ps = ps;
+    p.iq = p.iters / ps;
+    p.ir = p.iters % ps;
+    p.ktiles = ktiles;
+    p.nt = nt;
+    p.div_ps = make_fastdiv(ps);
+    p.div_kt = make_fastdiv(ktiles);
+    p.div_nt = make_fastdiv(nt);
+    p.ps_per_iter = (float)ps / (float)p.iters;
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;

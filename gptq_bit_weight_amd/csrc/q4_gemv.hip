@@ -1,12 +1,13 @@
 // Skinny fused GPTQ kernel for 1 <= M <= 32 (decode and small batches).
 //
-// q4_gemv_kernel<NGB, CT, XS, TAIL, XL, BF, W8, MB>: NGB groups per 128-row
-// block, CT 16-column tiles per wave, XS k-steps per activation load, TAIL (K
-// not a multiple of 128), XL (act-order activations staged in LDS), BF
-// (bfloat16 activations and output), W8 (8-bit codes; 4-bit otherwise), MB
-// blocks of 16 activation rows (1 for M <= 16; 2 for 16 < M <= 32, which
+// q4_gemv_kernel<NGB, CT, XS, TAIL, XL, BF, W8, MB, R1>: NGB groups per
+// 128-row block, CT 16-column tiles per wave, XS k-steps per activation load,
+// TAIL (K not a multiple of 128), XL (act-order activations staged in LDS),
+// BF (bfloat16 activations and output), W8 (8-bit codes; 4-bit otherwise),
+// MB blocks of 16 activation rows (1 for M <= 16; 2 for 16 < M <= 32, which
 // load one k-step per activation load and share each unpacked weight
-// fragment between the two row blocks' MFMAs). (Four row blocks, M <= 64,
+// fragment between the two row blocks' MFMAs), R1 (M = 1: one-row mode,
+// below). (Four row blocks, M <= 64,
 // measured 1.4-2.5x slower than the GEMM on the 7B and 70B MLP shapes: their
 // activation registers leave room for two column tiles at one workgroup per
 // CU, and the activation loads grow with every row block.)
@@ -32,6 +33,14 @@
 //    M <= R (R = 4 or 8): lane group s of each 16-lane row loads the R rows of
 //    k-step s, and a DPP row shift moves them into lanes 0 .. R-1 for that
 //    step's MFMA, instead of one mostly empty load per k-step.
+//  * One-row mode (M = 1, R1): no shift at all. Every k-step's MFMA takes the
+//    activation register as loaded, so A row 4s holds k-step s's activations
+//    and output row 4s of k-step i's product is x . W_i only for s = i. Each
+//    k-step's product starts from zero and only that row (the first element
+//    of lane group i) is folded into its own total; the four lane groups'
+//    totals are added in the cross-wave sum. That saves the twelve row shifts
+//    of a block (58 -> 42 vector instructions with the packed zero points
+//    below) and leaves the four products independent of each other.
 //  * B is the exact small integers q - z in fp16, and the per-group scale is
 //    applied once per group to the fp32 MFMA sum:
 //    sum_k x * s * (q - z) = s * sum_k x * (q - z). The weight s * (q - z) is
@@ -206,9 +215,9 @@ __device__ __forceinline__ u4 a_operand(const u4 a[4], int i)
 // the exact q - z as bfloat16 (both operands bfloat16 on the matrix pipe).
 // XL: block b's activations are read from the LDS copy (xl = this lane's
 // address in it for the first block of the workgroup's range, bs0).
-template <int NGB, int CT, int XS, bool XL, bool BF, bool W8, int MB>
+template <int NGB, int CT, int XS, bool XL, bool BF, bool W8, int MB, bool R1>
 __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f4 (&tot)[MB][CT],
-                                              const char* xl, int b, int bs0)
+                                              const char* xl, int b, int bs0, uint32_t magic)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
     u4 av[MB][4];
@@ -233,12 +242,12 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
         if constexpr (BF) asm("" : "+v"(one));
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-            const uint32_t z = B.sz[gi][j] >> 16;
-            if constexpr (BF) mz[j] = mix_consts(z, one);
-            else zp[j] = zero_pair(z);
+            if constexpr (BF) mz[j] = mix_consts(B.sz[gi][j] >> 16, one, magic);
+            else zp[j] = zero_pair_sz(B.sz[gi][j], magic);
             sf[j] = f16_bits_to_f32((uint16_t)B.sz[gi][j]);
         }
         f4 acc[MB][CT];
+        f4 pr[R1 ? SPG : 1][CT];   // one-row mode: the group's k-step products
 #pragma unroll
         for (int ii = 0; ii < SPG; ++ii) {
             const int i = gi * SPG + ii;
@@ -258,20 +267,48 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
                 } else {
                     bw = bitcast<u4>(sub_zero_word(B.w[j][0][i], zp[j]));
                 }
+                if constexpr (R1) {
+                    // One row: the activation register as loaded (lane group
+                    // s holds k-step s) against k-step i's weights. Output
+                    // row 4s of this product is x . W_i only for s = i: lane
+                    // group i's first element. Each k-step gets its own
+                    // product from zero and its own total, tot[0][j][i]; the
+                    // other rows are never read.
+                    if constexpr (BF) pr[ii][j] = mfma16(bitcast<b8>(av[0][0]), bitcast<b8>(bw), c0);
+                    else pr[ii][j] = mfma16(bitcast<h8>(av[0][0]), bitcast<h8>(bw), c0);
+                } else {
 #pragma unroll
-                for (int rb = 0; rb < MB; ++rb) {
-                    const u4 a = a_operand<XS>(av[rb], i);
-                    if constexpr (BF) acc[rb][j] = mfma16(bitcast<b8>(a), bitcast<b8>(bw), ii == 0 ? c0 : acc[rb][j]);
-                    else acc[rb][j] = mfma16(bitcast<h8>(a), bitcast<h8>(bw), ii == 0 ? c0 : acc[rb][j]);
+                    for (int rb = 0; rb < MB; ++rb) {
+                        const u4 a = a_operand<XS>(av[rb], i);
+                        if constexpr (BF) acc[rb][j] = mfma16(bitcast<b8>(a), bitcast<b8>(bw), ii == 0 ? c0 : acc[rb][j]);
+                        else acc[rb][j] = mfma16(bitcast<h8>(a), bitcast<h8>(bw), ii == 0 ? c0 : acc[rb][j]);
+                    }
                 }
             }
         }
+        if constexpr (R1) {
+            // (after all of the group's products, so that the matrix pipe
+            // runs them back to back)
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
+            for (int ii = 0; ii < SPG; ++ii)
 #pragma unroll
-            for (int j = 0; j < CT; ++j)
+                for (int j = 0; j < CT; ++j)
+                    tot[0][j][gi * SPG + ii] = __builtin_fmaf(sf[j], pr[ii][j][0], tot[0][j][gi * SPG + ii]);
+            // (the products' other registers stay allocated until here, past
+            // the read above, which waits for the matrix pipe; reused
+            // earlier, each reuse would wait for the product's last write)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tot[rb][j][e] = __builtin_fmaf(sf[j], acc[rb][j][e], tot[rb][j][e]);
+            for (int ii = 0; ii < SPG; ++ii)
+#pragma unroll
+                for (int j = 0; j < CT; ++j) asm volatile("" ::"v"(pr[ii][j]));
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+                for (int j = 0; j < CT; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tot[rb][j][e] = __builtin_fmaf(sf[j], acc[rb][j][e], tot[rb][j][e]);
+        }
     }
 }
 
@@ -308,9 +345,10 @@ __device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR]
         }
 }
 
-template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB>
+template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB, bool R1>
 __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 {
+    static_assert(!R1 || (XS == 4 && MB == 1), "one-row mode reads four k-steps per activation load");
     constexpr int COLS = 16 * CT;
     constexpr int ROWS = 16 * MB;
     __shared__ float red[WV][ROWS][COLS];
@@ -318,6 +356,12 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     extern __shared__ u4 xs_dyn[];   // XL: the workgroup's activations, [M][ldx] halfs
 
     const int tid = threadIdx.x;
+    // All kernel arguments the loads need, fetched together: otherwise the
+    // pointers are fetched after the first branch, a second wait on the
+    // argument fetch before the first weight load (about 0.07 us of a
+    // 4096 x 4096 layer).
+    asm volatile("" ::"s"(p.qweight), "s"(p.sz), "s"(p.x), "s"(p.M), "s"(p.K), "s"(p.N), "s"(p.kblocks),
+                 "s"(p.blocks_per_split), "s"(p.blocks_per_wave), "s"(p.gshift), "s"(p.ng));
     // The wave index is uniform across the wave; saying so keeps the block
     // bookkeeping in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -328,7 +372,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     // tiles share the cache lines of their scales and packed zeros (a 128-byte
     // line holds 64 columns of scales, 256 of zeros), and the XCDs' L2 caches
     // are separate, so each XCD takes a contiguous run of tiles.
-    const int T = gridDim.x;
+    const int T = (p.N + COLS - 1) / COLS;   // (the grid's x size, without a hidden-argument load)
     const int tile = (T & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (T >> 3) + (int)(blockIdx.x >> 3);
     const int n0 = tile * COLS;
 
@@ -369,6 +413,10 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
 #pragma unroll
         for (int j = 0; j < CT; ++j) tot[rb][j] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // the unpack's OR constant, kept in a register for the whole loop (as a
+    // constant it was rebuilt in every block)
+    uint32_t magic = kMagic2;
+    asm volatile("" : "+v"(magic));
     constexpr int D = depth<CT, MB>();
     // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
     // Once a block is multiplied its buffer is refilled with the block D
@@ -421,7 +469,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int rd = 1; rd < rounds; ++rd) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute_block<NGB, CT, XS, XL, BF, W8, MB>(buf[d], tot, xl, b0 + D * (rd - 1) + d, bs0);
+                compute_block<NGB, CT, XS, XL, BF, W8, MB, R1>(buf[d], tot, xl, b0 + D * (rd - 1) + d, bs0, magic);
                 load_block<NGB, CT, XS, TAIL, XL, W8, MB>(buf[d], p, r, ln, min(b0 + D * rd + d, bl));
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -429,30 +477,51 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         const int last = nb - D * (rounds - 1);   // 1 .. D blocks in the last round
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8, MB>(buf[d], tot, xl, b0 + D * (rounds - 1) + d, bs0);
+            if (d < last) compute_block<NGB, CT, XS, XL, BF, W8, MB, R1>(buf[d], tot, xl, b0 + D * (rounds - 1) + d, bs0, magic);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // Cross-wave reduction. Lane l holds rows 16 rb + 4 * (l / 16) + i of
-    // column l % 16 of each tile (16x16 MFMA output layout).
+    // column l % 16 of each tile (16x16 MFMA output layout). One-row mode:
+    // lane group g (= kb) holds row 0's sums over k-steps 4b + g in
+    // tot[0][j][g], written to row 4g; the sum below adds the four groups.
+    constexpr int LG = R1 ? 4 : 1;   // lane groups holding parts of one row
+    if constexpr (R1) {
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+        for (int j = 0; j < CT; ++j) {
+            const f4 t = tot[0][j];
+            red[wave][4 * kb][16 * j + c16] = kb == 0 ? t[0] : kb == 1 ? t[1] : kb == 2 ? t[2] : t[3];
+        }
+    } else {
 #pragma unroll
-        for (int j = 0; j < CT; ++j)
+        for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (16 * rb + 4 * kb + i < p.M) red[wave][16 * rb + 4 * kb + i][16 * j + c16] = tot[rb][j][i];
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * rb + 4 * kb + i < p.M) red[wave][16 * rb + 4 * kb + i][16 * j + c16] = tot[rb][j][i];
+    }
     __syncthreads();
+    // the workgroup's sum for row m, column c (waves in order, then groups)
+    auto wg_sum = [&](int m, int c) {
+        float y = 0.f;
+#pragma unroll
+        for (int g = 0; g < LG; ++g) {
+            float t = red[0][m + 4 * g][c];
+#pragma unroll
+            for (int w = 1; w < WV; ++w) t += red[w][m + 4 * g][c];
+            y = g == 0 ? t : y + t;
+        }
+        return y;
+    };
 
     const int n_elems = p.M * COLS;
     if (p.splits == 1) {
         for (int idx = tid; idx < n_elems; idx += NT) {
             const int m = idx / COLS, c = idx % COLS, n = n0 + c;
             if (n >= p.N) continue;
-            float y = red[0][m][c];
-#pragma unroll
-            for (int w = 1; w < WV; ++w) y += red[w][m][c];
+            float y = wg_sum(m, c);
             if (p.bias) y += act_to_f32<BF>(p.bias[n]);
             p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
         }
@@ -469,9 +538,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
     for (int idx = tid; idx < n_elems; idx += NT) {
         const int m = idx / COLS, c = idx % COLS, n = n0 + c;
         if (n >= p.N) continue;
-        float y = red[0][m][c];
-#pragma unroll
-        for (int w = 1; w < WV; ++w) y += red[w][m][c];
+        const float y = wg_sum(m, c);
         __hip_atomic_store(&p.partials[((size_t)split * p.M + m) * p.N + n], y, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -498,18 +565,18 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB>
+template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB, bool R1 = false>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
 {
     const dim3 block(NT);
     const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
     case 4:
         // (8-bit blocks are twice the registers: at most two tiles)
         if constexpr (W8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8, MB>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
+        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
         break;
     default: return hipErrorInvalidValue;
     }
@@ -531,6 +598,7 @@ hipError_t launch_ngb(const GemvArgs& p, int ct, int splits, hipStream_t stream)
         }
     }
     if (p.K % 128) return launch_ct<NGB, 1, true, XL, BF, W8, 1>(p, ct, splits, stream);
+    if (p.M == 1) return launch_ct<NGB, 4, false, XL, BF, W8, 1, true>(p, ct, splits, stream);
     if (p.M <= 4 || XL) return launch_ct<NGB, 4, false, XL, BF, W8, 1>(p, ct, splits, stream);
     if constexpr (!XL) {
         if (p.M <= 8) return launch_ct<NGB, 2, false, XL, BF, W8, 1>(p, ct, splits, stream);

@@ -143,7 +143,10 @@ q4_matrix* q4_make_bits(const int32_t* qweight, const int32_t* qzeros, const uin
  * x and out are caller-owned device buffers and must not overlap. M == 0 is
  * a no-op returning Q4_OK. M < 0, NULL pointers or a NULL handle give
  * Q4_ERR_INVALID_ARG. M <= Q4_GEMV_MAX_M runs the skinny kernel, larger M the
- * MFMA GEMM (q4_path_for tells which).
+ * MFMA GEMM (q4_path_for tells which). Sizes beyond the kernels' 32-bit
+ * offsets give Q4_ERR_UNSUPPORTED: M * K * 2 or M * N above 2^31 - 1, or
+ * more than 2^30 GEMM (output tile, 64-row k-step) pairs (about
+ * M * K * N / 2^19).
  *
  * Concurrency: the handle's workspace is shared by its calls, so calls on one
  * handle must be ordered on one stream (or synchronized); different handles
