@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "q4_last_error", "q4_path_for", "q4_dequant_dump", "q4_handle_info", "q4_check_shape",
     "q4_plan_actorder", "q4_plan_gemv", "q4_gemv_gather", "q4_plan_gemv_gather",
     "q4_matmul_bf16", "q4_matmul_ex_bf16", "q4_dequant_dump_bf16", "q4_make_bits", "q4_make_cat_bits",
-    "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm", "q4_read_probe",
+    "q4_handle_bits", "q4_check_shape_bits", "q4_plan_gemm", "q4_plan_gemm_waves", "q4_read_probe",
     "q4_matmul_static",
 )
 
@@ -114,6 +114,8 @@ def load_library():
     lib.q4_plan_gemv_gather.restype = I
     lib.q4_plan_gemm.argtypes = [I, I, I, I]
     lib.q4_plan_gemm.restype = I
+    lib.q4_plan_gemm_waves.argtypes = [I, I, I, I]
+    lib.q4_plan_gemm_waves.restype = I
     lib.q4_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
     lib.q4_read_probe.restype = I
     _lib = lib
@@ -169,12 +171,22 @@ def plan_gemv(M: int, K: int, N: int, groupsize: int, num_cu: int = 256) -> tupl
 
 
 def plan_gemm(M: int, N: int, K: int, num_cu: int = 256) -> int:
-    """Workgroups of the streaming GEMM for an M x N output with K rows:
-    the number of output tiles (one each; 64 x 128 when M <= 512, else
-    256 x 128) or a stream-K count (q4_plan_gemm)."""
+    """Workgroups of the streaming GEMM for an M x N output with K rows, at
+    the planned tile width: the number of output tiles (one each; 64 x 128
+    when M <= 512, else 256 x 128 or 256 x 256) or a stream-K count
+    (q4_plan_gemm)."""
     r = int(load_library().q4_plan_gemm(M, N, K, num_cu))
     if r < 0:
         raise ValueError(f"q4_plan_gemm: bad arguments M={M} N={N} K={K}")
+    return r
+
+
+def plan_gemm_waves(M: int, N: int, K: int, num_cu: int = 256) -> int:
+    """The streaming GEMM's planned tile width in waves of 32 columns: 8
+    (256-column tiles) or 4 (128-column tiles) (q4_plan_gemm_waves)."""
+    r = int(load_library().q4_plan_gemm_waves(M, N, K, num_cu))
+    if r < 0:
+        raise ValueError(f"q4_plan_gemm_waves: bad arguments M={M} N={N} K={K}")
     return r
 
 
@@ -331,8 +343,9 @@ class Q4Matrix:
         then bfloat16 too; the weights and fp16 scales are the same).
 
         path: 0 automatic, PATH_GEMV or PATH_MFMA. variant: skinny kernel --
-        16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- 0 or 3 (one
-        kernel: activations in LDS, weights streamed into registers).
+        16-column tiles per wave (0 planned, 1, 2, 4); GEMM -- the tile
+        width: 0 or 3 planned (plan_gemm_waves), 4 (128 columns) or 8 (256
+        columns, M > 512 only).
         splits: skinny kernel K splits (0 planned, 1..16); GEMM workgroups
         (0 planned, 1 one per output tile, 2..GEMM_MAX_WORKERS sharing the
         tiles' k-steps: stream-K)."""

@@ -21,7 +21,7 @@ hipError_t launch_gemv(const q4_matrix* h, const uint16_t* x, const uint16_t* bi
                        int M, int col_tiles, int splits, bool gather_x, bool bf16, float* partials,
                        uint32_t* counters, hipStream_t stream);
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, bool bf16, int workers, float* partials, uint32_t* counters,
+                              int M, bool bf16, int waves, int workers, float* partials, uint32_t* counters,
                               hipStream_t stream);
 hipError_t launch_repack(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K, int N,
                          int n_total, int col_off, int bits, hipStream_t stream);
@@ -352,19 +352,20 @@ q4_status ensure_partials(const q4_matrix* h, int splits, int M, hipStream_t str
 struct SkSpace {
     float* partials = nullptr;
     uint32_t* counters = nullptr;
-    int workers = 0;
+    size_t partial_bytes = 0;   // capacity of partials
+    int counter_count = 0;      // capacity of counters (one per workgroup)
 };
 std::mutex g_sk_mutex;
 auto* g_sk = new std::map<std::pair<int, hipStream_t>, SkSpace>;
 
-// Fills *ws for `workers` workgroups on (device, stream). Under stream
-// capture a missing or small workspace cannot be allocated: *ws is then left
-// empty (workers = 0).
-q4_status sk_workspace(int device, int num_cu, hipStream_t stream, int workers, SkSpace* ws)
+// Fills *ws for `workers` workgroups with partial-sum slots of slot_bytes
+// (two per workgroup) on (device, stream). Under stream capture a missing or
+// small workspace cannot be allocated: *ws is then left empty.
+q4_status sk_workspace(int device, int num_cu, hipStream_t stream, int workers, size_t slot_bytes, SkSpace* ws)
 {
     std::lock_guard<std::mutex> lock(g_sk_mutex);
     SkSpace& sp = (*g_sk)[{device, stream}];
-    if (sp.workers >= workers) {
+    if (sp.partial_bytes >= 2 * (size_t)workers * slot_bytes && sp.counter_count >= workers) {
         *ws = sp;
         return Q4_OK;
     }
@@ -372,18 +373,22 @@ q4_status sk_workspace(int device, int num_cu, hipStream_t stream, int workers, 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     Q4_HIP(hipStreamIsCapturing(stream, &cap), "q4_matmul: capture query");
     if (cap != hipStreamCaptureStatusNone) return Q4_OK;
+    // at least two 256 x 128 slots for each of 2 num_cu workgroups (what any
+    // planned call needs), doubled until this call fits
     int n = 2 * std::max(num_cu, 1);
     while (n < workers) n *= 2;
-    const size_t slot = (size_t)kGemmBM * kGemmBN * sizeof(float);
+    size_t bytes = 2 * (size_t)n * kGemmBM * kGemmBN * sizeof(float);
+    while (bytes < 2 * (size_t)workers * slot_bytes) bytes *= 2;
     SkSpace fresh;
-    Q4_HIP(hipMalloc(&fresh.partials, 2 * (size_t)n * slot), "q4_matmul: stream-K partials");
+    Q4_HIP(hipMalloc(&fresh.partials, bytes), "q4_matmul: stream-K partials");
     if (hipMalloc(&fresh.counters, (size_t)n * sizeof(uint32_t)) != hipSuccess) {
         (void)hipFree(fresh.partials);
         return fail(Q4_ERR_OOM, "q4_matmul: stream-K counters");
     }
     Q4_HIP(hipMemsetAsync(fresh.counters, 0, (size_t)n * sizeof(uint32_t), stream),
            "q4_matmul: stream-K counters");
-    fresh.workers = n;
+    fresh.partial_bytes = bytes;
+    fresh.counter_count = n;
     sp = fresh;
     *ws = sp;
     return Q4_OK;
@@ -435,8 +440,11 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
         if (h->bits == 8 && variant == 4)
             return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: 8-bit weights take at most 2 column tiles");
     } else {
-        if (variant != 0 && variant != 3)
-            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0 or 3", variant);
+        if (variant != 0 && variant != 3 && variant != 4 && variant != 8)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM variant %d is not 0, 3, 4 or 8", variant);
+        if (variant == 8 && gemm_bm(M) != kGemmBM)
+            return fail(Q4_ERR_INVALID_ARG, "q4_matmul: 256-column GEMM tiles (variant 8) need M > %d (M=%d)",
+                        kGemmSmallM, M);
         if (splits < 0 || splits > Q4_GEMM_MAX_WORKERS)
             return fail(Q4_ERR_INVALID_ARG, "q4_matmul: GEMM workgroups %d outside [0, %d]", splits,
                         Q4_GEMM_MAX_WORKERS);
@@ -506,27 +514,31 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
     } else {
         // splits: 0 planned, 1 one workgroup per output tile, P >= 2
         // workgroups sharing the tiles' k-iterations (stream-K)
-        const int tiles = gemm_tiles(M, h->N);
-        // (the GEMM's work split is 32-bit arithmetic)
-        if ((long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK) >= (1LL << 30))
+        // (the GEMM's work split is 32-bit arithmetic; the narrow tiles are
+        // the more numerous)
+        if ((long long)gemm_tiles(M, h->N, 4) * ((h->K + kGemmBK - 1) / kGemmBK) >= (1LL << 30))
             return fail(Q4_ERR_UNSUPPORTED, "q4_matmul: M=%d gives more than 2^30 GEMM (tile, k-step) pairs", M);
-        int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu) : splits == 1 ? tiles : splits;
+        // tile width: planned (variant 0 or 3) or explicit
+        const int waves = variant == 4 || variant == 8 ? variant : gemm_waves(M, h->N, h->K, h->num_cu, h->bits);
+        const int tiles = gemm_tiles(M, h->N, waves);
+        int workers = splits == 0 ? plan_gemm_workers(M, h->N, h->K, h->num_cu, waves) : splits == 1 ? tiles : splits;
         // every workgroup must get at least one (tile, k-step) iteration:
         // a split tile counts its contributors as a range of workgroups
         workers = (int)std::min<long long>(workers, (long long)tiles * ((h->K + kGemmBK - 1) / kGemmBK));
         SkSpace ws;
         if (stat && workers != tiles) {
             // as many stream-K workgroups as the plan asks for and the
-            // partials region holds (two slots of bm x 128 fp32 each), else
-            // one workgroup per tile
-            const size_t per_worker = 2 * (size_t)gemm_bm(M) * kGemmBN * sizeof(float);
+            // partials region holds (two slots of bm x (32 waves) fp32 each),
+            // else one workgroup per tile
+            const size_t per_worker = 2 * (size_t)gemm_bm(M) * (32 * waves) * sizeof(float);
             workers = (int)std::min<size_t>((size_t)workers, part_bytes / per_worker);
             workers = std::min(workers, kStaticCounters);
             if (workers < 2) workers = tiles;
             ws.partials = reinterpret_cast<float*>(base + kStaticCounterBytes + xp_bytes);
             ws.counters = reinterpret_cast<uint32_t*>(base);
         } else if (workers != tiles) {
-            q4_status st = sk_workspace(h->device, h->num_cu, stream, workers, &ws);
+            q4_status st = sk_workspace(h->device, h->num_cu, stream, workers,
+                                        (size_t)gemm_bm(M) * (32 * waves) * sizeof(float), &ws);
             if (st != Q4_OK) return st;
             if (!ws.partials) {
                 if (splits != 0)
@@ -536,7 +548,7 @@ q4_status matmul_impl(const q4_matrix* h, const uint16_t* x, const uint16_t* bia
                 workers = tiles;   // planned call under capture: one workgroup per tile
             }
         }
-        Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, workers, ws.partials, ws.counters, stream),
+        Q4_HIP(launch_gemm_stream(h, xe, bias, out, M, bf16, waves, workers, ws.partials, ws.counters, stream),
                "q4_matmul: gemm launch");
     }
     return Q4_OK;

@@ -47,32 +47,33 @@ namespace {
 
 using namespace q4dev;
 
-constexpr int BN = q4::kGemmBN;      // 128
 constexpr int BK = q4::kGemmBK;      // 64
-constexpr int NT = q4::kGemmThreads; // 256
-// The four waves sit side by side along N (1 x 4): each owns all BM rows of
-// 32 columns, so every packed word is dequantized by exactly one wave and each
-// wave reads the whole activation stage from LDS. (A 2 x 2 grid reads half the
-// activations per wave but dequantizes every word twice; measured slower:
-// M = 2048 948 -> 969 TFLOP/s on 4096x11008, M = 256 453 -> 601, M = 64
-// 264 -> 291. LDS reads stay under a third of the LDS bandwidth.)
-constexpr int WGN = 4;               // waves along N (the rest along M)
-constexpr int WGM = 4 / WGN;
-constexpr int WTN = BN / WGN;        // wave tile columns
-constexpr int NJ = WTN / 32;
-static_assert(BK == 64 && BN == 128 && NT == 256 && NJ >= 1 && WGM * WGN == 4, "index arithmetic below assumes these");
+// The NW waves of a workgroup sit side by side along N (1 x NW): each owns
+// all BM rows of 32 columns, so every packed word is dequantized by exactly
+// one wave and each wave reads the whole activation stage from LDS. (A 2 x 2
+// grid of four waves reads half the activations per wave but dequantizes
+// every word twice; measured slower: M = 2048 948 -> 969 TFLOP/s on
+// 4096x11008, M = 256 453 -> 601, M = 64 264 -> 291. LDS reads stay under a
+// third of the LDS bandwidth.) NW = 4 (128-column tiles, two workgroups per
+// CU) or 8 (256-column tiles, one per CU: the activation stage each copies
+// from L2 serves twice the columns).
+constexpr int NJ = 1;                // 32-column MFMA tiles per wave
+static_assert(BK == 64, "index arithmetic below assumes 64-row k-tiles");
 
-// Geometry that depends on the tile height BM (256, or 64 for few rows): a
-// WGM x WGN grid of waves, each WTM x WTN (MI x NJ MFMA tiles of 32 x 32); the
+// Geometry that depends on the tile height BM (256, or 64 for few rows) and
+// the waves NW: each wave owns BM x 32 (MI MFMA tiles of 32 x 32); the
 // activation stage is BM x BK halfs, filled by A_LOADS 16-byte direct loads
-// per thread (8 at BM = 256: 32 KiB a stage; 2 at BM = 64: 8 KiB).
-template <int BM>
+// per thread (BM = 256: 8 with four waves, 4 with eight; 32 KiB a stage;
+// BM = 64: 2 with four waves, 8 KiB).
+template <int BM, int NW>
 struct Geo {
-    static constexpr int WTM = BM / WGM;
-    static constexpr int MI = WTM / 32;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BN = 32 * NW;
+    static constexpr int MI = BM / 32;
     static constexpr int A_TILE_BYTES = BM * BK * 2;
     static constexpr int A_LOADS = A_TILE_BYTES / (NT * 16);
-    static_assert(MI >= 1 && A_LOADS >= 1 && A_TILE_BYTES == A_LOADS * NT * 16, "tile height");
+    static_assert((NW == 4 || NW == 8) && MI >= 1 && A_LOADS >= 1 && A_TILE_BYTES == A_LOADS * NT * 16,
+                  "tile shape");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -136,7 +137,7 @@ struct BRegs {
     uint32_t sz[NG][NJ];    // scale bits | zero point << 16
 };
 
-constexpr int kMaxALoads = Geo<256>::A_LOADS;
+constexpr int kMaxALoads = Geo<256, 4>::A_LOADS;
 struct Ctx {
     rsrc_t rx, rw, rsz;
     // (the first A_LOADS entries are used)
@@ -149,14 +150,14 @@ struct Ctx {
 // The k offset of the tile is wave-uniform (a scalar register); rows past M
 // lie past the end of x through the per-lane offset alone. Only with KT can a
 // chunk lie past K (in the last tile); its lanes are pushed out of range.
-template <bool KT, int A_LOADS>
+template <bool KT, int A_LOADS, int NW>
 __device__ __forceinline__ void load_a(const Ctx& c, const GemmArgs& p, char* stage, int wave, int kt)
 {
     const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
     for (int e = 0; e < A_LOADS; ++e) {
         const uint32_t kill = (!KT || c.a_k[e] + k0 < (uint32_t)p.K) ? 0u : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void*)(stage + (e * 4 + wave) * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void*)(stage + (e * NW + wave) * 1024), 16,
                                                  (int)(c.a_off[e] + kill), (int)(k0 * 2u), 0, 0);
     }
 }
@@ -188,19 +189,22 @@ __device__ __forceinline__ void load_b(BRegs<NG, W8>& R, const Ctx& c, const Gem
 // K (a separate instantiation, so that the common kernel has no branch
 // around the multiply: the accumulators stay in the same registers).
 // (Two workgroups per CU: the register budget is 256 per lane.)
-template <int BM, int NG, bool KT, bool BF, bool W8>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_stream_kernel(GemmArgs p)
+template <int BM, int NW, int NG, bool KT, bool BF, bool W8>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_stream_kernel(GemmArgs p)
 {
-    constexpr int WTM = Geo<BM>::WTM, MI = Geo<BM>::MI;
-    constexpr int A_TILE_BYTES = Geo<BM>::A_TILE_BYTES, A_LOADS = Geo<BM>::A_LOADS;
+    using G = Geo<BM, NW>;
+    constexpr int NT = G::NT, BN = G::BN, MI = G::MI, WTM = BM;
+    constexpr int A_TILE_BYTES = G::A_TILE_BYTES, A_LOADS = G::A_LOADS;
     // Ring depth: activation stages in LDS and weight register sets, both
-    // D - 1 k-tiles ahead: three for 64-row tiles (few rows), one for
-    // 256-row tiles. (Deeper 64-row rings first measured slower: the
-    // compiler then reused a few registers for the activation reads and
-    // waited out one LDS latency per sub-step. With all reads of a k-tile
-    // issued together (mma below), four stages beat three by 2-9% at
-    // M = 33 ... 128 on the 7B MLP shapes and 4096 x 4096.)
-    constexpr int D = BM == 64 ? 4 : 2;
+    // D - 1 k-tiles ahead: three for 64-row tiles (few rows), two for the
+    // 256-row, 256-column tiles (96 KiB of LDS, one workgroup per CU), one
+    // for 256-row, 128-column tiles (two workgroups per CU share 160 KiB).
+    // (Deeper 64-row rings first measured slower: the compiler then reused a
+    // few registers for the activation reads and waited out one LDS latency
+    // per sub-step. With all reads of a k-tile issued together (mma below),
+    // four stages beat three by 2-9% at M = 33 ... 128 on the 7B MLP shapes
+    // and 4096 x 4096.)
+    constexpr int D = BM == 64 ? 4 : NW == 8 ? 3 : 2;
     // vector-memory loads one step issues per thread (activation DMA, packed
     // weights, scale|zero words)
     constexpr int LPS = A_LOADS + 2 * NJ + NG * NJ;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     __shared__ int s_last;
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wm = 0, wn = wave;   // (waves side by side along N)
     // per-lane indices, recomputed for every segment (below) so that values
     // derived from them are not kept live across the k-loop
     int tid = 0, lane = 0, l32 = 0, lhi = 0;
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         lds_barrier();
         const int kn = min(kt + D - 1, seg_end - 1);
         if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
-        load_a<KT, A_LOADS>(c, p, stage(SN), wave, kn);
+        load_a<KT, A_LOADS, NW>(c, p, stage(SN), wave, kn);
         load_b(R[SN], c, p, kn);
         // (with D = 2 the wait above counts nothing, and leaving the loads
         // free to move measured 1-2% faster)
@@ -458,14 +462,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
             // instruction e of wave w fills rows 8 * (4e + w) .. +7 of the stage;
             // lane i lands in slot i % 8 of row i / 8, which holds chunk
             // slot ^ ((row >> 1) & 7)
-            const int row = 8 * (4 * e + wave) + (lane >> 3);
+            const int row = 8 * (NW * e + wave) + (lane >> 3);
             const int chunk = (lane & 7) ^ ((row >> 1) & 7);
             c.a_k[e] = 8u * (uint32_t)chunk;
             c.a_off[e] = ((uint32_t)(m0 + row) * (uint32_t)p.K + c.a_k[e]) * 2u;
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            lane_cols[j] = n0 + wn * WTN + 32 * j + l32;
+            lane_cols[j] = n0 + wn * 32 + 32 * j + l32;
             const uint32_t n = (uint32_t)min(lane_cols[j], p.N - 1);   // columns past N are never stored
 #pragma unroll
             for (int v = 0; v < 2; ++v) c.w_off[j][v] = q4::chunk_in_block(lhi + 2 * v, (int)n, p.N) * (W8 ? 32u : 16u);
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
 #pragma unroll
         for (int d = 0; d + 1 < D; ++d) {
             const int kd = min(kb + d, ke - 1);
-            load_a<KT, A_LOADS>(c, p, stage(d), wave, kd);
+            load_a<KT, A_LOADS, NW>(c, p, stage(d), wave, kd);
             load_b(R[d], c, p, kd);
             if constexpr (D > 2) __builtin_amdgcn_sched_barrier(0);
         }
@@ -525,6 +529,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
                 return p.partials + (size_t)(r == wf ? 2 * worker_id(r) + 1 : 2 * worker_id(r)) * (BM * BN);
             };
             uint32_t* counter = p.counters + worker_id(wf);
+            // (Reading the arrival count while the sums go out, rather than
+            // first, measured 4% slower on the 256-row tiles of 4096 x 11008:
+            // a last worker then publishes 128 KiB that nobody reads.)
             if (tid == 0)
                 s_last = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == others;
             __syncthreads();
@@ -608,7 +615,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
         for (int j = 0; j < NJ; ++j) {
             const int n = lane_cols[j];
             if (n >= p.N) continue;
-            const float bv = p.bias ? act_to_f32<BF>(bias_h[j]) : 0.f;
+            // (the conversion stays here: left to the compiler it moves up to
+            // the load and waits for it before the k-loop)
+            uint32_t bh = bias_h[j];
+            asm volatile("" : "+v"(bh));
+            const float bv = p.bias ? act_to_f32<BF>((uint16_t)bh) : 0.f;
             const int mb = m0 + wm * WTM + 4 * lhi;   // the lane's first row
             if (whole) {
                 // (m * N + n) * 2 < M * N * 2 <= 2^32 - 2: no wrap-around
@@ -633,28 +644,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void q4
     }
 }
 
-template <int BM, bool BF, bool W8>
+template <int BM, int NW, bool BF, bool W8>
 hipError_t launch_stream(const GemmArgs& p, int grid, bool g32, bool kt, hipStream_t stream)
 {
+    const dim3 block(64 * NW);
     if (g32 && kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 2, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, NW, 2, true, BF, W8>), dim3(grid), block, 0, stream, p);
     else if (g32)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 2, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, NW, 2, false, BF, W8>), dim3(grid), block, 0, stream, p);
     else if (kt)
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 1, true, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, NW, 1, true, BF, W8>), dim3(grid), block, 0, stream, p);
     else
-        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, 1, false, BF, W8>), dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((q4_gemm_stream_kernel<BM, NW, 1, false, BF, W8>), dim3(grid), block, 0, stream, p);
     return hipGetLastError();
 }
 
-template <int BM>
+template <int BM, int NW>
 hipError_t launch_bm(const GemmArgs& p, int grid, bool g32, bool kt, bool bf16, bool w8, hipStream_t stream)
 {
     if (w8)
-        return bf16 ? launch_stream<BM, true, true>(p, grid, g32, kt, stream)
-                    : launch_stream<BM, false, true>(p, grid, g32, kt, stream);
-    return bf16 ? launch_stream<BM, true, false>(p, grid, g32, kt, stream)
-                : launch_stream<BM, false, false>(p, grid, g32, kt, stream);
+        return bf16 ? launch_stream<BM, NW, true, true>(p, grid, g32, kt, stream)
+                    : launch_stream<BM, NW, false, true>(p, grid, g32, kt, stream);
+    return bf16 ? launch_stream<BM, NW, true, false>(p, grid, g32, kt, stream)
+                : launch_stream<BM, NW, false, false>(p, grid, g32, kt, stream);
 }
 
 }  // namespace
@@ -662,9 +674,13 @@ hipError_t launch_bm(const GemmArgs& p, int grid, bool g32, bool kt, bool bf16, 
 namespace q4 {
 
 hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint16_t* bias, uint16_t* out,
-                              int M, bool bf16, int workers, float* partials, uint32_t* counters,
+                              int M, bool bf16, int waves, int workers, float* partials, uint32_t* counters,
                               hipStream_t stream)
 {
+    // 256-column tiles (eight waves) only with 256-row tiles
+    const int bm = gemm_bm(M);
+    if (waves != 4 && !(waves == 8 && bm == kGemmBM)) return hipErrorInvalidValue;
+    const int BN = 32 * waves;
     GemmArgs p;
     p.qweight = h->qweight;
     p.sz = h->sz;
@@ -683,8 +699,6 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     p.partials = partials;
     p.counters = counters;
     p.workers = workers;
-    // tile height: 64 rows when that covers M (few rows), else 256
-    const int bm = gemm_bm(M);
     // XCD spaces need whole row tiles and workers per XCD
     const uint32_t mt = (uint32_t)((M + bm - 1) / bm), nt = (uint32_t)((h->N + BN - 1) / BN);
     const uint32_t ktiles = (uint32_t)((h->K + BK - 1) / BK);
@@ -707,8 +721,9 @@ hipError_t launch_gemm_stream(const q4_matrix* h, const uint16_t* x, const uint1
     // Groups of 64 rows or more never straddle a 64-row k-tile; groups of 32
     // change once inside it.
     const bool g32 = h->G % BK != 0 && h->G != h->K, kt = h->K % BK != 0;
-    return bm == 64 ? launch_bm<64>(p, workers, g32, kt, bf16, h->bits == 8, stream)
-                    : launch_bm<kGemmBM>(p, workers, g32, kt, bf16, h->bits == 8, stream);
+    if (bm == 64) return launch_bm<64, 4>(p, workers, g32, kt, bf16, h->bits == 8, stream);
+    return waves == 8 ? launch_bm<kGemmBM, 8>(p, workers, g32, kt, bf16, h->bits == 8, stream)
+                      : launch_bm<kGemmBM, 4>(p, workers, g32, kt, bf16, h->bits == 8, stream);
 }
 
 }  // namespace q4

@@ -67,19 +67,20 @@ constexpr int kGemvXLdsHalfs = 20480;
 
 // ---- prefill (MFMA GEMM) kernel geometry ---------------------------------
 constexpr int kGemmBM = 256;
-constexpr int kGemmBN = 128;
+constexpr int kGemmBN = 128;   // columns with four waves (256 with eight)
 constexpr int kGemmBK = 64;
-constexpr int kGemmThreads = 256;
 // The streaming GEMM takes 64-row output tiles when M <= kGemmSmallM (few
 // rows: 256-row tiles leave most CUs idle and multiply padding; measured on
 // the 7B MLP shapes, 64-row tiles are faster up to M = 384 (22-26% there),
 // within -2 .. +7% at 512 and 5-12% slower from 768 on), else 256-row tiles.
 constexpr int kGemmSmallM = 512;
 inline int gemm_bm(int M) { return M <= kGemmSmallM ? 64 : kGemmBM; }
-inline int gemm_tiles(int M, int N)
+// Output tiles of an M x N product with `waves` waves (32 columns each) per
+// workgroup: kGemmBN = 128 columns with four, 256 with eight.
+inline int gemm_tiles(int M, int N, int waves = 4)
 {
-    const int bm = gemm_bm(M);
-    return ((M + bm - 1) / bm) * ((N + kGemmBN - 1) / kGemmBN);
+    const int bm = gemm_bm(M), bn = 32 * waves;
+    return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 // Error reporting (thread-local status + message).
@@ -98,10 +99,15 @@ bool gemv_serves(int M, int K, int N, int G, int bits = 4);
 // Whether the skinny kernel stages act-order activations itself for this
 // M, K and number of K splits.
 bool gemv_gathers_x(int M, int K, int splits);
-// Workgroups of the streaming GEMM for an M x N output and K rows on a chip
-// of num_cu CUs: gemm_tiles(M, N) (one per output tile) when the tiles fill
-// whole rounds of two workgroups per CU, otherwise a stream-K split.
-int plan_gemm_workers(int M, int N, int K, int num_cu);
+// Waves per workgroup of the streaming GEMM (4: 128-column tiles, 8:
+// 256-column tiles, only with 256-row tiles) for an M x N output, K rows
+// and `bits`-bit weights.
+int gemm_waves(int M, int N, int K, int num_cu, int bits = 4);
+// Workgroups of the streaming GEMM with `waves` waves each for an M x N
+// output and K rows on a chip of num_cu CUs: gemm_tiles(M, N, waves) (one
+// per output tile) when the tiles fill whole rounds of the workgroups the
+// CUs hold at once, otherwise a stream-K split.
+int plan_gemm_workers(int M, int N, int K, int num_cu, int waves = 4);
 
 }  // namespace q4
 

@@ -179,6 +179,34 @@ bool gemv_gathers_x(int M, int K, int splits)
 // tiles: 735 -> 970 TFLOP/s; 688: 869 -> 913); from 1.5 rounds on, the lone
 // workgroups of a last half round run fast enough that stream-K measured no
 // better (768 tiles: equal; 1792: 1.5% slower).
+// The tile width (gemm_waves): 256-column tiles, eight waves a workgroup
+// and one workgroup per CU, copy each activation stage once for twice the
+// columns and keep two stages in flight (three in 96 KiB of LDS) instead of
+// one. Fewer tiles than CUs are shared by stream-K with 256 KiB partial
+// sums, which pays when the parts stay long. So the wide tiles serve
+// 256-row tiles when there is one for every CU, or one for every two CUs
+// with at least 64 k-steps a CU, or any count with at least 128 k-steps a
+// CU. Measured (us, planned four-wave against planned eight-wave launches,
+// weights from HBM): 4096x11008 at M = 1536 185.7 -> 128.6 (258 wide
+// tiles), 2048 172.5 -> 161.9, 4096 334.1 -> 310.4; 11008x4096 at 2048
+// (128 tiles, 86 k-steps a CU) 169.8 -> 162.7 but at 1024 (64 tiles)
+// 95.9 -> 106.5; 4096x4096 at 2048 (128 tiles, 32 k-steps a CU) 73.4 ->
+// 74.9, at 1536 62.5 -> 80.2, at 4096 122.4 -> 113.8; the 70B MLP layers
+// 3-12% faster at every M from 768 to 4096 (28672x8192 at 768: 96 tiles,
+// 168 k-steps a CU, 348.0 -> 312.1). Left on the table: 4096x11008 at
+// M = 768 and 1024 (129 and 172 tiles, 32 and 43 k-steps a CU), 4-6%
+// faster wide. 8-bit weights (twice the weight stream) keep the narrow
+// tiles: 11008x4096 at M = 2048 1062 TFLOP/s narrow, 993 wide.
+int gemm_waves(int M, int N, int K, int num_cu, int bits)
+{
+    if (num_cu <= 0) num_cu = 256;
+    if (gemm_bm(M) < kGemmBM || bits == 8) return 4;
+    const long long tiles = gemm_tiles(M, N, 8);
+    const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
+    const long long per_cu = tiles * ktiles / num_cu;
+    return tiles >= num_cu || (2 * tiles >= num_cu && per_cu >= 64) || per_cu >= 128 ? 8 : 4;
+}
+
 //  * 256-row tiles: 2 x tiles workgroups (a split tile has two or three
 //    contributors), but at least one per CU: with few rows the tiles are
 //    few (11008x4096 at M = 513 .. 768: 96), and too few workgroups leave
@@ -195,14 +223,25 @@ bool gemv_gathers_x(int M, int K, int splits)
 //    34.9 at 512 (256: 40.3 / 38.4), 4096x4096 19.5 at 256 (512: 20.9); the
 //    70B MLP layers at M <= 64 (28672 iterations) 58-62 us at 512 against
 //    63-70 us at 256 or 1024.
-int plan_gemm_workers(int M, int N, int K, int num_cu)
+//  * 256-column tiles (eight waves, one workgroup per CU): one per tile
+//    when the tiles fill whole rounds of CUs, otherwise exactly one round
+//    of num_cu workgroups sharing the tiles' k-steps (a second round of
+//    stream-K workgroups only waits for the first: 4096x11008 at M = 2048,
+//    344 tiles, 166 us with 256 workgroups, 184 us with 512, 188 us one per
+//    tile).
+int plan_gemm_workers(int M, int N, int K, int num_cu, int waves)
 {
     if (num_cu <= 0) num_cu = 256;
-    const long long tiles = gemm_tiles(M, N);
+    const long long tiles = gemm_tiles(M, N, waves);
+    const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
+    if (waves == 8) {
+        const long long rounds = (tiles + num_cu - 1) / num_cu;
+        if (tiles * 10 >= rounds * num_cu * 9) return (int)tiles;
+        return (int)std::min<long long>(std::min<long long>(num_cu, tiles * ktiles), Q4_GEMM_MAX_WORKERS);
+    }
     const long long cap = 2LL * num_cu;
     const long long rounds = (tiles + cap - 1) / cap;
     if (tiles * 10 >= rounds * cap * 9 || tiles * 2 >= cap * 3) return (int)tiles;
-    const long long ktiles = (K + kGemmBK - 1) / kGemmBK;
     const long long iters = tiles * ktiles;
     long long w;
     if (gemm_bm(M) < kGemmBM)
@@ -255,7 +294,13 @@ int q4_plan_gemv_gather(int M, int K, int splits)
 int q4_plan_gemm(int M, int N, int K, int num_cu)
 {
     if (M < 1 || N < 1 || K < 1) return -1;
-    return q4::plan_gemm_workers(M, N, K, num_cu);
+    return q4::plan_gemm_workers(M, N, K, num_cu, q4::gemm_waves(M, N, K, num_cu));
+}
+
+int q4_plan_gemm_waves(int M, int N, int K, int num_cu)
+{
+    if (M < 1 || N < 1 || K < 1) return -1;
+    return q4::gemm_waves(M, N, K, num_cu);
 }
 
 q4_status q4_plan_gemv(int M, int K, int N, int groupsize, int num_cu, int* col_tiles, int* splits)

@@ -203,10 +203,12 @@ q4_status q4_matmul_bias(const q4_matrix* h, const uint16_t* x, const uint16_t* 
  *   skinny kernel: variant = 16-column MFMA tiles per wave, 0 (planned), 1, 2
  *                  or 4; splits = K splits across workgroups, 0 (planned) or
  *                  1..16;
- *   GEMM:          variant = 0 or 3 (the same kernel: activations in LDS,
- *                  weights streamed into registers); splits = workgroups:
- *                  0 (planned, q4_plan_gemm), 1 (one per output tile:
- *                  256 x 128, or 64 x 128 when M <= 512) or
+ *   GEMM:          variant = the tile width: 0 or 3 (planned,
+ *                  q4_plan_gemm_waves), 4 (128 columns, four waves) or 8
+ *                  (256 columns, eight waves; M > 512 only); splits =
+ *                  workgroups: 0 (planned, q4_plan_gemm for the planned
+ *                  width; for an explicit width, the plan at that width),
+ *                  1 (one per output tile: 256 or 64 rows by the width) or
  *                  2..Q4_GEMM_MAX_WORKERS (the tiles' 64-row k-steps shared
  *                  evenly, stream-K; a count above the number of (tile,
  *                  k-step) pairs is reduced to it; under stream capture only
@@ -420,18 +422,32 @@ q4_status q4_plan_actorder(const int32_t* g_idx_host, int K, int groupsize, int3
 
 /*
  * q4_plan_gemm -- the streaming GEMM's planned workgroup count for an
- * M x N output with K rows on a chip of num_cu compute units (<= 0: 256).
- * Output tiles are 64 x 128 when M <= 512, else 256 x 128. One workgroup per
- * tile when the tiles fill whole rounds of two per CU (to within a tenth) or
- * make at least 1.5 such rounds; otherwise the tiles' 64-row k-steps are
- * shared evenly (stream-K): with 64-row tiles by 2 num_cu workgroups when
- * each gets at least 32 k-steps, by num_cu when each gets at least 16, else
- * by one per 16 k-steps (at least one per tile); with 256-row tiles by
- * min(2 num_cu, max(2 tiles, num_cu)); never more than there are (tile,
+ * M x N output with K rows on a chip of num_cu compute units (<= 0: 256), at
+ * the planned tile width for 4-bit weights (q4_plan_gemm_waves; an 8-bit
+ * handle plans as for four waves). Output tiles are 64 x 128
+ * when M <= 512, else 256 x 128 (four waves) or 256 x 256 (eight waves).
+ * Four waves: one workgroup per tile when the tiles fill whole rounds of two
+ * per CU (to within a tenth) or make at least 1.5 such rounds; otherwise the
+ * tiles' 64-row k-steps are shared evenly (stream-K): with 64-row tiles by
+ * 2 num_cu workgroups when each gets at least 32 k-steps, by num_cu when
+ * each gets at least 16, else by one per 16 k-steps (at least one per tile);
+ * with 256-row tiles by min(2 num_cu, max(2 tiles, num_cu)). Eight waves
+ * (one workgroup per CU): one per tile when the tiles fill whole rounds of
+ * num_cu to within a tenth, else num_cu. Never more than there are (tile,
  * k-step) pairs.
  * Host-only; -1 for M, N or K < 1.
  */
 int q4_plan_gemm(int M, int N, int K, int num_cu);
+
+/*
+ * q4_plan_gemm_waves -- the streaming GEMM's planned tile width, in waves of
+ * 32 columns: 8 (256-column tiles) for M > 512 when the 256 x 256 tiles are
+ * at least num_cu, or at least num_cu / 2 with at least 64 (tile, 64-row
+ * k-step) pairs per CU, or any number with at least 128 pairs per CU; else
+ * 4 (128-column tiles). For 4-bit weights: 8-bit handles always take 4.
+ * Host-only; -1 for M, N or K < 1.
+ */
+int q4_plan_gemm_waves(int M, int N, int K, int num_cu);
 
 /*
  * q4_plan_gemv -- the skinny kernel's launch plan for (M, K, N, groupsize) on

@@ -49,13 +49,14 @@ static struct {
     q4_status (*check_shape_bits)(int, int, int, int);
     q4_status (*plan_actorder)(const int32_t*, int, int, int32_t*, int*);
     int (*plan_gemm)(int, int, int, int);
+    int (*plan_gemm_waves)(int, int, int, int);
     q4_status (*plan_gemv)(int, int, int, int, int, int*, int*);
     int (*plan_gemv_gather)(int, int, int);
 } api = {
     q4_make, q4_make_bits, q4_make_cat, q4_make_cat_bits, q4_matmul, q4_matmul_bias, q4_matmul_ex,
     q4_matmul_static, q4_matmul_bf16, q4_matmul_ex_bf16, q4_free, q4_last_status, q4_last_error,
     q4_path_for, q4_dequant_dump, q4_dequant_dump_bf16, q4_gemv_gather, q4_handle_info, q4_handle_bits,
-    q4_read_probe, q4_check_shape, q4_check_shape_bits, q4_plan_actorder, q4_plan_gemm, q4_plan_gemv,
+    q4_read_probe, q4_check_shape, q4_check_shape_bits, q4_plan_actorder, q4_plan_gemm, q4_plan_gemm_waves, q4_plan_gemv,
     q4_plan_gemv_gather,
 };
 
@@ -86,6 +87,8 @@ int main(void)
         CHECK(9, api.plan_gemv(Q4_GEMV_MAX_M + 1, 4096, 4096, 128, 256, &ct, &sp) == Q4_ERR_INVALID_ARG);
         CHECK(10, api.plan_gemm(2048, 11008, 4096, 256) >= 1);
         CHECK(11, api.plan_gemm(2048, 11008, 4096, 256) <= Q4_GEMM_MAX_WORKERS);
+        CHECK(80, api.plan_gemm_waves(2048, 11008, 4096, 256) == 8);
+        CHECK(81, api.plan_gemm_waves(64, 11008, 4096, 256) == 4);
     }
 
     /* calls on a null handle fail cleanly, without a GPU */

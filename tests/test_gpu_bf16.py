@@ -166,7 +166,7 @@ def test_bf16_argument_errors():
     announce("bf16 errors")
     t = device_tensors(L)
     W = make_matrix(L, t)
-    with pytest.raises(ValueError, match="not 0 or 3"):
+    with pytest.raises(ValueError, match="not 0, 3, 4 or 8"):
         W.matmul(t["x"], path=q4.PATH_MFMA, variant=1)
     with pytest.raises(ValueError):
         W.matmul(t["x"], t["bias"].to(torch.float16))      # bias must match x

@@ -346,8 +346,8 @@ def test_m_zero_and_argument_errors():
         W.matmul(t["x"], splits=17)
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_MFMA, splits=q4.GEMM_MAX_WORKERS + 1)
-    for v in (1, 2, 4):
-        with pytest.raises(ValueError, match="not 0 or 3"):
+    for v in (1, 2, 5, 16):
+        with pytest.raises(ValueError, match="not 0, 3, 4 or 8"):
             W.matmul(t["x"], path=q4.PATH_MFMA, variant=v)
     with pytest.raises(ValueError):
         W.matmul(t["x"], path=q4.PATH_GEMV, variant=3)

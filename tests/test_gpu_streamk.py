@@ -36,9 +36,9 @@ def _layer(K, N, G, M, seed, **kw):
     return synth.make_layer(K, N, G, M, seed=synth.layer_seed("streamk", K, N, G, M, seed), **kw)
 
 
-def _tiles(M, N):
+def _tiles(M, N, waves=4):
     bm = 64 if M <= 512 else 256     # the tile height the library takes for M rows
-    return -(-M // bm) * -(-N // 128)
+    return -(-M // bm) * -(-N // (32 * waves))
 
 
 SK_CASES = [
@@ -68,8 +68,27 @@ SK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("K,N,G,M,act,bias,xfmt,bits,workers", SK_CASES)
-def test_stream_k_parity(K, N, G, M, act, bias, xfmt, bits, workers):
+# The same with 256 x 256 tiles (eight waves a workgroup, variant 8; only
+# with 256-row tiles): column tiles 256 wide with a ragged last one, a
+# partial last row tile, K tails, groups of 32, act-order, bfloat16, 8-bit.
+SK_WIDE_CASES = [
+    # 3 x 3 tiles (N = 520: 256 + 256 + 8 columns) of 16 k-steps: 144 iterations
+    (1024, 520, 128, 520, False, True, "f16", 4, (2, 3, 7, 9, 20, 144, 200)),
+    # groups of 32 and a K tail: 3 tiles of 2 k-steps
+    (96, 136, 32, 520, False, False, "f16", 4, (2, 5)),
+    # 8 row tiles x 3 column tiles: XCD-ordered spaces when the count divides by 8
+    (256, 600, 128, 2048, False, True, "f16", 4, (8, 16, 24, 40)),
+    (512, 520, 128, 520, True, True, "f16", 4, (5, 9)),
+    (512, 520, 128, 520, False, True, "bf16", 4, (5, 11)),
+    (512, 520, 64, 520, False, True, "f16", 8, (5, 11)),
+    (480, 264, 32, 516, True, True, "bf16", 4, (3, 7)),
+    (480, 264, 32, 516, False, False, "f16", 8, (3, 7)),
+]
+SK_ALL = [c + (0,) for c in SK_CASES] + [c + (8,) for c in SK_WIDE_CASES]
+
+
+@pytest.mark.parametrize("K,N,G,M,act,bias,xfmt,bits,workers,variant", SK_ALL)
+def test_stream_k_parity(K, N, G, M, act, bias, xfmt, bits, workers, variant):
     import gptq_bit_weight_amd as q4
     torch = torch_mod()
     L = _layer(K, N, G, M, 0, act_order=act, bias=bias, xfmt=xfmt, bits=bits)
@@ -78,23 +97,26 @@ def test_stream_k_parity(K, N, G, M, act, bias, xfmt, bits, workers):
     yD, A = oracle_full(L)
     tol = (dict(rel_a=BF16_GEMM_REL_A, rel_y=BF16_REL_Y) if xfmt == "bf16"
            else dict(rel_a=REL_A, rel_y=REL_Y))
-    announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} one-per-tile")
-    one = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=1)
+    waves = 8 if variant == 8 else 4
+    if variant == 0:
+        assert q4.plan_gemm_waves(M, N, K) == 4, "the narrow cases expect 128-column tiles planned"
+    announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} variant={variant} one-per-tile")
+    one = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=variant, splits=1)
     torch.cuda.synchronize()
     compare(to_float64(one), yD, A, f"one per tile K={K} N={N} M={M}", **tol)
     for P in workers:
-        announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} workers={P}")
-        a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
-        b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
+        announce(f"stream-k K={K} N={N} G={G} M={M} act={act} {xfmt} w{bits} variant={variant} workers={P}")
+        a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=variant, splits=P)
+        b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=variant, splits=P)
         torch.cuda.synchronize()
         compare(to_float64(a), yD, A, f"stream-k K={K} N={N} M={M} workers={P}", **tol)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"workers={P}: not repeatable"
-        if P == _tiles(M, N):
+        if P == _tiles(M, N, waves):
             assert torch.equal(a.view(torch.int16), one.view(torch.int16)), \
                 f"workers={P}: one workgroup per tile should match splits=1"
-        iters = _tiles(M, N) * -(-K // 64)
+        iters = _tiles(M, N, waves) * -(-K // 64)
         if P > iters:
-            c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=iters)
+            c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=variant, splits=iters)
             torch.cuda.synchronize()
             assert torch.equal(a.view(torch.int16), c.view(torch.int16)), \
                 f"workers={P} should run as {iters}"
@@ -115,6 +137,33 @@ def test_stream_k_planned_matches_explicit():
     b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=P)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_wide_tiles_planned():
+    """A product the plan gives 256 x 256 tiles (256 of them on 256 CUs: one
+    workgroup each): the planned call equals the explicit eight-wave launch
+    bit for bit, and it and the 128-column launch meet the acceptance rule
+    on whole rows and columns through every tile."""
+    import gptq_bit_weight_amd as q4
+    from tests.gpu_util import check_output
+    torch = torch_mod()
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    M, N, K = 2048, 32 * cu, 128
+    assert q4.plan_gemm_waves(M, N, K, cu) == 8
+    L = _layer(K, N, 128, M, 3, bias=True)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    P = q4.plan_gemm(M, N, K, cu)
+    announce(f"wide tiles planned M={M} N={N} K={K} workers={P}")
+    a = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA)
+    b = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=8, splits=P)
+    c = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, variant=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_output(L, a.cpu().numpy(), "wide tiles planned", seed=1)
+    check_output(L, c.cpu().numpy(), "narrow tiles", seed=2)
+    with pytest.raises(ValueError, match="variant 8"):
+        W.matmul(t["x"][:512].contiguous(), path=q4.PATH_MFMA, variant=8)
 
 
 def test_stream_k_graph_replay():

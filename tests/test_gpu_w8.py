@@ -199,7 +199,7 @@ def test_w8_argument_errors():
     W = make_matrix(L, t)
     with pytest.raises(NotImplementedError, match="2 column tiles"):
         W.matmul(t["x"][:4].contiguous(), path=q4.PATH_GEMV, variant=4)
-    with pytest.raises(ValueError, match="not 0 or 3"):
+    with pytest.raises(ValueError, match="not 0, 3, 4 or 8"):
         W.matmul(t["x"], path=q4.PATH_MFMA, variant=2)
     with pytest.raises(NotImplementedError):
         q4.Q4Matrix(t["qweight"], t["qzeros"], t["scales"], None, 128, bits=6)

@@ -160,20 +160,25 @@ def test_plan_gemv():
 
 
 def test_plan_gemm():
-    """One workgroup per output tile (256 x 128, or 64 x 128 for M <= 512)
-    when the tiles fill whole rounds of two per CU (to within a tenth) or make
-    1.5 rounds or more; otherwise the workgroups share the k-steps
-    (stream-K): for 64-row tiles 2 x CUs workgroups from 32 k-steps each, CUs
-    from 16, else 16 k-steps each (at least one per tile); for 256-row ones
-    min(2 CUs, max(2 tiles, CUs)); never more than there are (tile, 64-row
-    k-step) iterations."""
+    """At the planned tile width (q4_plan_gemm_waves). 128-column tiles (four
+    waves, two workgroups per CU): one workgroup per output tile (256 x 128,
+    or 64 x 128 for M <= 512) when the tiles fill whole rounds of two per CU
+    (to within a tenth) or make 1.5 rounds or more; otherwise the workgroups
+    share the k-steps (stream-K): for 64-row tiles 2 x CUs workgroups from
+    32 k-steps each, CUs from 16, else 16 k-steps each (at least one per
+    tile); for 256-row ones min(2 CUs, max(2 tiles, CUs)). 256 x 256 tiles
+    (eight waves, one workgroup per CU): one per tile when the tiles fill
+    whole rounds of CUs to within a tenth, else one round of CUs sharing the
+    k-steps. Never more than there are (tile, 64-row k-step) iterations."""
     p = q4.plan_gemm
-    assert p(2048, 4096, 11008, 256) == 512      # 256 tiles: every CU at one
-    assert p(2048, 11008, 4096, 256) == 512      # 688 tiles: 1.34 rounds
-    assert p(2048, 12288, 4096, 256) == 768      # fused q/k/v: 768 tiles, 1.5 rounds
-    assert p(4096, 4096, 4096, 256) == 512       # 512 tiles: one whole round
-    assert p(16384, 28672, 8192, 256) == 14336   # 28 whole rounds
-    assert p(2048, 28672, 8192, 256) == 1792     # 3.5 rounds
+    assert p(2048, 4096, 11008, 256) == 256      # 128 wide tiles, 172 k-steps: one round of CUs
+    assert p(2048, 11008, 4096, 256) == 256      # 344 wide tiles: 1.34 rounds
+    assert p(2048, 12288, 4096, 256) == 256      # fused q/k/v: 384 wide tiles, 1.5 rounds
+    assert p(4096, 4096, 4096, 256) == 256       # 256 wide tiles: one whole round
+    assert p(16384, 28672, 8192, 256) == 7168    # 28 whole rounds of wide tiles
+    assert p(2048, 28672, 8192, 256) == 256      # 896 wide tiles: 3.5 rounds
+    assert p(2048, 8192, 128, 256) == 256        # 256 wide tiles of 2 k-steps: one per tile
+    assert p(2048, 4096, 4096, 256) == 512       # 128 wide tiles, 32 k-steps a CU: narrow, 256 tiles
     assert p(17, 4096, 4096, 256) == 128         # 64-row tiles: 2048 iterations, 16 a workgroup
     assert p(64, 4096, 11008, 256) == 256        # 5504 iterations: 21.5 each on one a CU
     assert p(32, 28672, 8192, 256) == 512        # 28672: 56 each on two a CU
@@ -187,11 +192,30 @@ def test_plan_gemm():
     assert p(520, 4096, 11008, 256) == 256       # 3 x 32 tiles of 256 rows: at least one per CU
     assert p(520, 136, 96, 256) == 12            # 6 tiles of 2 k-steps: 12 iterations
     assert p(520, 136, 32, 256) == 6             # 6 tiles of 1 k-step: one each
-    assert p(2048, 4096, 11008, 64) == 256       # a smaller chip: two whole rounds
-    assert p(2048, 11008, 4096, 64) == 688       # 688 tiles: 5.4 rounds of 128
+    assert p(2048, 4096, 11008, 64) == 128       # a smaller chip: 128 wide tiles, two whole rounds
+    assert p(2048, 11008, 4096, 64) == 64        # 344 wide tiles: 5.4 rounds of 64, stream-K
     for bad in ((0, 8, 32), (1, 0, 32), (1, 8, 0)):
         with pytest.raises(ValueError):
             p(*bad)
+
+
+def test_plan_gemm_waves():
+    """256-column tiles (eight waves) only with 256-row tiles (M > 512), when
+    the 256 x 256 tiles are at least the CUs, or half of them with at least
+    64 (tile, k-step) pairs a CU, or any number with at least 128 a CU."""
+    w = q4.plan_gemm_waves
+    assert w(512, 28672, 8192, 256) == 4         # 64-row tiles: always four
+    assert w(1536, 11008, 4096, 256) == 8        # 6 x 43 = 258 tiles
+    assert w(1024, 11008, 4096, 256) == 4        # 172 tiles, 43 pairs a CU
+    assert w(2048, 4096, 11008, 256) == 8        # 128 tiles, 86 pairs a CU
+    assert w(1536, 4096, 11008, 256) == 4        # 96 tiles, 64 pairs a CU
+    assert w(2048, 4096, 4096, 256) == 4         # 128 tiles, 32 pairs a CU
+    assert w(4096, 4096, 4096, 256) == 8         # 256 tiles
+    assert w(768, 8192, 28672, 256) == 8         # 96 tiles, 168 pairs a CU
+    assert w(520, 136, 96, 256) == 4
+    for bad in ((0, 8, 32), (1, 0, 32), (1, 8, 0)):
+        with pytest.raises(ValueError):
+            w(*bad)
 
 
 def test_plan_gemv_gather():
