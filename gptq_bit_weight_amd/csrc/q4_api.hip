@@ -343,9 +343,11 @@ q4_status ensure_partials(const q4_matrix* h, int splits, int M, hipStream_t str
 }
 
 // Stream-K workspace of the streaming GEMM, one per (device, stream): two
-// 256 x 128 fp32 partial slots and one arrival counter per workgroup, for
-// max(workers, 2 x CUs) workgroups rounded up to a power of two (128 MiB on
-// 256 CUs). Calls on one stream run in order, so they can share it whatever
+// fp32 slots of one output tile and one arrival counter per workgroup. The
+// first one holds two 256 x 128 slots for each of max(workers, 2 x CUs)
+// workgroups rounded up to a power of two (128 MiB on 256 CUs, which is also
+// two 256 x 256 slots for each of 256 eight-wave workgroups); it is doubled
+// until a call fits. Calls on one stream run in order, so they can share it whatever
 // handle they use; calls on different streams get different buffers. A
 // workspace that is outgrown is replaced but never freed (a captured graph
 // may still name it); all are kept until the process ends.
