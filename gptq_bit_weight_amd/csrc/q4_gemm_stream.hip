@@ -266,6 +266,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     asm volatile("" : "+v"(magic));
     int m0 = 0, seg_end = 0;
     int lane_cols[NJ];
+    // Whether row group g (rows 8g .. 8g + 7) of MFMA row tile i of the
+    // current output tile has a row below M, a wave-uniform test: accumulator
+    // registers r with r / 4 == g hold those rows (in lane halves 0 and 1).
+    auto row_group_in = [&](int i, int g) { return m0 + 32 * i + 8 * g < p.M; };
 
     // Multiply k-tile kt: activations from `A`, weights from register set R.
     // Software-pipelined over the four 16-row sub-steps: the weights of
@@ -608,9 +612,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         // tile. A whole row tile stores through a buffer descriptor, the row
         // part of each offset wave-uniform, with no per-element checks (a
         // compare and branch per element cost about 1 us of a 64-row tile's
-        // epilogue); only the last, partial row tile checks its rows.
+        // epilogue); a partial row tile uses the descriptor's range instead
+        // (below).
         const rsrc_t ro = make_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
         const bool whole = m0 + BM <= p.M;
+        // A partial row tile stores through the same descriptor with the
+        // whole offset per lane, skipping the row groups that lie past M: a
+        // store to a row past M then lies past the descriptor's end, which
+        // drops it. Those rows are below M + 8, so their offsets stay under
+        // 2^32 unless (M + 8) N * 2 does not (then each element is checked).
+        const bool ranged = !whole && (uint64_t)(p.M + 8) * (uint64_t)p.N * 2u < (1ull << 32);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int n = lane_cols[j];
@@ -630,6 +641,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
                     for (int r = 0; r < 16; ++r) {
                         const uint32_t dr = (uint32_t)(32 * i + 8 * (r >> 2) + (r & 3));
                         buf_store2(ro, voff, dr * (uint32_t)p.N * 2u, f32_to_act<BF>(acc[i][j][r] + bv));
+                    }
+            } else if (ranged) {
+                const uint32_t voff = ((uint32_t)mb * (uint32_t)p.N + (uint32_t)n) * 2u;
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if (!row_group_in(i, r >> 2)) continue;
+                        const uint32_t dr = (uint32_t)(32 * i + 8 * (r >> 2) + (r & 3));
+                        buf_store2(ro, voff + dr * (uint32_t)p.N * 2u, 0u, f32_to_act<BF>(acc[i][j][r] + bv));
                     }
             } else {
 #pragma unroll

@@ -122,6 +122,28 @@ def test_stream_k_parity(K, N, G, M, act, bias, xfmt, bits, workers, variant):
                 f"workers={P} should run as {iters}"
 
 
+@pytest.mark.parametrize("M,splits", [(33, 0), (33, 7), (40, 1), (63, 0), (65, 0), (100, 5), (520, 0), (520, 7)])
+def test_partial_row_tile_stays_in_output(M, splits):
+    """A partial last row tile (64-row tiles up to M = 512, 256-row above)
+    drops its rows past M: written into the first M rows of a longer buffer,
+    the output equals the exact-size call bit for bit and the rows after it
+    keep their contents."""
+    import gptq_bit_weight_amd as q4
+    torch = torch_mod()
+    K, N = 1024, 520
+    L = _layer(K, N, 128, M, 4, bias=True)
+    t = device_tensors(L)
+    W = make_matrix(L, t)
+    announce(f"partial row tile M={M} splits={splits}")
+    ref = W.matmul(t["x"], t["bias"], path=q4.PATH_MFMA, splits=splits)
+    big = torch.empty((M + 80, N), dtype=torch.float16, device="cuda")
+    big.view(torch.int16).fill_(0x5A5A)
+    W.matmul(t["x"], t["bias"], out=big[:M], path=q4.PATH_MFMA, splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:M].view(torch.int16), ref.view(torch.int16))
+    assert bool((big[M:].view(torch.int16) == 0x5A5A).all()), "a store landed past row M"
+
+
 def test_stream_k_planned_matches_explicit():
     """The planned schedule (splits=0) is the one q4_plan_gemm names."""
     import gptq_bit_weight_amd as q4
