@@ -26,9 +26,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # written in the source.
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the fp32 epilogues
 # and group folds read them without v_accvgpr_read copies.
+# -amdgpu-kernarg-preload-count: leading scalar kernel arguments (up to 16
+# dwords) arrive in SGPRs, loaded by the hardware before the waves start,
+# instead of through scalar loads from the argument segment.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form"]
+          "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _sources():

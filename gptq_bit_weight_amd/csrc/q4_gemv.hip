@@ -345,23 +345,39 @@ __device__ __forceinline__ void stage_store(uint16_t* xs, const u4 (&xv)[XJ][XR]
         }
 }
 
+// The kernel takes the fields its first loads need as separate leading
+// arguments (the same values as in `args`): the build asks the compiler to
+// preload leading scalar kernel arguments into SGPRs, which the hardware
+// fills before the waves start, so the first weight loads need not wait for
+// a fetch of the argument segment (a struct argument is never preloaded).
+// Measured on the read probe: 0.05-0.1 us less per launch.
 template <int NGB, int CT, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB, bool R1>
-__global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
+__global__ __launch_bounds__(NT) void q4_gemv_kernel(const uint32_t* qweight, const uint32_t* sz,
+                                                      const uint16_t* x, int M, int K, int N, int kblocks,
+                                                      int blocks_per_split, int blocks_per_wave, int gshift,
+                                                      int ng, GemvArgs args)
 {
     static_assert(!R1 || (XS == 4 && MB == 1), "one-row mode reads four k-steps per activation load");
     constexpr int COLS = 16 * CT;
+    static_assert(NT % COLS == 0, "a thread's epilogue elements share one column");
     constexpr int ROWS = 16 * MB;
     __shared__ float red[WV][ROWS][COLS];
     __shared__ int last_flag;
     extern __shared__ u4 xs_dyn[];   // XL: the workgroup's activations, [M][ldx] halfs
 
+    GemvArgs p = args;
+    p.qweight = qweight;
+    p.sz = sz;
+    p.x = x;
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.kblocks = kblocks;
+    p.blocks_per_split = blocks_per_split;
+    p.blocks_per_wave = blocks_per_wave;
+    p.gshift = gshift;
+    p.ng = ng;
     const int tid = threadIdx.x;
-    // All kernel arguments the loads need, fetched together: otherwise the
-    // pointers are fetched after the first branch, a second wait on the
-    // argument fetch before the first weight load (about 0.07 us of a
-    // 4096 x 4096 layer).
-    asm volatile("" ::"s"(p.qweight), "s"(p.sz), "s"(p.x), "s"(p.M), "s"(p.K), "s"(p.N), "s"(p.kblocks),
-                 "s"(p.blocks_per_split), "s"(p.blocks_per_wave), "s"(p.gshift), "s"(p.ng));
     // The wave index is uniform across the wave; saying so keeps the block
     // bookkeeping in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,6 +469,16 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // The bias of the column this thread stores in the epilogues below
+    // (column tid % COLS for every element it takes), loaded now so that its
+    // latency hides behind the k-loop rather than following the cross-wave
+    // sum (after the first weight loads, which need not wait for its
+    // pointer). One unconditional load through a descriptor, empty without a
+    // bias and ending at column N, so that no branch around it makes the
+    // compiler wait for every load in flight at the join.
+    const uint16_t bias_h = (uint16_t)buf_load2(make_rsrc(p.bias, p.bias ? (uint32_t)p.N * 2u : 0u),
+                                                (uint32_t)(n0 + tid % COLS) * 2u);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (XL) {
         stage_store<XJ>(xs, xv, iv, p, tid, 0);
         for (int m0 = XR; m0 < p.M; m0 += XR) {
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
             const int m = idx / COLS, c = idx % COLS, n = n0 + c;
             if (n >= p.N) continue;
             float y = wg_sum(m, c);
-            if (p.bias) y += act_to_f32<BF>(p.bias[n]);
+            if (p.bias) y += act_to_f32<BF>(bias_h);
             p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
         }
         return;
@@ -558,12 +584,17 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(GemvArgs p)
         for (int s = 0; s < p.splits; ++s)
             y += __hip_atomic_load(&p.partials[((size_t)s * p.M + m) * p.N + n], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (p.bias) y += act_to_f32<BF>(p.bias[n]);
+        if (p.bias) y += act_to_f32<BF>(bias_h);
         p.out[(size_t)m * p.N + n] = f32_to_act<BF>(y);
     }
     if (tid == 0)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The kernel's leading arguments, then the whole argument struct.
+#define Q4_GEMV_ARGS(p)                                                                              \
+    (p).qweight, (p).sz, (p).x, (p).M, (p).K, (p).N, (p).kblocks, (p).blocks_per_split, (p).blocks_per_wave, \
+        (p).gshift, (p).ng, (p)
 
 template <int NGB, int XS, bool TAIL, bool XL, bool BF, bool W8, int MB, bool R1 = false>
 hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
@@ -571,12 +602,12 @@ hipError_t launch_ct(const GemvArgs& p, int ct, int splits, hipStream_t stream)
     const dim3 block(NT);
     const size_t lds = XL ? (size_t)p.M * p.ldx * 2 : 0;
     switch (ct) {
-    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 15) / 16, splits), block, lds, stream, p); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 31) / 32, splits), block, lds, stream, p); break;
+    case 1: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 1, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 15) / 16, splits), block, lds, stream, Q4_GEMV_ARGS(p)); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<NGB, 2, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 31) / 32, splits), block, lds, stream, Q4_GEMV_ARGS(p)); break;
     case 4:
         // (8-bit blocks are twice the registers: at most two tiles)
         if constexpr (W8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 63) / 64, splits), block, lds, stream, p);
+        else hipLaunchKernelGGL((q4_gemv_kernel<NGB, 4, XS, TAIL, XL, BF, W8, MB, R1>), dim3((p.N + 63) / 64, splits), block, lds, stream, Q4_GEMV_ARGS(p));
         break;
     default: return hipErrorInvalidValue;
     }
