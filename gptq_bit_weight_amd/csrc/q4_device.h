@@ -34,9 +34,6 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 __host__ __device__ constexpr int slot_of(int i) { return (i >> 1) + 4 * (i & 1); }
 
 constexpr uint32_t kMagic2 = 0x64006400u;     // (1024.0, 1024.0) in fp16
-constexpr uint32_t kMagicBf2 = 0x43004300u;   // (128.0, 128.0) in bfloat16
-constexpr uint32_t kOnes2 = 0x3C003C00u;      // (1.0, 1.0) in fp16
-constexpr uint32_t kOnesBf2 = 0x3F803F80u;    // (1.0, 1.0) in bfloat16
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& f)
@@ -143,12 +140,6 @@ __device__ __forceinline__ h8 sub_zero_word8(uint32_t w0, uint32_t w1, zero_t z)
     return h8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
-// The same k-step as eight fp16 values 1024 + q (no zero point).
-__device__ __forceinline__ u4 biased_word8(uint32_t w0, uint32_t w1)
-{
-    return u4{byte_pair(w0, kPairLo), byte_pair(w0, kPairHi), byte_pair(w1, kPairLo), byte_pair(w1, kPairHi)};
-}
-
 __device__ __forceinline__ h8 dequant_word8(uint32_t w0, uint32_t w1, zero_t z, h2 s2)
 {
     const h8 d = sub_zero_word8(w0, w1, z);
@@ -230,22 +221,6 @@ __device__ __forceinline__ b8 mix_word(uint32_t w, const mix_t& m)
     o[2] = mix_pair(and_or(w8, 0x000F000Fu, magic), m.t, m.c0);
     o[3] = mix_pair(and_or(w8, 0x00F000F0u, magic), f1, m.c1);
     return bitcast<b8>(o);
-}
-
-// One private-layout word as eight values B + q in k order, the bits of
-// `magic` (a register, see and_or) deciding the type: kMagic2 gives fp16
-// 1024 + q, kMagicBf2 bfloat16 128 + q. The spacing of either type is 1 at
-// B, so B + q for q < 16 is the magic with q in its low bits, exact. Pair j
-// (k-offsets 2j, 2j + 1) sits at bits 4j and 16 + 4j: one shift and one
-// v_and_or_b32 a pair.
-__device__ __forceinline__ u4 biased_word(uint32_t w, uint32_t magic)
-{
-    u4 o;
-    o[0] = and_or(w, 0x000F000Fu, magic);
-    o[1] = and_or(w >> 4, 0x000F000Fu, magic);
-    o[2] = and_or(w >> 8, 0x000F000Fu, magic);
-    o[3] = and_or(w >> 12, 0x000F000Fu, magic);
-    return o;
 }
 
 // ---- raw buffer loads ------------------------------------------------------

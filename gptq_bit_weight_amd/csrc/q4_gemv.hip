@@ -48,19 +48,6 @@
 //    accumulated in fp32, and the vector ALU does one unpack and one packed
 //    subtract per two weights. (BF: the same exact q - z as bfloat16, formed
 //    by one fused multiply-add per value; the MFMA takes bfloat16.)
-//  * One-row mode takes B = c + q instead (c = 1024 in fp16, 128 in
-//    bfloat16: exact, the magic constant with q in its low bits, one shift
-//    and one v_and_or_b32 per two 4-bit weights, one v_perm_b32 per two
-//    8-bit ones, and no subtract; 8-bit codes with bfloat16 keep the exact
-//    q - z, as 128 + q is not exact there for q >= 128, and so does fp16
-//    with more than one tile a wave, where it measured slower) and takes the zero
-//    point out of the fp32 sums: sum x (q - z) = sum x (c + q) -
-//    (c + z) sum x, where one more MFMA per block, against ones, gives every
-//    k-step's sum x. The products are still exact (11- or 8-bit factors);
-//    the fp32 sums now carry c + q instead of q - z, so their rounding is
-//    that of numbers up to c / |q - z| times larger, far inside the
-//    acceptance rule. Per block: bfloat16 79 -> 38 vector instructions (the
-//    7B block with bfloat16 activations 37.2 -> 33.4 us), fp16 33.4 -> 33.0 us.
 //  * the weights are read exactly once, with the non-temporal hint (5-7%
 //    faster on the 7B layers than default caching), and so are the group
 //    words (5-6% faster on the 7B layers than cached loads of them, 1%
@@ -233,17 +220,6 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
                                               const char* xl, int b, int bs0, uint32_t magic)
 {
     constexpr int SPG = 4 / NGB;   // k-steps per group inside the block
-    // One-row mode folds the zero point out of the sum: the B operand is
-    // c + q (c = 1024 in fp16, 128 in bfloat16), exact and formed from the
-    // bits alone, and sum x (q - z) = sum x (c + q) - (c + z) sum x, with
-    // sum x over each k-step from one product against ones (row 4s of it
-    // holds k-step s's sum, the row one-row mode reads). Not for 8-bit
-    // codes with bfloat16 activations: 128 + q is not exact in bfloat16 for
-    // q >= 128. With fp16 only at one tile a wave: at two, the fp16 subtract
-    // it saves costs less than the fold (4096 x 22016 at M = 1: 10.75 us
-    // without, 10.98 with).
-    constexpr bool FOLD = R1 && !(W8 && BF) && (BF || CT == 1);
-    constexpr float C = BF ? 128.0f : 1024.0f;
     u4 av[MB][4];
     if constexpr (XL) {
         const char* src = xl + (b - bs0) * 256;
@@ -255,26 +231,18 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
 #pragma unroll
             for (int i = 0; i < 4 / XS; ++i) av[rb][i] = B.a[rb][i];
     }
-    f4 sx;
-    if constexpr (FOLD) {
-        constexpr uint32_t o = BF ? kOnesBf2 : kOnes2;
-        if constexpr (BF) sx = mfma16(bitcast<b8>(av[0][0]), bitcast<b8>(u4{o, o, o, o}), f4{0.f, 0.f, 0.f, 0.f});
-        else sx = mfma16(bitcast<h8>(av[0][0]), bitcast<h8>(u4{o, o, o, o}), f4{0.f, 0.f, 0.f, 0.f});
-    }
 #pragma unroll
     for (int gi = 0; gi < NGB; ++gi) {
         zero_t zp[CT];
         mix_t mz[CT];
         float sf[CT];
-        float hz[CT];   // FOLD: c + z
         // (1 kept opaque, so that f * h + c stays one v_fma_mix_f32 instead
         // of a conversion and an add)
         float one = 1.0f;
         if constexpr (BF) asm("" : "+v"(one));
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-            if constexpr (FOLD) hz[j] = (float)(B.sz[gi][j] >> 16) + C;
-            else if constexpr (BF) mz[j] = mix_consts(B.sz[gi][j] >> 16, one, magic);
+            if constexpr (BF) mz[j] = mix_consts(B.sz[gi][j] >> 16, one, magic);
             else zp[j] = zero_pair_sz(B.sz[gi][j], magic);
             sf[j] = f16_bits_to_f32((uint16_t)B.sz[gi][j]);
         }
@@ -293,10 +261,7 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
                     // k-step i: words 2i, 2i + 1 of the lane's 32-byte chunk
                     const uint32_t w0 = B.w[j][i >> 1][2 * (i & 1)], w1 = B.w[j][i >> 1][2 * (i & 1) + 1];
                     if constexpr (BF) bw = bitcast<u4>(mix_word8(w0, w1, mz[j]));
-                    else if constexpr (FOLD) bw = biased_word8(w0, w1);
                     else bw = bitcast<u4>(sub_zero_word8(w0, w1, zp[j]));
-                } else if constexpr (FOLD) {
-                    bw = biased_word(B.w[j][0][i], magic);
                 } else if constexpr (BF) {
                     bw = bitcast<u4>(mix_word(B.w[j][0][i], mz[j]));
                 } else {
@@ -327,11 +292,8 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
 #pragma unroll
             for (int ii = 0; ii < SPG; ++ii)
 #pragma unroll
-                for (int j = 0; j < CT; ++j) {
-                    float d = pr[ii][j][0];
-                    if constexpr (FOLD) d = __builtin_fmaf(-hz[j], sx[0], d);
-                    tot[0][j][gi * SPG + ii] = __builtin_fmaf(sf[j], d, tot[0][j][gi * SPG + ii]);
-                }
+                for (int j = 0; j < CT; ++j)
+                    tot[0][j][gi * SPG + ii] = __builtin_fmaf(sf[j], pr[ii][j][0], tot[0][j][gi * SPG + ii]);
             // (the products' other registers stay allocated until here, past
             // the read above, which waits for the matrix pipe; reused
             // earlier, each reuse would wait for the product's last write)
@@ -339,7 +301,6 @@ __device__ __forceinline__ void compute_block(const Block<NGB, CT, W8, MB>& B, f
             for (int ii = 0; ii < SPG; ++ii)
 #pragma unroll
                 for (int j = 0; j < CT; ++j) asm volatile("" ::"v"(pr[ii][j]));
-            if constexpr (FOLD) asm volatile("" ::"v"(sx));
         } else {
 #pragma unroll
             for (int rb = 0; rb < MB; ++rb)
@@ -470,7 +431,7 @@ __global__ __launch_bounds__(NT) void q4_gemv_kernel(const uint32_t* qweight, co
 
     // the unpack's OR constant, kept in a register for the whole loop (as a
     // constant it was rebuilt in every block)
-    uint32_t magic = (R1 && BF && !W8) ? kMagicBf2 : kMagic2;   // (the fold's c + q in bfloat16)
+    uint32_t magic = kMagic2;
     asm volatile("" : "+v"(magic));
     constexpr int D = depth<CT, MB>();
     // Ring of D register buffers: block b0 + D * rd + d lives in buf[d].
