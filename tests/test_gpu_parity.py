@@ -393,9 +393,10 @@ def test_special_values_propagate():
     assert fin[:, keep].all()
 
 
+@pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("xfmt", ["f16", "bf16"])
 @pytest.mark.parametrize("M,path", [(1, 1), (2, 1), (16, 1), (24, 1), (40, 2)])
-def test_zero_and_sparse_columns(M, path, xfmt):
+def test_zero_and_sparse_columns(M, path, xfmt, bits):
     """Degenerate columns against the acceptance rule, which scales with
     A = sum |x| |w| rather than with sum |x|: a column whose codes all equal
     their zero points (W = 0, so A = 0 and, without a bias, the output must
@@ -405,17 +406,18 @@ def test_zero_and_sparse_columns(M, path, xfmt):
     sum as (c + z) * sum x) fails these."""
     from tests.gpu_util import BF16_GEMM_REL_A, BF16_REL_Y, REL_A, REL_Y
     K, N, G = 1024, 128, 128
-    L = _layer(K, N, G, M, 13, xfmt=xfmt)
-    z = oracle.unpack_qzeros(L.qzeros, N)
-    q = oracle.unpack_qweight(L.qweight, K)
+    L = _layer(K, N, G, M, 13, xfmt=xfmt, bits=bits)
+    z = oracle.unpack_qzeros(L.qzeros, N, bits=bits)
+    q = oracle.unpack_qweight(L.qweight, K, bits=bits)
+    levels = 1 << bits
     for c in (3, 7, 11):
         q[:, c] = np.repeat(z[:, c], G)
-    q[517, 7] = (z[517 // G, 7] + 1) % 16
+    q[517, 7] = (int(z[517 // G, 7]) + 1) % levels
     for t in range(K // 32):
         k = 32 * t + (7 * t) % 32
-        q[k, 11] = (z[k // G, 11] + 3) % 16
-    L.qweight = pack_rows(q)
-    announce(f"zero and sparse columns M={M} path={path} {xfmt}")
+        q[k, 11] = (int(z[k // G, 11]) + 3) % levels
+    L.qweight = pack_rows(q, bits)
+    announce(f"zero and sparse columns M={M} path={path} {xfmt} w{bits}")
     y = run(L, path=path)
     yD, A = oracle_full(L)
     assert A[:, 3].max() == 0 and np.all(y[:, 3] == 0)
