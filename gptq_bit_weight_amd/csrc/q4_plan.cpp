@@ -126,14 +126,20 @@ void plan_gemv(int M, int K, int N, int G, int num_cu, int* col_tiles, int* spli
         while (2 * s <= kMaxSplits && tiles * 2 * s <= num_cu && kb >= 2 * s * kGemvWaves * min_blocks) s *= 2;
         return s;
     };
+    // At M <= 2 the wider tiles' small gain holds only where one-tile tiles
+    // fill whole rounds of CUs; otherwise the finer grid balances the last
+    // round better, and one tile wins ties (4096 x 22016 at M = 1: 9.9 us at
+    // one tile a wave, 10.4 at two; 28672 x 8192, whose 512 one-tile tiles
+    // fill two rounds: 20.7 at two, 21.0 at one).
+    const bool fine = mi == 0 && ((N + 15) / 16) % num_cu != 0;
     int ct = 1;
     long long best = -1;
     for (int c = 1, ci = 0; c <= max_ct; c *= 2, ++ci) {
         const long long tiles = (N + 16 * c - 1) / (16 * c);
         const long long rounds = (tiles + num_cu - 1) / num_cu;
         const long long s = M > 4 ? splits_for(tiles, 4) : 1;
-        const long long score = tiles * s * 1000 * gain[mi][ci] / (rounds * num_cu);
-        if (score >= best) {
+        const long long score = tiles * s * 1000 * (fine ? 100 : gain[mi][ci]) / (rounds * num_cu);
+        if (score > best || (score == best && !fine)) {
             best = score;
             ct = c;
         }

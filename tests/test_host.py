@@ -134,6 +134,8 @@ def test_plan_gemv():
     assert q4.plan_gemv(8, 4096, 11008, 128, num_cu=256) == (4, 1)      # reuse wins with 8 rows
     assert q4.plan_gemv(1, 28672, 8192, 128, num_cu=256) == (2, 1)      # 256 tiles of 32
     assert q4.plan_gemv(1, 8192, 28672, 128, num_cu=256) == (1, 1)      # 1792 tiles fill 7 rounds
+    assert q4.plan_gemv(1, 4096, 22016, 128, num_cu=256) == (1, 1)      # 1376 tiles: finer last round
+    assert q4.plan_gemv(1, 4096, 12288, 128, num_cu=256) == (1, 1)      # 768 tiles fill 3 rounds
     assert q4.plan_gemv(4, 8192, 28672, 128, num_cu=256) == (4, 1)
     assert q4.plan_gemv(16, 8192, 28672, 32, num_cu=256)[0] == 2        # groups of 32: at most 2
     assert q4.plan_gemv(1, 4096, 1024, 128, num_cu=256) == (1, 4)       # 64 tiles, 32 blocks
